@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the self-synchronizing one-shot bf16 all-reduce on one MI355X.
+
+One step = one decode token's worth of all-reduces for the workload: `nops`
+back-to-back one-shot all-reduces (2 per layer) run by one persistent launch
+of the simulator -- encode, poll + validate, fixed-order reduce, sentinel
+re-arm and epoch flip for every op, N simulated ranks as producer waves on
+other XCDs writing rank 0's receive buffer (one rank's share).  Inputs are
+resident in HBM before the timed region.
+
+Prints ONE JSON line: value = microseconds per all-reduce (lower is better),
+with the roofline of the simulator kernel (algorithmic HBM bytes per launch /
+HIP-event duration of the launch), the measured one-chip floor, and the CPU
+oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("µs per all-reduce and achieved HBM GB/s vs roofline, "
+          "N simulated ranks, 1 MI355X")
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "collective_synchronization_amd", "csrc", n)
+    for n in ("ar_kernels.hip", "ar_protocols.h", "ar_device.h")
+]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(proto: str, nranks: int, count: int, nconsumers: int) -> int:
+    """HBM bytes one op must move (re-polls not counted):
+    producers read N*S, write E into each of C receive buffers per rank,
+    consumers read N*E each, write S each, and (sentinel) re-arm N*E each."""
+    from collective_synchronization_amd import abi
+    S = 2 * count
+    E = abi.ar_encoded_bytes(proto, count)
+    b = nranks * S + nconsumers * nranks * E + nconsumers * nranks * E + nconsumers * S
+    if proto == "sentinel":
+        b += nconsumers * nranks * E
+    return b
+
+
+def measure_floor(torch, abi, iters=2000):
+    """One-chip floor in the form 2*L_load + L_oneway (cross-XCD)."""
+    hz = abi.ar_wallclock_hz()
+    work = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    res = torch.zeros(8, dtype=torch.int64, device="cuda")
+    oneway = []
+    for xb in range(1, 8):
+        work.zero_()
+        res.zero_()
+        abi.ar_probe_pingpong(work, iters, 0, xb, res)
+        torch.cuda.synchronize()
+        r = res.cpu().tolist()
+        if r[4] == 0 and r[1] == iters:
+            oneway.append(r[0] / iters / hz / 2 * 1e6)
+    chain_bytes = 16 << 20
+    cw = torch.zeros(chain_bytes, dtype=torch.uint8, device="cuda")
+    res.zero_()
+    abi.ar_probe_loadchain(cw, chain_bytes, iters, res)
+    torch.cuda.synchronize()
+    r = res.cpu().tolist()
+    load_us = r[0] / r[1] / hz * 1e6
+    ow = statistics.median(oneway) if oneway else float("nan")
+    return {"oneway_us": round(ow, 4), "load_us": round(load_us, 4),
+            "sol_us": round(2 * load_us + ow, 4),
+            "pingpong_pairs": len(oneway)}
+
+
+def cpu_baseline(x, proto, seconds):
+    import oracle
+    us, ops = oracle.time_allreduce(x, proto, seconds=seconds)
+    return us, ops
+
+
+def load_traffic(kernel_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    try:
+        with open(PROFILE_TRAFFIC) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(kernel_name)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--proto", default="sentinel",
+                    choices=["ll", "ll128", "sentinel", "barrier"])
+    ap.add_argument("--mode", default="share", choices=["share", "system"])
+    ap.add_argument("--nranks", type=int, default=8)
+    ap.add_argument("--rows", type=int, default=1)
+    ap.add_argument("--hidden", type=int, default=4096)
+    ap.add_argument("--nops", type=int, default=64)
+    ap.add_argument("--waves-per-rank", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-floor", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures "
+              "N simulated ranks on ONE GPU; there is no multi-GPU path.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from collective_synchronization_amd import abi, buffers, inputs
+    from collective_synchronization_amd.configs import CONFIGS
+
+    torch.cuda.set_device(0)
+    cfg = CONFIGS[2]
+    nranks, count, nops, proto = args.nranks, args.rows * args.hidden, args.nops, args.proto
+    nconsumers = nranks if args.mode == "system" else 1
+    default_workload = (nranks, args.rows, args.hidden, nops, proto, args.mode) == \
+        (cfg["nranks"], 1, cfg["hidden"], cfg["nops"], "sentinel", "share")
+    workload = cfg["name"] if default_workload else \
+        f"n{nranks}_{proto}_{args.rows}x{args.hidden}_{nops}ops_{args.mode}"
+
+    x = inputs.payload(cfg["seed"], (nops, nranks, count), "normal")
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * nconsumers, stride), dtype=torch.int16, device="cuda")
+    ws = buffers.Workspace(nranks, count, proto, nconsumers)
+    stream = torch.cuda.current_stream()
+    kw = dict(timeout_ns=2_000_000_000, waves_per_rank=args.waves_per_rank)
+
+    for _ in range(args.warmup):
+        ws.sim(nops, xd, stride, outd, stride, **kw)
+    torch.cuda.synchronize()
+    if ws.status() != 0:
+        print(f"bench.py: device status {abi.status_string(ws.status())}", file=sys.stderr)
+        return 1
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        if proto == "barrier":
+            ws.reset_ctrl()
+        starts[k].record(stream)
+        p = ws.sim_params(nops, xd, stride, outd, stride, **kw)
+        abi.ar_sim_run(p, stream)
+        ws.flip(nops)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ws.status() != 0:
+        print(f"bench.py: device status {abi.status_string(ws.status())}", file=sys.stderr)
+        return 1
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride, **kw))
+
+    ms_per_step = wall * 1e3 / args.steps
+    us_per_op = ms_per_step * 1e3 / nops
+    avg_launch_ms = statistics.mean(launch_ms)
+    kernel_us_per_op = statistics.median(launch_ms) * 1e3 / nops
+    b_op = algorithmic_bytes(proto, nranks, count, nconsumers)
+    b_launch = b_op * nops
+    achieved = b_launch / (avg_launch_ms * 1e-3) / 1e9
+    kname = f"k_sim<{abi.proto_id(proto)}>"
+
+    line = {
+        "metric": METRIC,
+        "value": round(us_per_op, 4),
+        "unit": "us per all-reduce",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": workload, "nranks": nranks, "shape": [args.rows, args.hidden],
+            "protocol": proto, "ops_per_step": nops, "mode": args.mode,
+            "nconsumers": nconsumers, "values": "N(0,1) seed %d" % cfg["seed"],
+            "waves_per_rank": geo["waves_per_rank"], "blocks": geo["blocks"],
+            "input_sha256": inputs.sha256(x)[:16],
+        },
+        "kernel_us_per_op": round(kernel_us_per_op, 4),
+        "kernel_us_per_op_p10_p90": [
+            round(float(np.percentile(launch_ms, 10)) * 1e3 / nops, 4),
+            round(float(np.percentile(launch_ms, 90)) * 1e3 / nops, 4)],
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
+            "traffic": load_traffic(kname),
+            "kernel": kname, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": b_launch,
+            "algorithmic_bytes_per_op": b_op,
+        },
+    }
+
+    if not args.no_floor:
+        fl = measure_floor(torch, abi)
+        fl["frac_of_op"] = round(fl["sol_us"] / kernel_us_per_op, 4)
+        line["floor"] = fl
+
+    if not args.no_cpu_baseline:
+        us, ops = cpu_baseline(x, proto, args.cpu_seconds)
+        line["cpu_baseline"] = {
+            "value": round(us, 3), "unit": "us per all-reduce", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"{ops} ops of the same workload (N={nranks}, [{args.rows},"
+                       f"{args.hidden}], {proto}: encode N + validate/decode N + "
+                       f"fixed-order reduce, single thread, ~{args.cpu_seconds:g} s)"),
+        }
+
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

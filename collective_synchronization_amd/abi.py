@@ -1,0 +1,310 @@
+"""ctypes binding of ``libcsync_ar.so`` (C ABI declared in ``include/ar.h``).
+
+Argument marshalling only: every step of the all-reduce runs in the HIP
+kernels of the library.  Functions keep the C names.  Device buffers may be
+given as torch tensors (their ``data_ptr()`` is passed) or as integer device
+addresses; ``stream=None`` means torch's current stream on the current
+device.  A negative return code raises :class:`ArError`.
+
+The library must be built first (``__graft_entry__.build()``); importing this
+module without it raises ImportError -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsync_ar.so")
+
+AR_OK, AR_EINVAL, AR_EALIGN, AR_ESIZE, AR_ELAUNCH = 0, -1, -2, -3, -4
+AR_ETIMEOUT, AR_ECORRUPT, AR_ENODEV, AR_ECAPACITY = -5, -6, -7, -8
+AR_LL, AR_LL128, AR_SENTINEL, AR_BARRIER, AR_AUTO = 0, 1, 2, 3, 4
+AR_FLAG_REARM = 1
+AR_MAX_RANKS = 16
+PROTO_IDS = {"ll": AR_LL, "ll128": AR_LL128, "sentinel": AR_SENTINEL,
+             "barrier": AR_BARRIER}
+PROTO_NAMES = {v: k for k, v in PROTO_IDS.items()}
+
+
+class ar_desc(ctypes.Structure):
+    _fields_ = [("nranks", ctypes.c_int32), ("nconsumers", ctypes.c_int32),
+                ("count", ctypes.c_int64), ("proto", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class ar_epoch(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_uint32), ("parity", ctypes.c_uint32)]
+
+    def __repr__(self):
+        return f"ar_epoch(seq={self.seq}, parity={self.parity})"
+
+
+class ar_sim_params(ctypes.Structure):
+    _fields_ = [("desc", ar_desc), ("nops", ctypes.c_int32),
+                ("waves_per_rank", ctypes.c_int32),
+                ("in_", ctypes.c_void_p), ("in_stride", ctypes.c_int64),
+                ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64),
+                ("scratch", ctypes.c_void_p), ("ctrl", ctypes.c_void_p),
+                ("epoch", ar_epoch), ("timeout_ns", ctypes.c_uint64),
+                ("delay_ticks", ctypes.c_void_p), ("tile_order", ctypes.c_void_p),
+                ("trace", ctypes.c_void_p)]
+
+
+class ar_cost_entry(ctypes.Structure):
+    _fields_ = [("nranks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("alpha_us", ctypes.c_double * 4),
+                ("beta_us_per_byte", ctypes.c_double * 4)]
+
+
+class ArError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = f"{where}: {status_string(code)} ({code})"
+        if code == AR_ELAUNCH:
+            msg += f", hipError {_lib.ar_last_hip_error()}"
+        super().__init__(msg)
+
+
+# torch is imported first so that the one HIP runtime in the process is the one
+# torch uses (both carry the soname libamdhip64.so.7): the library then shares
+# torch's device context, allocations and streams.
+import torch  # noqa: E402,F401
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library with "
+        "`python -c 'import __graft_entry__ as g; g.build()'` (no CPU fallback exists)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i32, _i64, _u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+_SIGS = {
+    "ar_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "ar_abi_version": ([], ctypes.c_int),
+    "ar_last_hip_error": ([], ctypes.c_int),
+    "ar_encoded_bytes": ([_i32, _i64], _i64),
+    "ar_slot_bytes": ([_i32, _i64], _i64),
+    "ar_scratch_bytes": ([ctypes.POINTER(ar_desc)], _i64),
+    "ar_ctrl_bytes": ([], _i64),
+    "ar_ctrl_reset": ([_vp, _vp], ctypes.c_int),
+    "ar_epoch_init": ([ctypes.POINTER(ar_epoch)], ctypes.c_int),
+    "ar_epoch_flip": ([ctypes.POINTER(ar_epoch)], ctypes.c_int),
+    "ar_epoch_advance": ([ctypes.POINTER(ar_epoch), _u64], ctypes.c_int),
+    "ar_pack_ll": ([ctypes.POINTER(ar_desc), _vp, _i64, _vp, ar_epoch, _vp], ctypes.c_int),
+    "ar_pack_ll128": ([ctypes.POINTER(ar_desc), _vp, _i64, _vp, ar_epoch, _vp], ctypes.c_int),
+    "ar_pack_sentinel": ([ctypes.POINTER(ar_desc), _vp, _i64, _vp, ar_epoch, _vp], ctypes.c_int),
+    "ar_pack_plain": ([ctypes.POINTER(ar_desc), _vp, _i64, _vp, ar_epoch, _vp], ctypes.c_int),
+    "ar_arm_sentinel": ([ctypes.POINTER(ar_desc), _vp, _i32, _vp], ctypes.c_int),
+    "ar_reduce_validate": ([ctypes.POINTER(ar_desc), _vp, _vp, _i64, ar_epoch, _vp,
+                            _u64, _i32, _vp], ctypes.c_int),
+    "ar_sim_run": ([ctypes.POINTER(ar_sim_params), _vp], ctypes.c_int),
+    "ar_sim_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
+                         ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                         ctypes.POINTER(_i32)], ctypes.c_int),
+    "ar_wallclock_hz": ([ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+    "ar_select_protocol": ([ctypes.POINTER(ar_cost_entry), _i32, _i64, _i32,
+                            ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)],
+                           ctypes.c_int),
+    "ar_probe_pingpong": ([_vp, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "ar_probe_loadchain": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
+    "ar_probe_copy": ([_vp, _vp, _i64, _vp], ctypes.c_int),
+    "ar_probe_empty": ([_vp], ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+def raw():
+    """The ctypes CDLL handle (for tests of the bare C ABI)."""
+    return _lib
+
+
+# ------------------------------------------------------------ marshalling --
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(code: int, where: str) -> int:
+    if code < 0:
+        raise ArError(code, where)
+    return code
+
+
+def status_string(code: int) -> str:
+    return _lib.ar_status_string(code).decode()
+
+
+def proto_id(p) -> int:
+    return PROTO_IDS[p] if isinstance(p, str) else int(p)
+
+
+def make_desc(nranks: int, count: int, proto, nconsumers: int = 1) -> ar_desc:
+    return ar_desc(nranks, nconsumers, count, proto_id(proto), 0)
+
+
+# ---------------------------------------------------------------- sizes ---
+
+def ar_encoded_bytes(proto, count: int) -> int:
+    return _check(_lib.ar_encoded_bytes(proto_id(proto), count), "ar_encoded_bytes")
+
+
+def ar_slot_bytes(proto, count: int) -> int:
+    return _check(_lib.ar_slot_bytes(proto_id(proto), count), "ar_slot_bytes")
+
+
+def ar_scratch_bytes(desc: ar_desc) -> int:
+    return _check(_lib.ar_scratch_bytes(ctypes.byref(desc)), "ar_scratch_bytes")
+
+
+def ar_ctrl_bytes() -> int:
+    return _check(_lib.ar_ctrl_bytes(), "ar_ctrl_bytes")
+
+
+# --------------------------------------------------------------- epochs ---
+
+def ar_epoch_init() -> ar_epoch:
+    e = ar_epoch()
+    _check(_lib.ar_epoch_init(ctypes.byref(e)), "ar_epoch_init")
+    return e
+
+
+def ar_epoch_flip(e: ar_epoch) -> ar_epoch:
+    _check(_lib.ar_epoch_flip(ctypes.byref(e)), "ar_epoch_flip")
+    return e
+
+
+def ar_epoch_advance(e: ar_epoch, nops: int) -> ar_epoch:
+    _check(_lib.ar_epoch_advance(ctypes.byref(e), nops), "ar_epoch_advance")
+    return e
+
+
+# --------------------------------------------------------------- device ---
+
+def ar_ctrl_reset(ctrl, stream=None) -> None:
+    _check(_lib.ar_ctrl_reset(_ptr(ctrl), _stream(stream)), "ar_ctrl_reset")
+
+
+def _pack(name, desc, inp, in_stride, scratch, epoch, stream):
+    fn = getattr(_lib, name)
+    _check(fn(ctypes.byref(desc), _ptr(inp), in_stride, _ptr(scratch), epoch,
+              _stream(stream)), name)
+
+
+def ar_pack_ll(desc, inp, in_stride, scratch, epoch, stream=None) -> None:
+    _pack("ar_pack_ll", desc, inp, in_stride, scratch, epoch, stream)
+
+
+def ar_pack_ll128(desc, inp, in_stride, scratch, epoch, stream=None) -> None:
+    _pack("ar_pack_ll128", desc, inp, in_stride, scratch, epoch, stream)
+
+
+def ar_pack_sentinel(desc, inp, in_stride, scratch, epoch, stream=None) -> None:
+    _pack("ar_pack_sentinel", desc, inp, in_stride, scratch, epoch, stream)
+
+
+def ar_pack_plain(desc, inp, in_stride, scratch, epoch, stream=None) -> None:
+    _pack("ar_pack_plain", desc, inp, in_stride, scratch, epoch, stream)
+
+
+PACK_BY_PROTO = {AR_LL: ar_pack_ll, AR_LL128: ar_pack_ll128,
+                 AR_SENTINEL: ar_pack_sentinel, AR_BARRIER: ar_pack_plain}
+
+
+def ar_arm_sentinel(desc, scratch, parity: int = -1, stream=None) -> None:
+    _check(_lib.ar_arm_sentinel(ctypes.byref(desc), _ptr(scratch), parity,
+                                _stream(stream)), "ar_arm_sentinel")
+
+
+def ar_reduce_validate(desc, scratch, out, out_stride, epoch, ctrl,
+                       timeout_ns: int = 0, flags: int = 0, stream=None) -> None:
+    _check(_lib.ar_reduce_validate(ctypes.byref(desc), _ptr(scratch), _ptr(out),
+                                   out_stride, epoch, _ptr(ctrl), timeout_ns, flags,
+                                   _stream(stream)), "ar_reduce_validate")
+
+
+def sim_params(desc, nops, inp, in_stride, out, out_stride, scratch, ctrl, epoch,
+               timeout_ns=0, waves_per_rank=0, delay_ticks=None, tile_order=None,
+               trace=None) -> ar_sim_params:
+    return ar_sim_params(desc, nops, waves_per_rank, _ptr(inp), in_stride, _ptr(out),
+                         out_stride, _ptr(scratch), _ptr(ctrl), epoch, timeout_ns,
+                         _ptr(delay_ticks), _ptr(tile_order), _ptr(trace))
+
+
+def ar_sim_run(params: ar_sim_params, stream=None) -> None:
+    _check(_lib.ar_sim_run(ctypes.byref(params), _stream(stream)), "ar_sim_run")
+
+
+def ar_sim_geometry(params: ar_sim_params) -> dict:
+    w, t, tpw, b = _i32(), _i32(), _i32(), _i32()
+    _check(_lib.ar_sim_geometry(ctypes.byref(params), ctypes.byref(w), ctypes.byref(t),
+                                ctypes.byref(tpw), ctypes.byref(b)), "ar_sim_geometry")
+    return {"waves_per_rank": w.value, "tiles_per_rank": t.value,
+            "tiles_per_wave": tpw.value, "blocks": b.value}
+
+
+def ar_wallclock_hz() -> float:
+    hz = ctypes.c_double()
+    _check(_lib.ar_wallclock_hz(ctypes.byref(hz)), "ar_wallclock_hz")
+    return hz.value
+
+
+def cost_table(entries) -> "ctypes.Array":
+    """entries: iterable of dicts {nranks, alpha_us[4], beta_us_per_byte[4]}."""
+    entries = list(entries)
+    arr = (ar_cost_entry * len(entries))()
+    for i, e in enumerate(entries):
+        arr[i].nranks = int(e["nranks"])
+        for p in range(4):
+            arr[i].alpha_us[p] = float(e["alpha_us"][p])
+            arr[i].beta_us_per_byte[p] = float(e["beta_us_per_byte"][p])
+    return arr
+
+
+def ar_select_protocol(table, payload_bytes: int, nranks: int):
+    """Returns (protocol id, predicted microseconds)."""
+    out = _i32()
+    pred = ctypes.c_double()
+    _check(_lib.ar_select_protocol(table, len(table), payload_bytes, nranks,
+                                   ctypes.byref(out), ctypes.byref(pred)),
+           "ar_select_protocol")
+    return out.value, pred.value
+
+
+def ar_probe_pingpong(work, iters, xcd_a, xcd_b, result, stream=None) -> None:
+    _check(_lib.ar_probe_pingpong(_ptr(work), iters, xcd_a, xcd_b, _ptr(result),
+                                  _stream(stream)), "ar_probe_pingpong")
+
+
+def ar_probe_loadchain(work, nbytes, iters, result, stream=None) -> None:
+    _check(_lib.ar_probe_loadchain(_ptr(work), nbytes, iters, _ptr(result),
+                                   _stream(stream)), "ar_probe_loadchain")
+
+
+def ar_probe_copy(src, dst, nbytes, stream=None) -> None:
+    _check(_lib.ar_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)),
+           "ar_probe_copy")
+
+
+def ar_probe_empty(stream=None) -> None:
+    _check(_lib.ar_probe_empty(_stream(stream)), "ar_probe_empty")

@@ -1,0 +1,110 @@
+"""Device buffers for the C ABI, allocated with torch (marshalling only).
+
+torch supplies device memory and streams; every step of the all-reduce runs
+in the library's kernels.  bf16 payloads are held as int16 tensors of raw
+bit patterns, rows padded to a multiple of 8 elements (16 bytes).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import abi
+
+ALIGN = 256
+
+
+def round_up(n: int, m: int) -> int:
+    return (n + m - 1) // m * m
+
+
+def row_stride(count: int) -> int:
+    return max(8, round_up(count, 8))
+
+
+def device_bytes(nbytes: int, device="cuda", fill: int = 0) -> torch.Tensor:
+    """A uint8 device tensor of nbytes (>= 256), 256-byte aligned, filled."""
+    t = torch.full((max(int(nbytes), ALIGN),), fill, dtype=torch.uint8, device=device)
+    if t.data_ptr() % ALIGN:
+        raise RuntimeError("allocator returned a buffer that is not 256-byte aligned")
+    return t
+
+
+def rows_to_device(x: np.ndarray, device="cuda"):
+    """uint16 [..., count] -> (int16 device tensor [rows, stride], stride)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    count = x.shape[-1]
+    stride = row_stride(count)
+    flat = x.reshape(-1, count)
+    host = np.zeros((flat.shape[0], stride), dtype=np.uint16)
+    host[:, :count] = flat
+    t = torch.from_numpy(host.view(np.int16)).to(device)
+    return t, stride
+
+
+def rows_from_device(t: torch.Tensor, count: int, shape) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)[:, :count].reshape(tuple(shape) + (count,))
+
+
+class Workspace:
+    """Receive buffers and control block for one descriptor on one device.
+
+    The epoch advances by one flip per op issued through this workspace, as
+    the C ABI requires for reused receive buffers.
+    """
+
+    def __init__(self, nranks: int, count: int, proto, nconsumers: int = 1,
+                 device="cuda"):
+        self.desc = abi.make_desc(nranks, count, proto, nconsumers)
+        self.device = device
+        self.scratch_bytes = abi.ar_scratch_bytes(self.desc)
+        self.scratch = device_bytes(self.scratch_bytes, device)
+        self.ctrl = device_bytes(abi.ar_ctrl_bytes(), device)
+        self.epoch = abi.ar_epoch_init()
+        if self.desc.proto == abi.AR_SENTINEL:
+            abi.ar_arm_sentinel(self.desc, self.scratch, -1)
+
+    @property
+    def proto(self) -> int:
+        return self.desc.proto
+
+    def status(self) -> int:
+        return int(self.ctrl[:4].view(torch.int32).item())
+
+    def reset_ctrl(self, stream=None) -> None:
+        abi.ar_ctrl_reset(self.ctrl, stream)
+
+    def slot_view(self) -> np.ndarray:
+        """Host copy of the receive buffers: uint8 [nconsumers, 2, nranks, slot]."""
+        d = self.desc
+        slot = abi.ar_slot_bytes(d.proto, d.count)
+        raw = self.scratch[: self.scratch_bytes].cpu().numpy()
+        return raw.reshape(d.nconsumers, 2, d.nranks, slot)
+
+    # -------------------------------------------------- stream-ordered op --
+    def pack(self, x_dev, in_stride, stream=None) -> None:
+        abi.PACK_BY_PROTO[self.desc.proto](self.desc, x_dev, in_stride, self.scratch,
+                                           self.epoch, stream)
+
+    def reduce(self, out_dev, out_stride, timeout_ns=0, rearm=True, stream=None) -> None:
+        flags = abi.AR_FLAG_REARM if (rearm and self.desc.proto == abi.AR_SENTINEL) else 0
+        abi.ar_reduce_validate(self.desc, self.scratch, out_dev, out_stride, self.epoch,
+                               self.ctrl, timeout_ns, flags, stream)
+
+    def flip(self, nops: int = 1) -> None:
+        abi.ar_epoch_advance(self.epoch, nops)
+
+    # -------------------------------------------------------- simulator --
+    def sim_params(self, nops, x_dev, in_stride, out_dev, out_stride, timeout_ns=0,
+                   waves_per_rank=0, delay_ticks=None, tile_order=None, trace=None):
+        return abi.sim_params(self.desc, nops, x_dev, in_stride, out_dev, out_stride,
+                              self.scratch, self.ctrl, self.epoch, timeout_ns,
+                              waves_per_rank, delay_ticks, tile_order, trace)
+
+    def sim(self, nops, x_dev, in_stride, out_dev, out_stride, stream=None, **kw) -> None:
+        """nops back-to-back ops in one persistent launch; advances the epoch."""
+        if self.desc.proto == abi.AR_BARRIER:
+            self.reset_ctrl(stream)
+        p = self.sim_params(nops, x_dev, in_stride, out_dev, out_stride, **kw)
+        abi.ar_sim_run(p, stream)
+        self.flip(nops)

@@ -1,0 +1,921 @@
+// ar_kernels.hip -- HIP kernels (gfx950) and the C-ABI entry points of the
+// self-synchronizing small-message one-shot bf16 all-reduce.
+//
+// Build: hipcc --offload-arch=gfx950 -O3 -fPIC -shared
+//        -fno-gpu-flush-denormals-to-zero -ffp-contract=off
+//        -Xclang -target-feature -Xclang -packed-fp32-ops
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/ar.h"
+#include "ar_protocols.h"
+
+namespace ar {
+
+constexpr int kBlock = 256;              // 4 waves
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// ================================================================ kernels ==
+
+struct PackArgs {
+  const uint16_t* in;
+  int64_t in_stride;
+  int64_t count;
+  const uint8_t* scratch;
+  uint32_t scratch_bytes;
+  uint32_t E, slot_bytes;
+  int32_t nranks, nconsumers, tiles;
+  uint32_t seq, parity;
+};
+
+// One wave per (rank, tile): encode and store into every consumer's buffer.
+template <int P>
+__global__ __launch_bounds__(kBlock) void k_pack(PackArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int r = gw / a.tiles;
+  const int tile = gw - r * a.tiles;
+  if (r >= a.nranks) return;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t cstride = 2u * (uint32_t)a.nranks * a.slot_bytes;
+  const uint32_t dst0 = (a.parity * (uint32_t)a.nranks + (uint32_t)r) * a.slot_bytes;
+  const uint16_t* row = a.in + (int64_t)r * a.in_stride;
+  produce_data<P>(rs, dst0, cstride, a.nconsumers, row, a.count, tile, a.E,
+                  a.seq, lane);
+  if (P == kLL128) {
+    fence_release();
+    produce_flags(rs, dst0, cstride, a.nconsumers, tile, a.E, a.seq, lane);
+  }
+}
+
+struct ReduceArgs {
+  uint16_t* out;
+  int64_t out_stride;
+  int64_t count;
+  const uint8_t* scratch;
+  uint32_t scratch_bytes;
+  uint32_t E, slot_bytes;
+  int32_t nranks, nconsumers, tiles;
+  uint32_t seq, parity;
+  int* ctrl;
+  uint64_t timeout_ticks;
+  int32_t rearm;
+};
+
+// One wave per (consumer, tile): poll, validate, reduce in rank order.
+template <int P, int NMAX>
+__global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int c = gw / a.tiles;
+  const int tile = gw - c * a.tiles;
+  if (c >= a.nconsumers) return;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t src0 =
+      ((uint32_t)c * 2u + a.parity) * (uint32_t)a.nranks * a.slot_bytes;
+  const uint32_t stale = seq_prev(seq_prev(a.seq));
+  consume_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, tile, a.E, a.seq,
+                        stale, a.rearm != 0,
+                        a.out + (int64_t)c * a.out_stride, a.count, a.ctrl,
+                        a.timeout_ticks, lane);
+}
+
+// Fill byte range [begin, begin+bytes) of the buffer with 0xFF, 16 bytes a
+// lane, with device-scope coherent stores.
+__global__ __launch_bounds__(kBlock) void k_arm(const uint8_t* scratch,
+                                                uint32_t scratch_bytes,
+                                                uint32_t region0,
+                                                uint32_t region_stride,
+                                                uint32_t region_bytes,
+                                                int32_t nregions) {
+  const rsrc_t rs = make_rsrc(scratch, scratch_bytes);
+  const u32x4 armed = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  const uint64_t chunks = region_bytes / 16u;
+  const uint64_t total = chunks * (uint64_t)nregions;
+  for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < total;
+       i += (uint64_t)gridDim.x * kBlock) {
+    const uint32_t reg = (uint32_t)(i / chunks);
+    const uint32_t k = (uint32_t)(i - (uint64_t)reg * chunks);
+    st16(rs, region0 + reg * region_stride + k * 16u, armed);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_fill_zero(uint32_t* p, uint32_t words) {
+  for (uint32_t i = blockIdx.x * kBlock + threadIdx.x; i < words;
+       i += gridDim.x * kBlock)
+    __hip_atomic_store(p + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------- simulator --
+
+struct SimArgs {
+  const uint16_t* in;
+  int64_t in_stride;
+  uint16_t* out;
+  int64_t out_stride;
+  const uint8_t* scratch;
+  uint32_t scratch_bytes;
+  int* ctrl;
+  int64_t count;
+  uint32_t E, slot_bytes;
+  int32_t nranks, nconsumers, nops;
+  int32_t W, Q, T, TPW;
+  uint32_t seq0, parity0;
+  uint64_t timeout_ticks;
+  const uint32_t* delay;
+  const uint16_t* order;
+  uint64_t* trace;
+  uint32_t p_total, c_total;
+};
+
+__device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
+                                         Waiter& wt, int lane) {
+  while (ld_agent_u32(p) < target)
+    if (!wt.again(lane)) return false;
+  return true;
+}
+
+// Persistent role-split kernel.  Workgroup b sits on XCD b % 8 (round-robin
+// dispatch).  Rank g owns Q workgroups per XCD; its wave index wr (0..W-1)
+// is rotated by g so that the producer of a tile and the consumer that
+// reads it sit on different XCDs, and the same wr owns the same tiles
+// {wr, wr + W, ...} in every rank.
+template <int P, int NMAX, bool SHARE>
+__global__ __launch_bounds__(kBlock) void k_sim(SimArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  const int x = b & 7;
+  const int q = b >> 3;
+  const int g = q / a.Q;
+  const int qq = q - g * a.Q;
+  if (g >= a.nranks) return;
+  const int rot = SHARE ? (g == 0 ? 0 : 1 + (g - 1) % 7) : (g & 7);
+  const int xr = (x - rot) & 7;
+  const int wr = (qq * 8 + xr) * kWavesPerBlock + wave;
+  if (wr >= a.T) return;
+  const int mine = (a.T - 1 - wr) / a.W + 1;
+  const bool consumer = SHARE ? (g == 0) : true;
+  const int cself = SHARE ? 0 : g;
+
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t N = (uint32_t)a.nranks;
+  const uint32_t cstride = 2u * N * a.slot_bytes;
+  uint32_t* const progress = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlProgress;
+  uint32_t* const arrive = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlArrive;
+  uint32_t* const done = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlDone;
+  const int tstride = 2 * a.nranks;
+
+  if (a.trace && lane == 0)
+    __hip_atomic_fetch_min(reinterpret_cast<unsigned long long*>(a.trace) +
+                               (int64_t)a.nops * tstride,
+                           (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+
+  uint32_t seq = a.seq0;
+  uint32_t par = a.parity0;
+  for (int op = 0; op < a.nops; ++op) {
+    const uint32_t stale = seq_prev(seq_prev(seq));
+    const uint32_t pp = (P == kBarrier) ? 0u : par;
+
+    // ---- licence to write this parity / bottom barrier of the baseline --
+    if (P == kBarrier) {
+      if (op >= 1) {
+        Waiter wt(a.timeout_ticks, a.ctrl);
+        if (!wait_geq(done, (uint32_t)op * a.c_total, wt, lane)) return;
+        fence_acquire();
+      }
+    } else if (SHARE && g != 0 && op >= 2) {
+      // Rank 0's wave wr publishes seq when it starts an op, i.e. after it
+      // finished reading (and re-arming) the parity this op overwrites.
+      Waiter wt(a.timeout_ticks, a.ctrl);
+      const uint32_t prev = seq_prev(seq);
+      while (true) {
+        const uint32_t v = ld_agent_u32(progress + wr);
+        if (v == prev || v == seq) break;
+        if (!wt.again(lane)) return;
+      }
+      fence_acquire();
+    }
+    if (SHARE && g == 0 && P != kBarrier && lane == 0)
+      st_agent_u32(progress + wr, seq);
+
+    // ---- producer skew ----
+    if (a.delay) {
+      const uint32_t d = a.delay[(int64_t)op * a.nranks + g];
+      if (d) {
+        const uint64_t t0 = now_ticks();
+        while (now_ticks() - t0 < (uint64_t)d) __builtin_amdgcn_s_sleep(2);
+      }
+    }
+
+    // ---- produce(op): slot g of parity pp in every consumer's buffer ----
+    const uint16_t* row = a.in + ((int64_t)op * a.nranks + g) * a.in_stride;
+    const uint32_t dst0 = (pp * N + (uint32_t)g) * a.slot_bytes;
+    const uint16_t* ord = a.order ? a.order + ((int64_t)op * a.nranks + g) * a.TPW : nullptr;
+    for (int j = 0; j < a.TPW; ++j) {
+      const int k = ord ? (int)ord[j] : j;
+      if (k >= mine) continue;
+      produce_data<P>(rs, dst0, cstride, a.nconsumers, row, a.count,
+                      wr + k * a.W, a.E, seq, lane);
+    }
+    if (P == kLL128) {
+      fence_release();
+      for (int k = 0; k < mine; ++k)
+        produce_flags(rs, dst0, cstride, a.nconsumers, wr + k * a.W, a.E, seq,
+                      lane);
+    }
+    if (P == kBarrier) {
+      fence_release();
+      if (lane == 0)
+        __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (a.trace) {
+      fence_release();   // stores acknowledged before the timestamp
+      if (lane == 0)
+        __hip_atomic_fetch_max(
+            reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride + g,
+            (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+            __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- consume(op) ----
+    if (consumer) {
+      if (P == kBarrier) {
+        Waiter wt(a.timeout_ticks, a.ctrl);
+        if (!wait_geq(arrive, (uint32_t)(op + 1) * a.p_total, wt, lane)) return;
+        fence_acquire();
+      }
+      uint16_t* orow = a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride;
+      const uint32_t src0 = ((uint32_t)cself * 2u + pp) * N * a.slot_bytes;
+      for (int k = 0; k < mine; ++k) {
+        if (consume_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, wr + k * a.W,
+                                  a.E, seq, stale, true, orow, a.count, a.ctrl,
+                                  a.timeout_ticks, lane) != 0)
+          return;
+      }
+      if (P == kBarrier) {
+        fence_release();
+        if (lane == 0)
+          __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        // every read (and re-arm) of this op completes before the next
+        // op's stores are issued
+        fence_acq_rel();
+      }
+      if (a.trace && lane == 0)
+        __hip_atomic_fetch_max(
+            reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride +
+                a.nranks + cself,
+            (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+            __HIP_MEMORY_SCOPE_AGENT);
+    }
+    seq = seq_next(seq);
+    par ^= 1u;
+  }
+}
+
+// ---------------------------------------------------------------- probes --
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  // HW_REG_XCC_ID (id 20), bits [3:0]
+  return (uint32_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 0xFu;
+}
+
+__global__ void k_pingpong(uint32_t* work, int32_t iters, int32_t xa,
+                           int32_t xb, uint64_t* res, uint64_t timeout_ticks) {
+  if (threadIdx.x != 0) return;
+  uint32_t* fa = work;        // a -> b, own 128-byte line
+  uint32_t* fb = work + 32;   // b -> a
+  const int b = blockIdx.x;
+  if (b == xa) {
+    res[2] = xcc_id();
+    const uint64_t deadline = now_ticks() + timeout_ticks;
+    const uint64_t t0 = now_ticks();
+    for (uint32_t k = 1; k <= (uint32_t)iters; ++k) {
+      st_agent_u32(fa, k);
+      while (ld_agent_u32(fb) != k) {
+        if (now_ticks() > deadline) { res[4] = 1; return; }
+      }
+    }
+    res[0] = now_ticks() - t0;
+    res[1] = (uint64_t)iters;
+  } else if (b == xb) {
+    res[3] = xcc_id();
+    const uint64_t deadline = now_ticks() + timeout_ticks;
+    for (uint32_t k = 1; k <= (uint32_t)iters; ++k) {
+      while (ld_agent_u32(fa) != k) {
+        if (now_ticks() > deadline) { res[4] = 2; return; }
+      }
+      st_agent_u32(fb, k);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_chain_init(uint32_t* work, uint32_t n,
+                                                       uint32_t stride) {
+  for (uint32_t i = blockIdx.x * kBlock + threadIdx.x; i < n; i += gridDim.x * kBlock)
+    work[i] = (uint32_t)(((uint64_t)i + stride) & (uint64_t)(n - 1));
+}
+
+__global__ void k_chain(const uint32_t* work, uint32_t bytes, int32_t iters,
+                        uint64_t* res) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const rsrc_t rs = make_rsrc(work, bytes);
+  uint32_t idx = 0;
+  const uint64_t t0 = now_ticks();
+  for (int i = 0; i < iters; ++i) {
+    idx = __builtin_amdgcn_raw_buffer_load_b32(rs, idx * 4u, 0, kCpAgent);
+    compiler_barrier();
+  }
+  res[0] = now_ticks() - t0;
+  res[1] = (uint64_t)iters;
+  res[2] = idx;
+}
+
+__global__ __launch_bounds__(kBlock) void k_copy(const u32x4* __restrict__ src,
+                                                 u32x4* __restrict__ dst,
+                                                 uint64_t n16) {
+  for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n16;
+       i += (uint64_t)gridDim.x * kBlock)
+    dst[i] = src[i];
+}
+
+__global__ void k_empty() {}
+
+// ============================================================ host side ==
+
+struct DeviceInfo {
+  bool ok = false;
+  int cus = 0;
+  double wallclock_hz = 0.0;
+  int coop = 0;
+};
+
+static std::mutex g_mu;
+static DeviceInfo g_info[64];
+
+static int device_info(DeviceInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return AR_ENODEV;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo& d = g_info[dev];
+  if (!d.ok) {
+    int cus = 0, khz = 0, coop = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return AR_ENODEV;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+      return AR_ENODEV;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
+      coop = 0;
+    d.cus = cus;
+    d.wallclock_hz = (double)khz * 1000.0;
+    d.coop = coop;
+    d.ok = true;
+  }
+  *out = d;
+  return AR_OK;
+}
+
+static uint64_t ns_to_ticks(uint64_t ns, double hz) {
+  if (ns == 0) ns = 1000000000ull;
+  const double t = (double)ns * hz * 1e-9;
+  return t < 1.0 ? 1ull : (uint64_t)t;
+}
+
+static int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static int64_t encoded_bytes(int32_t proto, int64_t count) {
+  if (count < 0) return AR_EINVAL;
+  switch (proto) {
+    case kLL: return 16 * ceil_div64(count, 4);
+    case kLL128: return 128 * ceil_div64(count, 60);
+    case kSentinel:
+    case kBarrier: return 16 * ceil_div64(count, 8);
+    default: return AR_EINVAL;
+  }
+}
+
+static int64_t slot_bytes_of(int32_t proto, int64_t count) {
+  const int64_t E = encoded_bytes(proto, count);
+  if (E < 0) return E;
+  return ceil_div64(E, 128) * 128;
+}
+
+static bool aligned(const void* p, uintptr_t a) {
+  return ((uintptr_t)p & (a - 1)) == 0;
+}
+
+static int check_desc(const ar_desc* d) {
+  if (!d) return AR_EINVAL;
+  if (d->nranks < 1 || d->nranks > AR_MAX_RANKS) return AR_EINVAL;
+  if (d->nconsumers != 1 && d->nconsumers != d->nranks) return AR_EINVAL;
+  if (d->count < 0) return AR_EINVAL;
+  if (d->proto < 0 || d->proto > kBarrier) return AR_EINVAL;
+  if (d->reserved != 0) return AR_EINVAL;
+  const int64_t slot = slot_bytes_of(d->proto, d->count);
+  if (slot > (int64_t(1) << 30)) return AR_ESIZE;
+  const int64_t total = (int64_t)d->nconsumers * 2 * d->nranks * slot;
+  if (total >= (int64_t(1) << 32)) return AR_ESIZE;
+  return AR_OK;
+}
+
+static int check_rows(const void* p, int64_t stride, int64_t count) {
+  if (count == 0) return AR_OK;
+  if (!p) return AR_EINVAL;
+  if (stride < count) return AR_EINVAL;
+  if (!aligned(p, 16) || (stride % 8) != 0) return AR_EALIGN;
+  return AR_OK;
+}
+
+static thread_local int g_last_hip_error = 0;
+
+static int map_hip(hipError_t e) {
+  if (e == hipSuccess) return AR_OK;
+  g_last_hip_error = (int)e;
+  return AR_ELAUNCH;
+}
+
+// Launch with the runtime's own return code (not the sticky last error,
+// which may hold an unrelated earlier failure of the calling thread).
+template <typename... KArgs, typename... Args>
+static hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                         hipStream_t s, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel arity");
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
+                         argv, 0, s);
+}
+
+template <int P>
+static hipError_t launch_pack(PackArgs a, int blocks, hipStream_t s) {
+  return launch(k_pack<P>, dim3(blocks), dim3(kBlock), s, a);
+}
+
+static int pack_common(int32_t want_proto, const ar_desc* d, const void* in,
+                       int64_t in_stride, void* scratch, ar_epoch e,
+                       void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->proto != want_proto) return AR_EINVAL;
+  if (e.parity > 1u || e.seq == 0u) return AR_EINVAL;
+  rc = check_rows(in, in_stride, d->count);
+  if (rc) return rc;
+  if (d->count == 0) return AR_OK;
+  if (!scratch) return AR_EINVAL;
+  if (!aligned(scratch, 256)) return AR_EALIGN;
+  PackArgs a;
+  a.in = static_cast<const uint16_t*>(in);
+  a.in_stride = in_stride;
+  a.count = d->count;
+  a.scratch = static_cast<const uint8_t*>(scratch);
+  a.slot_bytes = (uint32_t)slot_bytes_of(d->proto, d->count);
+  a.scratch_bytes = (uint32_t)((int64_t)d->nconsumers * 2 * d->nranks * a.slot_bytes);
+  a.E = (uint32_t)encoded_bytes(d->proto, d->count);
+  a.nranks = d->nranks;
+  a.nconsumers = d->nconsumers;
+  a.tiles = (int32_t)ceil_div64(a.E, kTileBytes);
+  a.seq = e.seq;
+  a.parity = e.parity;
+  const int64_t waves = (int64_t)a.tiles * d->nranks;
+  const int blocks = (int)ceil_div64(waves, kWavesPerBlock);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  switch (want_proto) {
+    case kLL: err = launch_pack<kLL>(a, blocks, s); break;
+    case kLL128: err = launch_pack<kLL128>(a, blocks, s); break;
+    case kSentinel: err = launch_pack<kSentinel>(a, blocks, s); break;
+    default: err = launch_pack<kBarrier>(a, blocks, s); break;
+  }
+  return map_hip(err);
+}
+
+template <int P, int NMAX>
+static hipError_t launch_reduce(ReduceArgs a, int blocks, hipStream_t s) {
+  return launch(k_reduce<P, NMAX>, dim3(blocks), dim3(kBlock), s, a);
+}
+
+template <int P>
+static hipError_t launch_reduce_n(const ReduceArgs& a, int blocks, hipStream_t s) {
+  if (a.nranks <= 4) return launch_reduce<P, 4>(a, blocks, s);
+  if (a.nranks <= 8) return launch_reduce<P, 8>(a, blocks, s);
+  return launch_reduce<P, 16>(a, blocks, s);
+}
+
+template <int P, int NMAX, bool SHARE>
+static hipError_t launch_sim(const SimArgs& a, int blocks, hipStream_t s) {
+  SimArgs copy = a;
+  void* args[] = {&copy};
+  return hipLaunchCooperativeKernel(
+      reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>), dim3(blocks),
+      dim3(kBlock), args, 0, s);
+}
+
+template <int P, int NMAX, bool SHARE>
+static int occupancy_of() {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &nb, reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>), kBlock, 0) !=
+      hipSuccess)
+    return 0;
+  return nb;
+}
+
+template <int P>
+static hipError_t dispatch_sim_p(const SimArgs& a, bool share, int blocks,
+                                 hipStream_t s) {
+  if (a.nranks <= 4)
+    return share ? launch_sim<P, 4, true>(a, blocks, s) : launch_sim<P, 4, false>(a, blocks, s);
+  if (a.nranks <= 8)
+    return share ? launch_sim<P, 8, true>(a, blocks, s) : launch_sim<P, 8, false>(a, blocks, s);
+  return share ? launch_sim<P, 16, true>(a, blocks, s) : launch_sim<P, 16, false>(a, blocks, s);
+}
+
+template <int P>
+static int occupancy_p(int nranks, bool share) {
+  if (nranks <= 4) return share ? occupancy_of<P, 4, true>() : occupancy_of<P, 4, false>();
+  if (nranks <= 8) return share ? occupancy_of<P, 8, true>() : occupancy_of<P, 8, false>();
+  return share ? occupancy_of<P, 16, true>() : occupancy_of<P, 16, false>();
+}
+
+static int sim_occupancy(int proto, int nranks, bool share) {
+  switch (proto) {
+    case kLL: return occupancy_p<kLL>(nranks, share);
+    case kLL128: return occupancy_p<kLL128>(nranks, share);
+    case kSentinel: return occupancy_p<kSentinel>(nranks, share);
+    default: return occupancy_p<kBarrier>(nranks, share);
+  }
+}
+
+struct SimGeom {
+  int32_t W, Q, T, TPW, blocks;
+};
+
+static int sim_geometry(const ar_sim_params* p, const DeviceInfo& di,
+                        SimGeom* g) {
+  const ar_desc* d = &p->desc;
+  const int64_t E = encoded_bytes(d->proto, d->count);
+  const int64_t T = ceil_div64(E, kTileBytes);
+  if (T <= 0) {
+    *g = SimGeom{0, 0, 0, 0, 0};
+    return AR_OK;
+  }
+  if (T > (int64_t(1) << 24)) return AR_ESIZE;
+  const bool share = d->nconsumers == 1 && d->nranks > 1;
+  const int occ = sim_occupancy(d->proto, d->nranks, share);
+  if (occ <= 0) return AR_ELAUNCH;
+  const int64_t capacity = (int64_t)occ * di.cus;
+  const int64_t qmax_dev = capacity / (8 * (int64_t)d->nranks);
+  const int64_t qmax = qmax_dev < kCtrlMaxProgress / 32 ? qmax_dev : kCtrlMaxProgress / 32;
+  if (qmax < 1) return AR_ECAPACITY;
+  int64_t Q;
+  if (p->waves_per_rank > 0) {
+    if (p->waves_per_rank % 32) return AR_EINVAL;
+    Q = p->waves_per_rank / 32;
+    if (Q > qmax) return AR_ECAPACITY;
+  } else {
+    Q = ceil_div64(T, 32);
+    if (Q > qmax) Q = qmax;
+    if (Q < 1) Q = 1;
+  }
+  const int64_t W = 32 * Q;
+  g->W = (int32_t)W;
+  g->Q = (int32_t)Q;
+  g->T = (int32_t)T;
+  g->TPW = (int32_t)ceil_div64(T, W);
+  g->blocks = (int32_t)(8 * Q * d->nranks);
+  return AR_OK;
+}
+
+static int check_sim(const ar_sim_params* p) {
+  if (!p) return AR_EINVAL;
+  int rc = check_desc(&p->desc);
+  if (rc) return rc;
+  const ar_desc* d = &p->desc;
+  if (p->nops < 1) return AR_EINVAL;
+  if (p->waves_per_rank < 0) return AR_EINVAL;
+  if (p->epoch.parity > 1u || p->epoch.seq == 0u) return AR_EINVAL;
+  rc = check_rows(p->in, p->in_stride, d->count);
+  if (rc) return rc;
+  rc = check_rows(p->out, p->out_stride, d->count);
+  if (rc) return rc;
+  if (!p->scratch || !p->ctrl) return AR_EINVAL;
+  if (!aligned(p->scratch, 256) || !aligned(p->ctrl, 256)) return AR_EALIGN;
+  if (p->trace && !aligned(p->trace, 8)) return AR_EALIGN;
+  if (p->delay_ticks && !aligned(p->delay_ticks, 4)) return AR_EALIGN;
+  if (p->tile_order && !aligned(p->tile_order, 2)) return AR_EALIGN;
+  return AR_OK;
+}
+
+}  // namespace ar
+
+// ============================================================ C ABI ======
+
+using namespace ar;
+
+extern "C" {
+
+const char* ar_status_string(int code) {
+  switch (code) {
+    case AR_OK: return "AR_OK";
+    case AR_EINVAL: return "AR_EINVAL: invalid argument";
+    case AR_EALIGN: return "AR_EALIGN: misaligned pointer or stride";
+    case AR_ESIZE: return "AR_ESIZE: size limit exceeded";
+    case AR_ELAUNCH: return "AR_ELAUNCH: HIP runtime error";
+    case AR_ETIMEOUT: return "AR_ETIMEOUT: poll deadline passed";
+    case AR_ECORRUPT: return "AR_ECORRUPT: impossible readiness flag";
+    case AR_ENODEV: return "AR_ENODEV: no usable device";
+    case AR_ECAPACITY: return "AR_ECAPACITY: grid cannot be co-resident";
+    default: return "AR_UNKNOWN";
+  }
+}
+
+int ar_abi_version(void) { return 1; }
+
+int64_t ar_encoded_bytes(int32_t proto, int64_t count) {
+  return encoded_bytes(proto, count);
+}
+
+int64_t ar_slot_bytes(int32_t proto, int64_t count) {
+  return slot_bytes_of(proto, count);
+}
+
+int64_t ar_scratch_bytes(const ar_desc* d) {
+  const int rc = check_desc(d);
+  if (rc) return rc;
+  return (int64_t)d->nconsumers * 2 * d->nranks * slot_bytes_of(d->proto, d->count);
+}
+
+int64_t ar_ctrl_bytes(void) {
+  return (int64_t)(kCtrlProgress + kCtrlMaxProgress) * 4 + 256;
+}
+
+int ar_epoch_init(ar_epoch* e) {
+  if (!e) return AR_EINVAL;
+  e->seq = 1u;
+  e->parity = 0u;
+  return AR_OK;
+}
+
+int ar_epoch_flip(ar_epoch* e) {
+  if (!e || e->parity > 1u || e->seq == 0u) return AR_EINVAL;
+  e->seq = e->seq == 0xFFFFFFFFu ? 1u : e->seq + 1u;
+  e->parity ^= 1u;
+  return AR_OK;
+}
+
+int ar_epoch_advance(ar_epoch* e, uint64_t nops) {
+  if (!e || e->parity > 1u || e->seq == 0u) return AR_EINVAL;
+  // seq runs through 1..2^32-1 (period 2^32-1); parity has period 2
+  const uint64_t period = 0xFFFFFFFFull;
+  const uint64_t s = (uint64_t)(e->seq - 1u);
+  e->seq = (uint32_t)((s + nops % period) % period) + 1u;
+  e->parity ^= (uint32_t)(nops & 1u);
+  return AR_OK;
+}
+
+int ar_ctrl_reset(void* ctrl, void* stream) {
+  if (!ctrl) return AR_EINVAL;
+  if (!aligned(ctrl, 256)) return AR_EALIGN;
+  const uint32_t words = (uint32_t)(ar_ctrl_bytes() / 4);
+  return map_hip(launch(k_fill_zero, dim3((words + kBlock - 1) / kBlock), dim3(kBlock),
+                        static_cast<hipStream_t>(stream), static_cast<uint32_t*>(ctrl),
+                        words));
+}
+
+int ar_pack_ll(const ar_desc* d, const void* in, int64_t in_stride,
+               void* scratch, ar_epoch e, void* stream) {
+  return pack_common(kLL, d, in, in_stride, scratch, e, stream);
+}
+
+int ar_pack_ll128(const ar_desc* d, const void* in, int64_t in_stride,
+                  void* scratch, ar_epoch e, void* stream) {
+  return pack_common(kLL128, d, in, in_stride, scratch, e, stream);
+}
+
+int ar_pack_sentinel(const ar_desc* d, const void* in, int64_t in_stride,
+                     void* scratch, ar_epoch e, void* stream) {
+  return pack_common(kSentinel, d, in, in_stride, scratch, e, stream);
+}
+
+int ar_pack_plain(const ar_desc* d, const void* in, int64_t in_stride,
+                  void* scratch, ar_epoch e, void* stream) {
+  return pack_common(kBarrier, d, in, in_stride, scratch, e, stream);
+}
+
+int ar_arm_sentinel(const ar_desc* d, void* scratch, int32_t parity,
+                    void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->proto != kSentinel) return AR_EINVAL;
+  if (parity < -1 || parity > 1) return AR_EINVAL;
+  if (d->count == 0) return AR_OK;
+  if (!scratch) return AR_EINVAL;
+  if (!aligned(scratch, 256)) return AR_EALIGN;
+  const uint32_t slot = (uint32_t)slot_bytes_of(d->proto, d->count);
+  const uint32_t total = (uint32_t)((int64_t)d->nconsumers * 2 * d->nranks * slot);
+  const uint32_t region = (uint32_t)d->nranks * slot;   // one parity of one consumer
+  uint32_t region0, stride;
+  int32_t nregions;
+  if (parity < 0) {
+    region0 = 0;
+    stride = region;
+    nregions = 2 * d->nconsumers;
+  } else {
+    region0 = (uint32_t)parity * region;
+    stride = 2u * region;
+    nregions = d->nconsumers;
+  }
+  const uint64_t chunks = (uint64_t)(region / 16u) * (uint64_t)nregions;
+  uint64_t blocks = (chunks + kBlock - 1) / kBlock;
+  if (blocks > 4096) blocks = 4096;
+  return map_hip(launch(k_arm, dim3((unsigned)blocks), dim3(kBlock),
+                        static_cast<hipStream_t>(stream),
+                        static_cast<const uint8_t*>(scratch), total, region0, stride,
+                        region, nregions));
+}
+
+int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
+                       int64_t out_stride, ar_epoch e, void* ctrl,
+                       uint64_t timeout_ns, int32_t flags, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (e.parity > 1u || e.seq == 0u) return AR_EINVAL;
+  if (flags & ~AR_FLAG_REARM) return AR_EINVAL;
+  rc = check_rows(out, out_stride, d->count);
+  if (rc) return rc;
+  if (d->count == 0) return AR_OK;
+  if (!scratch || !ctrl) return AR_EINVAL;
+  if (!aligned(scratch, 256) || !aligned(ctrl, 256)) return AR_EALIGN;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  ReduceArgs a;
+  a.out = static_cast<uint16_t*>(out);
+  a.out_stride = out_stride;
+  a.count = d->count;
+  a.scratch = static_cast<const uint8_t*>(scratch);
+  a.slot_bytes = (uint32_t)slot_bytes_of(d->proto, d->count);
+  a.scratch_bytes = (uint32_t)((int64_t)d->nconsumers * 2 * d->nranks * a.slot_bytes);
+  a.E = (uint32_t)encoded_bytes(d->proto, d->count);
+  a.nranks = d->nranks;
+  a.nconsumers = d->nconsumers;
+  a.tiles = (int32_t)ceil_div64(a.E, kTileBytes);
+  a.seq = e.seq;
+  a.parity = e.parity;
+  a.ctrl = static_cast<int*>(ctrl);
+  a.timeout_ticks = ns_to_ticks(timeout_ns, di.wallclock_hz);
+  a.rearm = (flags & AR_FLAG_REARM) && d->proto == kSentinel;
+  const int64_t waves = (int64_t)a.tiles * d->nconsumers;
+  const int blocks = (int)ceil_div64(waves, kWavesPerBlock);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  switch (d->proto) {
+    case kLL: err = launch_reduce_n<kLL>(a, blocks, s); break;
+    case kLL128: err = launch_reduce_n<kLL128>(a, blocks, s); break;
+    case kSentinel: err = launch_reduce_n<kSentinel>(a, blocks, s); break;
+    default: err = launch_reduce_n<kBarrier>(a, blocks, s); break;
+  }
+  return map_hip(err);
+}
+
+int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
+                    int32_t* tiles_per_rank, int32_t* tiles_per_wave,
+                    int32_t* blocks) {
+  if (!p) return AR_EINVAL;
+  int rc = check_desc(&p->desc);
+  if (rc) return rc;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  SimGeom g;
+  rc = sim_geometry(p, di, &g);
+  if (rc) return rc;
+  if (waves_per_rank) *waves_per_rank = g.W;
+  if (tiles_per_rank) *tiles_per_rank = g.T;
+  if (tiles_per_wave) *tiles_per_wave = g.TPW;
+  if (blocks) *blocks = g.blocks;
+  return AR_OK;
+}
+
+int ar_sim_run(const ar_sim_params* p, void* stream) {
+  int rc = check_sim(p);
+  if (rc) return rc;
+  const ar_desc* d = &p->desc;
+  if (d->count == 0) return AR_OK;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  if (!di.coop) return AR_ENODEV;
+  SimGeom g;
+  rc = sim_geometry(p, di, &g);
+  if (rc) return rc;
+  const bool share = d->nconsumers == 1 && d->nranks > 1;
+  SimArgs a;
+  a.in = static_cast<const uint16_t*>(p->in);
+  a.in_stride = p->in_stride;
+  a.out = static_cast<uint16_t*>(p->out);
+  a.out_stride = p->out_stride;
+  a.scratch = static_cast<const uint8_t*>(p->scratch);
+  a.slot_bytes = (uint32_t)slot_bytes_of(d->proto, d->count);
+  a.scratch_bytes = (uint32_t)((int64_t)d->nconsumers * 2 * d->nranks * a.slot_bytes);
+  a.ctrl = static_cast<int*>(p->ctrl);
+  a.count = d->count;
+  a.E = (uint32_t)encoded_bytes(d->proto, d->count);
+  a.nranks = d->nranks;
+  a.nconsumers = d->nconsumers;
+  a.nops = p->nops;
+  a.W = g.W;
+  a.Q = g.Q;
+  a.T = g.T;
+  a.TPW = g.TPW;
+  a.seq0 = p->epoch.seq;
+  a.parity0 = p->epoch.parity;
+  a.timeout_ticks = ns_to_ticks(p->timeout_ns, di.wallclock_hz);
+  a.delay = p->delay_ticks;
+  a.order = p->tile_order;
+  a.trace = p->trace;
+  const uint32_t wt = (uint32_t)(g.T < g.W ? g.T : g.W);   // waves with tiles per rank
+  a.p_total = wt * (uint32_t)d->nranks;
+  a.c_total = wt * (uint32_t)d->nconsumers;
+  if ((uint64_t)a.p_total * (uint64_t)(p->nops + 1) >= 0xFFFFFFFFull) return AR_ESIZE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (d->proto) {
+    case kLL: e = dispatch_sim_p<kLL>(a, share, g.blocks, s); break;
+    case kLL128: e = dispatch_sim_p<kLL128>(a, share, g.blocks, s); break;
+    case kSentinel: e = dispatch_sim_p<kSentinel>(a, share, g.blocks, s); break;
+    default: e = dispatch_sim_p<kBarrier>(a, share, g.blocks, s); break;
+  }
+  return map_hip(e);
+}
+
+int ar_wallclock_hz(double* hz) {
+  if (!hz) return AR_EINVAL;
+  DeviceInfo di;
+  const int rc = device_info(&di);
+  if (rc) return rc;
+  *hz = di.wallclock_hz;
+  return AR_OK;
+}
+
+int ar_probe_pingpong(void* work, int32_t iters, int32_t xcd_a, int32_t xcd_b,
+                      void* result, void* stream) {
+  if (!work || !result || iters < 1) return AR_EINVAL;
+  if (xcd_a < 0 || xcd_a > 7 || xcd_b < 0 || xcd_b > 7 || xcd_a == xcd_b) return AR_EINVAL;
+  if (!aligned(work, 256) || !aligned(result, 8)) return AR_EALIGN;
+  DeviceInfo di;
+  int rc = device_info(&di);
+  if (rc) return rc;
+  if (!di.coop) return AR_ENODEV;
+  uint32_t* w = static_cast<uint32_t*>(work);
+  uint64_t* r = static_cast<uint64_t*>(result);
+  uint64_t to = ns_to_ticks(2000000000ull, di.wallclock_hz);
+  int32_t xa = xcd_a, xb = xcd_b;
+  void* args[] = {&w, &iters, &xa, &xb, &r, &to};
+  return map_hip(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_pingpong),
+                                            dim3(8), dim3(64), args, 0,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int ar_probe_loadchain(void* work, int64_t bytes, int32_t iters, void* result,
+                       void* stream) {
+  if (!work || !result || iters < 1) return AR_EINVAL;
+  if (bytes < 4096 || bytes > (int64_t(1) << 31) || (bytes & (bytes - 1))) return AR_EINVAL;
+  if (!aligned(work, 256) || !aligned(result, 8)) return AR_EALIGN;
+  const uint32_t n = (uint32_t)(bytes / 4);
+  const uint32_t stride = 4099u;   // ~16 KiB hops, odd: one cycle through n
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = map_hip(launch(k_chain_init, dim3(1024), dim3(kBlock), s,
+                          static_cast<uint32_t*>(work), n, stride));
+  if (rc) return rc;
+  return map_hip(launch(k_chain, dim3(1), dim3(64), s,
+                        static_cast<const uint32_t*>(work), (uint32_t)bytes, iters,
+                        static_cast<uint64_t*>(result)));
+}
+
+int ar_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst || bytes < 0 || (bytes % 16)) return AR_EINVAL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return AR_EALIGN;
+  if (bytes == 0) return AR_OK;
+  const uint64_t n16 = (uint64_t)bytes / 16;
+  uint64_t blocks = (n16 + kBlock - 1) / kBlock;
+  if (blocks > 8192) blocks = 8192;
+  return map_hip(launch(k_copy, dim3((unsigned)blocks), dim3(kBlock),
+                        static_cast<hipStream_t>(stream),
+                        static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16));
+}
+
+int ar_probe_empty(void* stream) {
+  return map_hip(launch(k_empty, dim3(1), dim3(64), static_cast<hipStream_t>(stream)));
+}
+
+int ar_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,319 @@
+// ar_protocols.h -- per-protocol encode (producer) and poll/validate/reduce
+// (consumer) for one tile: 1 KiB of a receive slot, one wave, 16 bytes a lane.
+//
+// Lane -> element map of tile t (the slot layout is fixed by the encoding):
+//   LL        4 elements at 256t + 4*lane       (two 8-byte words: data|flag)
+//   SENTINEL  8 elements at 512t + 8*lane       (plain bf16, 0xFFFF = empty)
+//   BARRIER   8 elements at 512t + 8*lane       (plain bf16)
+//   LL128     line L = 8t + lane/8, chunk j = lane%8:
+//             j < 7: 8 elements at 60L + 8j; j = 7: 4 elements at 60L + 56
+//             followed by the line's u64 flag.
+#pragma once
+
+#include "ar_device.h"
+
+namespace ar {
+
+template <int P>
+__device__ __forceinline__ void lane_elems(int tile, int lane, int64_t& first,
+                                           int& n) {
+  if (P == kLL) {
+    first = (int64_t)tile * 256 + lane * 4;
+    n = 4;
+  } else if (P == kLL128) {
+    const int64_t line = (int64_t)tile * 8 + (lane >> 3);
+    const int j = lane & 7;
+    first = 60 * line + 8 * j;
+    n = (j == 7) ? 4 : 8;
+  } else {
+    first = (int64_t)tile * 512 + lane * 8;
+    n = 8;
+  }
+}
+
+// Load n (4 or 8) bf16 from row[first..] as packed dwords w[0..n/2), zero
+// past `count`.  first is a multiple of 4, so 8-byte loads are aligned;
+// 16-byte loads are used when first is a multiple of 8.
+__device__ __forceinline__ void load_elems(const uint16_t* __restrict__ row,
+                                           int64_t count, int64_t first, int n,
+                                           uint32_t w[4]) {
+  if (first + n <= count) {
+    if (n == 8 && (first & 7) == 0) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(row + first);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(row + first);
+      w[0] = a.x; w[1] = a.y;
+      if (n == 8) {
+        const u32x2 b = *reinterpret_cast<const u32x2*>(row + first + 4);
+        w[2] = b.x; w[3] = b.y;
+      }
+    }
+  } else {
+    for (int k = 0; k < n; k += 2) {
+      const uint32_t lo = (first + k < count) ? row[first + k] : 0u;
+      const uint32_t hi = (first + k + 1 < count) ? row[first + k + 1] : 0u;
+      w[k >> 1] = pack2(lo, hi);
+    }
+  }
+}
+
+// Store n (4 or 8) bf16 packed in w to row[first..], only below `count`.
+__device__ __forceinline__ void store_elems(uint16_t* __restrict__ row,
+                                            int64_t count, int64_t first,
+                                            int n, const uint32_t w[4]) {
+  if (first + n <= count) {
+    if (n == 8 && (first & 7) == 0) {
+      u32x4 v;
+      v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+      *reinterpret_cast<u32x4*>(row + first) = v;
+    } else {
+      u32x2 a;
+      a.x = w[0]; a.y = w[1];
+      *reinterpret_cast<u32x2*>(row + first) = a;
+      if (n == 8) {
+        u32x2 b;
+        b.x = w[2]; b.y = w[3];
+        *reinterpret_cast<u32x2*>(row + first + 4) = b;
+      }
+    }
+  } else {
+    for (int k = 0; k < n; ++k) {
+      if (first + k < count) {
+        const uint32_t d = w[k >> 1];
+        row[first + k] = (uint16_t)((k & 1) ? (d >> 16) : (d & 0xFFFFu));
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------- producer ---
+
+// The lane's 16 encoded bytes of tile `tile` for epoch `seq`.
+template <int P>
+__device__ __forceinline__ u32x4 encode_chunk(const uint16_t* __restrict__ row,
+                                              int64_t count, int tile,
+                                              int lane, uint32_t seq) {
+  int64_t first;
+  int n;
+  lane_elems<P>(tile, lane, first, n);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  load_elems(row, count, first, n, w);
+  u32x4 v;
+  if (P == kLL) {
+    // two LL words: data then flag, each single-copy atomic on its own
+    v.x = w[0]; v.y = seq; v.z = w[1]; v.w = seq;
+  } else if (P == kLL128) {
+    if ((lane & 7) == 7) {
+      v.x = w[0]; v.y = w[1]; v.z = seq; v.w = 0u;   // last data + u64 flag
+    } else {
+      v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+    }
+  } else if (P == kSentinel) {
+    v.x = canon_word(w[0]); v.y = canon_word(w[1]);
+    v.z = canon_word(w[2]); v.w = canon_word(w[3]);
+  } else {
+    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+  }
+  return v;
+}
+
+// Write one tile of rank payload `row` into `ncons` receive buffers: slot
+// offsets dst0, dst0 + cstride, ...  For LL128 only the data part is
+// written here; the flags follow a release fence (produce_flags).
+template <int P>
+__device__ __forceinline__ void produce_data(rsrc_t rs, uint32_t dst0,
+                                             uint32_t cstride, int ncons,
+                                             const uint16_t* __restrict__ row,
+                                             int64_t count, int tile,
+                                             uint32_t E, uint32_t seq,
+                                             int lane) {
+  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+  if (loff >= E) return;
+  const u32x4 v = encode_chunk<P>(row, count, tile, lane, seq);
+  if (P == kLL128 && (lane & 7) == 7) {
+    u32x2 d;
+    d.x = v.x; d.y = v.y;
+    for (int c = 0; c < ncons; ++c) st8(rs, dst0 + c * cstride + loff, d);
+  } else {
+    for (int c = 0; c < ncons; ++c) st16(rs, dst0 + c * cstride + loff, v);
+  }
+}
+
+// LL128 second phase: the u64 line flags (lane 7 of each line).
+__device__ __forceinline__ void produce_flags(rsrc_t rs, uint32_t dst0,
+                                              uint32_t cstride, int ncons,
+                                              int tile, uint32_t E,
+                                              uint32_t seq, int lane) {
+  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+  if (loff >= E || (lane & 7) != 7) return;
+  u32x2 f;
+  f.x = seq; f.y = 0u;
+  for (int c = 0; c < ncons; ++c) st8(rs, dst0 + c * cstride + loff + 8u, f);
+}
+
+// ----------------------------------------------------------- consumer ---
+
+// Per-lane readiness of one 16-byte chunk: ok = delivered for epoch seq;
+// bad = holds a flag that is neither seq, the stale seq of two ops before,
+// nor 0 (never written).
+template <int P>
+__device__ __forceinline__ void classify(const u32x4 v, uint32_t seq,
+                                         uint32_t stale, bool& ok, bool& bad) {
+  if (P == kLL) {
+    ok = (v.y == seq) && (v.w == seq);
+    const bool b1 = v.y != seq && v.y != stale && v.y != 0u;
+    const bool b2 = v.w != seq && v.w != stale && v.w != 0u;
+    bad = b1 || b2;
+  } else if (P == kSentinel) {
+    ok = word_delivered(v.x) && word_delivered(v.y) && word_delivered(v.z) &&
+         word_delivered(v.w);
+    bad = false;
+  } else {
+    ok = true;
+    bad = false;
+  }
+}
+
+// Poll, validate and reduce one tile for one consumer.  `src0` is the byte
+// offset of slot 0 of this consumer and parity; slot r is at
+// src0 + r*slot_bytes.  Returns 0, kEtimeout or kEcorrupt.
+template <int P, int NMAX>
+__device__ __forceinline__ int consume_tile(
+    rsrc_t rs, uint32_t src0, uint32_t slot_bytes, int nranks, int tile,
+    uint32_t E, uint32_t seq, uint32_t stale, bool rearm,
+    uint16_t* __restrict__ out_row, int64_t count, int* ctrl,
+    uint64_t timeout_ticks, int lane) {
+  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+  const bool active = loff < E;
+  u32x4 v[NMAX];
+#pragma unroll
+  for (int r = 0; r < NMAX; ++r) v[r] = u32x4{0u, 0u, 0u, 0u};
+  uint32_t pending = (1u << nranks) - 1u;   // wave-uniform set of ranks
+  Waiter wt(timeout_ticks, ctrl);
+
+  if (P == kLL128) {
+    const bool flag_lane = (lane & 7) == 7;
+    while (true) {
+      u32x2 f[NMAX];
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r) {
+        f[r] = u32x2{0u, 0u};
+        if (r < nranks && ((pending >> r) & 1u) && active && flag_lane)
+          f[r] = ld8(rs, src0 + r * slot_bytes + loff + 8u);
+      }
+      uint32_t fresh = 0u;
+      bool corrupt = false;
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r) {
+        if (r < nranks && ((pending >> r) & 1u)) {
+          bool ok = true, bad = false;
+          if (active && flag_lane) {
+            ok = (f[r].x == seq) && (f[r].y == 0u);
+            bad = !ok && !(f[r].y == 0u && (f[r].x == 0u || f[r].x == stale));
+          }
+          if (__ballot(bad) != 0ull) corrupt = true;
+          if (__ballot(!ok) == 0ull) fresh |= 1u << r;
+        }
+      }
+      if (corrupt) {
+        if (lane == 0) report_error(ctrl, kEcorrupt);
+        return kEcorrupt;
+      }
+      if (fresh != 0u) {
+        // The flags were stored after a release fence that followed the
+        // data; order the data loads after the flag loads.
+        fence_acquire();
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r)
+          if (r < nranks && ((fresh >> r) & 1u) && active)
+            v[r] = ld16(rs, src0 + r * slot_bytes + loff);
+        pending &= ~fresh;
+      }
+      if (pending == 0u) break;
+      if (!wt.again(lane)) return kEtimeout;
+    }
+  } else {
+    while (true) {
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r)
+        if (r < nranks && ((pending >> r) & 1u) && active)
+          v[r] = ld16(rs, src0 + r * slot_bytes + loff);
+      uint32_t fresh = 0u;
+      bool corrupt = false;
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r) {
+        if (r < nranks && ((pending >> r) & 1u)) {
+          bool ok = true, bad = false;
+          if (active) classify<P>(v[r], seq, stale, ok, bad);
+          if (__ballot(bad) != 0ull) corrupt = true;
+          if (__ballot(!ok) == 0ull) fresh |= 1u << r;
+        }
+      }
+      if (corrupt) {
+        if (lane == 0) report_error(ctrl, kEcorrupt);
+        return kEcorrupt;
+      }
+      if (P == kSentinel && rearm && fresh != 0u) {
+        const u32x4 armed = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu,
+                                  0xFFFFFFFFu};
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r)
+          if (r < nranks && ((fresh >> r) & 1u) && active)
+            st16(rs, src0 + r * slot_bytes + loff, armed);
+      }
+      pending &= ~fresh;
+      if (pending == 0u) break;
+      if (!wt.again(lane)) return kEtimeout;
+    }
+  }
+
+  if (!active) return 0;
+  // Fixed rank order: start from rank 0, add ranks 1..N-1 one at a time.
+  float acc[8];
+  {
+    const u32x4 d = v[0];
+    if (P == kLL) {
+      acc[0] = bf_lo(d.x); acc[1] = bf_hi(d.x);
+      acc[2] = bf_lo(d.z); acc[3] = bf_hi(d.z);
+    } else {
+      acc[0] = bf_lo(d.x); acc[1] = bf_hi(d.x);
+      acc[2] = bf_lo(d.y); acc[3] = bf_hi(d.y);
+      acc[4] = bf_lo(d.z); acc[5] = bf_hi(d.z);
+      acc[6] = bf_lo(d.w); acc[7] = bf_hi(d.w);
+    }
+  }
+#pragma unroll
+  for (int r = 1; r < NMAX; ++r) {
+    if (r < nranks) {
+      const u32x4 d = v[r];
+      if (P == kLL) {
+        acc[0] += bf_lo(d.x); acc[1] += bf_hi(d.x);
+        acc[2] += bf_lo(d.z); acc[3] += bf_hi(d.z);
+      } else {
+        acc[0] += bf_lo(d.x); acc[1] += bf_hi(d.x);
+        acc[2] += bf_lo(d.y); acc[3] += bf_hi(d.y);
+        acc[4] += bf_lo(d.z); acc[5] += bf_hi(d.z);
+        acc[6] += bf_lo(d.w); acc[7] += bf_hi(d.w);
+      }
+    }
+  }
+  uint32_t o[4];
+  if (P == kLL) {
+    o[0] = pack2(to_bf16(acc[0]), to_bf16(acc[1]));
+    o[1] = pack2(to_bf16(acc[2]), to_bf16(acc[3]));
+    o[2] = 0u; o[3] = 0u;
+  } else {
+    o[0] = pack2(to_bf16(acc[0]), to_bf16(acc[1]));
+    o[1] = pack2(to_bf16(acc[2]), to_bf16(acc[3]));
+    o[2] = pack2(to_bf16(acc[4]), to_bf16(acc[5]));
+    o[3] = pack2(to_bf16(acc[6]), to_bf16(acc[7]));
+  }
+  int64_t first;
+  int n;
+  lane_elems<P>(tile, lane, first, n);
+  store_elems(out_row, count, first, n, o);
+  return 0;
+}
+
+}  // namespace ar

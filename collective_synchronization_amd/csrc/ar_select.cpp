@@ -1,0 +1,51 @@
+// ar_select.cpp -- host-side cost-guided protocol selector.
+//
+// "flash-comm: Self-Synchronizing Collective Communication for LLM
+// Decoding", abstract: the readiness encoding is chosen by message size and
+// the number of participating GPUs, trading synchronization overhead against
+// the extra bytes an encoding moves.  "Why Microseconds Matter in AI
+// Infrastructure", sections "What I learned from it" and "Where I think this
+// is heading": the choice is made from measurements, with a performance model
+// as the next step.  Here the model is the two-term latency/bandwidth form
+// T_p(S) = alpha_p + beta_p * S per protocol p and rank count, fitted to
+// measurements from this GPU by the Python side and passed in as a table.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/ar.h"
+
+extern "C" int ar_select_protocol(const ar_cost_entry* table, int32_t nentries,
+                                  int64_t payload_bytes, int32_t nranks,
+                                  int32_t* proto_out, double* predicted_us) {
+  if (!table || nentries < 1 || !proto_out) return AR_EINVAL;
+  if (payload_bytes < 0 || nranks < 1 || nranks > AR_MAX_RANKS) return AR_EINVAL;
+  // entry with the nearest rank count; ties go to the smaller rank count
+  int best = -1;
+  int best_dist = 0;
+  for (int i = 0; i < nentries; ++i) {
+    const int dist = abs(table[i].nranks - nranks);
+    if (best < 0 || dist < best_dist ||
+        (dist == best_dist && table[i].nranks < table[best].nranks)) {
+      best = i;
+      best_dist = dist;
+    }
+  }
+  const ar_cost_entry& e = table[best];
+  int choice = -1;
+  double t_best = 0.0;
+  for (int p = 0; p < 4; ++p) {
+    const double a = e.alpha_us[p];
+    const double b = e.beta_us_per_byte[p];
+    if (!(a >= 0.0) || !isfinite(a) || !isfinite(b)) continue;   // unavailable
+    const double t = a + b * (double)payload_bytes;
+    if (choice < 0 || t < t_best) {   // strict: ties keep the lower id
+      choice = p;
+      t_best = t;
+    }
+  }
+  if (choice < 0) return AR_EINVAL;
+  *proto_out = choice;
+  if (predicted_us) *predicted_us = t_best;
+  return AR_OK;
+}

@@ -1,0 +1,333 @@
+/*
+ * ar.h -- C ABI of the self-synchronizing small-message one-shot bf16
+ * all-reduce for MI355X (gfx950).
+ *
+ * The operation ("SiFAR: Synchronization-Free All-Reduce for Low-Latency LLM
+ * Inference", abstract; "flash-comm: Self-Synchronizing Collective
+ * Communication for LLM Decoding", abstract): every rank r contributes a bf16
+ * payload x_r[0..count); every receiving rank obtains
+ *     out[j] = bf16_rne(((f32(x_0[j]) + f32(x_1[j])) + ...) + f32(x_{N-1}[j]))
+ * with each '+' one binary32 round-to-nearest-even addition in fixed rank
+ * order 0..N-1 (independent of the order in which payloads arrive) and any
+ * NaN result written as 0x7FC0.  Each payload travels with its own readiness
+ * evidence ("Why Microseconds Matter in AI Infrastructure", section "Latency
+ * can matter more than bandwidth"): an LL flag in the same 8-byte store as
+ * 4 bytes of data, an LL128-style flag per 128-byte line, or a receive buffer
+ * armed with the negative-NaN sentinel 0xFFFF and polled until overwritten.
+ * Two buffer parities alternate by epoch (the same section's double
+ * buffering; SiFAR's dual buffering), which removes the bottom barrier.
+ *
+ * On one GPU, N ranks are simulated: rank r's producer writes slot r of a
+ * receive buffer, and a consumer polls, validates and reduces.  A receive
+ * buffer belongs to one consumer rank; "nconsumers = 1" simulates one rank's
+ * share (the receive side of rank 0), "nconsumers = nranks" every rank.
+ *
+ * Conventions for every call:
+ *  - Device pointers are plain device addresses (for example from
+ *    hipMalloc or a framework allocator).  The caller owns every buffer; the
+ *    library allocates no device memory and keeps no global mutable state
+ *    apart from a per-device cache of occupancy figures.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Device work is enqueued asynchronously; AR_OK means "enqueued".
+ *  - Return codes: AR_OK (0) or a negative ar_status.  Host-detected errors
+ *    are returned before anything is enqueued.  Errors detected on the
+ *    device (timeouts, corrupt flags) are written to the status word of the
+ *    caller's control block (first error wins) and are read by the caller
+ *    after synchronizing.
+ *  - bf16 values are passed as raw 16-bit patterns (uint16_t), rows are
+ *    row-major, `*_stride` is the distance between rows in elements.
+ */
+#ifndef AR_H_
+#define AR_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------- status --- */
+typedef enum {
+    AR_OK = 0,
+    AR_EINVAL = -1,     /* null pointer, rank count outside 1..16, count < 0,
+                           unknown protocol, reserved field not 0 */
+    AR_EALIGN = -2,     /* in/out not 16-byte aligned, stride not a multiple
+                           of 8 elements, scratch/ctrl not 256-byte aligned */
+    AR_ESIZE = -3,      /* a size limit is exceeded (slot > 1 GiB, too many
+                           ops, buffer offsets beyond 32 bits) */
+    AR_ELAUNCH = -4,    /* a HIP runtime call failed */
+    AR_ETIMEOUT = -5,   /* device: a poll passed its deadline */
+    AR_ECORRUPT = -6,   /* device: a readiness flag that can never be legal */
+    AR_ENODEV = -7,     /* no device, or cooperative launch unsupported */
+    AR_ECAPACITY = -8   /* the simulator grid cannot be co-resident */
+} ar_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* ar_status_string(int code);
+
+/* ----------------------------------------------------------- protocols --- */
+typedef enum {
+    AR_LL = 0,        /* 8-byte words: u32 data (2 bf16) | u32 flag = seq     */
+    AR_LL128 = 1,     /* 128-byte lines: 60 bf16 (120 B) | u64 flag = seq      */
+    AR_SENTINEL = 2,  /* bf16 copy, negative NaNs sent as 0x7FC0, buffer armed
+                         with 0xFFFF and polled until overwritten            */
+    AR_BARRIER = 3,   /* plain copy; readiness from counters (baseline)       */
+    AR_AUTO = 4       /* only for ar_select_protocol                          */
+} ar_proto;
+
+#define AR_MAX_RANKS 16
+
+/*
+ * Encoded bytes E of one rank's payload of `count` elements:
+ *   LL 16*ceil(count/4), LL128 128*ceil(count/60), SENTINEL and BARRIER
+ *   16*ceil(count/8).  Bytes past `count` are zero (LL pad words carry the
+ *   flag).  Returns a negative ar_status for a bad protocol or count < 0.
+ */
+int64_t ar_encoded_bytes(int32_t proto, int64_t count);
+
+/* One slot = E rounded up to 128 bytes (one line). */
+int64_t ar_slot_bytes(int32_t proto, int64_t count);
+
+/* ------------------------------------------------------------ epochs --- */
+/*
+ * Epoch of one op.  seq is the flag value written by LL and LL128 producers
+ * (a u32 that starts at 1 and skips 0 on wrap); parity selects one of the two
+ * receive-buffer halves and toggles every op.  A buffer half can only hold
+ * the current seq, the seq of two ops before (same parity), or 0 (never
+ * written); any other flag value is corruption.  The caller owns the epoch
+ * and must advance it by one flip per op issued on a receive buffer.
+ */
+typedef struct {
+    uint32_t seq;
+    uint32_t parity;
+} ar_epoch;
+
+int ar_epoch_init(ar_epoch* e);                      /* {seq 1, parity 0} */
+/* Next op ("Why Microseconds Matter in AI Infrastructure", "Latency can
+ * matter more than bandwidth": reuse of the other buffer is licensed by the
+ * exchange itself).  seq = seq+1 (0 skipped), parity ^= 1. */
+int ar_epoch_flip(ar_epoch* e);
+int ar_epoch_advance(ar_epoch* e, uint64_t nops);    /* nops flips */
+
+/* -------------------------------------------------------- descriptors --- */
+typedef struct {
+    int32_t nranks;      /* N simulated ranks, 1..AR_MAX_RANKS              */
+    int32_t nconsumers;  /* receive buffers: 1 (rank 0's share) or nranks    */
+    int64_t count;       /* bf16 elements per rank payload, >= 0             */
+    int32_t proto;       /* AR_LL, AR_LL128, AR_SENTINEL or AR_BARRIER       */
+    int32_t reserved;    /* must be 0                                        */
+} ar_desc;
+
+/*
+ * Receive-buffer ("scratch") layout, caller-owned, 256-byte aligned:
+ *   scratch[consumer c][parity p][source rank r][slot_bytes]
+ * at byte offset ((c*2 + p)*nranks + r) * slot_bytes.  LL and LL128 scratch
+ * must be zero-filled once before first use (a zero flag is "never
+ * written"); SENTINEL scratch must be armed with ar_arm_sentinel.
+ */
+int64_t ar_scratch_bytes(const ar_desc* d);
+
+/*
+ * Control block, caller-owned device memory of ar_ctrl_bytes() bytes,
+ * 256-byte aligned, zero-filled before first use and after any error:
+ *   int32 word 0 = status (0 or a negative ar_status, first error wins),
+ *   word 1 = abort flag, words 2.. = barrier counters of the simulator.
+ */
+int64_t ar_ctrl_bytes(void);
+/* Zero the control block with a small fill kernel (safe inside graphs). */
+int ar_ctrl_reset(void* ctrl, void* stream);
+
+/* ------------------------------------------------------------ producer --- */
+/*
+ * Producers: encode every simulated rank's payload for epoch `e` into slot r
+ * of parity e.parity of every consumer's receive buffer.
+ *   in:   device, rank r's payload at in + r*in_stride (elements), bf16.
+ *         16-byte aligned, in_stride a multiple of 8 and >= count.
+ *   scratch: device, ar_scratch_bytes(d) bytes (layout above).
+ * Stores use device-scope coherent (sc1) 16-byte accesses.
+ *
+ * ar_pack_ll -- LL: each 8-byte word holds 4 data bytes and the u32 flag
+ * seq, written by one store, so a reader that sees the flag sees the data
+ * ("Why Microseconds Matter in AI Infrastructure", "Latency can matter more
+ * than bandwidth": data and readiness flag in one atomic store).
+ */
+int ar_pack_ll(const ar_desc* d, const void* in, int64_t in_stride,
+               void* scratch, ar_epoch e, void* stream);
+
+/*
+ * ar_pack_ll128 -- LL128-style: 120 data bytes then a u64 flag per 128-byte
+ * line (same section names an LL128 atomic design).  gfx950 documents no
+ * 128-byte store atomicity, so each wave stores the data, issues a
+ * device-scope release fence, then stores the flags.
+ */
+int ar_pack_ll128(const ar_desc* d, const void* in, int64_t in_stride,
+                  void* scratch, ar_epoch e, void* stream);
+
+/*
+ * ar_pack_sentinel -- copy with every negative NaN replaced by 0x7FC0, so the
+ * armed value 0xFFFF is never transmitted (same section: the sentinel must
+ * not appear in transmitted data).
+ */
+int ar_pack_sentinel(const ar_desc* d, const void* in, int64_t in_stride,
+                     void* scratch, ar_epoch e, void* stream);
+
+/* ar_pack_plain -- raw copy for the plain-barrier baseline (SiFAR abstract:
+ * the one-shot baseline separates data from its top and bottom barriers). */
+int ar_pack_plain(const ar_desc* d, const void* in, int64_t in_stride,
+                  void* scratch, ar_epoch e, void* stream);
+
+/*
+ * ar_arm_sentinel -- fill the SENTINEL slots of parity `parity` (0 or 1; -1 =
+ * both) of every consumer with 0xFFFF ("Why Microseconds Matter in AI
+ * Infrastructure", "Latency can matter more than bandwidth": the receive
+ * buffer is initialized to a negative NaN).  A fill kernel, not a memset.
+ */
+int ar_arm_sentinel(const ar_desc* d, void* scratch, int32_t parity,
+                    void* stream);
+
+/* ------------------------------------------------------------ consumer --- */
+#define AR_FLAG_REARM 1   /* SENTINEL: re-arm each slot chunk after reading */
+
+/*
+ * ar_reduce_validate -- every consumer c polls its receive buffer (parity
+ * e.parity) with device-scope coherent 16-byte loads, validates each block
+ * from its own evidence in whatever order blocks arrive, and reduces the N
+ * rank rows in fixed rank order ("flash-comm", abstract: receivers validate
+ * the blocks they need; reduction order is decoupled from transport order).
+ *   out: device, consumer c's result at out + c*out_stride, 16-byte aligned,
+ *        out_stride a multiple of 8 and >= count.
+ *   ctrl: device control block; a poll that passes timeout_ns writes
+ *        AR_ETIMEOUT, an impossible LL/LL128 flag writes AR_ECORRUPT (the
+ *        output of that tile is then not written).  timeout_ns 0 = 1 s.
+ *   flags: AR_FLAG_REARM (SENTINEL only) re-arms what was read, so the same
+ *        parity is ready for the op two epochs later.
+ * BARRIER payloads carry no evidence: this call then trusts stream order
+ * (the kernel boundary after ar_pack_plain is the barrier).
+ */
+int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
+                       int64_t out_stride, ar_epoch e, void* ctrl,
+                       uint64_t timeout_ns, int32_t flags, void* stream);
+
+/* ------------------------------------------------------------ simulator --- */
+/*
+ * ar_sim_run -- `nops` back-to-back one-shot all-reduces in one persistent
+ * cooperative kernel: N simulated ranks as groups of waves placed on
+ * different XCDs, producers and consumers running concurrently with no top
+ * barrier (consumers start polling at once: "SiFAR", abstract, speculative
+ * reduction validated by the readiness evidence) and no bottom barrier
+ * (dual-buffered epochs).  Each rank runs consume(i) -> produce(i+1), so a
+ * buffer half is reused only after the exchange that licenses it ("Why
+ * Microseconds Matter in AI Infrastructure", "Latency can matter more than
+ * bandwidth").  With nconsumers = 1 the producers of ranks 1..N-1 take that
+ * license from rank 0's block of the previous op.  AR_BARRIER runs the plain
+ * baseline instead: one buffer, a top barrier (arrival counter) and a bottom
+ * barrier (completion counter) per op, both global.
+ *
+ * Buffers (device):
+ *   in:  op i, rank r at in + (i*nranks + r)*in_stride elements.
+ *   out: op i, consumer c at out + (i*nconsumers + c)*out_stride elements.
+ *   scratch, ctrl: as above; for AR_BARRIER only parity 0 is used and the
+ *        control block must be zero at launch (ar_ctrl_reset).
+ *   delay_ticks (optional, NULL = none): uint32 [nops][nranks] wall-clock
+ *        ticks (ar_wallclock_hz) that each wave of rank r waits before
+ *        producing op i.
+ *   tile_order (optional): uint16 [nops][nranks][tiles_per_wave] giving, per
+ *        op and rank, the order in which each wave writes its own tiles
+ *        (a permutation of 0..tiles_per_wave-1; see ar_sim_geometry).
+ *   trace (optional): uint64 [nops*2*nranks + 1]; element i*2N + r = latest
+ *        wall clock after rank r's last store of op i, element i*2N + N + c
+ *        = latest completion of op i at consumer c, last element = earliest
+ *        start.  Must be zero-filled, and the last element set to all ones,
+ *        by the caller.
+ */
+typedef struct {
+    ar_desc desc;
+    int32_t nops;               /* >= 1 */
+    int32_t waves_per_rank;     /* multiple of 32; 0 = library choice */
+    const void* in;
+    int64_t in_stride;
+    void* out;
+    int64_t out_stride;
+    void* scratch;
+    void* ctrl;
+    ar_epoch epoch;             /* epoch of op 0 */
+    uint64_t timeout_ns;        /* per poll; 0 = 1 s */
+    const uint32_t* delay_ticks;
+    const uint16_t* tile_order;
+    uint64_t* trace;
+} ar_sim_params;
+
+int ar_sim_run(const ar_sim_params* p, void* stream);
+
+/*
+ * Geometry ar_sim_run will use for these parameters: waves per rank,
+ * tiles per rank (1 KiB of slot each), tiles per wave, total workgroups.
+ */
+int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
+                    int32_t* tiles_per_rank, int32_t* tiles_per_wave,
+                    int32_t* blocks);
+
+/* Wall-clock counter frequency of the current device in Hz. */
+int ar_wallclock_hz(double* hz);
+
+/* ------------------------------------------------------------- selector --- */
+/*
+ * Cost-guided protocol selector ("flash-comm", abstract: the readiness
+ * encoding is chosen by message size and number of GPUs, trading
+ * synchronization cost against extra bytes; "Why Microseconds Matter in AI
+ * Infrastructure", "What I learned from it": selection from measurements).
+ * Model per protocol p and rank count: T_p(S) = alpha_us[p] + beta_us_per_byte[p] * S,
+ * with S = 2*count payload bytes per rank.  The entry with the nearest
+ * nranks is used (ties: the smaller).  A protocol with alpha_us < 0 is
+ * unavailable.  Ties go to the lower protocol id (LL < LL128 < SENTINEL <
+ * BARRIER).  Host only; writes the chosen id and, if non-NULL, its predicted
+ * time.
+ */
+typedef struct {
+    int32_t nranks;
+    int32_t reserved;
+    double alpha_us[4];
+    double beta_us_per_byte[4];
+} ar_cost_entry;
+
+int ar_select_protocol(const ar_cost_entry* table, int32_t nentries,
+                       int64_t payload_bytes, int32_t nranks,
+                       int32_t* proto_out, double* predicted_us);
+
+/* -------------------------------------------------------- floor probes --- */
+/*
+ * Probes for the one-chip floor, the analogue of the speed-of-light bound of
+ * "Why Microseconds Matter in AI Infrastructure", section "Defining the
+ * physical lower bound" (two round trips to the coherent cache level plus
+ * one remote store).
+ *
+ * ar_probe_pingpong: two single-lane waves on the XCDs `xcd_a` != `xcd_b`
+ *   (workgroups are placed round-robin over the 8 XCDs) bounce a flag
+ *   `iters` times with device-scope coherent stores and polls.
+ *   work: device, >= 512 bytes, zeroed.  result: device uint64[6] =
+ *   {total ticks at a, iters, XCC id of a, XCC id of b, status, 0}.
+ * ar_probe_loadchain: one lane follows `iters` dependent device-scope
+ *   coherent loads through `bytes` of `work` (initialized by the probe).
+ *   result: device uint64[2] = {ticks, iters}.
+ * ar_probe_copy: streaming 16-byte copy of `bytes` (multiple of 16).
+ * ar_probe_empty: an empty kernel (launch floor).
+ */
+int ar_probe_pingpong(void* work, int32_t iters, int32_t xcd_a, int32_t xcd_b,
+                      void* result, void* stream);
+int ar_probe_loadchain(void* work, int64_t bytes, int32_t iters, void* result,
+                       void* stream);
+int ar_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+int ar_probe_empty(void* stream);
+
+/* Library ABI version (bumped on any signature change). */
+int ar_abi_version(void);
+
+/* hipError_t code of the last HIP call that made an entry point return
+ * AR_ELAUNCH on the calling thread (0 if none). */
+int ar_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_H_ */

@@ -1,0 +1,185 @@
+"""Host-side tests of the C ABI (CPU only, no device work is enqueued).
+
+* the library loads and exports every function include/ar.h declares;
+* size and epoch helpers agree with the oracle's independent definitions;
+* argument checks return the documented codes before touching a device;
+* the protocol selector's argmin, nearest-rank choice and tie rule.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+from collective_synchronization_amd import abi
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "ar.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ar_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_all_exported():
+    names = _declared_functions()
+    assert len(names) >= 20
+    lib = abi.raw()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ar.h but not exported"
+    # and the binding covers exactly the declared functions
+    assert sorted(abi.EXPORTED) == names
+
+
+def test_abi_version_and_status_strings():
+    assert abi.raw().ar_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        assert abi.status_string(code).startswith("AR_")
+    assert abi.status_string(-99) == "AR_UNKNOWN"
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel", "barrier"])
+@pytest.mark.parametrize("count", [0, 1, 3, 4, 5, 59, 60, 61, 4096, 8192, 32768, 131072,
+                                   2097152])
+def test_sizes_match_oracle(proto, count):
+    E = abi.ar_encoded_bytes(proto, count)
+    assert E == oracle.encoded_bytes(proto, count)
+    assert abi.ar_slot_bytes(proto, count) == (E + 127) // 128 * 128
+    d = abi.make_desc(8, count, proto, nconsumers=8)
+    assert abi.ar_scratch_bytes(d) == 8 * 2 * 8 * abi.ar_slot_bytes(proto, count)
+
+
+def test_epochs_match_oracle():
+    e = abi.ar_epoch_init()
+    assert (e.seq, e.parity) == (1, 0)
+    seq = 1
+    for i in range(5):
+        abi.ar_epoch_flip(e)
+        seq = oracle.epoch_next(seq)
+        assert e.seq == seq and e.parity == (i + 1) % 2
+    e = abi.ar_epoch(0xFFFFFFFE, 1)
+    abi.ar_epoch_flip(e)
+    assert (e.seq, e.parity) == (0xFFFFFFFF, 0)
+    abi.ar_epoch_flip(e)
+    assert (e.seq, e.parity) == (1, 1)        # 0 is skipped
+    for start, k in [(1, 0), (1, 1), (7, 64), (0xFFFFFFF0, 100), (5, 2 ** 32 + 3)]:
+        e = abi.ar_epoch(start, 0)
+        abi.ar_epoch_advance(e, k)
+        s = start
+        for _ in range(k % (2 ** 32 - 1)):
+            s = oracle.epoch_next(s)
+        assert e.seq == s and e.parity == k % 2
+    with pytest.raises(abi.ArError):
+        abi.ar_epoch_flip(abi.ar_epoch(0, 0))
+
+
+FAKE = 1 << 20          # a 256-byte aligned address; never dereferenced
+
+
+def _code(fn, *args):
+    return getattr(abi.raw(), fn)(*args)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("nranks", 0, abi.AR_EINVAL), ("nranks", 17, abi.AR_EINVAL),
+    ("nconsumers", 3, abi.AR_EINVAL), ("count", -1, abi.AR_EINVAL),
+    ("proto", 7, abi.AR_EINVAL), ("reserved", 1, abi.AR_EINVAL),
+])
+def test_desc_checks(field, value, code):
+    d = abi.make_desc(4, 4096, "ll")
+    setattr(d, field, value)
+    assert _code("ar_pack_ll", ctypes.byref(d), FAKE, 4096, FAKE, abi.ar_epoch(1, 0), None) == code
+    assert _code("ar_scratch_bytes", ctypes.byref(d)) == code
+
+
+def test_pack_argument_checks():
+    d = abi.make_desc(4, 4096, "ll")
+    ep = abi.ar_epoch(1, 0)
+    pk = lambda *a: _code("ar_pack_ll", ctypes.byref(d), *a)
+    assert pk(None, 4096, FAKE, ep, None) == abi.AR_EINVAL          # null input
+    assert pk(FAKE + 8, 4096, FAKE, ep, None) == abi.AR_EALIGN      # in not 16-B aligned
+    assert pk(FAKE, 4100, FAKE, ep, None) == abi.AR_EALIGN          # stride % 8
+    assert pk(FAKE, 4000, FAKE, ep, None) == abi.AR_EINVAL          # stride < count
+    assert pk(FAKE, 4096, None, ep, None) == abi.AR_EINVAL          # null scratch
+    assert pk(FAKE, 4096, FAKE + 128, ep, None) == abi.AR_EALIGN    # scratch alignment
+    assert pk(FAKE, 4096, FAKE, abi.ar_epoch(0, 0), None) == abi.AR_EINVAL
+    assert pk(FAKE, 4096, FAKE, abi.ar_epoch(1, 2), None) == abi.AR_EINVAL
+    # the protocol must match the entry point
+    d2 = abi.make_desc(4, 4096, "sentinel")
+    assert _code("ar_pack_ll", ctypes.byref(d2), FAKE, 4096, FAKE, ep, None) == abi.AR_EINVAL
+    assert _code("ar_arm_sentinel", ctypes.byref(d), FAKE, -1, None) == abi.AR_EINVAL
+    assert _code("ar_arm_sentinel", ctypes.byref(d2), FAKE, 2, None) == abi.AR_EINVAL
+    # count 0 is a no-op that succeeds without touching the device
+    d0 = abi.make_desc(4, 0, "ll")
+    assert _code("ar_pack_ll", ctypes.byref(d0), None, 0, None, ep, None) == abi.AR_OK
+
+
+def test_size_limits():
+    big = abi.make_desc(16, 2 ** 29, "ll", nconsumers=16)     # slot 1 GiB -> too big
+    assert _code("ar_scratch_bytes", ctypes.byref(big)) == abi.AR_ESIZE
+
+
+def test_reduce_argument_checks():
+    d = abi.make_desc(8, 4096, "sentinel")
+    ep = abi.ar_epoch(1, 0)
+    rv = lambda *a: _code("ar_reduce_validate", ctypes.byref(d), *a)
+    assert rv(FAKE, FAKE, 4096, ep, None, 0, 0, None) == abi.AR_EINVAL      # null ctrl
+    assert rv(FAKE, FAKE, 4096, ep, FAKE + 4, 0, 0, None) == abi.AR_EALIGN  # ctrl align
+    assert rv(FAKE, FAKE + 2, 4096, ep, FAKE, 0, 0, None) == abi.AR_EALIGN  # out align
+    assert rv(FAKE, FAKE, 4096, ep, FAKE, 0, 4, None) == abi.AR_EINVAL      # bad flag
+
+
+def test_sim_argument_checks():
+    d = abi.make_desc(8, 4096, "ll")
+    base = dict(desc=d, nops=4, inp=FAKE, in_stride=4096, out=FAKE, out_stride=4096,
+                scratch=FAKE, ctrl=FAKE, epoch=abi.ar_epoch(1, 0))
+
+    def run(**over):
+        kw = dict(base)
+        kw.update(over)
+        p = abi.sim_params(kw["desc"], kw["nops"], kw["inp"], kw["in_stride"], kw["out"],
+                           kw["out_stride"], kw["scratch"], kw["ctrl"], kw["epoch"],
+                           waves_per_rank=kw.get("waves_per_rank", 0))
+        return _code("ar_sim_run", ctypes.byref(p), None)
+
+    assert run(nops=0) == abi.AR_EINVAL
+    assert run(ctrl=None) == abi.AR_EINVAL
+    assert run(scratch=FAKE + 16) == abi.AR_EALIGN
+    assert run(out=FAKE + 8) == abi.AR_EALIGN
+    assert run(waves_per_rank=-32) == abi.AR_EINVAL
+    assert run(epoch=abi.ar_epoch(0, 1)) == abi.AR_EINVAL
+
+
+def _table(rows):
+    return abi.cost_table(rows)
+
+
+def test_selector_argmin_and_crossover():
+    # LL cheap fixed cost, twice the bytes; LL128 higher fixed cost, fewer bytes
+    t = _table([dict(nranks=8, alpha_us=[2.0, 3.0, 4.0, 5.0],
+                     beta_us_per_byte=[2e-4, 1.07e-4, 1.5e-4, 1.2e-4])])
+    assert abi.ar_select_protocol(t, 2048, 8)[0] == abi.AR_LL
+    p, pred = abi.ar_select_protocol(t, 4 << 20, 8)
+    assert p == abi.AR_LL128
+    assert math.isclose(pred, 3.0 + 1.07e-4 * (4 << 20))
+    # crossover between LL and LL128 at S = 1 / (2e-4 - 1.07e-4) ~ 10753 bytes
+    assert abi.ar_select_protocol(t, 10000, 8)[0] == abi.AR_LL
+    assert abi.ar_select_protocol(t, 11000, 8)[0] == abi.AR_LL128
+
+
+def test_selector_ties_nearest_and_unavailable():
+    t = _table([
+        dict(nranks=4, alpha_us=[1.0, 1.0, 1.0, 1.0], beta_us_per_byte=[0, 0, 0, 0]),
+        dict(nranks=16, alpha_us=[-1.0, 5.0, 4.0, 9.0], beta_us_per_byte=[0, 0, 0, 0]),
+    ])
+    assert abi.ar_select_protocol(t, 100, 4)[0] == abi.AR_LL          # tie -> lowest id
+    assert abi.ar_select_protocol(t, 100, 10)[0] == abi.AR_LL         # nearest: 4 (tie -> smaller)
+    assert abi.ar_select_protocol(t, 100, 12)[0] == abi.AR_SENTINEL   # nearest: 16, LL unavailable
+    with pytest.raises(abi.ArError):
+        abi.ar_select_protocol(t, -1, 4)
+    with pytest.raises(abi.ArError):
+        abi.ar_select_protocol(t, 100, 17)

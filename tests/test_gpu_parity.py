@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact comparisons (the encoding is integer work, the reduction is the
+fixed-order binary32 sum whose exact result the oracle defines):
+* every encoded slot byte written by ar_pack_* equals the oracle's encoding;
+* ar_reduce_validate outputs equal the oracle's all-reduce for every
+  consumer, over several ops on alternating parities, ragged counts that
+  leave partial tiles, 1..16 ranks, special values (NaN, Inf, -0, denormals);
+* the persistent simulator (ar_sim_run) equals the oracle on every op and
+  every consumer, in share and system mode, for every protocol;
+* failure handling forced from the host: a missing producer times out, an
+  impossible flag is reported corrupt, a skipped re-arm is observable.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from collective_synchronization_amd import abi, buffers, inputs
+
+pytestmark = pytest.mark.gpu
+
+PROTOS = ("ll", "ll128", "sentinel", "barrier")
+TIMEOUT_NS = 2_000_000_000
+
+
+def _x(seed, shape, specials=False):
+    x = inputs.payload(seed, shape, "normal")
+    if specials:
+        x = inputs.inject(x, seed + 7, 1 / 64,
+                          values=(0xFFFF, 0xFFC0, 0xFF81, 0x7FC0, 0x7F80, 0xFF80,
+                                  0x8000, 0x0001, 0x8001))
+    return x
+
+
+SHAPES = [(4, 1, 4096), (3, 3, 1000), (8, 8, 61), (16, 1, 32768), (1, 1, 5),
+          (2, 2, 4099), (5, 1, 60 * 17 + 1), (16, 16, 777)]
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("nranks,ncons,count", SHAPES)
+def test_pack_encoding_bit_exact(proto, nranks, ncons, count):
+    print(f"[pack] {proto} N={nranks} C={ncons} count={count}", flush=True)
+    ws = buffers.Workspace(nranks, count, proto, ncons)
+    x = _x(10 + count, (nranks, count), specials=True)
+    xd, stride = buffers.rows_to_device(x)
+    ws.epoch = abi.ar_epoch(12345, 1)
+    ws.pack(xd, stride)
+    torch.cuda.synchronize()
+    slots = ws.slot_view()
+    E = oracle.encoded_bytes(proto, count)
+    for c in range(ncons):
+        for r in range(nranks):
+            want = oracle.encode(proto, x[r], 12345)
+            assert np.array_equal(slots[c, 1, r, :E], want), (c, r)
+            # nothing written past the encoding, nor to the other parity
+            rest = slots[c, 1, r, E:]
+            other = slots[c, 0, r]
+            fill = 0xFF if proto == "sentinel" else 0
+            assert np.all(rest == fill) and np.all(other == fill)
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("nranks,ncons,count", SHAPES)
+def test_stream_ordered_allreduce(proto, nranks, ncons, count):
+    print(f"[reduce] {proto} N={nranks} C={ncons} count={count}", flush=True)
+    ws = buffers.Workspace(nranks, count, proto, ncons)
+    stride = buffers.row_stride(count)
+    outd = torch.zeros((ncons, stride), dtype=torch.int16, device="cuda")
+    for op in range(4):                    # both parities, twice
+        x = _x(100 * op + count, (nranks, count), specials=(op % 2 == 1))
+        xd, _ = buffers.rows_to_device(x)
+        ws.pack(xd, stride)
+        ws.reduce(outd, stride, timeout_ns=TIMEOUT_NS)
+        torch.cuda.synchronize()
+        assert ws.status() == 0, abi.status_string(ws.status())
+        st, want = oracle.allreduce(x, proto, ws.epoch.seq)
+        assert st == oracle.READY
+        got = buffers.rows_from_device(outd, count, (ncons,))
+        for c in range(ncons):
+            assert np.array_equal(got[c], want), (op, c)
+        ws.flip()
+    if proto == "sentinel":                # every slot read was re-armed
+        assert np.all(ws.slot_view() == 0xFF)
+
+
+def test_missing_producer_times_out():
+    ws = buffers.Workspace(4, 4096, "ll", 1)
+    stride = buffers.row_stride(4096)
+    outd = torch.full((1, stride), 7, dtype=torch.int16, device="cuda")
+    ws.reduce(outd, stride, timeout_ns=2_000_000)       # nothing was packed
+    torch.cuda.synchronize()
+    assert ws.status() == abi.AR_ETIMEOUT
+    assert torch.all(outd == 7)                          # nothing delivered
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+def test_impossible_flag_is_corrupt(proto):
+    ws = buffers.Workspace(4, 1000, proto, 1)
+    stride = buffers.row_stride(1000)
+    xd, _ = buffers.rows_to_device(_x(3, (4, 1000)))
+    ws.epoch = abi.ar_epoch(5, 0)
+    ws.pack(xd, stride)                                  # flags = 5
+    ws.epoch = abi.ar_epoch(9, 0)                        # expects 9 (stale 7)
+    outd = torch.zeros((1, stride), dtype=torch.int16, device="cuda")
+    ws.reduce(outd, stride, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == abi.AR_ECORRUPT
+
+
+def test_sentinel_rearm_is_required():
+    """Without re-arming, a reduce issued before its producers returns the
+    stale payload of two ops before; with re-arming it waits (times out)."""
+    n, count = 4, 2048
+    stride = buffers.row_stride(count)
+    outd = torch.zeros((1, stride), dtype=torch.int16, device="cuda")
+    for rearm in (False, True):
+        ws = buffers.Workspace(n, count, "sentinel", 1)
+        x0 = _x(41, (n, count))
+        xd, _ = buffers.rows_to_device(x0)
+        ws.pack(xd, stride)
+        ws.reduce(outd, stride, timeout_ns=TIMEOUT_NS, rearm=rearm)
+        ws.flip(2)                                       # same parity again
+        ws.reduce(outd, stride, timeout_ns=2_000_000, rearm=rearm)
+        torch.cuda.synchronize()
+        if rearm:
+            assert ws.status() == abi.AR_ETIMEOUT
+        else:
+            assert ws.status() == 0
+            got = buffers.rows_from_device(outd, count, (1,))[0]
+            assert np.array_equal(got, oracle.allreduce(x0, "sentinel", 1)[1])
+
+
+SIM_CASES = [(4, 1, 4096, 4), (4, 4, 4096, 4), (8, 1, 4096, 8), (8, 8, 4099, 6),
+             (16, 16, 32768, 3), (16, 1, 32768, 4), (3, 1, 1000, 5), (2, 2, 60, 7),
+             (1, 1, 100, 3)]
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("nranks,ncons,count,nops", SIM_CASES)
+def test_sim_parity(proto, nranks, ncons, count, nops):
+    print(f"[sim] {proto} N={nranks} C={ncons} count={count} ops={nops}", flush=True)
+    ws = buffers.Workspace(nranks, count, proto, ncons)
+    x = _x(7 * count + nops, (nops, nranks, count), specials=True)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * ncons, stride), dtype=torch.int16, device="cuda")
+    seq0 = ws.epoch.seq
+    for run in range(2):                                 # the epoch carries over
+        ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS)
+        torch.cuda.synchronize()
+        assert ws.status() == 0, abi.status_string(ws.status())
+        got = buffers.rows_from_device(outd, count, (nops, ncons))
+        want = oracle.allreduce_ops(x, proto, seq0)
+        for i in range(nops):
+            for c in range(ncons):
+                assert np.array_equal(got[i, c], want[i]), (run, i, c)
+        outd.zero_()
+    if proto == "sentinel":
+        assert np.all(ws.slot_view() == 0xFF)
+
+
+@pytest.mark.parametrize("proto", ["ll", "sentinel"])
+def test_sim_waves_per_rank_override(proto):
+    nranks, count, nops = 4, 8192, 4
+    ws = buffers.Workspace(nranks, count, proto, 1)
+    x = _x(99, (nops, nranks, count))
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops, stride), dtype=torch.int16, device="cuda")
+    p = ws.sim_params(nops, xd, stride, outd, stride, waves_per_rank=32)
+    geo = abi.ar_sim_geometry(p)
+    assert geo["waves_per_rank"] == 32 and geo["tiles_per_wave"] >= 1
+    ws.sim(nops, xd, stride, outd, stride, waves_per_rank=32, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == 0
+    got = buffers.rows_from_device(outd, count, (nops, 1))
+    want = oracle.allreduce_ops(x, proto)
+    assert np.array_equal(got[:, 0], want)
