@@ -4,8 +4,11 @@
 One step = one decode token's worth of all-reduces for the workload: `nops`
 back-to-back one-shot all-reduces (2 per layer) run by one persistent launch
 of the simulator -- encode, poll + validate, fixed-order reduce, sentinel
-re-arm and epoch flip for every op, N simulated ranks as producer waves on
-other XCDs writing rank 0's receive buffer (one rank's share).  Inputs are
+re-arm and epoch flip for every op.  The N simulated ranks are wave groups
+placed on different XCDs; by default (system mode) every rank runs the full
+per-rank program, consume(op) -> produce(op+1), into its own receive buffer,
+so each op carries the real cross-rank dependency.  Share mode (one receive
+buffer, rank 0's share of the traffic) is reported beside it.  Inputs are
 resident in HBM before the timed region.
 
 Prints ONE JSON line: value = microseconds per all-reduce (lower is better),
@@ -46,15 +49,18 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic_bytes(proto: str, nranks: int, count: int, nconsumers: int) -> int:
-    """HBM bytes one op must move (re-polls not counted):
-    producers read N*S, write E into each of C receive buffers per rank,
-    consumers read N*E each, write S each, and (sentinel) re-arm N*E each."""
+    """HBM bytes one op must move (re-polls not counted).  Every rank reads
+    its payload (N*S); every consumer receives E from each of the N-1 other
+    ranks (written once, read once) and writes S of output; sentinel slots
+    are re-armed after reading (another (N-1)*E per consumer).  A rank's own
+    contribution stays in registers."""
     from collective_synchronization_amd import abi
     S = 2 * count
     E = abi.ar_encoded_bytes(proto, count)
-    b = nranks * S + nconsumers * nranks * E + nconsumers * nranks * E + nconsumers * S
+    recv = nconsumers * (nranks - 1) * E
+    b = nranks * S + 2 * recv + nconsumers * S
     if proto == "sentinel":
-        b += nconsumers * nranks * E
+        b += recv
     return b
 
 
@@ -105,6 +111,63 @@ def load_traffic(kernel_name: str):
     return ent.get("bytes_per_launch")
 
 
+def measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, warmup,
+            waves_per_rank=0, flags=0):
+    """Time `steps` launches of the simulator (one step = nops ops).
+
+    Returns per-launch HIP-event durations (ms, on the launch stream), the
+    wall-clock duration of the timed region (s), geometry and status."""
+    nconsumers = nranks if mode == "system" else 1
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * nconsumers, stride), dtype=torch.int16, device="cuda")
+    ws = buffers.Workspace(nranks, count, proto, nconsumers)
+    stream = torch.cuda.current_stream()
+    kw = dict(timeout_ns=2_000_000_000, waves_per_rank=waves_per_rank, flags=flags)
+    for _ in range(warmup):
+        ws.sim(nops, xd, stride, outd, stride, **kw)
+    torch.cuda.synchronize()
+    if ws.status() != 0:
+        raise RuntimeError(f"device status {abi.status_string(ws.status())}")
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    params = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        if proto == "barrier":
+            ws.reset_ctrl()
+        p = ws.sim_params(nops, xd, stride, outd, stride, **kw)
+        params.append(p)
+        starts[k].record(stream)
+        abi.ar_sim_run(p, stream)
+        ends[k].record(stream)
+        ws.flip(nops)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ws.status() != 0:
+        raise RuntimeError(f"device status {abi.status_string(ws.status())}")
+    launch_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    geo = abi.ar_sim_geometry(params[0])
+    return dict(launch_ms=launch_ms, wall=wall, geo=geo, nconsumers=nconsumers)
+
+
+def summarize(res, proto, nranks, count, nops, steps):
+    import numpy as np
+    launch_ms = res["launch_ms"]
+    b_op = algorithmic_bytes(proto, nranks, count, res["nconsumers"])
+    avg = statistics.mean(launch_ms)
+    return dict(
+        us_per_op=res["wall"] * 1e6 / (steps * nops),
+        ms_per_step=res["wall"] * 1e3 / steps,
+        kernel_us_per_op=statistics.median(launch_ms) * 1e3 / nops,
+        p10=float(np.percentile(launch_ms, 10)) * 1e3 / nops,
+        p90=float(np.percentile(launch_ms, 90)) * 1e3 / nops,
+        avg_launch_us=avg * 1e3,
+        bytes_op=b_op, bytes_launch=b_op * nops,
+        gbs=b_op * nops / (avg * 1e-3) / 1e9,
+    )
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,15 +175,17 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--proto", default="sentinel",
                     choices=["ll", "ll128", "sentinel", "barrier"])
-    ap.add_argument("--mode", default="share", choices=["share", "system"])
+    ap.add_argument("--mode", default="system", choices=["share", "system"])
     ap.add_argument("--nranks", type=int, default=8)
     ap.add_argument("--rows", type=int, default=1)
     ap.add_argument("--hidden", type=int, default=4096)
     ap.add_argument("--nops", type=int, default=64)
     ap.add_argument("--waves-per-rank", type=int, default=0)
+    ap.add_argument("--cooperative", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-floor", action="store_true")
+    ap.add_argument("--no-share", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -129,7 +194,6 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     from collective_synchronization_amd import abi, buffers, inputs
@@ -138,63 +202,31 @@ def main() -> int:
     torch.cuda.set_device(0)
     cfg = CONFIGS[2]
     nranks, count, nops, proto = args.nranks, args.rows * args.hidden, args.nops, args.proto
-    nconsumers = nranks if args.mode == "system" else 1
     default_workload = (nranks, args.rows, args.hidden, nops, proto, args.mode) == \
-        (cfg["nranks"], 1, cfg["hidden"], cfg["nops"], "sentinel", "share")
+        (cfg["nranks"], 1, cfg["hidden"], cfg["nops"], "sentinel", "system")
     workload = cfg["name"] if default_workload else \
         f"n{nranks}_{proto}_{args.rows}x{args.hidden}_{nops}ops_{args.mode}"
+    flags = abi.AR_SIM_COOPERATIVE if args.cooperative else 0
 
     x = inputs.payload(cfg["seed"], (nops, nranks, count), "normal")
-    xd, stride = buffers.rows_to_device(x)
-    outd = torch.zeros((nops * nconsumers, stride), dtype=torch.int16, device="cuda")
-    ws = buffers.Workspace(nranks, count, proto, nconsumers)
-    stream = torch.cuda.current_stream()
-    kw = dict(timeout_ns=2_000_000_000, waves_per_rank=args.waves_per_rank)
-
-    for _ in range(args.warmup):
-        ws.sim(nops, xd, stride, outd, stride, **kw)
-    torch.cuda.synchronize()
-    if ws.status() != 0:
-        print(f"bench.py: device status {abi.status_string(ws.status())}", file=sys.stderr)
+    try:
+        res = measure(torch, abi, buffers, x, proto, nranks, count, nops, args.mode,
+                      args.steps, args.warmup, args.waves_per_rank, flags)
+    except RuntimeError as e:
+        print(f"bench.py: {e}", file=sys.stderr)
         return 1
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        if proto == "barrier":
-            ws.reset_ctrl()
-        starts[k].record(stream)
-        p = ws.sim_params(nops, xd, stride, outd, stride, **kw)
-        abi.ar_sim_run(p, stream)
-        ws.flip(nops)
-        ends[k].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if ws.status() != 0:
-        print(f"bench.py: device status {abi.status_string(ws.status())}", file=sys.stderr)
-        return 1
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride, **kw))
-
-    ms_per_step = wall * 1e3 / args.steps
-    us_per_op = ms_per_step * 1e3 / nops
-    avg_launch_ms = statistics.mean(launch_ms)
-    kernel_us_per_op = statistics.median(launch_ms) * 1e3 / nops
-    b_op = algorithmic_bytes(proto, nranks, count, nconsumers)
-    b_launch = b_op * nops
-    achieved = b_launch / (avg_launch_ms * 1e-3) / 1e9
-    kname = f"k_sim<{abi.proto_id(proto)}>"
+    m = summarize(res, proto, nranks, count, nops, args.steps)
+    kname = ("k_sim_wide" if res["geo"]["kernel"] == "wide" else "k_sim") + \
+        f"<{abi.proto_id(proto)}>"
 
     line = {
         "metric": METRIC,
-        "value": round(us_per_op, 4),
+        "value": round(m["us_per_op"], 4),
         "unit": "us per all-reduce",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(m["ms_per_step"], 5),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -203,27 +235,42 @@ def main() -> int:
         "config": {
             "workload": workload, "nranks": nranks, "shape": [args.rows, args.hidden],
             "protocol": proto, "ops_per_step": nops, "mode": args.mode,
-            "nconsumers": nconsumers, "values": "N(0,1) seed %d" % cfg["seed"],
-            "waves_per_rank": geo["waves_per_rank"], "blocks": geo["blocks"],
+            "nconsumers": res["nconsumers"], "values": "N(0,1) seed %d" % cfg["seed"],
+            "tile_groups_per_rank": res["geo"]["waves_per_rank"],
+            "blocks": res["geo"]["blocks"], "kernel": res["geo"]["kernel"],
+            "launch": "cooperative" if args.cooperative else "ordinary",
             "input_sha256": inputs.sha256(x)[:16],
         },
-        "kernel_us_per_op": round(kernel_us_per_op, 4),
-        "kernel_us_per_op_p10_p90": [
-            round(float(np.percentile(launch_ms, 10)) * 1e3 / nops, 4),
-            round(float(np.percentile(launch_ms, 90)) * 1e3 / nops, 4)],
+        "kernel_us_per_op": round(m["kernel_us_per_op"], 4),
+        "kernel_us_per_op_p10_p90": [round(m["p10"], 4), round(m["p90"], 4)],
         "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
+            "bound": "hbm", "achieved": round(m["gbs"], 3), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(m["gbs"] / HBM_PEAK_GBS, 6),
             "traffic": load_traffic(kname),
-            "kernel": kname, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
-            "algorithmic_bytes_per_launch": b_launch,
-            "algorithmic_bytes_per_op": b_op,
+            "kernel": kname, "avg_launch_us": round(m["avg_launch_us"], 3),
+            "algorithmic_bytes_per_launch": m["bytes_launch"],
+            "algorithmic_bytes_per_op": m["bytes_op"],
         },
     }
 
+    if not args.no_share and args.mode == "system":
+        try:
+            rs = measure(torch, abi, buffers, x, proto, nranks, count, nops, "share",
+                         args.steps, args.warmup, args.waves_per_rank, flags)
+            ms = summarize(rs, proto, nranks, count, nops, args.steps)
+            line["share_mode"] = {
+                "us_per_op": round(ms["us_per_op"], 4),
+                "kernel_us_per_op": round(ms["kernel_us_per_op"], 4),
+                "achieved_gbs": round(ms["gbs"], 3),
+                "frac": round(ms["gbs"] / HBM_PEAK_GBS, 6),
+                "algorithmic_bytes_per_op": ms["bytes_op"],
+            }
+        except RuntimeError as e:
+            line["share_mode"] = {"error": str(e)}
+
     if not args.no_floor:
         fl = measure_floor(torch, abi)
-        fl["frac_of_op"] = round(fl["sol_us"] / kernel_us_per_op, 4)
+        fl["frac_of_op"] = round(fl["sol_us"] / m["kernel_us_per_op"], 4)
         line["floor"] = fl
 
     if not args.no_cpu_baseline:
@@ -233,7 +280,8 @@ def main() -> int:
             "kind": "oracle",
             "sample": (f"{ops} ops of the same workload (N={nranks}, [{args.rows},"
                        f"{args.hidden}], {proto}: encode N + validate/decode N + "
-                       f"fixed-order reduce, single thread, ~{args.cpu_seconds:g} s)"),
+                       f"fixed-order reduce for one receiving rank, single thread, "
+                       f"~{args.cpu_seconds:g} s)"),
         }
 
     print(json.dumps(line), flush=True)

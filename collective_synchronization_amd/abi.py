@@ -22,6 +22,8 @@ AR_OK, AR_EINVAL, AR_EALIGN, AR_ESIZE, AR_ELAUNCH = 0, -1, -2, -3, -4
 AR_ETIMEOUT, AR_ECORRUPT, AR_ENODEV, AR_ECAPACITY = -5, -6, -7, -8
 AR_LL, AR_LL128, AR_SENTINEL, AR_BARRIER, AR_AUTO = 0, 1, 2, 3, 4
 AR_FLAG_REARM = 1
+AR_SIM_COOPERATIVE = 1
+AR_SIM_NARROW = 2
 AR_MAX_RANKS = 16
 PROTO_IDS = {"ll": AR_LL, "ll128": AR_LL128, "sentinel": AR_SENTINEL,
              "barrier": AR_BARRIER}
@@ -44,6 +46,7 @@ class ar_epoch(ctypes.Structure):
 class ar_sim_params(ctypes.Structure):
     _fields_ = [("desc", ar_desc), ("nops", ctypes.c_int32),
                 ("waves_per_rank", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("in_", ctypes.c_void_p), ("in_stride", ctypes.c_int64),
                 ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64),
                 ("scratch", ctypes.c_void_p), ("ctrl", ctypes.c_void_p),
@@ -103,13 +106,14 @@ _SIGS = {
     "ar_sim_run": ([ctypes.POINTER(ar_sim_params), _vp], ctypes.c_int),
     "ar_sim_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
                          ctypes.POINTER(_i32), ctypes.POINTER(_i32),
-                         ctypes.POINTER(_i32)], ctypes.c_int),
+                         ctypes.POINTER(_i32), ctypes.POINTER(_i32)], ctypes.c_int),
     "ar_wallclock_hz": ([ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     "ar_select_protocol": ([ctypes.POINTER(ar_cost_entry), _i32, _i64, _i32,
                             ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)],
                            ctypes.c_int),
     "ar_probe_pingpong": ([_vp, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
     "ar_probe_loadchain": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
+    "ar_probe_litmus": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
     "ar_probe_copy": ([_vp, _vp, _i64, _vp], ctypes.c_int),
     "ar_probe_empty": ([_vp], ctypes.c_int),
 }
@@ -245,10 +249,10 @@ def ar_reduce_validate(desc, scratch, out, out_stride, epoch, ctrl,
 
 def sim_params(desc, nops, inp, in_stride, out, out_stride, scratch, ctrl, epoch,
                timeout_ns=0, waves_per_rank=0, delay_ticks=None, tile_order=None,
-               trace=None) -> ar_sim_params:
-    return ar_sim_params(desc, nops, waves_per_rank, _ptr(inp), in_stride, _ptr(out),
-                         out_stride, _ptr(scratch), _ptr(ctrl), epoch, timeout_ns,
-                         _ptr(delay_ticks), _ptr(tile_order), _ptr(trace))
+               trace=None, flags=0) -> ar_sim_params:
+    return ar_sim_params(desc, nops, waves_per_rank, flags, 0, _ptr(inp), in_stride,
+                         _ptr(out), out_stride, _ptr(scratch), _ptr(ctrl), epoch,
+                         timeout_ns, _ptr(delay_ticks), _ptr(tile_order), _ptr(trace))
 
 
 def ar_sim_run(params: ar_sim_params, stream=None) -> None:
@@ -256,11 +260,13 @@ def ar_sim_run(params: ar_sim_params, stream=None) -> None:
 
 
 def ar_sim_geometry(params: ar_sim_params) -> dict:
-    w, t, tpw, b = _i32(), _i32(), _i32(), _i32()
+    w, t, tpw, b, wide = _i32(), _i32(), _i32(), _i32(), _i32()
     _check(_lib.ar_sim_geometry(ctypes.byref(params), ctypes.byref(w), ctypes.byref(t),
-                                ctypes.byref(tpw), ctypes.byref(b)), "ar_sim_geometry")
+                                ctypes.byref(tpw), ctypes.byref(b), ctypes.byref(wide)),
+           "ar_sim_geometry")
     return {"waves_per_rank": w.value, "tiles_per_rank": t.value,
-            "tiles_per_wave": tpw.value, "blocks": b.value}
+            "tiles_per_wave": tpw.value, "blocks": b.value,
+            "kernel": "wide" if wide.value else "narrow"}
 
 
 def ar_wallclock_hz() -> float:
@@ -299,6 +305,11 @@ def ar_probe_pingpong(work, iters, xcd_a, xcd_b, result, stream=None) -> None:
 def ar_probe_loadchain(work, nbytes, iters, result, stream=None) -> None:
     _check(_lib.ar_probe_loadchain(_ptr(work), nbytes, iters, _ptr(result),
                                    _stream(stream)), "ar_probe_loadchain")
+
+
+def ar_probe_litmus(work, iters, xcd_a, xcd_b, kind, result, stream=None) -> None:
+    _check(_lib.ar_probe_litmus(_ptr(work), iters, xcd_a, xcd_b, kind, _ptr(result),
+                                _stream(stream)), "ar_probe_litmus")
 
 
 def ar_probe_copy(src, dst, nbytes, stream=None) -> None:

@@ -96,10 +96,11 @@ class Workspace:
 
     # -------------------------------------------------------- simulator --
     def sim_params(self, nops, x_dev, in_stride, out_dev, out_stride, timeout_ns=0,
-                   waves_per_rank=0, delay_ticks=None, tile_order=None, trace=None):
+                   waves_per_rank=0, delay_ticks=None, tile_order=None, trace=None,
+                   flags=0):
         return abi.sim_params(self.desc, nops, x_dev, in_stride, out_dev, out_stride,
                               self.scratch, self.ctrl, self.epoch, timeout_ns,
-                              waves_per_rank, delay_ticks, tile_order, trace)
+                              waves_per_rank, delay_ticks, tile_order, trace, flags)
 
     def sim(self, nops, x_dev, in_stride, out_dev, out_stride, stream=None, **kw) -> None:
         """nops back-to-back ops in one persistent launch; advances the epoch."""

@@ -71,14 +71,50 @@ __device__ __forceinline__ void st8(rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpAgent);
 }
 
+// Ordering between device-scope coherent accesses.
+//
+// Every access that another XCD observes in this library (slots, flags,
+// counters, progress words) is an sc1 access, which bypasses the per-XCD
+// caches for coherence.  A full agent-scope fence adds an L2 writeback
+// (release) or invalidate (acquire) of the whole XCD cache, which only
+// matters for non-sc1 data; for sc1-only traffic what orders a later access
+// after an earlier one is that the earlier one has completed, i.e. its
+// acknowledgement has returned: s_waitcnt vmcnt(0).  The three orderings
+// the protocols need -- data before flag (LL128, barrier), flag before data
+// (LL128 consumer), re-arm before the next op's stores (sentinel dual
+// buffer) -- are exercised across XCD pairs by ar_probe_litmus, which a GPU
+// test runs.  AR_FORMAL_FENCES=1 selects the full agent-scope fences instead
+// (the compiler's sequence, with the L2 writeback/invalidate).
+#ifndef AR_FORMAL_FENCES
+#define AR_FORMAL_FENCES 0
+#endif
+
+__device__ __forceinline__ void wait_vm() {
+  compiler_barrier();
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), other counters untouched
+  compiler_barrier();
+}
+
 __device__ __forceinline__ void fence_release() {
+#if AR_FORMAL_FENCES
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#else
+  wait_vm();
+#endif
 }
 __device__ __forceinline__ void fence_acquire() {
+#if AR_FORMAL_FENCES
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#else
+  wait_vm();
+#endif
 }
 __device__ __forceinline__ void fence_acq_rel() {
+#if AR_FORMAL_FENCES
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+#else
+  wait_vm();
+#endif
 }
 
 __device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {

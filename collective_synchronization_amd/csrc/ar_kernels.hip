@@ -19,6 +19,16 @@ namespace ar {
 constexpr int kBlock = 256;              // 4 waves
 constexpr int kWavesPerBlock = kBlock / kWave;
 
+// Waves per workgroup of the simulator.  One wave per workgroup spreads a
+// rank's waves over as many CUs as possible: each CU's path to the L2 then
+// carries one wave's write-through stores instead of four.
+#ifndef AR_SIM_WAVES_PER_BLOCK
+#define AR_SIM_WAVES_PER_BLOCK 1
+#endif
+constexpr int kSimWPB = AR_SIM_WAVES_PER_BLOCK;
+constexpr int kSimBlock = kSimWPB * kWave;
+constexpr int kSimWavesPerQ = 8 * kSimWPB;    // waves of one rank per Q step
+
 // ================================================================ kernels ==
 
 struct PackArgs {
@@ -44,11 +54,11 @@ __global__ __launch_bounds__(kBlock) void k_pack(PackArgs a) {
   const uint32_t cstride = 2u * (uint32_t)a.nranks * a.slot_bytes;
   const uint32_t dst0 = (a.parity * (uint32_t)a.nranks + (uint32_t)r) * a.slot_bytes;
   const uint16_t* row = a.in + (int64_t)r * a.in_stride;
-  produce_data<P>(rs, dst0, cstride, a.nconsumers, row, a.count, tile, a.E,
+  produce_data<P>(rs, dst0, cstride, a.nconsumers, -1, row, a.count, tile, a.E,
                   a.seq, lane);
   if (P == kLL128) {
     fence_release();
-    produce_flags(rs, dst0, cstride, a.nconsumers, tile, a.E, a.seq, lane);
+    produce_flags(rs, dst0, cstride, a.nconsumers, -1, tile, a.E, a.seq, lane);
   }
 }
 
@@ -144,8 +154,16 @@ __device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
 // is rotated by g so that the producer of a tile and the consumer that
 // reads it sit on different XCDs, and the same wr owns the same tiles
 // {wr, wr + W, ...} in every rank.
+//
+// A rank's own contribution never goes through memory: its consumer takes
+// the encoded chunk from registers and its producer skips its own buffer.
+// When a wave owns a single tile (the small-message case) the op loop is
+// software-pipelined: the next op's payload is loaded while this op is
+// polled, and this op's output is stored after the next op's stores are
+// out, so neither input load nor output store sits between one op's
+// validation and the next op's transmission.
 template <int P, int NMAX, bool SHARE>
-__global__ __launch_bounds__(kBlock) void k_sim(SimArgs a) {
+__global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int b = blockIdx.x;
@@ -156,11 +174,13 @@ __global__ __launch_bounds__(kBlock) void k_sim(SimArgs a) {
   if (g >= a.nranks) return;
   const int rot = SHARE ? (g == 0 ? 0 : 1 + (g - 1) % 7) : (g & 7);
   const int xr = (x - rot) & 7;
-  const int wr = (qq * 8 + xr) * kWavesPerBlock + wave;
+  const int wr = (qq * 8 + xr) * kSimWPB + wave;
   if (wr >= a.T) return;
   const int mine = (a.T - 1 - wr) / a.W + 1;
   const bool consumer = SHARE ? (g == 0) : true;
   const int cself = SHARE ? 0 : g;
+  const int skip = consumer ? cself : -1;       // own buffer, fed from registers
+  const bool fast = (mine == 1) && (P != kBarrier);
 
   const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
   const uint32_t N = (uint32_t)a.nranks;
@@ -169,12 +189,18 @@ __global__ __launch_bounds__(kBlock) void k_sim(SimArgs a) {
   uint32_t* const arrive = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlArrive;
   uint32_t* const done = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlDone;
   const int tstride = 2 * a.nranks;
+  const int64_t op_rows = a.nranks;
 
   if (a.trace && lane == 0)
     __hip_atomic_fetch_min(reinterpret_cast<unsigned long long*>(a.trace) +
                                (int64_t)a.nops * tstride,
                            (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+
+  uint32_t wnext[4] = {0u, 0u, 0u, 0u};     // fast path: next op's payload
+  u32x4 v[NMAX];                            // fast path: last validated op
+  bool out_pending = false;
+  if (fast) load_chunk<P>(a.in + (int64_t)g * a.in_stride, a.count, wr, lane, wnext);
 
   uint32_t seq = a.seq0;
   uint32_t par = a.parity0;
@@ -195,8 +221,8 @@ __global__ __launch_bounds__(kBlock) void k_sim(SimArgs a) {
       Waiter wt(a.timeout_ticks, a.ctrl);
       const uint32_t prev = seq_prev(seq);
       while (true) {
-        const uint32_t v = ld_agent_u32(progress + wr);
-        if (v == prev || v == seq) break;
+        const uint32_t pv = ld_agent_u32(progress + wr);
+        if (pv == prev || pv == seq) break;
         if (!wt.again(lane)) return;
       }
       fence_acquire();
@@ -213,27 +239,46 @@ __global__ __launch_bounds__(kBlock) void k_sim(SimArgs a) {
       }
     }
 
-    // ---- produce(op): slot g of parity pp in every consumer's buffer ----
-    const uint16_t* row = a.in + ((int64_t)op * a.nranks + g) * a.in_stride;
+    // ---- produce(op): slot g of parity pp in every other consumer's buffer
+    const uint16_t* row = a.in + ((int64_t)op * op_rows + g) * a.in_stride;
     const uint32_t dst0 = (pp * N + (uint32_t)g) * a.slot_bytes;
-    const uint16_t* ord = a.order ? a.order + ((int64_t)op * a.nranks + g) * a.TPW : nullptr;
-    for (int j = 0; j < a.TPW; ++j) {
-      const int k = ord ? (int)ord[j] : j;
-      if (k >= mine) continue;
-      produce_data<P>(rs, dst0, cstride, a.nconsumers, row, a.count,
-                      wr + k * a.W, a.E, seq, lane);
-    }
-    if (P == kLL128) {
-      fence_release();
-      for (int k = 0; k < mine; ++k)
-        produce_flags(rs, dst0, cstride, a.nconsumers, wr + k * a.W, a.E, seq,
-                      lane);
-    }
-    if (P == kBarrier) {
-      fence_release();
-      if (lane == 0)
-        __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    u32x4 own_v = u32x4{0u, 0u, 0u, 0u};
+    if (fast) {
+      own_v = encode_words<P>(wnext, lane, seq);
+      store_chunk<P>(rs, dst0, cstride, a.nconsumers, skip, wr, a.E, lane, own_v);
+      if (P == kLL128) {
+        fence_release();
+        produce_flags(rs, dst0, cstride, a.nconsumers, skip, wr, a.E, seq, lane);
+      }
+      if (out_pending) {   // previous op's output, now that this op is sent
+        reduce_store_tile<P, NMAX>(
+            v, a.nranks, wr, a.E, lane,
+            a.out + ((int64_t)(op - 1) * a.nconsumers + cself) * a.out_stride, a.count);
+        out_pending = false;
+      }
+      if (op + 1 < a.nops)
+        load_chunk<P>(row + op_rows * a.in_stride, a.count, wr, lane, wnext);
+    } else {
+      const uint16_t* ord =
+          a.order ? a.order + ((int64_t)op * a.nranks + g) * a.TPW : nullptr;
+      for (int j = 0; j < a.TPW; ++j) {
+        const int k = ord ? (int)ord[j] : j;
+        if (k >= mine) continue;
+        produce_data<P>(rs, dst0, cstride, a.nconsumers, skip, row, a.count,
+                        wr + k * a.W, a.E, seq, lane);
+      }
+      if (P == kLL128) {
+        fence_release();
+        for (int k = 0; k < mine; ++k)
+          produce_flags(rs, dst0, cstride, a.nconsumers, skip, wr + k * a.W, a.E,
+                        seq, lane);
+      }
+      if (P == kBarrier) {
+        fence_release();
+        if (lane == 0)
+          __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     if (a.trace) {
       fence_release();   // stores acknowledged before the timestamp
@@ -246,35 +291,210 @@ __global__ __launch_bounds__(kBlock) void k_sim(SimArgs a) {
 
     // ---- consume(op) ----
     if (consumer) {
-      if (P == kBarrier) {
-        Waiter wt(a.timeout_ticks, a.ctrl);
-        if (!wait_geq(arrive, (uint32_t)(op + 1) * a.p_total, wt, lane)) return;
-        fence_acquire();
-      }
-      uint16_t* orow = a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride;
       const uint32_t src0 = ((uint32_t)cself * 2u + pp) * N * a.slot_bytes;
-      for (int k = 0; k < mine; ++k) {
-        if (consume_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, wr + k * a.W,
-                                  a.E, seq, stale, true, orow, a.count, a.ctrl,
-                                  a.timeout_ticks, lane) != 0)
+      if (fast) {
+        if (poll_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, wr, a.E, seq,
+                               stale, true, g, own_v, a.ctrl, a.timeout_ticks,
+                               lane, v) != 0)
           return;
-      }
-      if (P == kBarrier) {
-        fence_release();
-        if (lane == 0)
-          __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+        out_pending = true;
       } else {
-        // every read (and re-arm) of this op completes before the next
-        // op's stores are issued
-        fence_acq_rel();
+        if (P == kBarrier) {
+          Waiter wt(a.timeout_ticks, a.ctrl);
+          if (!wait_geq(arrive, (uint32_t)(op + 1) * a.p_total, wt, lane)) return;
+          fence_acquire();
+        }
+        uint16_t* orow = a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride;
+        u32x4 vt[NMAX];
+        for (int k = 0; k < mine; ++k) {
+          const int tile = wr + k * a.W;
+          const u32x4 mine_v = encode_chunk<P>(row, a.count, tile, lane, seq);
+          if (poll_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, tile, a.E, seq,
+                                 stale, true, g, mine_v, a.ctrl, a.timeout_ticks,
+                                 lane, vt) != 0)
+            return;
+          reduce_store_tile<P, NMAX>(vt, a.nranks, tile, a.E, lane, orow, a.count);
+        }
+        if (P == kBarrier) {
+          fence_release();
+          if (lane == 0)
+            __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
+      // SENTINEL: the re-arm stores of this op complete before any store of
+      // the next op (whose arrival licenses peers to refill this parity).
+      // LL/LL128 read only: their loads have returned (the values were used).
+      if (P == kSentinel) fence_release();
       if (a.trace && lane == 0)
         __hip_atomic_fetch_max(
             reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride +
                 a.nranks + cself,
             (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    seq = seq_next(seq);
+    par ^= 1u;
+  }
+  if (out_pending)
+    reduce_store_tile<P, NMAX>(
+        v, a.nranks, wr, a.E, lane,
+        a.out + ((int64_t)(a.nops - 1) * a.nconsumers + cself) * a.out_stride, a.count);
+}
+
+// Wide simulator for latency-bound sizes: one workgroup of nranks waves per
+// (rank g, tile group tg); wave w is paired with peer w.  Wave w sends this
+// rank's chunk to consumer w and, in a consumer, polls peer w's chunk, so
+// every wave carries one store stream and one poll stream.  Validated chunks
+// are staged in LDS (double-buffered by tile iteration); after one
+// workgroup barrier the wave of the rank itself (the "own" wave, whose
+// contribution never leaves registers) reduces in fixed rank order.
+// Sentinel: the wave that re-arms peer w's slot is the wave that next sends
+// to peer w, so waiting for its own stores orders re-arm before refill.
+// Share mode: only rank 0 consumes; a producer rank's workgroup keeps its
+// wave 0, which takes the dual-buffer licence from rank 0's progress word.
+// Placement: workgroup (g, tg) sits on XCD (tg + rot(g)) mod 8 as in k_sim.
+template <int P, int NMAX, bool SHARE>
+__global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
+  __shared__ u32x4 lds[2][NMAX][kWave];
+  __shared__ int lds_err;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  const int x = b & 7;
+  const int q = b >> 3;
+  const int g = q / a.Q;
+  const int qq = q - g * a.Q;
+  if (g >= a.nranks) return;                       // whole workgroup
+  const int rot = SHARE ? (g == 0 ? 0 : 1 + (g - 1) % 7) : (g & 7);
+  const int tg = qq * 8 + ((x - rot) & 7);
+  if (tg >= a.T) return;                           // whole workgroup
+  const int G = a.W;
+  const int mine = (a.T - 1 - tg) / G + 1;
+  const bool consumer = SHARE ? (g == 0) : true;
+  if (!consumer && w != 0) return;                 // producer-only rank: one wave
+  const int cself = SHARE ? 0 : g;
+  const bool sender = SHARE ? (g != 0) : (w != g);
+  const int dst_c = SHARE ? 0 : w;
+  const bool own = consumer && w == g;
+  const bool poller = consumer && w != g;
+
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t N = (uint32_t)a.nranks;
+  uint32_t* const progress = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlProgress;
+  const int tstride = 2 * a.nranks;
+  const int64_t op_rows = a.nranks;
+  const bool pipelined = mine == 1;
+  if (threadIdx.x == 0) lds_err = 0;
+  if (consumer) __syncthreads();
+
+  if (a.trace && lane == 0 && w == 0)
+    __hip_atomic_fetch_min(reinterpret_cast<unsigned long long*>(a.trace) +
+                               (int64_t)a.nops * tstride,
+                           (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+
+  uint32_t wnext[4] = {0u, 0u, 0u, 0u};
+  const bool needs_input = sender || own;
+  if (pipelined && needs_input)
+    load_chunk<P>(a.in + (int64_t)g * a.in_stride, a.count, tg, lane, wnext);
+
+  uint32_t seq = a.seq0;
+  uint32_t par = a.parity0;
+  int buf = 0;
+  for (int op = 0; op < a.nops; ++op) {
+    const uint32_t stale = seq_prev(seq_prev(seq));
+    const uint32_t pp = par;
+    const uint16_t* row = a.in + ((int64_t)op * op_rows + g) * a.in_stride;
+
+    if (SHARE && !consumer && op >= 2) {
+      Waiter wt(a.timeout_ticks, a.ctrl);
+      const uint32_t prev = seq_prev(seq);
+      while (true) {
+        const uint32_t pv = ld_agent_u32(progress + tg);
+        if (pv == prev || pv == seq) break;
+        if (!wt.again(lane)) return;
+      }
+      fence_acquire();
+    }
+    if (SHARE && consumer && w == 0 && lane == 0) st_agent_u32(progress + tg, seq);
+    if (sender && a.delay) {
+      const uint32_t d = a.delay[(int64_t)op * a.nranks + g];
+      if (d) {
+        const uint64_t t0 = now_ticks();
+        while (now_ticks() - t0 < (uint64_t)d) __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    // sentinel: this wave's re-arm stores of the previous op complete before
+    // its next store to the same peer
+    if (P == kSentinel && !SHARE && sender) fence_release();
+
+    const uint32_t dst0 = ((uint32_t)dst_c * 2u * N + pp * N + (uint32_t)g) * a.slot_bytes;
+    const uint32_t src0 = ((uint32_t)cself * 2u * N + pp * N) * a.slot_bytes;
+    for (int k = 0; k < mine; ++k) {
+      const int tile = tg + k * G;
+      const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+      const bool active = loff < a.E;
+      u32x4 mine_v = u32x4{0u, 0u, 0u, 0u};
+      if (needs_input) {
+        if (pipelined) {
+          mine_v = encode_words<P>(wnext, lane, seq);
+          if (op + 1 < a.nops)
+            load_chunk<P>(row + op_rows * a.in_stride, a.count, tile, lane, wnext);
+        } else {
+          mine_v = encode_chunk<P>(row, a.count, tile, lane, seq);
+        }
+      }
+      // ---- send ----
+      if (sender) {
+        store_chunk<P>(rs, dst0, 0u, 1, -1, tile, a.E, lane, mine_v);
+        if (P == kLL128) {
+          fence_release();
+          produce_flags(rs, dst0, 0u, 1, -1, tile, a.E, seq, lane);
+        }
+        if (a.trace) {
+          fence_release();
+          if (lane == 0)
+            __hip_atomic_fetch_max(
+                reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride + g,
+                (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+                __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (!consumer) continue;
+      // ---- receive: peer w's chunk (or the own chunk) into LDS row w ----
+      if (poller) {
+        u32x4 got;
+        const int st = poll_chunk<P>(rs, src0 + (uint32_t)w * a.slot_bytes + loff, active,
+                                     seq, stale, true, a.ctrl, a.timeout_ticks, lane, got);
+        if (st != 0) {
+          if (lane == 0) lds_err = 1;
+        } else {
+          if (P == kSentinel && SHARE) fence_release();   // re-arm before the progress word
+          lds[buf][w][lane] = got;
+        }
+      } else {
+        lds[buf][w][lane] = mine_v;
+      }
+      __syncthreads();
+      if (lds_err) return;                         // whole workgroup
+      // ---- reduce in rank order (own wave) ----
+      if (own) {
+        u32x4 v[NMAX];
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r)
+          v[r] = (r < a.nranks) ? lds[buf][r][lane] : u32x4{0u, 0u, 0u, 0u};
+        reduce_store_tile<P, NMAX>(
+            v, a.nranks, tile, a.E, lane,
+            a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride, a.count);
+        if (a.trace && lane == 0)
+          __hip_atomic_fetch_max(
+              reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride +
+                  a.nranks + cself,
+              (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+              __HIP_MEMORY_SCOPE_AGENT);
+      }
+      buf ^= 1;
     }
     seq = seq_next(seq);
     par ^= 1u;
@@ -314,6 +534,90 @@ __global__ void k_pingpong(uint32_t* work, int32_t iters, int32_t xa,
         if (now_ticks() > deadline) { res[4] = 2; return; }
       }
       st_agent_u32(fb, k);
+    }
+  }
+}
+
+// Ordering litmus between a writer wave (block xa) and a reader wave (block
+// xb); see ar_probe_litmus in ar.h for the three kinds.
+__global__ void k_litmus(uint8_t* work, int32_t iters, int32_t xa, int32_t xb,
+                         int32_t kind, uint64_t* res, uint64_t timeout_ticks) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  uint32_t* const flag = reinterpret_cast<uint32_t*>(work);         // line 0
+  uint32_t* const ack = reinterpret_cast<uint32_t*>(work + 128);    // line 1
+  uint32_t* const wrote = reinterpret_cast<uint32_t*>(work + 256);  // line 2
+  const rsrc_t rs = make_rsrc(work, 4096);
+  const uint32_t blk = 1024;                                        // 1 KiB block
+  const uint64_t deadline = now_ticks() + timeout_ticks;
+  if (b == xa) {
+    if (lane == 0) res[2] = xcc_id();
+    for (uint32_t k = 1; k <= (uint32_t)iters; ++k) {
+      if (kind == 0) {
+        st16(rs, blk + lane * 16u, u32x4{k, k, k, k});
+        fence_release();
+        if (lane == 0) st_agent_u32(flag, k);
+      } else if (kind == 1) {
+        st16(rs, blk + lane * 16u, u32x4{k, k, k, k});
+      } else {
+        if (lane == 0) {
+          while (ld_agent_u32(ack) != k - 1u) {
+            if (now_ticks() > deadline) { res[4] = 1; return; }
+          }
+          fence_acquire();
+          __builtin_amdgcn_raw_buffer_store_b32(k, rs, blk, 0, kCpAgent);
+          fence_release();
+          st_agent_u32(wrote, k);
+        }
+      }
+    }
+  } else if (b == xb) {
+    if (lane == 0) res[3] = xcc_id();
+    uint64_t viol = 0, obs = 0, second = 0;
+    uint32_t last = 0;
+    if (kind == 0) {
+      while (true) {
+        const uint32_t f = ld_agent_u32(flag);
+        fence_acquire();
+        const u32x4 d = ld16(rs, blk + lane * 16u);
+        const bool bad = d.x < f || d.y < f || d.z < f || d.w < f;
+        viol += __popcll(__ballot(bad));
+        ++obs;
+        last = f;
+        if (f == (uint32_t)iters) break;
+        if (now_ticks() > deadline) { if (lane == 0) res[4] = 2; break; }
+      }
+    } else if (kind == 1) {
+      while (true) {
+        const u32x4 d = ld16(rs, blk + lane * 16u);
+        viol += __popcll(__ballot(d.x != d.y || d.z != d.w));
+        second += __popcll(__ballot(d.x != d.z));
+        ++obs;
+        last = d.x;
+        if (__ballot(d.x != (uint32_t)iters || d.z != (uint32_t)iters) == 0ull) break;
+        if (now_ticks() > deadline) { if (lane == 0) res[4] = 2; break; }
+      }
+    } else if (lane == 0) {
+      for (uint32_t k = 1; k <= (uint32_t)iters; ++k) {
+        while (ld_agent_u32(wrote) != k) {
+          if (now_ticks() > deadline) { res[4] = 2; goto out; }
+        }
+        fence_acquire();
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rs, blk, 0, kCpAgent);
+        viol += (w != k);
+        ++obs;
+        last = w;
+        __builtin_amdgcn_raw_buffer_store_b32(0u, rs, blk, 0, kCpAgent);   // re-arm
+        fence_release();
+        st_agent_u32(ack, k);
+      }
+    }
+  out:
+    if (lane == 0) {
+      res[0] = viol;
+      res[1] = obs;
+      res[5] = last;
+      res[6] = second;
     }
   }
 }
@@ -444,13 +748,20 @@ static int map_hip(hipError_t e) {
 
 // Launch with the runtime's own return code (not the sticky last error,
 // which may hold an unrelated earlier failure of the calling thread).
+template <typename... KArgs>
+static hipError_t launch_typed(void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                               hipStream_t s, KArgs... args) {
+  void* argv[sizeof...(KArgs) + 1] = {static_cast<void*>(&args)..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
+                         argv, 0, s);
+}
+
+// Every argument is converted to the kernel's own parameter type first.
 template <typename... KArgs, typename... Args>
 static hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block,
                          hipStream_t s, Args... args) {
   static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel arity");
-  void* argv[] = {static_cast<void*>(&args)...};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
-                         argv, 0, s);
+  return launch_typed<KArgs...>(kernel, grid, block, s, static_cast<KArgs>(args)...);
 }
 
 template <int P>
@@ -509,88 +820,124 @@ static hipError_t launch_reduce_n(const ReduceArgs& a, int blocks, hipStream_t s
 }
 
 template <int P, int NMAX, bool SHARE>
-static hipError_t launch_sim(const SimArgs& a, int blocks, hipStream_t s) {
+static hipError_t launch_sim(const SimArgs& a, int blocks, bool coop, bool wide,
+                             hipStream_t s) {
   SimArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchCooperativeKernel(
-      reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>), dim3(blocks),
-      dim3(kBlock), args, 0, s);
+  const void* fn = wide ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE>)
+                        : reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>);
+  const dim3 block(wide ? kWave * a.nranks : kSimBlock);
+  if (coop) return hipLaunchCooperativeKernel(fn, dim3(blocks), block, args, 0, s);
+  return hipLaunchKernel(fn, dim3(blocks), block, args, 0, s);
 }
 
 template <int P, int NMAX, bool SHARE>
-static int occupancy_of() {
+static int occupancy_of(bool wide, int nranks) {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &nb, reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>), kBlock, 0) !=
-      hipSuccess)
+  const void* fn = wide ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE>)
+                        : reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>);
+  const int threads = wide ? kWave * nranks : kSimBlock;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, 0) != hipSuccess)
     return 0;
   return nb;
 }
 
 template <int P>
-static hipError_t dispatch_sim_p(const SimArgs& a, bool share, int blocks,
-                                 hipStream_t s) {
+static hipError_t dispatch_sim_p(const SimArgs& a, bool share, int blocks, bool coop,
+                                 bool wide, hipStream_t s) {
   if (a.nranks <= 4)
-    return share ? launch_sim<P, 4, true>(a, blocks, s) : launch_sim<P, 4, false>(a, blocks, s);
+    return share ? launch_sim<P, 4, true>(a, blocks, coop, wide, s)
+                 : launch_sim<P, 4, false>(a, blocks, coop, wide, s);
   if (a.nranks <= 8)
-    return share ? launch_sim<P, 8, true>(a, blocks, s) : launch_sim<P, 8, false>(a, blocks, s);
-  return share ? launch_sim<P, 16, true>(a, blocks, s) : launch_sim<P, 16, false>(a, blocks, s);
+    return share ? launch_sim<P, 8, true>(a, blocks, coop, wide, s)
+                 : launch_sim<P, 8, false>(a, blocks, coop, wide, s);
+  return share ? launch_sim<P, 16, true>(a, blocks, coop, wide, s)
+               : launch_sim<P, 16, false>(a, blocks, coop, wide, s);
 }
 
 template <int P>
-static int occupancy_p(int nranks, bool share) {
-  if (nranks <= 4) return share ? occupancy_of<P, 4, true>() : occupancy_of<P, 4, false>();
-  if (nranks <= 8) return share ? occupancy_of<P, 8, true>() : occupancy_of<P, 8, false>();
-  return share ? occupancy_of<P, 16, true>() : occupancy_of<P, 16, false>();
+static int occupancy_p(int nranks, bool share, bool wide) {
+  if (nranks <= 4)
+    return share ? occupancy_of<P, 4, true>(wide, nranks) : occupancy_of<P, 4, false>(wide, nranks);
+  if (nranks <= 8)
+    return share ? occupancy_of<P, 8, true>(wide, nranks) : occupancy_of<P, 8, false>(wide, nranks);
+  return share ? occupancy_of<P, 16, true>(wide, nranks) : occupancy_of<P, 16, false>(wide, nranks);
 }
 
-static int sim_occupancy(int proto, int nranks, bool share) {
+static int sim_occupancy(int proto, int nranks, bool share, bool wide) {
   switch (proto) {
-    case kLL: return occupancy_p<kLL>(nranks, share);
-    case kLL128: return occupancy_p<kLL128>(nranks, share);
-    case kSentinel: return occupancy_p<kSentinel>(nranks, share);
-    default: return occupancy_p<kBarrier>(nranks, share);
+    case kLL: return occupancy_p<kLL>(nranks, share, wide);
+    case kLL128: return occupancy_p<kLL128>(nranks, share, wide);
+    case kSentinel: return occupancy_p<kSentinel>(nranks, share, wide);
+    default: return occupancy_p<kBarrier>(nranks, share, wide);
   }
 }
 
 struct SimGeom {
   int32_t W, Q, T, TPW, blocks;
+  bool wide;
 };
 
-static int sim_geometry(const ar_sim_params* p, const DeviceInfo& di,
-                        SimGeom* g) {
+// The wide kernel (a workgroup of one wave per peer) serves LL, LL128 and
+// SENTINEL unless AR_SIM_NARROW asks for the one-wave-per-tile kernel; the
+// barrier baseline always uses the latter.
+static bool sim_is_wide(const ar_sim_params* p) {
+  return p->desc.proto != kBarrier && (p->flags & AR_SIM_NARROW) == 0;
+}
+
+static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wide,
+                           SimGeom* g) {
   const ar_desc* d = &p->desc;
   const int64_t E = encoded_bytes(d->proto, d->count);
   const int64_t T = ceil_div64(E, kTileBytes);
   if (T <= 0) {
-    *g = SimGeom{0, 0, 0, 0, 0};
+    *g = SimGeom{0, 0, 0, 0, 0, wide};
     return AR_OK;
   }
   if (T > (int64_t(1) << 24)) return AR_ESIZE;
   const bool share = d->nconsumers == 1 && d->nranks > 1;
-  const int occ = sim_occupancy(d->proto, d->nranks, share);
+  const int occ = sim_occupancy(d->proto, d->nranks, share, wide);
   if (occ <= 0) return AR_ELAUNCH;
   const int64_t capacity = (int64_t)occ * di.cus;
   const int64_t qmax_dev = capacity / (8 * (int64_t)d->nranks);
-  const int64_t qmax = qmax_dev < kCtrlMaxProgress / 32 ? qmax_dev : kCtrlMaxProgress / 32;
+  const int64_t per_q = wide ? 8 : kSimWavesPerQ;   // tile groups / waves per Q
+  const int64_t qcap = kCtrlMaxProgress / per_q;
+  const int64_t qmax = qmax_dev < qcap ? qmax_dev : qcap;
   if (qmax < 1) return AR_ECAPACITY;
   int64_t Q;
   if (p->waves_per_rank > 0) {
-    if (p->waves_per_rank % 32) return AR_EINVAL;
-    Q = p->waves_per_rank / 32;
+    if (p->waves_per_rank % per_q) return AR_EINVAL;
+    Q = p->waves_per_rank / per_q;
     if (Q > qmax) return AR_ECAPACITY;
   } else {
-    Q = ceil_div64(T, 32);
+    Q = ceil_div64(T, per_q);
     if (Q > qmax) Q = qmax;
     if (Q < 1) Q = 1;
   }
-  const int64_t W = 32 * Q;
+  const int64_t W = per_q * Q;
   g->W = (int32_t)W;
   g->Q = (int32_t)Q;
   g->T = (int32_t)T;
   g->TPW = (int32_t)ceil_div64(T, W);
   g->blocks = (int32_t)(8 * Q * d->nranks);
+  g->wide = wide;
   return AR_OK;
+}
+
+// Kernel choice: the wide kernel when every one of its workgroups owns a
+// single tile (the latency-bound sizes); otherwise, or with AR_SIM_NARROW,
+// or for the barrier baseline, the one-wave-per-tile kernel.
+static int sim_geometry(const ar_sim_params* p, const DeviceInfo& di, SimGeom* g) {
+  if (sim_is_wide(p)) {
+    SimGeom gw;
+    const int rc = sim_geometry_as(p, di, true, &gw);
+    if (rc == AR_OK && gw.TPW <= 1) {
+      *g = gw;
+      return AR_OK;
+    }
+    if (rc != AR_OK && rc != AR_ECAPACITY && rc != AR_EINVAL) return rc;
+  }
+  return sim_geometry_as(p, di, false, g);
 }
 
 static int check_sim(const ar_sim_params* p) {
@@ -600,6 +947,8 @@ static int check_sim(const ar_sim_params* p) {
   const ar_desc* d = &p->desc;
   if (p->nops < 1) return AR_EINVAL;
   if (p->waves_per_rank < 0) return AR_EINVAL;
+  if ((p->flags & ~(AR_SIM_COOPERATIVE | AR_SIM_NARROW)) != 0 || p->reserved != 0)
+    return AR_EINVAL;
   if (p->epoch.parity > 1u || p->epoch.seq == 0u) return AR_EINVAL;
   rc = check_rows(p->in, p->in_stride, d->count);
   if (rc) return rc;
@@ -787,7 +1136,7 @@ int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
 
 int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
                     int32_t* tiles_per_rank, int32_t* tiles_per_wave,
-                    int32_t* blocks) {
+                    int32_t* blocks, int32_t* wide) {
   if (!p) return AR_EINVAL;
   int rc = check_desc(&p->desc);
   if (rc) return rc;
@@ -801,6 +1150,7 @@ int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
   if (tiles_per_rank) *tiles_per_rank = g.T;
   if (tiles_per_wave) *tiles_per_wave = g.TPW;
   if (blocks) *blocks = g.blocks;
+  if (wide) *wide = g.wide ? 1 : 0;
   return AR_OK;
 }
 
@@ -812,7 +1162,8 @@ int ar_sim_run(const ar_sim_params* p, void* stream) {
   DeviceInfo di;
   rc = device_info(&di);
   if (rc) return rc;
-  if (!di.coop) return AR_ENODEV;
+  const bool coop = (p->flags & AR_SIM_COOPERATIVE) != 0;
+  if (coop && !di.coop) return AR_ENODEV;
   SimGeom g;
   rc = sim_geometry(p, di, &g);
   if (rc) return rc;
@@ -848,10 +1199,10 @@ int ar_sim_run(const ar_sim_params* p, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (d->proto) {
-    case kLL: e = dispatch_sim_p<kLL>(a, share, g.blocks, s); break;
-    case kLL128: e = dispatch_sim_p<kLL128>(a, share, g.blocks, s); break;
-    case kSentinel: e = dispatch_sim_p<kSentinel>(a, share, g.blocks, s); break;
-    default: e = dispatch_sim_p<kBarrier>(a, share, g.blocks, s); break;
+    case kLL: e = dispatch_sim_p<kLL>(a, share, g.blocks, coop, g.wide, s); break;
+    case kLL128: e = dispatch_sim_p<kLL128>(a, share, g.blocks, coop, g.wide, s); break;
+    case kSentinel: e = dispatch_sim_p<kSentinel>(a, share, g.blocks, coop, g.wide, s); break;
+    default: e = dispatch_sim_p<kBarrier>(a, share, g.blocks, coop, g.wide, s); break;
   }
   return map_hip(e);
 }
@@ -873,15 +1224,27 @@ int ar_probe_pingpong(void* work, int32_t iters, int32_t xcd_a, int32_t xcd_b,
   DeviceInfo di;
   int rc = device_info(&di);
   if (rc) return rc;
-  if (!di.coop) return AR_ENODEV;
   uint32_t* w = static_cast<uint32_t*>(work);
   uint64_t* r = static_cast<uint64_t*>(result);
-  uint64_t to = ns_to_ticks(2000000000ull, di.wallclock_hz);
-  int32_t xa = xcd_a, xb = xcd_b;
-  void* args[] = {&w, &iters, &xa, &xb, &r, &to};
-  return map_hip(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_pingpong),
-                                            dim3(8), dim3(64), args, 0,
-                                            static_cast<hipStream_t>(stream)));
+  const uint64_t to = ns_to_ticks(2000000000ull, di.wallclock_hz);
+  // 8 one-wave workgroups, one per XCD: resident together on an idle device
+  return map_hip(launch(k_pingpong, dim3(8), dim3(64), static_cast<hipStream_t>(stream),
+                        w, iters, xcd_a, xcd_b, r, to));
+}
+
+int ar_probe_litmus(void* work, int32_t iters, int32_t xcd_a, int32_t xcd_b,
+                    int32_t kind, void* result, void* stream) {
+  if (!work || !result || iters < 1 || kind < 0 || kind > 2) return AR_EINVAL;
+  if (xcd_a < 0 || xcd_a > 7 || xcd_b < 0 || xcd_b > 7 || xcd_a == xcd_b) return AR_EINVAL;
+  if (!aligned(work, 256) || !aligned(result, 8)) return AR_EALIGN;
+  DeviceInfo di;
+  int rc = device_info(&di);
+  if (rc) return rc;
+  uint8_t* w = static_cast<uint8_t*>(work);
+  uint64_t* r = static_cast<uint64_t*>(result);
+  const uint64_t to = ns_to_ticks(5000000000ull, di.wallclock_hz);
+  return map_hip(launch(k_litmus, dim3(8), dim3(64), static_cast<hipStream_t>(stream),
+                        w, iters, xcd_a, xcd_b, kind, r, to));
 }
 
 int ar_probe_loadchain(void* work, int64_t bytes, int32_t iters, void* result,

@@ -89,16 +89,22 @@ __device__ __forceinline__ void store_elems(uint16_t* __restrict__ row,
 
 // ----------------------------------------------------------- producer ---
 
-// The lane's 16 encoded bytes of tile `tile` for epoch `seq`.
+// The lane's raw input words (bf16 pairs) of tile `tile`, zero past count.
 template <int P>
-__device__ __forceinline__ u32x4 encode_chunk(const uint16_t* __restrict__ row,
-                                              int64_t count, int tile,
-                                              int lane, uint32_t seq) {
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ row,
+                                           int64_t count, int tile, int lane,
+                                           uint32_t w[4]) {
   int64_t first;
   int n;
   lane_elems<P>(tile, lane, first, n);
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  w[0] = 0u; w[1] = 0u; w[2] = 0u; w[3] = 0u;
   load_elems(row, count, first, n, w);
+}
+
+// The lane's 16 encoded bytes for epoch `seq` from its raw input words.
+template <int P>
+__device__ __forceinline__ u32x4 encode_words(const uint32_t w[4], int lane,
+                                              uint32_t seq) {
   u32x4 v;
   if (P == kLL) {
     // two LL words: data then flag, each single-copy atomic on its own
@@ -118,38 +124,63 @@ __device__ __forceinline__ u32x4 encode_chunk(const uint16_t* __restrict__ row,
   return v;
 }
 
-// Write one tile of rank payload `row` into `ncons` receive buffers: slot
-// offsets dst0, dst0 + cstride, ...  For LL128 only the data part is
-// written here; the flags follow a release fence (produce_flags).
+template <int P>
+__device__ __forceinline__ u32x4 encode_chunk(const uint16_t* __restrict__ row,
+                                              int64_t count, int tile,
+                                              int lane, uint32_t seq) {
+  uint32_t w[4];
+  load_chunk<P>(row, count, tile, lane, w);
+  return encode_words<P>(w, lane, seq);
+}
+
+// Store one encoded tile chunk into `ncons` receive buffers at slot offsets
+// dst0, dst0 + cstride, ..., except buffer `skip` (the producer's own: its
+// consumer takes the value from registers; -1 = none).  For LL128 only the
+// data part is stored here; the flags follow an ordering point
+// (produce_flags).
+template <int P>
+__device__ __forceinline__ void store_chunk(rsrc_t rs, uint32_t dst0,
+                                            uint32_t cstride, int ncons,
+                                            int skip, int tile, uint32_t E,
+                                            int lane, u32x4 v) {
+  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+  if (loff >= E) return;
+  if (P == kLL128 && (lane & 7) == 7) {
+    u32x2 d;
+    d.x = v.x; d.y = v.y;
+    for (int c = 0; c < ncons; ++c)
+      if (c != skip) st8(rs, dst0 + c * cstride + loff, d);
+  } else {
+    for (int c = 0; c < ncons; ++c)
+      if (c != skip) st16(rs, dst0 + c * cstride + loff, v);
+  }
+}
+
 template <int P>
 __device__ __forceinline__ void produce_data(rsrc_t rs, uint32_t dst0,
                                              uint32_t cstride, int ncons,
+                                             int skip,
                                              const uint16_t* __restrict__ row,
                                              int64_t count, int tile,
                                              uint32_t E, uint32_t seq,
                                              int lane) {
   const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
   if (loff >= E) return;
-  const u32x4 v = encode_chunk<P>(row, count, tile, lane, seq);
-  if (P == kLL128 && (lane & 7) == 7) {
-    u32x2 d;
-    d.x = v.x; d.y = v.y;
-    for (int c = 0; c < ncons; ++c) st8(rs, dst0 + c * cstride + loff, d);
-  } else {
-    for (int c = 0; c < ncons; ++c) st16(rs, dst0 + c * cstride + loff, v);
-  }
+  store_chunk<P>(rs, dst0, cstride, ncons, skip, tile, E, lane,
+                 encode_chunk<P>(row, count, tile, lane, seq));
 }
 
 // LL128 second phase: the u64 line flags (lane 7 of each line).
 __device__ __forceinline__ void produce_flags(rsrc_t rs, uint32_t dst0,
                                               uint32_t cstride, int ncons,
-                                              int tile, uint32_t E,
+                                              int skip, int tile, uint32_t E,
                                               uint32_t seq, int lane) {
   const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
   if (loff >= E || (lane & 7) != 7) return;
   u32x2 f;
   f.x = seq; f.y = 0u;
-  for (int c = 0; c < ncons; ++c) st8(rs, dst0 + c * cstride + loff + 8u, f);
+  for (int c = 0; c < ncons; ++c)
+    if (c != skip) st8(rs, dst0 + c * cstride + loff + 8u, f);
 }
 
 // ----------------------------------------------------------- consumer ---
@@ -175,101 +206,182 @@ __device__ __forceinline__ void classify(const u32x4 v, uint32_t seq,
   }
 }
 
-// Poll, validate and reduce one tile for one consumer.  `src0` is the byte
-// offset of slot 0 of this consumer and parity; slot r is at
-// src0 + r*slot_bytes.  Returns 0, kEtimeout or kEcorrupt.
+// Poll and validate one tile of every rank's slot for one consumer, in
+// whatever order the blocks arrive; the validated 16-byte chunks end in
+// v[0..nranks).  `src0` is the byte offset of slot 0 of this consumer and
+// parity; slot r is at src0 + r*slot_bytes.  Rank `own` (-1 = none) is not
+// polled: its chunk is `own_v`, already in registers.  SENTINEL with `rearm`
+// stores the sentinel back over every chunk it has read.  Returns 0,
+// kEtimeout or kEcorrupt.
+//
+// Two phases.  (1) Probe: lane r polls one 16-byte probe of rank r -- the
+// last chunk of the tile, which the producer wave writes in the same store
+// instruction as the rest -- so one load per iteration watches every rank
+// and the polling traffic stays off the lines still being written.
+// (2) Read: once every probe holds readiness evidence, every pending rank's
+// whole chunk is read and validated from its own evidence; chunks not yet
+// complete are read again.  Correctness rests on phase 2 alone.
+// LL128: the probe is the flag of the tile's last line; the producer stored
+// every data byte of its wave (and waited for the stores to complete) before
+// any flag, so phase 2 reads data issued after a flag was seen.
 template <int P, int NMAX>
-__device__ __forceinline__ int consume_tile(
-    rsrc_t rs, uint32_t src0, uint32_t slot_bytes, int nranks, int tile,
-    uint32_t E, uint32_t seq, uint32_t stale, bool rearm,
-    uint16_t* __restrict__ out_row, int64_t count, int* ctrl,
-    uint64_t timeout_ticks, int lane) {
-  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+__device__ __forceinline__ int poll_tile(rsrc_t rs, uint32_t src0,
+                                         uint32_t slot_bytes, int nranks,
+                                         int tile, uint32_t E, uint32_t seq,
+                                         uint32_t stale, bool rearm, int own,
+                                         u32x4 own_v, int* ctrl,
+                                         uint64_t timeout_ticks, int lane,
+                                         u32x4 (&v)[NMAX]) {
+  const uint32_t tile0 = (uint32_t)tile * kTileBytes;
+  const uint32_t loff = tile0 + (uint32_t)lane * 16u;
   const bool active = loff < E;
-  u32x4 v[NMAX];
-#pragma unroll
-  for (int r = 0; r < NMAX; ++r) v[r] = u32x4{0u, 0u, 0u, 0u};
   uint32_t pending = (1u << nranks) - 1u;   // wave-uniform set of ranks
-  Waiter wt(timeout_ticks, ctrl);
-
-  if (P == kLL128) {
-    const bool flag_lane = (lane & 7) == 7;
-    while (true) {
-      u32x2 f[NMAX];
 #pragma unroll
-      for (int r = 0; r < NMAX; ++r) {
-        f[r] = u32x2{0u, 0u};
-        if (r < nranks && ((pending >> r) & 1u) && active && flag_lane)
-          f[r] = ld8(rs, src0 + r * slot_bytes + loff + 8u);
-      }
-      uint32_t fresh = 0u;
-      bool corrupt = false;
-#pragma unroll
-      for (int r = 0; r < NMAX; ++r) {
-        if (r < nranks && ((pending >> r) & 1u)) {
-          bool ok = true, bad = false;
-          if (active && flag_lane) {
-            ok = (f[r].x == seq) && (f[r].y == 0u);
-            bad = !ok && !(f[r].y == 0u && (f[r].x == 0u || f[r].x == stale));
-          }
-          if (__ballot(bad) != 0ull) corrupt = true;
-          if (__ballot(!ok) == 0ull) fresh |= 1u << r;
-        }
-      }
-      if (corrupt) {
-        if (lane == 0) report_error(ctrl, kEcorrupt);
-        return kEcorrupt;
-      }
-      if (fresh != 0u) {
-        // The flags were stored after a release fence that followed the
-        // data; order the data loads after the flag loads.
-        fence_acquire();
-#pragma unroll
-        for (int r = 0; r < NMAX; ++r)
-          if (r < nranks && ((fresh >> r) & 1u) && active)
-            v[r] = ld16(rs, src0 + r * slot_bytes + loff);
-        pending &= ~fresh;
-      }
-      if (pending == 0u) break;
-      if (!wt.again(lane)) return kEtimeout;
-    }
-  } else {
-    while (true) {
-#pragma unroll
-      for (int r = 0; r < NMAX; ++r)
-        if (r < nranks && ((pending >> r) & 1u) && active)
-          v[r] = ld16(rs, src0 + r * slot_bytes + loff);
-      uint32_t fresh = 0u;
-      bool corrupt = false;
-#pragma unroll
-      for (int r = 0; r < NMAX; ++r) {
-        if (r < nranks && ((pending >> r) & 1u)) {
-          bool ok = true, bad = false;
-          if (active) classify<P>(v[r], seq, stale, ok, bad);
-          if (__ballot(bad) != 0ull) corrupt = true;
-          if (__ballot(!ok) == 0ull) fresh |= 1u << r;
-        }
-      }
-      if (corrupt) {
-        if (lane == 0) report_error(ctrl, kEcorrupt);
-        return kEcorrupt;
-      }
-      if (P == kSentinel && rearm && fresh != 0u) {
-        const u32x4 armed = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu,
-                                  0xFFFFFFFFu};
-#pragma unroll
-        for (int r = 0; r < NMAX; ++r)
-          if (r < nranks && ((fresh >> r) & 1u) && active)
-            st16(rs, src0 + r * slot_bytes + loff, armed);
-      }
-      pending &= ~fresh;
-      if (pending == 0u) break;
-      if (!wt.again(lane)) return kEtimeout;
+  for (int r = 0; r < NMAX; ++r) {
+    v[r] = u32x4{0u, 0u, 0u, 0u};
+    if (r == own) {
+      v[r] = own_v;
+      pending &= ~(1u << r);
     }
   }
+  if (pending == 0u) return 0;
+  Waiter wt(timeout_ticks, ctrl);
 
-  if (!active) return 0;
-  // Fixed rank order: start from rank 0, add ranks 1..N-1 one at a time.
+  // ---- phase 1: one probe per rank, lane r watches rank r ----
+  if (P != kBarrier) {
+    const uint32_t tile_end = (tile0 + kTileBytes < E) ? tile0 + kTileBytes : E;
+    const uint32_t probe = tile_end - 16u;   // last chunk of the tile
+    uint32_t waiting = pending;
+    while (true) {
+      const bool mine = lane < nranks && ((waiting >> lane) & 1u);
+      bool ok = true, bad = false;
+      if (mine) {
+        const uint32_t at = src0 + (uint32_t)lane * slot_bytes + probe;
+        if (P == kLL128) {
+          const u32x2 f = ld8(rs, at + 8u);
+          ok = (f.x == seq) && (f.y == 0u);
+          bad = !ok && !(f.y == 0u && (f.x == 0u || f.x == stale));
+        } else {
+          classify<P>(ld16(rs, at), seq, stale, ok, bad);
+        }
+      }
+      if (__ballot(bad) != 0ull) {
+        if (lane == 0) report_error(ctrl, kEcorrupt);
+        return kEcorrupt;
+      }
+      waiting &= ~(uint32_t)__ballot(mine && ok);
+      if (waiting == 0u) break;
+      if (!wt.again(lane)) return kEtimeout;
+    }
+    if (P == kLL128) fence_acquire();
+  }
+
+  // ---- phase 2: read and validate every pending rank's whole chunk ----
+  while (true) {
+#pragma unroll
+    for (int r = 0; r < NMAX; ++r)
+      if (r < nranks && ((pending >> r) & 1u) && active)
+        v[r] = ld16(rs, src0 + r * slot_bytes + loff);
+    uint32_t fresh = 0u;
+    bool corrupt = false;
+#pragma unroll
+    for (int r = 0; r < NMAX; ++r) {
+      if (r < nranks && ((pending >> r) & 1u)) {
+        bool ok = true, bad = false;
+        if (active) {
+          if (P == kLL128) {
+            if ((lane & 7) == 7) {
+              ok = (v[r].z == seq) && (v[r].w == 0u);
+              bad = !ok && !(v[r].w == 0u && (v[r].z == 0u || v[r].z == stale));
+            }
+          } else {
+            classify<P>(v[r], seq, stale, ok, bad);
+          }
+        }
+        if (__ballot(bad) != 0ull) corrupt = true;
+        if (__ballot(!ok) == 0ull) fresh |= 1u << r;
+      }
+    }
+    if (corrupt) {
+      if (lane == 0) report_error(ctrl, kEcorrupt);
+      return kEcorrupt;
+    }
+    if (P == kSentinel && rearm && fresh != 0u) {
+      const u32x4 armed = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu,
+                                0xFFFFFFFFu};
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r)
+        if (r < nranks && ((fresh >> r) & 1u) && active)
+          st16(rs, src0 + r * slot_bytes + loff, armed);
+    }
+    pending &= ~fresh;
+    if (pending == 0u) break;
+    if (!wt.again(lane)) return kEtimeout;
+  }
+  return 0;
+}
+
+// Poll and validate one rank's chunk (the lane's 16 bytes at byte offset
+// `at`) until the whole wave's chunk carries evidence for epoch `seq`.
+// SENTINEL with `rearm` stores the sentinel back over it once read.
+// Returns 0, kEtimeout or kEcorrupt; the chunk ends in `v`.
+template <int P>
+__device__ __forceinline__ int poll_chunk(rsrc_t rs, uint32_t at, bool active,
+                                          uint32_t seq, uint32_t stale,
+                                          bool rearm, int* ctrl,
+                                          uint64_t timeout_ticks, int lane,
+                                          u32x4& v) {
+  v = u32x4{0u, 0u, 0u, 0u};
+  Waiter wt(timeout_ticks, ctrl);
+  if (P == kLL128) {
+    // Flags first (lane 7 of each line), data only after a flag was seen:
+    // the producer's data stores all completed before its first flag store.
+    const bool flag_lane = active && (lane & 7) == 7;
+    while (true) {
+      bool ok = true, bad = false;
+      if (flag_lane) {
+        const u32x2 f = ld8(rs, at + 8u);
+        ok = (f.x == seq) && (f.y == 0u);
+        bad = !ok && !(f.y == 0u && (f.x == 0u || f.x == stale));
+      }
+      if (__ballot(bad) != 0ull) {
+        if (lane == 0) report_error(ctrl, kEcorrupt);
+        return kEcorrupt;
+      }
+      if (__ballot(!ok) == 0ull) break;
+      if (!wt.again(lane)) return kEtimeout;
+    }
+    fence_acquire();
+    if (active) v = ld16(rs, at);
+    return 0;
+  }
+  while (true) {
+    if (active) v = ld16(rs, at);
+    bool ok = true, bad = false;
+    if (active) classify<P>(v, seq, stale, ok, bad);
+    if (__ballot(bad) != 0ull) {
+      if (lane == 0) report_error(ctrl, kEcorrupt);
+      return kEcorrupt;
+    }
+    if (__ballot(!ok) == 0ull) break;
+    if (!wt.again(lane)) return kEtimeout;
+  }
+  if (P == kSentinel && rearm && active)
+    st16(rs, at, u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
+  return 0;
+}
+
+// Fixed rank order: start from rank 0, add ranks 1..N-1 one binary32
+// addition at a time, round to bf16 (NaN -> 0x7FC0), store the lane's
+// elements of tile `tile` below `count`.
+template <int P, int NMAX>
+__device__ __forceinline__ void reduce_store_tile(const u32x4 (&v)[NMAX],
+                                                  int nranks, int tile,
+                                                  uint32_t E, int lane,
+                                                  uint16_t* __restrict__ out_row,
+                                                  int64_t count) {
+  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+  if (loff >= E) return;
   float acc[8];
   {
     const u32x4 d = v[0];
@@ -313,6 +425,21 @@ __device__ __forceinline__ int consume_tile(
   int n;
   lane_elems<P>(tile, lane, first, n);
   store_elems(out_row, count, first, n, o);
+}
+
+// Poll, validate and reduce one tile for one consumer (all ranks polled).
+template <int P, int NMAX>
+__device__ __forceinline__ int consume_tile(
+    rsrc_t rs, uint32_t src0, uint32_t slot_bytes, int nranks, int tile,
+    uint32_t E, uint32_t seq, uint32_t stale, bool rearm,
+    uint16_t* __restrict__ out_row, int64_t count, int* ctrl,
+    uint64_t timeout_ticks, int lane) {
+  u32x4 v[NMAX];
+  const int st = poll_tile<P, NMAX>(rs, src0, slot_bytes, nranks, tile, E, seq,
+                                    stale, rearm, -1, u32x4{0u, 0u, 0u, 0u},
+                                    ctrl, timeout_ticks, lane, v);
+  if (st) return st;
+  reduce_store_tile<P, NMAX>(v, nranks, tile, E, lane, out_row, count);
   return 0;
 }
 

@@ -223,6 +223,13 @@ int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
  * baseline instead: one buffer, a top barrier (arrival counter) and a bottom
  * barrier (completion counter) per op, both global.
  *
+ * Every wave of the grid must be resident at once (waves wait on each
+ * other).  With AR_SIM_COOPERATIVE the runtime guarantees it; otherwise the
+ * library checks the grid against the kernel's occupancy on the whole
+ * device and uses an ordinary launch, which needs the device to be free of
+ * other work for the duration (otherwise waits end in AR_ETIMEOUT, never in
+ * a hang).
+ *
  * Buffers (device):
  *   in:  op i, rank r at in + (i*nranks + r)*in_stride elements.
  *   out: op i, consumer c at out + (i*nconsumers + c)*out_stride elements.
@@ -240,10 +247,17 @@ int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
  *        start.  Must be zero-filled, and the last element set to all ones,
  *        by the caller.
  */
+#define AR_SIM_COOPERATIVE 1   /* launch with hipLaunchCooperativeKernel */
+#define AR_SIM_NARROW 2        /* one wave per tile serving every peer, instead
+                                  of a workgroup of one wave per peer */
+
 typedef struct {
     ar_desc desc;
     int32_t nops;               /* >= 1 */
-    int32_t waves_per_rank;     /* multiple of 32; 0 = library choice */
+    int32_t waves_per_rank;     /* tile groups (wide) or waves (narrow) per
+                                   rank, a multiple of 8; 0 = library choice */
+    int32_t flags;              /* AR_SIM_COOPERATIVE | AR_SIM_NARROW, or 0 */
+    int32_t reserved;           /* must be 0 */
     const void* in;
     int64_t in_stride;
     void* out;
@@ -260,12 +274,15 @@ typedef struct {
 int ar_sim_run(const ar_sim_params* p, void* stream);
 
 /*
- * Geometry ar_sim_run will use for these parameters: waves per rank,
- * tiles per rank (1 KiB of slot each), tiles per wave, total workgroups.
+ * Geometry ar_sim_run will use for these parameters: tile groups per rank
+ * (a wave each in the narrow kernel, a workgroup each in the wide kernel),
+ * tiles per rank (1 KiB of slot each), tiles per group, total workgroups and
+ * the kernel (1 = wide: a workgroup of one wave per peer; 0 = narrow: one
+ * wave per tile serving every peer).  Any output pointer may be NULL.
  */
 int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
                     int32_t* tiles_per_rank, int32_t* tiles_per_wave,
-                    int32_t* blocks);
+                    int32_t* blocks, int32_t* wide);
 
 /* Wall-clock counter frequency of the current device in Hz. */
 int ar_wallclock_hz(double* hz);
@@ -318,6 +335,27 @@ int ar_probe_loadchain(void* work, int64_t bytes, int32_t iters, void* result,
                        void* stream);
 int ar_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
 int ar_probe_empty(void* stream);
+
+/*
+ * ar_probe_litmus: ordering evidence for the coherent accesses the protocols
+ * rely on, between one writer wave on XCD `xcd_a` and one reader wave on XCD
+ * `xcd_b`, `iters` rounds (work: >= 4096 bytes, zeroed; result: device
+ * uint64[8] = {violations, observations, XCC a, XCC b, status, last value,
+ * secondary count, 0}).
+ *   kind 0, message passing: the writer stores k into a 1 KiB block
+ *     (16 bytes a lane), orders, then stores flag k; the reader loads the
+ *     flag, orders, loads the block; a violation is a block value older
+ *     than the flag it followed.
+ *   kind 1, LL word tear: the writer stores 16-byte {k,k,k,k} chunks; the
+ *     reader checks that each 8-byte half is self-consistent (violation) and
+ *     counts 16-byte chunks whose halves differ (secondary count).
+ *   kind 2, re-arm ordering (the dual-buffer chain): the reader re-arms
+ *     (stores 0) a word after reading value k, orders, then publishes k; the
+ *     writer waits for k, then stores k+1 into the same word; a violation
+ *     is the reader finding 0 where k+1 must have landed after its re-arm.
+ */
+int ar_probe_litmus(void* work, int32_t iters, int32_t xcd_a, int32_t xcd_b,
+                    int32_t kind, void* result, void* stream);
 
 /* Library ABI version (bumped on any signature change). */
 int ar_abi_version(void);

@@ -136,17 +136,19 @@ SIM_CASES = [(4, 1, 4096, 4), (4, 4, 4096, 4), (8, 1, 4096, 8), (8, 8, 4099, 6),
              (1, 1, 100, 3)]
 
 
+@pytest.mark.parametrize("kernel", ["auto", "narrow"])
 @pytest.mark.parametrize("proto", PROTOS)
 @pytest.mark.parametrize("nranks,ncons,count,nops", SIM_CASES)
-def test_sim_parity(proto, nranks, ncons, count, nops):
-    print(f"[sim] {proto} N={nranks} C={ncons} count={count} ops={nops}", flush=True)
+def test_sim_parity(proto, nranks, ncons, count, nops, kernel):
+    print(f"[sim] {kernel} {proto} N={nranks} C={ncons} count={count} ops={nops}", flush=True)
+    flags = abi.AR_SIM_NARROW if kernel == "narrow" else 0
     ws = buffers.Workspace(nranks, count, proto, ncons)
     x = _x(7 * count + nops, (nops, nranks, count), specials=True)
     xd, stride = buffers.rows_to_device(x)
     outd = torch.zeros((nops * ncons, stride), dtype=torch.int16, device="cuda")
     seq0 = ws.epoch.seq
     for run in range(2):                                 # the epoch carries over
-        ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS)
+        ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS, flags=flags)
         torch.cuda.synchronize()
         assert ws.status() == 0, abi.status_string(ws.status())
         got = buffers.rows_from_device(outd, count, (nops, ncons))

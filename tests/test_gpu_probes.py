@@ -1,0 +1,91 @@
+"""GPU tests of the ordering probes, the floor probes and the launch modes.
+
+The protocols order device-scope coherent (sc1) accesses with a wait for
+outstanding memory operations rather than a full cache-flushing fence; the
+litmus probe checks the three orderings they rely on between waves on
+different XCDs (message passing, LL word atomicity, re-arm before refill).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from collective_synchronization_amd import abi, buffers, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _litmus(kind, xa, xb, iters):
+    work = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    res = torch.zeros(8, dtype=torch.int64, device="cuda")
+    abi.ar_probe_litmus(work, iters, xa, xb, kind, res)
+    torch.cuda.synchronize()
+    return res.cpu().tolist()
+
+
+@pytest.mark.parametrize("kind,iters", [(0, 50000), (1, 50000), (2, 20000)])
+@pytest.mark.parametrize("xa,xb", [(0, 1), (2, 6), (7, 4)])
+def test_litmus_no_violation(kind, xa, xb, iters):
+    print(f"[litmus] kind={kind} xcd {xa}->{xb}", flush=True)
+    r = _litmus(kind, xa, xb, iters)
+    viol, obs, xcc_a, xcc_b, status, last, second = r[:7]
+    print(f"  observations={obs} xcc=({xcc_a},{xcc_b}) 16B-split={second}", flush=True)
+    assert status == 0
+    assert obs > 0 and last == iters
+    assert viol == 0
+    assert 0 <= xcc_a < 8 and 0 <= xcc_b < 8
+
+
+def test_litmus_argument_checks():
+    work = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    res = torch.zeros(8, dtype=torch.int64, device="cuda")
+    with pytest.raises(abi.ArError):
+        abi.ar_probe_litmus(work, 10, 3, 3, 0, res)
+    with pytest.raises(abi.ArError):
+        abi.ar_probe_litmus(work, 10, 0, 1, 5, res)
+
+
+def test_floor_probes():
+    hz = abi.ar_wallclock_hz()
+    assert hz > 1e6
+    work = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    res = torch.zeros(8, dtype=torch.int64, device="cuda")
+    abi.ar_probe_pingpong(work, 500, 0, 3, res)
+    torch.cuda.synchronize()
+    r = res.cpu().tolist()
+    assert r[4] == 0 and r[1] == 500
+    rtt_us = r[0] / 500 / hz * 1e6
+    assert 0.01 < rtt_us < 100
+    chain = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    res.zero_()
+    abi.ar_probe_loadchain(chain, 1 << 22, 500, res)
+    torch.cuda.synchronize()
+    r = res.cpu().tolist()
+    assert r[1] == 500 and 0.01 < r[0] / 500 / hz * 1e6 < 100
+
+
+def test_copy_probe():
+    src = torch.randint(-2 ** 15, 2 ** 15, (1 << 20,), dtype=torch.int16, device="cuda")
+    dst = torch.zeros_like(src)
+    abi.ar_probe_copy(src, dst, src.numel() * 2)
+    abi.ar_probe_empty()
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel", "barrier"])
+def test_sim_cooperative_launch(proto):
+    nranks, count, nops = 8, 4096, 6
+    ws = buffers.Workspace(nranks, count, proto, nranks)
+    x = inputs.payload(77, (nops, nranks, count), "normal")
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=2_000_000_000,
+           flags=abi.AR_SIM_COOPERATIVE)
+    torch.cuda.synchronize()
+    assert ws.status() == 0
+    got = buffers.rows_from_device(outd, count, (nops, nranks))
+    want = oracle.allreduce_ops(x, proto)
+    for i in range(nops):
+        for c in range(nranks):
+            assert np.array_equal(got[i, c], want[i])
