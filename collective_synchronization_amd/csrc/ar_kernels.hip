@@ -898,7 +898,13 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
   const bool share = d->nconsumers == 1 && d->nranks > 1;
   const int occ = sim_occupancy(d->proto, d->nranks, share, wide);
   if (occ <= 0) return AR_ELAUNCH;
-  const int64_t capacity = (int64_t)occ * di.cus;
+  // Every workgroup waits on others, so the whole grid must be resident at
+  // once.  The grid is kept to half of what the occupancy query reports (a
+  // margin for limits the query does not model) and, for the one-wave
+  // kernel, to 8 workgroups per CU: the large sizes that use it are bound by
+  // memory bandwidth, which that many waves already saturate.
+  int64_t capacity = (int64_t)occ * di.cus / 2;
+  if (!wide && capacity > 8 * (int64_t)di.cus) capacity = 8 * (int64_t)di.cus;
   const int64_t qmax_dev = capacity / (8 * (int64_t)d->nranks);
   const int64_t per_q = wide ? 8 : kSimWavesPerQ;   // tile groups / waves per Q
   const int64_t qcap = kCtrlMaxProgress / per_q;

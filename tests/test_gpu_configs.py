@@ -1,0 +1,161 @@
+"""GPU parity on the five workloads at their full sizes, in the launch
+configuration bench.py times (persistent simulator, ordinary launch, library
+geometry), against the CPU oracle.
+
+1. 4 ranks, bf16 [1,4096], LL, one op (share and system mode), plus the
+   encoded slot bytes of the same inputs through ar_pack_ll.
+2. 8 ranks, bf16 [1,4096], sentinel, dual-buffered, 64 ops; and the same with
+   negative NaNs (0xFFFF, 0xFFC0, 0xFF81) injected at 1/1024 of positions.
+3. 4 ranks, bf16 [B,8192], B in {1,4,16}, LL128, 160 ops.
+4. 8 ranks, 2 KiB .. 4 MiB payloads, U[-1,1), LL / LL128 / sentinel /
+   barrier (sampled ops at the largest sizes).
+5. 16 ranks, bf16 [8,4096], seeded 0-20 us producer skew and shuffled tile
+   order per (op, producer), every consumer bit-identical to the oracle.
+
+Every comparison is bit-exact (the method reaches the oracle's result
+exactly: integer encodings and one fixed-order binary32 sum per element).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from collective_synchronization_amd import abi, buffers, inputs
+from collective_synchronization_amd.configs import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+TIMEOUT_NS = 2_000_000_000
+
+
+def _run_sim(x, proto, nranks, ncons, nops, **kw):
+    count = x.shape[-1]
+    ws = buffers.Workspace(nranks, count, proto, ncons)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * ncons, stride), dtype=torch.int16, device="cuda")
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS, **kw)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    return ws, buffers.rows_from_device(outd, count, (nops, ncons)), seq0
+
+
+def _check_all(got, want_ops, ops=None):
+    nops, ncons = got.shape[:2]
+    for i in (range(nops) if ops is None else ops):
+        for c in range(ncons):
+            assert np.array_equal(got[i, c], want_ops[i]), (i, c)
+
+
+@pytest.mark.parametrize("mode", ["share", "system"])
+def test_config1_ll_n4(mode):
+    cfg = CONFIGS[1]
+    n, count = cfg["nranks"], cfg["hidden"]
+    x = inputs.payload(cfg["seed"], (1, n, count), cfg["dist"])
+    ncons = n if mode == "system" else 1
+    _, got, seq0 = _run_sim(x, "ll", n, ncons, 1)
+    _check_all(got, oracle.allreduce_ops(x, "ll", seq0))
+    # encoded bytes of the same payloads (single epoch, seq 1)
+    ws = buffers.Workspace(n, count, "ll", 1)
+    xd, stride = buffers.rows_to_device(x[0])
+    ws.pack(xd, stride)
+    torch.cuda.synchronize()
+    slots = ws.slot_view()
+    for r in range(n):
+        assert np.array_equal(slots[0, 0, r, :16384], oracle.encode("ll", x[0, r], 1))
+
+
+@pytest.mark.parametrize("inject", [False, True])
+def test_config2_sentinel_n8_64ops(inject):
+    cfg = CONFIGS[2]
+    n, count, nops = cfg["nranks"], cfg["hidden"], cfg["nops"]
+    x = inputs.payload(cfg["seed"], (nops, n, count), cfg["dist"])
+    if inject:
+        x = inputs.inject(x, cfg["seed"] + 1, 1 / 1024)
+        assert np.any(x == 0xFFFF)
+    ws, got, seq0 = _run_sim(x, "sentinel", n, n, nops)
+    want = oracle.allreduce_ops(x, "sentinel", seq0)
+    _check_all(got, want)
+    assert not np.any(got == 0xFFFF)             # the sentinel is never delivered
+    assert np.all(ws.slot_view() == 0xFF)        # every slot re-armed
+    # dual buffering across launches: the epoch continues, results repeat
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == 0
+    _check_all(buffers.rows_from_device(outd, count, (nops, n)), want)
+
+
+@pytest.mark.parametrize("batch", [1, 4, 16])
+def test_config3_ll128_n4_160ops(batch):
+    cfg = CONFIGS[3]
+    n, nops = cfg["nranks"], cfg["nops"]
+    count = batch * cfg["hidden"]
+    x = inputs.payload(cfg["seed"] + batch, (nops, n, count), cfg["dist"])
+    _, got, seq0 = _run_sim(x, "ll128", n, n, nops)
+    _check_all(got, oracle.allreduce_ops(x, "ll128", seq0))
+
+
+def _config4_cases():
+    cfg = CONFIGS[4]
+    for size in cfg["sizes"]:
+        if size not in (2048, 16384, 131072, 1 << 20, 4 << 20):
+            continue
+        for proto in cfg["protos"]:
+            yield size, proto
+
+
+@pytest.mark.parametrize("size,proto", list(_config4_cases()))
+def test_config4_sweep_n8(size, proto):
+    cfg = CONFIGS[4]
+    n = cfg["nranks"]
+    count = size // 2
+    nops = 64 if size <= 131072 else 8
+    x = inputs.payload(cfg["seed"] + size, (nops, n, count), cfg["dist"])
+    _, got, seq0 = _run_sim(x, proto, n, n, nops)
+    ops = range(nops) if size <= 131072 else (0, nops // 2, nops - 1)
+    want = {}
+    seq = seq0
+    for i in range(nops):
+        if i in ops:
+            st, want[i] = oracle.allreduce(x[i], proto, seq)
+            assert st == oracle.READY
+        seq = oracle.epoch_next(seq)
+    _check_all(got, want, ops)
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel"])
+def test_config5_skew_shuffle_n16(proto):
+    cfg = CONFIGS[5]
+    n, nops = cfg["nranks"], cfg["nops"]
+    count = cfg["batches"][0] * cfg["hidden"]
+    x = inputs.payload(cfg["seed"], (nops, n, count), cfg["dist"])
+    hz = abi.ar_wallclock_hz()
+    d_us = inputs.delays_us(cfg["seed"] + 1, nops, n, cfg["delay_max_us"])
+    ticks = torch.from_numpy(np.round(d_us * hz * 1e-6).astype(np.int32)).to("cuda")
+    ws = buffers.Workspace(n, count, proto, n)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride))
+    order = inputs.tile_orders(cfg["seed"] + 2, nops, n, geo["tiles_per_wave"])
+    order_d = torch.from_numpy(order.view(np.int16)).to("cuda")
+    trace = torch.zeros(nops * 2 * n + 1, dtype=torch.int64, device="cuda")
+    trace[-1] = -1
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS,
+           delay_ticks=ticks, tile_order=order_d, trace=trace)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    got = buffers.rows_from_device(outd, count, (nops, n))
+    want = oracle.allreduce_ops(x, proto, seq0)
+    _check_all(got, want)
+    # every rank holds identical bits
+    assert all(np.array_equal(got[:, c], got[:, 0]) for c in range(n))
+    t = trace.cpu().numpy()[:-1].reshape(nops, 2, n).astype(np.float64)
+    last_store = t[:, 0, :].max(axis=1)
+    done = t[:, 1, :].max(axis=1)
+    post = (done - last_store) / hz * 1e6
+    print(f"[config5 {proto}] median post-arrival latency {np.median(post):.3f} us, "
+          f"kernel {geo['kernel']}", flush=True)
+    assert np.all(last_store > 0) and np.all(done >= last_store)
