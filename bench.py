@@ -186,6 +186,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-floor", action="store_true")
     ap.add_argument("--no-share", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="also run ar_probe_copy over BYTES, 3 times (reference "
+                         "dispatches for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -209,6 +212,14 @@ def main() -> int:
     flags = abi.AR_SIM_COOPERATIVE if args.cooperative else 0
 
     x = inputs.payload(cfg["seed"], (nops, nranks, count), "normal")
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy // 16 * 16
+        src = torch.ones(n // 2, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            abi.ar_probe_copy(src, dst, n)
+        torch.cuda.synchronize()
+        del src, dst
     try:
         res = measure(torch, abi, buffers, x, proto, nranks, count, nops, args.mode,
                       args.steps, args.warmup, args.waves_per_rank, flags)

@@ -1,0 +1,197 @@
+"""Cost-guided protocol selector: measurement sweep, fit and table.
+
+"flash-comm: Self-Synchronizing Collective Communication for LLM Decoding",
+abstract: the readiness encoding is chosen by message size and the number of
+GPUs, trading synchronization overhead against the extra bytes an encoding
+moves.  "Why Microseconds Matter in AI Infrastructure", sections "What I
+learned from it" and "Where I think this is heading": the choice is made from
+measurements of the kernels, with a performance model as the next step.
+
+Model per protocol p and rank count N: T_p(S) = alpha_p + beta_p * S, with S
+the payload bytes per rank.  alpha and beta are fitted to per-op times
+measured with the persistent simulator on this GPU (system mode, every rank
+running the full program), minimising relative error so that the
+latency-bound small sizes count as much as the large ones.  The argmin itself
+runs in the library (``ar_select_protocol``); this module measures, fits,
+stores and loads the table.
+
+    python -m collective_synchronization_amd.selector --out cost_table.json
+
+runs the sweep on cuda:0 and writes the table next to this file.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TABLE_PATH = os.path.join(HERE, "cost_table.json")
+PROTOS = ("ll", "ll128", "sentinel", "barrier")
+SIZES = tuple(2 ** k for k in range(11, 23))          # 2 KiB .. 4 MiB per rank
+
+
+def fit_alpha_beta(sizes, times):
+    """Relative least squares for T = alpha + beta * S (alpha, beta >= 0)."""
+    S = np.asarray(sizes, dtype=np.float64)
+    T = np.asarray(times, dtype=np.float64)
+    A = np.stack([1.0 / T, S / T], axis=1)
+    coef, *_ = np.linalg.lstsq(A, np.ones_like(T), rcond=None)
+    alpha, beta = float(coef[0]), float(coef[1])
+    if beta < 0.0:                       # flat data: constant model
+        beta = 0.0
+        alpha = float(len(T) / np.sum(1.0 / T))
+    if alpha < 0.0:
+        alpha = 0.0
+        beta = float(np.sum(S / T) / np.sum((S / T) ** 2))
+    return alpha, beta
+
+
+def fit_table(points):
+    """points: list of {nranks, proto, bytes, us}.  Returns table entries."""
+    entries = []
+    for n in sorted({p["nranks"] for p in points}):
+        alpha = [-1.0] * 4
+        beta = [0.0] * 4
+        for pi, proto in enumerate(PROTOS):
+            pts = [p for p in points if p["nranks"] == n and p["proto"] == proto]
+            if len(pts) >= 2:
+                alpha[pi], beta[pi] = fit_alpha_beta([p["bytes"] for p in pts],
+                                                     [p["us"] for p in pts])
+        entries.append({"nranks": n, "alpha_us": alpha, "beta_us_per_byte": beta})
+    return entries
+
+
+def argmin_py(entry, nbytes):
+    best, tbest = -1, 0.0
+    for p in range(4):
+        a, b = entry["alpha_us"][p], entry["beta_us_per_byte"][p]
+        if not a >= 0.0:
+            continue
+        t = a + b * nbytes
+        if best < 0 or t < tbest:
+            best, tbest = p, t
+    return best, tbest
+
+
+def regret(points, entries):
+    """Measured time of the selected protocol over the best measured time."""
+    from . import abi
+    table = abi.cost_table(entries)
+    out = []
+    for n in sorted({p["nranks"] for p in points}):
+        for s in sorted({p["bytes"] for p in points if p["nranks"] == n}):
+            meas = {p["proto"]: p["us"] for p in points
+                    if p["nranks"] == n and p["bytes"] == s}
+            if len(meas) < 2:
+                continue
+            pick, _ = abi.ar_select_protocol(table, s, n)
+            chosen = meas.get(PROTOS[pick])
+            best = min(meas.values())
+            out.append({"nranks": n, "bytes": s, "pick": PROTOS[pick],
+                        "best": min(meas, key=meas.get),
+                        "regret": (chosen / best) if chosen else None})
+    return out
+
+
+def load_table(path: str = TABLE_PATH):
+    with open(path) as fh:
+        return json.load(fh)
+
+
+def select(nbytes: int, nranks: int, path: str = TABLE_PATH):
+    """Protocol name chosen by the library for a payload of nbytes per rank."""
+    from . import abi
+    t = load_table(path)
+    pick, pred = abi.ar_select_protocol(abi.cost_table(t["entries"]), nbytes, nranks)
+    return PROTOS[pick], pred
+
+
+# ------------------------------------------------------------------ sweep --
+
+def measure_point(torch, abi, buffers, inputs, proto, nranks, nbytes, nops, reps,
+                  seed=1004):
+    count = nbytes // 2
+    x = inputs.payload(seed + nbytes, (nops, nranks, count), "uniform")
+    ws = buffers.Workspace(nranks, count, proto, nranks)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    for _ in range(2):
+        ws.sim(nops, xd, stride, outd, stride, timeout_ns=2_000_000_000)
+    torch.cuda.synchronize()
+    if ws.status() != 0:
+        raise RuntimeError(f"{proto} N={nranks} S={nbytes}: {abi.status_string(ws.status())}")
+    st = torch.cuda.current_stream()
+    ms = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        if proto == "barrier":
+            ws.reset_ctrl()
+        p = ws.sim_params(nops, xd, stride, outd, stride, timeout_ns=2_000_000_000)
+        a.record(st)
+        abi.ar_sim_run(p, st)
+        b.record(st)
+        ws.flip(nops)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    if ws.status() != 0:
+        raise RuntimeError(f"{proto} N={nranks} S={nbytes}: {abi.status_string(ws.status())}")
+    return statistics.median(ms) * 1e3 / nops
+
+
+def sweep(ranks=(4, 8, 16), sizes=SIZES, protos=PROTOS, reps=7):
+    import torch
+    from . import abi, buffers, inputs
+    torch.cuda.set_device(0)
+    points = []
+    for n in ranks:
+        for s in sizes:
+            # system-mode receive buffers must stay below 4 GiB in total
+            E_max = 2 * s
+            if n * 2 * n * E_max >= (1 << 32):
+                continue
+            nops = 64 if s <= (256 << 10) else 16
+            for proto in protos:
+                us = measure_point(torch, abi, buffers, inputs, proto, n, s, nops, reps)
+                points.append({"nranks": n, "proto": proto, "bytes": s, "us": round(us, 4)})
+                print(json.dumps(points[-1]), flush=True)
+    return points
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description="measure, fit and write the cost table")
+    ap.add_argument("--out", default=TABLE_PATH)
+    ap.add_argument("--ranks", default="4,8,16")
+    ap.add_argument("--reps", type=int, default=7)
+    args = ap.parse_args()
+    t0 = time.time()
+    points = sweep(tuple(int(r) for r in args.ranks.split(",")), reps=args.reps)
+    entries = fit_table(points)
+    reg = regret(points, entries)
+    worst = max(r["regret"] for r in reg if r["regret"])
+    table = {
+        "model": "T_p(S) = alpha_us[p] + beta_us_per_byte[p] * S; S = payload bytes per rank",
+        "protocols": list(PROTOS),
+        "measured_with": "python -m collective_synchronization_amd.selector "
+                         f"--ranks {args.ranks} --reps {args.reps} (one MI355X, "
+                         "system mode, persistent simulator, median per-op time)",
+        "entries": entries,
+        "points": points,
+        "regret": reg,
+        "max_regret": worst,
+        "sweep_seconds": round(time.time() - t0, 1),
+    }
+    with open(args.out, "w") as fh:
+        json.dump(table, fh, indent=1)
+    print(json.dumps({"max_regret": worst, "entries": entries}), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,68 @@
+"""Host tests of the protocol selector's fit and table (CPU only).
+
+The fit is checked on synthetic exact data, and the library's argmin
+(ar_select_protocol) is checked against a plain Python argmin over the same
+table.  When the committed cost table (measured on an MI355X) is present, its
+structure and recorded regret are checked too.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from collective_synchronization_amd import abi, selector
+
+
+def test_fit_recovers_exact_line():
+    sizes = [2 ** k for k in range(11, 23)]
+    alpha, beta = 2.5, 3e-4
+    times = [alpha + beta * s for s in sizes]
+    a, b = selector.fit_alpha_beta(sizes, times)
+    assert abs(a - alpha) < 1e-9 and abs(b - beta) < 1e-12
+
+
+def test_fit_flat_data_is_constant():
+    sizes = [2048, 4096, 8192]
+    a, b = selector.fit_alpha_beta(sizes, [3.0, 3.0, 3.0])
+    assert b == pytest.approx(0.0, abs=1e-15) and a == pytest.approx(3.0)
+
+
+def test_fit_table_and_regret_on_synthetic_points():
+    pts = []
+    model = {"ll": (2.0, 2e-4), "ll128": (3.0, 1.1e-4), "sentinel": (2.2, 1.5e-4),
+             "barrier": (5.0, 1.2e-4)}
+    for n in (4, 8):
+        for s in selector.SIZES:
+            for p, (a, b) in model.items():
+                pts.append({"nranks": n, "proto": p, "bytes": s, "us": a + b * s})
+    entries = selector.fit_table(pts)
+    assert [e["nranks"] for e in entries] == [4, 8]
+    reg = selector.regret(pts, entries)
+    assert all(r["regret"] == pytest.approx(1.0) for r in reg)
+
+
+def test_library_argmin_matches_python():
+    rng = np.random.default_rng(3)
+    entries = [{"nranks": n, "alpha_us": list(rng.uniform(1, 6, 4)),
+                "beta_us_per_byte": list(rng.uniform(5e-5, 3e-4, 4))} for n in (4, 8, 16)]
+    table = abi.cost_table(entries)
+    for n in (4, 8, 16):
+        e = [x for x in entries if x["nranks"] == n][0]
+        for s in [2 ** k for k in range(8, 24)]:
+            pick, pred = abi.ar_select_protocol(table, s, n)
+            ref, tref = selector.argmin_py(e, s)
+            assert pick == ref and pred == pytest.approx(tref)
+
+
+@pytest.mark.skipif(not os.path.exists(selector.TABLE_PATH), reason="no measured table")
+def test_committed_table():
+    t = selector.load_table()
+    assert t["protocols"] == list(selector.PROTOS)
+    assert {e["nranks"] for e in t["entries"]} >= {4, 8}
+    for e in t["entries"]:
+        assert len(e["alpha_us"]) == 4 and len(e["beta_us_per_byte"]) == 4
+    # the library's choice on every measured point is within the recorded regret
+    recomputed = selector.regret(t["points"], t["entries"])
+    worst = max(r["regret"] for r in recomputed if r["regret"])
+    assert worst == pytest.approx(t["max_regret"])
+    assert worst < 1.5
