@@ -54,7 +54,8 @@ __global__ __launch_bounds__(kBlock) void k_pack(PackArgs a) {
   const uint32_t cstride = 2u * (uint32_t)a.nranks * a.slot_bytes;
   const uint32_t dst0 = (a.parity * (uint32_t)a.nranks + (uint32_t)r) * a.slot_bytes;
   const uint16_t* row = a.in + (int64_t)r * a.in_stride;
-  produce_data<P>(rs, dst0, cstride, a.nconsumers, -1, row, a.count, tile, a.E,
+  produce_data<P>(rs, dst0, cstride, a.nconsumers, -1, row,
+                  (uint32_t)(((a.count * 2) + 15) & ~int64_t(15)), a.count, tile, a.E,
                   a.seq, lane);
   if (P == kLL128) {
     fence_release();
@@ -200,7 +201,9 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
   uint32_t wnext[4] = {0u, 0u, 0u, 0u};     // fast path: next op's payload
   u32x4 v[NMAX];                            // fast path: last validated op
   bool out_pending = false;
-  if (fast) load_chunk<P>(a.in + (int64_t)g * a.in_stride, a.count, wr, lane, wnext);
+  const uint32_t row_bytes = (uint32_t)(((a.count * 2) + 15) & ~int64_t(15));
+  const int keep = chunk_keep<P>(a.count, wr, lane);
+  if (fast) load_chunk<P>(a.in + (int64_t)g * a.in_stride, row_bytes, wr, lane, wnext);
 
   uint32_t seq = a.seq0;
   uint32_t par = a.parity0;
@@ -244,6 +247,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
     const uint32_t dst0 = (pp * N + (uint32_t)g) * a.slot_bytes;
     u32x4 own_v = u32x4{0u, 0u, 0u, 0u};
     if (fast) {
+      mask_words(wnext, keep);
       own_v = encode_words<P>(wnext, lane, seq);
       store_chunk<P>(rs, dst0, cstride, a.nconsumers, skip, wr, a.E, lane, own_v);
       if (P == kLL128) {
@@ -257,15 +261,15 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
         out_pending = false;
       }
       if (op + 1 < a.nops)
-        load_chunk<P>(row + op_rows * a.in_stride, a.count, wr, lane, wnext);
+        load_chunk<P>(row + op_rows * a.in_stride, row_bytes, wr, lane, wnext);
     } else {
       const uint16_t* ord =
           a.order ? a.order + ((int64_t)op * a.nranks + g) * a.TPW : nullptr;
       for (int j = 0; j < a.TPW; ++j) {
         const int k = ord ? (int)ord[j] : j;
         if (k >= mine) continue;
-        produce_data<P>(rs, dst0, cstride, a.nconsumers, skip, row, a.count,
-                        wr + k * a.W, a.E, seq, lane);
+        produce_data<P>(rs, dst0, cstride, a.nconsumers, skip, row, row_bytes,
+                        a.count, wr + k * a.W, a.E, seq, lane);
       }
       if (P == kLL128) {
         fence_release();
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
         u32x4 vt[NMAX];
         for (int k = 0; k < mine; ++k) {
           const int tile = wr + k * a.W;
-          const u32x4 mine_v = encode_chunk<P>(row, a.count, tile, lane, seq);
+          const u32x4 mine_v = encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq);
           if (poll_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, tile, a.E, seq,
                                  stale, true, g, mine_v, a.ctrl, a.timeout_ticks,
                                  lane, vt) != 0)
@@ -396,8 +400,10 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
 
   uint32_t wnext[4] = {0u, 0u, 0u, 0u};
   const bool needs_input = sender || own;
+  const uint32_t row_bytes = (uint32_t)(((a.count * 2) + 15) & ~int64_t(15));
+  const int keep = chunk_keep<P>(a.count, tg, lane);
   if (pipelined && needs_input)
-    load_chunk<P>(a.in + (int64_t)g * a.in_stride, a.count, tg, lane, wnext);
+    load_chunk<P>(a.in + (int64_t)g * a.in_stride, row_bytes, tg, lane, wnext);
 
   uint32_t seq = a.seq0;
   uint32_t par = a.parity0;
@@ -438,11 +444,12 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
       u32x4 mine_v = u32x4{0u, 0u, 0u, 0u};
       if (needs_input) {
         if (pipelined) {
+          mask_words(wnext, keep);
           mine_v = encode_words<P>(wnext, lane, seq);
           if (op + 1 < a.nops)
-            load_chunk<P>(row + op_rows * a.in_stride, a.count, tile, lane, wnext);
+            load_chunk<P>(row + op_rows * a.in_stride, row_bytes, tile, lane, wnext);
         } else {
-          mine_v = encode_chunk<P>(row, a.count, tile, lane, seq);
+          mine_v = encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq);
         }
       }
       // ---- send ----
@@ -735,6 +742,7 @@ static int check_rows(const void* p, int64_t stride, int64_t count) {
   if (!p) return AR_EINVAL;
   if (stride < count) return AR_EINVAL;
   if (!aligned(p, 16) || (stride % 8) != 0) return AR_EALIGN;
+  if (stride >= (int64_t(1) << 30)) return AR_ESIZE;   // row byte offsets stay 32-bit
   return AR_OK;
 }
 

@@ -89,16 +89,53 @@ __device__ __forceinline__ void store_elems(uint16_t* __restrict__ row,
 
 // ----------------------------------------------------------- producer ---
 
-// The lane's raw input words (bf16 pairs) of tile `tile`, zero past count.
+// Elements of the lane's chunk of tile `tile` that lie below `count`.
 template <int P>
-__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ row,
-                                           int64_t count, int tile, int lane,
-                                           uint32_t w[4]) {
+__device__ __forceinline__ int chunk_keep(int64_t count, int tile, int lane) {
   int64_t first;
   int n;
   lane_elems<P>(tile, lane, first, n);
-  w[0] = 0u; w[1] = 0u; w[2] = 0u; w[3] = 0u;
-  load_elems(row, count, first, n, w);
+  const int64_t left = count - first;
+  return (int)(left < 0 ? 0 : (left < n ? left : n));
+}
+
+// The lane's raw input words (bf16 pairs) of tile `tile`.  Branch-free:
+// every lane issues the same buffer loads through a resource whose range is
+// the row (`row_bytes`; reads past it return 0).  The words are returned
+// unmasked, so that a load issued for the next op can stay in flight across
+// the op loop; mask_words(w, chunk_keep(...)) clears what lies past count.
+template <int P>
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ row,
+                                           uint32_t row_bytes, int tile,
+                                           int lane, uint32_t w[4]) {
+  int64_t first;
+  int n;
+  lane_elems<P>(tile, lane, first, n);
+  const rsrc_t rr = make_rsrc(row, row_bytes);
+  const int64_t off64 = first * 2;
+  const uint32_t off = off64 < (int64_t)row_bytes ? (uint32_t)off64 : row_bytes;
+  if (P == kLL) {
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = 0u; w[3] = 0u;
+  } else if (P == kLL128) {
+    // 8-byte aligned only (60 elements per line): two 8-byte loads
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 0);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(rr, off + 8u, 0, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y;
+  } else {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+}
+
+// Keep the first `keep` bf16 halves of w, clear the rest.
+__device__ __forceinline__ void mask_words(uint32_t w[4], int keep) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t lo_ok = (2 * d < keep) ? 0x0000FFFFu : 0u;
+    const uint32_t hi_ok = (2 * d + 1 < keep) ? 0xFFFF0000u : 0u;
+    w[d] &= (lo_ok | hi_ok);
+  }
 }
 
 // The lane's 16 encoded bytes for epoch `seq` from its raw input words.
@@ -126,10 +163,11 @@ __device__ __forceinline__ u32x4 encode_words(const uint32_t w[4], int lane,
 
 template <int P>
 __device__ __forceinline__ u32x4 encode_chunk(const uint16_t* __restrict__ row,
-                                              int64_t count, int tile,
-                                              int lane, uint32_t seq) {
+                                              uint32_t row_bytes, int64_t count,
+                                              int tile, int lane, uint32_t seq) {
   uint32_t w[4];
-  load_chunk<P>(row, count, tile, lane, w);
+  load_chunk<P>(row, row_bytes, tile, lane, w);
+  mask_words(w, chunk_keep<P>(count, tile, lane));
   return encode_words<P>(w, lane, seq);
 }
 
@@ -161,13 +199,13 @@ __device__ __forceinline__ void produce_data(rsrc_t rs, uint32_t dst0,
                                              uint32_t cstride, int ncons,
                                              int skip,
                                              const uint16_t* __restrict__ row,
-                                             int64_t count, int tile,
-                                             uint32_t E, uint32_t seq,
+                                             uint32_t row_bytes, int64_t count,
+                                             int tile, uint32_t E, uint32_t seq,
                                              int lane) {
   const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
   if (loff >= E) return;
   store_chunk<P>(rs, dst0, cstride, ncons, skip, tile, E, lane,
-                 encode_chunk<P>(row, count, tile, lane, seq));
+                 encode_chunk<P>(row, row_bytes, count, tile, lane, seq));
 }
 
 // LL128 second phase: the u64 line flags (lane 7 of each line).

@@ -142,7 +142,9 @@ int ar_ctrl_reset(void* ctrl, void* stream);
  * Producers: encode every simulated rank's payload for epoch `e` into slot r
  * of parity e.parity of every consumer's receive buffer.
  *   in:   device, rank r's payload at in + r*in_stride (elements), bf16.
- *         16-byte aligned, in_stride a multiple of 8 and >= count.
+ *         16-byte aligned, in_stride a multiple of 8 and >= count.  Each
+ *         row is read up to the 16-byte boundary after element count-1
+ *         (never past in_stride); elements at or past count are ignored.
  *   scratch: device, ar_scratch_bytes(d) bytes (layout above).
  * Stores use device-scope coherent (sc1) 16-byte accesses.
  *
