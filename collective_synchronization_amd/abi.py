@@ -24,6 +24,7 @@ AR_LL, AR_LL128, AR_SENTINEL, AR_BARRIER, AR_AUTO = 0, 1, 2, 3, 4
 AR_FLAG_REARM = 1
 AR_SIM_COOPERATIVE = 1
 AR_SIM_NARROW = 2
+AR_SIM_WIDE = 4
 AR_MAX_RANKS = 16
 PROTO_IDS = {"ll": AR_LL, "ll128": AR_LL128, "sentinel": AR_SENTINEL,
              "barrier": AR_BARRIER}

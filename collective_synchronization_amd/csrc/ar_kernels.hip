@@ -349,10 +349,12 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
 // Wide simulator for latency-bound sizes: one workgroup of nranks waves per
 // (rank g, tile group tg); wave w is paired with peer w.  Wave w sends this
 // rank's chunk to consumer w and, in a consumer, polls peer w's chunk, so
-// every wave carries one store stream and one poll stream.  Validated chunks
-// are staged in LDS (double-buffered by tile iteration); after one
-// workgroup barrier the wave of the rank itself (the "own" wave, whose
-// contribution never leaves registers) reduces in fixed rank order.
+// every wave carries one store stream and one poll stream.  Per op, every
+// wave first sends all tiles of its tile group, then the workgroup receives
+// them tile by tile: validated chunks are staged in LDS (double-buffered by
+// tile iteration) and, after one workgroup barrier, the wave of the rank
+// itself (the "own" wave, whose contribution never leaves registers when
+// the group holds one tile) reduces in fixed rank order.
 // Sentinel: the wave that re-arms peer w's slot is the wave that next sends
 // to peer w, so waiting for its own stores orders re-arm before refill.
 // Share mode: only rank 0 consumes; a producer rank's workgroup keeps its
@@ -437,39 +439,54 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
 
     const uint32_t dst0 = ((uint32_t)dst_c * 2u * N + pp * N + (uint32_t)g) * a.slot_bytes;
     const uint32_t src0 = ((uint32_t)cself * 2u * N + pp * N) * a.slot_bytes;
-    for (int k = 0; k < mine; ++k) {
-      const int tile = tg + k * G;
-      const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
-      const bool active = loff < a.E;
-      u32x4 mine_v = u32x4{0u, 0u, 0u, 0u};
-      if (needs_input) {
+    // ---- send every tile of this op first ----
+    u32x4 own_v = u32x4{0u, 0u, 0u, 0u};       // single-tile case: own chunk
+    if (sender || (own && pipelined)) {
+      // senders take their tiles in the caller's order, if one is given
+      const uint16_t* ord = (sender && a.order)
+                                ? a.order + ((int64_t)op * a.nranks + g) * a.TPW
+                                : nullptr;
+      const int nsteps = ord ? a.TPW : mine;
+      for (int j = 0; j < nsteps; ++j) {
+        const int k = ord ? (int)ord[j] : j;
+        if (k >= mine) continue;
+        const int tile = tg + k * G;
+        u32x4 mine_v;
         if (pipelined) {
           mask_words(wnext, keep);
           mine_v = encode_words<P>(wnext, lane, seq);
           if (op + 1 < a.nops)
             load_chunk<P>(row + op_rows * a.in_stride, row_bytes, tile, lane, wnext);
+          own_v = mine_v;
         } else {
           mine_v = encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq);
         }
+        if (sender) store_chunk<P>(rs, dst0, 0u, 1, -1, tile, a.E, lane, mine_v);
       }
-      // ---- send ----
-      if (sender) {
-        store_chunk<P>(rs, dst0, 0u, 1, -1, tile, a.E, lane, mine_v);
-        if (P == kLL128) {
-          fence_release();
-          produce_flags(rs, dst0, 0u, 1, -1, tile, a.E, seq, lane);
-        }
-        if (a.trace) {
-          fence_release();
-          if (lane == 0)
-            __hip_atomic_fetch_max(
-                reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride + g,
-                (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
-                __HIP_MEMORY_SCOPE_AGENT);
-        }
+      if (sender && P == kLL128) {
+        fence_release();
+        for (int k = 0; k < mine; ++k)
+          produce_flags(rs, dst0, 0u, 1, -1, tg + k * G, a.E, seq, lane);
       }
-      if (!consumer) continue;
-      // ---- receive: peer w's chunk (or the own chunk) into LDS row w ----
+      if (sender && a.trace) {
+        fence_release();
+        if (lane == 0)
+          __hip_atomic_fetch_max(
+              reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride + g,
+              (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+              __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (!consumer) {
+      seq = seq_next(seq);
+      par ^= 1u;
+      continue;
+    }
+    // ---- then receive tile by tile: peer w's chunk (or the own chunk) ----
+    for (int k = 0; k < mine; ++k) {
+      const int tile = tg + k * G;
+      const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+      const bool active = loff < a.E;
       if (poller) {
         u32x4 got;
         const int st = poll_chunk<P>(rs, src0 + (uint32_t)w * a.slot_bytes + loff, active,
@@ -481,7 +498,8 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
           lds[buf][w][lane] = got;
         }
       } else {
-        lds[buf][w][lane] = mine_v;
+        lds[buf][w][lane] = pipelined ? own_v
+                                      : encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq);
       }
       __syncthreads();
       if (lds_err) return;                         // whole workgroup
@@ -494,7 +512,7 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
         reduce_store_tile<P, NMAX>(
             v, a.nranks, tile, a.E, lane,
             a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride, a.count);
-        if (a.trace && lane == 0)
+        if (a.trace && lane == 0 && k == mine - 1)
           __hip_atomic_fetch_max(
               reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride +
                   a.nranks + cself,
@@ -892,6 +910,9 @@ struct SimGeom {
 static bool sim_is_wide(const ar_sim_params* p) {
   return p->desc.proto != kBarrier && (p->flags & AR_SIM_NARROW) == 0;
 }
+static bool sim_force_wide(const ar_sim_params* p) {
+  return p->desc.proto != kBarrier && (p->flags & AR_SIM_WIDE) != 0;
+}
 
 static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wide,
                            SimGeom* g) {
@@ -938,17 +959,23 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
   return AR_OK;
 }
 
-// Kernel choice: the wide kernel when every one of its workgroups owns a
-// single tile (the latency-bound sizes); otherwise, or with AR_SIM_NARROW,
-// or for the barrier baseline, the one-wave-per-tile kernel.
+// Kernel choice: the wide kernel when each of its workgroups walks at most
+// kWideMaxTiles tiles (the latency-bound sizes) or AR_SIM_WIDE asks for it;
+// otherwise, or with AR_SIM_NARROW, or for the barrier baseline, the
+// one-wave-per-tile kernel.  Measured on MI355X at 4, 8 and 16 ranks: the
+// wide kernel wins by up to 2.7x where a workgroup owns one or two tiles;
+// from three tiles on, the one-wave kernel's larger resident grid (more
+// loads in flight) wins, by up to 2.6x at 512 KiB and beyond.
+static constexpr int kWideMaxTiles = 2;
 static int sim_geometry(const ar_sim_params* p, const DeviceInfo& di, SimGeom* g) {
   if (sim_is_wide(p)) {
     SimGeom gw;
     const int rc = sim_geometry_as(p, di, true, &gw);
-    if (rc == AR_OK && gw.TPW <= 1) {
+    if (rc == AR_OK && (gw.TPW <= kWideMaxTiles || sim_force_wide(p))) {
       *g = gw;
       return AR_OK;
     }
+    if (sim_force_wide(p)) return rc;
     if (rc != AR_OK && rc != AR_ECAPACITY && rc != AR_EINVAL) return rc;
   }
   return sim_geometry_as(p, di, false, g);
@@ -961,8 +988,10 @@ static int check_sim(const ar_sim_params* p) {
   const ar_desc* d = &p->desc;
   if (p->nops < 1) return AR_EINVAL;
   if (p->waves_per_rank < 0) return AR_EINVAL;
-  if ((p->flags & ~(AR_SIM_COOPERATIVE | AR_SIM_NARROW)) != 0 || p->reserved != 0)
+  if ((p->flags & ~(AR_SIM_COOPERATIVE | AR_SIM_NARROW | AR_SIM_WIDE)) != 0 ||
+      p->reserved != 0)
     return AR_EINVAL;
+  if ((p->flags & AR_SIM_NARROW) && (p->flags & AR_SIM_WIDE)) return AR_EINVAL;
   if (p->epoch.parity > 1u || p->epoch.seq == 0u) return AR_EINVAL;
   rc = check_rows(p->in, p->in_stride, d->count);
   if (rc) return rc;

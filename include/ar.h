@@ -252,13 +252,16 @@ int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
 #define AR_SIM_COOPERATIVE 1   /* launch with hipLaunchCooperativeKernel */
 #define AR_SIM_NARROW 2        /* one wave per tile serving every peer, instead
                                   of a workgroup of one wave per peer */
+#define AR_SIM_WIDE 4          /* the workgroup-of-one-wave-per-peer kernel even
+                                  when its workgroups must walk several tiles */
 
 typedef struct {
     ar_desc desc;
     int32_t nops;               /* >= 1 */
     int32_t waves_per_rank;     /* tile groups (wide) or waves (narrow) per
                                    rank, a multiple of 8; 0 = library choice */
-    int32_t flags;              /* AR_SIM_COOPERATIVE | AR_SIM_NARROW, or 0 */
+    int32_t flags;              /* AR_SIM_COOPERATIVE | AR_SIM_NARROW or
+                                   AR_SIM_WIDE, or 0 (library choice) */
     int32_t reserved;           /* must be 0 */
     const void* in;
     int64_t in_stride;

@@ -136,12 +136,12 @@ SIM_CASES = [(4, 1, 4096, 4), (4, 4, 4096, 4), (8, 1, 4096, 8), (8, 8, 4099, 6),
              (1, 1, 100, 3)]
 
 
-@pytest.mark.parametrize("kernel", ["auto", "narrow"])
+@pytest.mark.parametrize("kernel", ["auto", "narrow", "wide"])
 @pytest.mark.parametrize("proto", PROTOS)
 @pytest.mark.parametrize("nranks,ncons,count,nops", SIM_CASES)
 def test_sim_parity(proto, nranks, ncons, count, nops, kernel):
     print(f"[sim] {kernel} {proto} N={nranks} C={ncons} count={count} ops={nops}", flush=True)
-    flags = abi.AR_SIM_NARROW if kernel == "narrow" else 0
+    flags = {"auto": 0, "narrow": abi.AR_SIM_NARROW, "wide": abi.AR_SIM_WIDE}[kernel]
     ws = buffers.Workspace(nranks, count, proto, ncons)
     x = _x(7 * count + nops, (nops, nranks, count), specials=True)
     xd, stride = buffers.rows_to_device(x)
@@ -177,3 +177,32 @@ def test_sim_waves_per_rank_override(proto):
     got = buffers.rows_from_device(outd, count, (nops, 1))
     want = oracle.allreduce_ops(x, proto)
     assert np.array_equal(got[:, 0], want)
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel"])
+def test_sim_wide_shuffled_and_skewed(proto):
+    """The wide kernel with two tiles per workgroup, a shuffled send order
+    per (op, producer) and seeded producer delays, every consumer bit-exact."""
+    n, count, nops = 16, 4096 if proto != "sentinel" else 8192, 8
+    ws = buffers.Workspace(n, count, proto, n)
+    x = _x(500 + count, (nops, n, count), specials=True)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride))
+    print(f"[wide-order] {proto} N={n} count={count} geo={geo}", flush=True)
+    assert geo["kernel"] == "wide" and geo["tiles_per_wave"] == 2
+    order = inputs.tile_orders(17, nops, n, geo["tiles_per_wave"])
+    order_d = torch.from_numpy(order.view(np.int16)).to("cuda")
+    hz = abi.ar_wallclock_hz()
+    d_us = inputs.delays_us(18, nops, n, 5.0)
+    ticks = torch.from_numpy(np.round(d_us * hz * 1e-6).astype(np.int32)).to("cuda")
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS,
+           delay_ticks=ticks, tile_order=order_d)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    got = buffers.rows_from_device(outd, count, (nops, n))
+    want = oracle.allreduce_ops(x, proto, seq0)
+    for i in range(nops):
+        for c in range(n):
+            assert np.array_equal(got[i, c], want[i]), (i, c)
