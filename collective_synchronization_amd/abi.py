@@ -58,6 +58,7 @@ class ar_sim_params(ctypes.Structure):
 
 class ar_cost_entry(ctypes.Structure):
     _fields_ = [("nranks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_bytes", ctypes.c_int64),
                 ("alpha_us", ctypes.c_double * 4),
                 ("beta_us_per_byte", ctypes.c_double * 4)]
 
@@ -277,11 +278,14 @@ def ar_wallclock_hz() -> float:
 
 
 def cost_table(entries) -> "ctypes.Array":
-    """entries: iterable of dicts {nranks, alpha_us[4], beta_us_per_byte[4]}."""
+    """entries: iterable of dicts {nranks, alpha_us[4], beta_us_per_byte[4]}
+    and optionally max_bytes (upper end of the size range; absent or <= 0:
+    no upper end)."""
     entries = list(entries)
     arr = (ar_cost_entry * len(entries))()
     for i, e in enumerate(entries):
         arr[i].nranks = int(e["nranks"])
+        arr[i].max_bytes = int(e.get("max_bytes", 0))
         for p in range(4):
             arr[i].alpha_us[p] = float(e["alpha_us"][p])
             arr[i].beta_us_per_byte[p] = float(e["beta_us_per_byte"][p])

@@ -360,9 +360,11 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
 // Share mode: only rank 0 consumes; a producer rank's workgroup keeps its
 // wave 0, which takes the dual-buffer licence from rank 0's progress word.
 // Placement: workgroup (g, tg) sits on XCD (tg + rot(g)) mod 8 as in k_sim.
-template <int P, int NMAX, bool SHARE>
+// BATCH: tiles received per workgroup barrier (1 when every workgroup owns a
+// single tile, 2 otherwise; the two chunks of a peer are polled together).
+template <int P, int NMAX, bool SHARE, int BATCH>
 __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
-  __shared__ u32x4 lds[2][NMAX][kWave];
+  __shared__ u32x4 lds[2][BATCH][NMAX][kWave];
   __shared__ int lds_err;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
@@ -482,37 +484,58 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
       par ^= 1u;
       continue;
     }
-    // ---- then receive tile by tile: peer w's chunk (or the own chunk) ----
-    for (int k = 0; k < mine; ++k) {
-      const int tile = tg + k * G;
-      const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
-      const bool active = loff < a.E;
+    // ---- then receive, BATCH tiles per workgroup barrier ----
+    for (int k0 = 0; k0 < mine; k0 += BATCH) {
+      const int nb = (mine - k0) < BATCH ? (mine - k0) : BATCH;
       if (poller) {
-        u32x4 got;
-        const int st = poll_chunk<P>(rs, src0 + (uint32_t)w * a.slot_bytes + loff, active,
-                                     seq, stale, true, a.ctrl, a.timeout_ticks, lane, got);
+        uint32_t at[BATCH];
+        bool active[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          const uint32_t loff = (uint32_t)(tg + (k0 + j) * G) * kTileBytes + (uint32_t)lane * 16u;
+          at[j] = src0 + (uint32_t)w * a.slot_bytes + loff;
+          active[j] = j < nb && loff < a.E;
+        }
+        u32x4 got[BATCH];
+        int st;
+        if constexpr (BATCH == 1)
+          st = poll_chunk<P>(rs, at[0], active[0], seq, stale, true, a.ctrl,
+                             a.timeout_ticks, lane, got[0]);
+        else
+          st = poll_chunks<P, BATCH>(rs, at, active, nb, seq, stale, true, a.ctrl,
+                                     a.timeout_ticks, lane, got);
         if (st != 0) {
           if (lane == 0) lds_err = 1;
         } else {
           if (P == kSentinel && SHARE) fence_release();   // re-arm before the progress word
-          lds[buf][w][lane] = got;
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j)
+            if (j < nb) lds[buf][j][w][lane] = got[j];
         }
       } else {
-        lds[buf][w][lane] = pipelined ? own_v
-                                      : encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq);
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j)
+          if (j < nb)
+            lds[buf][j][w][lane] =
+                pipelined ? own_v
+                          : encode_chunk<P>(row, row_bytes, a.count, tg + (k0 + j) * G, lane, seq);
       }
       __syncthreads();
       if (lds_err) return;                         // whole workgroup
       // ---- reduce in rank order (own wave) ----
       if (own) {
-        u32x4 v[NMAX];
 #pragma unroll
-        for (int r = 0; r < NMAX; ++r)
-          v[r] = (r < a.nranks) ? lds[buf][r][lane] : u32x4{0u, 0u, 0u, 0u};
-        reduce_store_tile<P, NMAX>(
-            v, a.nranks, tile, a.E, lane,
-            a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride, a.count);
-        if (a.trace && lane == 0 && k == mine - 1)
+        for (int j = 0; j < BATCH; ++j) {
+          if (j >= nb) break;
+          u32x4 v[NMAX];
+#pragma unroll
+          for (int r = 0; r < NMAX; ++r)
+            v[r] = (r < a.nranks) ? lds[buf][j][r][lane] : u32x4{0u, 0u, 0u, 0u};
+          reduce_store_tile<P, NMAX>(
+              v, a.nranks, tg + (k0 + j) * G, a.E, lane,
+              a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride, a.count);
+        }
+        if (a.trace && lane == 0 && k0 + nb == mine)
           __hip_atomic_fetch_max(
               reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride +
                   a.nranks + cself,
@@ -850,8 +873,10 @@ static hipError_t launch_sim(const SimArgs& a, int blocks, bool coop, bool wide,
                              hipStream_t s) {
   SimArgs copy = a;
   void* args[] = {&copy};
-  const void* fn = wide ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE>)
-                        : reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>);
+  const void* fn =
+      !wide ? reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>)
+      : a.TPW <= 1 ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 1>)
+                   : reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 2>);
   const dim3 block(wide ? kWave * a.nranks : kSimBlock);
   if (coop) return hipLaunchCooperativeKernel(fn, dim3(blocks), block, args, 0, s);
   return hipLaunchKernel(fn, dim3(blocks), block, args, 0, s);
@@ -860,7 +885,8 @@ static hipError_t launch_sim(const SimArgs& a, int blocks, bool coop, bool wide,
 template <int P, int NMAX, bool SHARE>
 static int occupancy_of(bool wide, int nranks) {
   int nb = 0;
-  const void* fn = wide ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE>)
+  // the two-tile variant holds the larger LDS array: its residency bounds both
+  const void* fn = wide ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 2>)
                         : reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>);
   const int threads = wide ? kWave * nranks : kSimBlock;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, 0) != hipSuccess)
@@ -959,19 +985,19 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
   return AR_OK;
 }
 
-// Kernel choice: the wide kernel when each of its workgroups walks at most
-// kWideMaxTiles tiles (the latency-bound sizes) or AR_SIM_WIDE asks for it;
-// otherwise, or with AR_SIM_NARROW, or for the barrier baseline, the
-// one-wave-per-tile kernel.  Measured on MI355X at 4, 8 and 16 ranks: the
-// wide kernel wins by up to 2.7x where a workgroup owns one or two tiles;
-// from three tiles on, the one-wave kernel's larger resident grid (more
-// loads in flight) wins, by up to 2.6x at 512 KiB and beyond.
-static constexpr int kWideMaxTiles = 2;
+// Kernel choice: the wide kernel when each of its workgroups owns one tile,
+// or two tiles above 4 ranks, or when AR_SIM_WIDE asks for it; otherwise,
+// or with AR_SIM_NARROW, or for the barrier baseline, the one-wave-per-tile
+// kernel.  Measured on MI355X: with one tile per workgroup the wide kernel
+// wins everywhere (up to 2.6x); with two it wins at 8 and 16 ranks (up to
+// 1.7x) but loses up to 13% at 4 ranks, where one wave serves few peers;
+// from three tiles on, the one-wave kernel's larger resident grid wins.
 static int sim_geometry(const ar_sim_params* p, const DeviceInfo& di, SimGeom* g) {
   if (sim_is_wide(p)) {
     SimGeom gw;
     const int rc = sim_geometry_as(p, di, true, &gw);
-    if (rc == AR_OK && (gw.TPW <= kWideMaxTiles || sim_force_wide(p))) {
+    const int max_tiles = p->desc.nranks > 4 ? 2 : 1;
+    if (rc == AR_OK && (gw.TPW <= max_tiles || sim_force_wide(p))) {
       *g = gw;
       return AR_OK;
     }
@@ -1028,7 +1054,7 @@ const char* ar_status_string(int code) {
   }
 }
 
-int ar_abi_version(void) { return 1; }
+int ar_abi_version(void) { return 2; }
 
 int64_t ar_encoded_bytes(int32_t proto, int64_t count) {
   return encoded_bytes(proto, count);

@@ -409,6 +409,85 @@ __device__ __forceinline__ int poll_chunk(rsrc_t rs, uint32_t at, bool active,
   return 0;
 }
 
+// Poll up to B chunks of one peer at once (nb <= B of them in use): every
+// round issues the loads of all chunks still missing before waiting on any,
+// so a wave that owns several tiles pays one poll latency, not one per tile.
+// Same checks, order and re-arm as poll_chunk.
+template <int P, int B>
+__device__ __forceinline__ int poll_chunks(rsrc_t rs, const uint32_t (&at)[B],
+                                           const bool (&active)[B], int nb,
+                                           uint32_t seq, uint32_t stale,
+                                           bool rearm, int* ctrl,
+                                           uint64_t timeout_ticks, int lane,
+                                           u32x4 (&v)[B]) {
+  bool done[B];
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    v[j] = u32x4{0u, 0u, 0u, 0u};
+    done[j] = j >= nb;                              // wave-uniform
+  }
+  Waiter wt(timeout_ticks, ctrl);
+  if (P == kLL128) {
+    const bool flag_lane = (lane & 7) == 7;
+    u32x2 f[B];
+    while (true) {
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+        if (!done[j] && flag_lane && active[j]) f[j] = ld8(rs, at[j] + 8u);
+      bool all = true;
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (done[j]) continue;
+        bool ok = true, bad = false;
+        if (flag_lane && active[j]) {
+          ok = (f[j].x == seq) && (f[j].y == 0u);
+          bad = !ok && !(f[j].y == 0u && (f[j].x == 0u || f[j].x == stale));
+        }
+        if (__ballot(bad) != 0ull) {
+          if (lane == 0) report_error(ctrl, kEcorrupt);
+          return kEcorrupt;
+        }
+        if (__ballot(!ok) == 0ull) done[j] = true;
+        else all = false;
+      }
+      if (all) break;
+      if (!wt.again(lane)) return kEtimeout;
+    }
+    fence_acquire();
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (j < nb && active[j]) v[j] = ld16(rs, at[j]);
+    return 0;
+  }
+  while (true) {
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (!done[j] && active[j]) v[j] = ld16(rs, at[j]);
+    bool all = true;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (done[j]) continue;
+      bool ok = true, bad = false;
+      if (active[j]) classify<P>(v[j], seq, stale, ok, bad);
+      if (__ballot(bad) != 0ull) {
+        if (lane == 0) report_error(ctrl, kEcorrupt);
+        return kEcorrupt;
+      }
+      if (__ballot(!ok) == 0ull) done[j] = true;
+      else all = false;
+    }
+    if (all) break;
+    if (!wt.again(lane)) return kEtimeout;
+  }
+  if (P == kSentinel && rearm) {
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (j < nb && active[j])
+        st16(rs, at[j], u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
+  }
+  return 0;
+}
+
 // Fixed rank order: start from rank 0, add ranks 1..N-1 one binary32
 // addition at a time, round to bf16 (NaN -> 0x7FC0), store the lane's
 // elements of tile `tile` below `count`.

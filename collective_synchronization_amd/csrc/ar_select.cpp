@@ -7,8 +7,10 @@
 // Infrastructure", sections "What I learned from it" and "Where I think this
 // is heading": the choice is made from measurements, with a performance model
 // as the next step.  Here the model is the two-term latency/bandwidth form
-// T_p(S) = alpha_p + beta_p * S per protocol p and rank count, fitted to
-// measurements from this GPU by the Python side and passed in as a table.
+// T_p(S) = alpha_p + beta_p * S per protocol p, rank count and size range
+// (the simulator kernels change regime with size, so one line per regime),
+// fitted to measurements from this GPU by the Python side and passed in as a
+// table.
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -20,17 +22,30 @@ extern "C" int ar_select_protocol(const ar_cost_entry* table, int32_t nentries,
                                   int32_t* proto_out, double* predicted_us) {
   if (!table || nentries < 1 || !proto_out) return AR_EINVAL;
   if (payload_bytes < 0 || nranks < 1 || nranks > AR_MAX_RANKS) return AR_EINVAL;
-  // entry with the nearest rank count; ties go to the smaller rank count
-  int best = -1;
+  // rank count nearest to nranks; ties go to the smaller rank count
+  int32_t n_use = -1;
   int best_dist = 0;
   for (int i = 0; i < nentries; ++i) {
     const int dist = abs(table[i].nranks - nranks);
-    if (best < 0 || dist < best_dist ||
-        (dist == best_dist && table[i].nranks < table[best].nranks)) {
-      best = i;
+    if (n_use < 0 || dist < best_dist || (dist == best_dist && table[i].nranks < n_use)) {
+      n_use = table[i].nranks;
       best_dist = dist;
     }
   }
+  // size range holding the payload: smallest upper end >= payload (no upper
+  // end counts as infinite); if all end below it, the one ending last
+  auto upper = [&](int i) {
+    return table[i].max_bytes > 0 ? table[i].max_bytes : INT64_MAX;
+  };
+  int best = -1;
+  int last = -1;
+  for (int i = 0; i < nentries; ++i) {
+    if (table[i].nranks != n_use) continue;
+    const int64_t hi = upper(i);
+    if (hi >= payload_bytes && (best < 0 || hi < upper(best))) best = i;
+    if (last < 0 || hi > upper(last)) last = i;
+  }
+  if (best < 0) best = last;
   const ar_cost_entry& e = table[best];
   int choice = -1;
   double t_best = 0.0;

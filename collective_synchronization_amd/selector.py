@@ -7,11 +7,14 @@ moves.  "Why Microseconds Matter in AI Infrastructure", sections "What I
 learned from it" and "Where I think this is heading": the choice is made from
 measurements of the kernels, with a performance model as the next step.
 
-Model per protocol p and rank count N: T_p(S) = alpha_p + beta_p * S, with S
-the payload bytes per rank.  alpha and beta are fitted to per-op times
-measured with the persistent simulator on this GPU (system mode, every rank
-running the full program), minimising relative error so that the
-latency-bound small sizes count as much as the large ones.  The argmin itself
+Model per protocol p, rank count N and size range: T_p(S) = alpha_p +
+beta_p * S, with S the payload bytes per rank.  alpha and beta are fitted to
+per-op times measured with the persistent simulator on this GPU (system mode,
+every rank running the full program), minimising relative error so that the
+latency-bound small sizes count as much as the large ones.  The simulator
+changes kernel and geometry with size (a workgroup per peer at the smallest
+sizes, a wave per tile beyond), so each rank count may get two ranges, split
+where that lowers the worst-case regret on the measured points.  The argmin itself
 runs in the library (``ar_select_protocol``); this module measures, fits,
 stores and loads the table.
 
@@ -52,19 +55,84 @@ def fit_alpha_beta(sizes, times):
     return alpha, beta
 
 
-def fit_table(points):
-    """points: list of {nranks, proto, bytes, us}.  Returns table entries."""
+def _fit_range(points, n, sizes):
+    alpha = [-1.0] * 4
+    beta = [0.0] * 4
+    for pi, proto in enumerate(PROTOS):
+        pts = [p for p in points
+               if p["nranks"] == n and p["proto"] == proto and p["bytes"] in sizes]
+        if len(pts) >= 2:
+            alpha[pi], beta[pi] = fit_alpha_beta([p["bytes"] for p in pts],
+                                                 [p["us"] for p in pts])
+    return alpha, beta
+
+
+def _fit_ranges(points, n, cuts):
+    """One entry per size range; cuts are the inclusive upper ends of all
+    ranges but the last (which has no upper end)."""
+    sizes = sorted({p["bytes"] for p in points if p["nranks"] == n})
+    entries, lo = [], -1
+    for hi in list(cuts) + [None]:
+        rng = {s for s in sizes if s > lo and (hi is None or s <= hi)}
+        alpha, beta = _fit_range(points, n, rng)
+        entries.append({"nranks": n, "max_bytes": 0 if hi is None else int(hi),
+                        "alpha_us": alpha, "beta_us_per_byte": beta})
+        lo = hi if hi is not None else lo
+    return entries
+
+
+def _score(points, n, entries):
+    """(max regret, sum of squared relative model errors) on the measured
+    points of rank count n."""
+    worst, sq = 1.0, 0.0
+    for s in sorted({p["bytes"] for p in points if p["nranks"] == n}):
+        meas = {p["proto"]: p["us"] for p in points if p["nranks"] == n and p["bytes"] == s}
+        e = _range_entry(entries, s)
+        pick, _ = argmin_py(e, s)
+        if pick >= 0 and PROTOS[pick] in meas:
+            worst = max(worst, meas[PROTOS[pick]] / min(meas.values()))
+        for pi, proto in enumerate(PROTOS):
+            if proto in meas and e["alpha_us"][pi] >= 0:
+                t = e["alpha_us"][pi] + e["beta_us_per_byte"][pi] * s
+                sq += ((t - meas[proto]) / meas[proto]) ** 2
+    return worst, sq
+
+
+def fit_table(points, max_ranges=2):
+    """points: list of {nranks, proto, bytes, us}.  Returns table entries.
+
+    Per rank count, one alpha-beta line per protocol over the whole sweep,
+    or, with max_ranges=2, two lines split at the measured size that gives
+    the lowest worst-case regret on the measured points (ties: one range,
+    then the smaller squared relative error).  Each range holds at least two
+    measured sizes."""
     entries = []
     for n in sorted({p["nranks"] for p in points}):
-        alpha = [-1.0] * 4
-        beta = [0.0] * 4
-        for pi, proto in enumerate(PROTOS):
-            pts = [p for p in points if p["nranks"] == n and p["proto"] == proto]
-            if len(pts) >= 2:
-                alpha[pi], beta[pi] = fit_alpha_beta([p["bytes"] for p in pts],
-                                                     [p["us"] for p in pts])
-        entries.append({"nranks": n, "alpha_us": alpha, "beta_us_per_byte": beta})
+        sizes = sorted({p["bytes"] for p in points if p["nranks"] == n})
+        best = None
+        cands = [()]
+        if max_ranges >= 2:
+            cands += [(c,) for c in sizes[1:-2]]
+        for cuts in cands:
+            ent = _fit_ranges(points, n, cuts)
+            worst, sq = _score(points, n, ent)
+            key = (round(worst, 9), len(cuts), sq)
+            if best is None or key < best[0]:
+                best = (key, ent)
+        entries.extend(best[1])
     return entries
+
+
+def _range_entry(entries, nbytes):
+    """The entry of one rank count whose size range holds nbytes (the same
+    rule as the library)."""
+    def upper(e):
+        m = e.get("max_bytes", 0)
+        return m if m > 0 else float("inf")
+    fit = [e for e in entries if upper(e) >= nbytes]
+    if fit:
+        return min(fit, key=upper)
+    return max(entries, key=upper)
 
 
 def argmin_py(entry, nbytes):
@@ -77,6 +145,15 @@ def argmin_py(entry, nbytes):
         if best < 0 or t < tbest:
             best, tbest = p, t
     return best, tbest
+
+
+def select_py(entries, nbytes, nranks):
+    """Plain-Python statement of the library's choice: nearest rank count
+    (ties: smaller), then the size range, then the argmin."""
+    ns = sorted({e["nranks"] for e in entries})
+    n_use = min(ns, key=lambda n: (abs(n - nranks), n))
+    return argmin_py(_range_entry([e for e in entries if e["nranks"] == n_use], nbytes),
+                     nbytes)
 
 
 def regret(points, entries):
@@ -169,23 +246,34 @@ def main() -> int:
     ap.add_argument("--out", default=TABLE_PATH)
     ap.add_argument("--ranks", default="4,8,16")
     ap.add_argument("--reps", type=int, default=7)
+    ap.add_argument("--refit", metavar="TABLE",
+                    help="refit the points stored in an existing table instead of measuring")
     args = ap.parse_args()
     t0 = time.time()
-    points = sweep(tuple(int(r) for r in args.ranks.split(",")), reps=args.reps)
+    old = None
+    if args.refit:
+        old = load_table(args.refit)
+        points = old["points"]
+        measured_with = old["measured_with"]
+    else:
+        points = sweep(tuple(int(r) for r in args.ranks.split(",")), reps=args.reps)
+        measured_with = ("python -m collective_synchronization_amd.selector "
+                         f"--ranks {args.ranks} --reps {args.reps} (one MI355X, "
+                         "system mode, persistent simulator, median per-op time)")
     entries = fit_table(points)
     reg = regret(points, entries)
     worst = max(r["regret"] for r in reg if r["regret"])
     table = {
-        "model": "T_p(S) = alpha_us[p] + beta_us_per_byte[p] * S; S = payload bytes per rank",
+        "model": "T_p(S) = alpha_us[p] + beta_us_per_byte[p] * S for S <= max_bytes "
+                 "(0: no upper end); S = payload bytes per rank",
         "protocols": list(PROTOS),
-        "measured_with": "python -m collective_synchronization_amd.selector "
-                         f"--ranks {args.ranks} --reps {args.reps} (one MI355X, "
-                         "system mode, persistent simulator, median per-op time)",
+        "measured_with": measured_with,
         "entries": entries,
         "points": points,
         "regret": reg,
         "max_regret": worst,
-        "sweep_seconds": round(time.time() - t0, 1),
+        "sweep_seconds": (old.get("sweep_seconds") if old
+                          else round(time.time() - t0, 1)),
     }
     with open(args.out, "w") as fh:
         json.dump(table, fh, indent=1)

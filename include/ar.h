@@ -298,16 +298,23 @@ int ar_wallclock_hz(double* hz);
  * encoding is chosen by message size and number of GPUs, trading
  * synchronization cost against extra bytes; "Why Microseconds Matter in AI
  * Infrastructure", "What I learned from it": selection from measurements).
- * Model per protocol p and rank count: T_p(S) = alpha_us[p] + beta_us_per_byte[p] * S,
- * with S = 2*count payload bytes per rank.  The entry with the nearest
- * nranks is used (ties: the smaller).  A protocol with alpha_us < 0 is
- * unavailable.  Ties go to the lower protocol id (LL < LL128 < SENTINEL <
- * BARRIER).  Host only; writes the chosen id and, if non-NULL, its predicted
- * time.
+ * Model per protocol p, rank count and size range:
+ *   T_p(S) = alpha_us[p] + beta_us_per_byte[p] * S,
+ * with S = 2*count payload bytes per rank.  The entries with the nearest
+ * nranks are used (ties: the smaller).  Among them, the entry whose range
+ * holds S: the smallest max_bytes >= S, where max_bytes <= 0 means no upper
+ * bound; if every range ends below S, the one that ends last.  Several
+ * entries per rank count give a piecewise model (the kernels change regime
+ * with size).  A protocol with alpha_us < 0 is unavailable.  Ties go to the
+ * lower protocol id (LL < LL128 < SENTINEL < BARRIER).  Host only; writes the
+ * chosen id and, if non-NULL, its predicted time.  AR_EINVAL for a NULL
+ * table or proto_out, nentries < 1, S < 0, nranks outside 1..16, or no
+ * available protocol in the chosen entry.
  */
 typedef struct {
     int32_t nranks;
-    int32_t reserved;
+    int32_t reserved;           /* 0 */
+    int64_t max_bytes;          /* inclusive upper end of the range; <= 0: none */
     double alpha_us[4];
     double beta_us_per_byte[4];
 } ar_cost_entry;

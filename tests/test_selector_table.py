@@ -66,3 +66,53 @@ def test_committed_table():
     worst = max(r["regret"] for r in recomputed if r["regret"])
     assert worst == pytest.approx(t["max_regret"])
     assert worst < 1.5
+
+
+def test_library_ranges_match_python():
+    """Piecewise tables: the library picks the nearest rank count, then the
+    size range holding the payload, then the argmin, as select_py states."""
+    rng = np.random.default_rng(11)
+    entries = []
+    for n in (4, 8, 16):
+        cuts = sorted(rng.choice([2 ** k for k in range(10, 22)], size=2, replace=False))
+        for hi in list(cuts) + [0]:
+            entries.append({"nranks": n, "max_bytes": int(hi),
+                            "alpha_us": list(rng.uniform(1, 6, 4)),
+                            "beta_us_per_byte": list(rng.uniform(5e-5, 3e-4, 4))})
+    rng.shuffle(entries)
+    table = abi.cost_table(entries)
+    for n in (1, 4, 6, 8, 12, 16):
+        for s in [0] + [2 ** k for k in range(8, 24)] + [3000, 70000]:
+            pick, pred = abi.ar_select_protocol(table, s, n)
+            ref, tref = selector.select_py(entries, s, n)
+            assert pick == ref and pred == pytest.approx(tref), (n, s)
+
+
+def test_library_closed_ranges_fall_back_to_last():
+    e = [{"nranks": 8, "max_bytes": 4096, "alpha_us": [1, 2, 3, 4],
+          "beta_us_per_byte": [0, 0, 0, 0]},
+         {"nranks": 8, "max_bytes": 65536, "alpha_us": [4, 3, 2, 1],
+          "beta_us_per_byte": [0, 0, 0, 0]}]
+    t = abi.cost_table(e)
+    assert abi.ar_select_protocol(t, 4096, 8)[0] == abi.AR_LL
+    assert abi.ar_select_protocol(t, 4097, 8)[0] == abi.AR_BARRIER
+    assert abi.ar_select_protocol(t, 1 << 30, 8)[0] == abi.AR_BARRIER
+
+
+def test_fit_finds_regime_change():
+    """Two regimes (a cheap latency line that turns steep past 16 KiB for
+    LL): one line per protocol cannot rank the protocols right on both
+    sides; the two-range fit splits at 16 KiB and has no regret."""
+    pts = []
+    for s in selector.SIZES:
+        ll = 1.5 + 2e-5 * s if s <= 16384 else 1.0 + 2e-4 * s
+        sent = 2.0 + 1e-5 * s
+        for proto, us in (("ll", ll), ("ll128", sent + 1.0), ("sentinel", sent),
+                          ("barrier", 4.0 + 4e-4 * s)):
+            pts.append({"nranks": 8, "proto": proto, "bytes": s, "us": us})
+    one = selector.fit_table(pts, max_ranges=1)
+    two = selector.fit_table(pts, max_ranges=2)
+    assert len(one) == 1 and len(two) == 2
+    assert sorted(e["max_bytes"] for e in two) == [0, 16384]
+    assert max(r["regret"] for r in selector.regret(pts, one)) > 1.05
+    assert max(r["regret"] for r in selector.regret(pts, two)) == pytest.approx(1.0)
