@@ -1,4 +1,5 @@
-"""CPU oracle for the self-synchronizing one-shot bf16 all-reduce.
+"""CPU oracle for the self-synchronizing bf16 all-reduce (one-shot and
+two-shot) and all-gather.
 
 TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
@@ -15,7 +16,10 @@ arithmetic is in the C file, which cites the pages it follows:
 * "flash-comm: Self-Synchronizing Collective Communication for LLM Decoding",
   abstract -- per-block readiness evidence, fixed reduction order;
 * "SiFAR: Synchronization-Free All-Reduce for Low-Latency LLM Inference",
-  abstract -- one-shot all-reduce with dual buffering.
+  abstract -- one-shot all-reduce with dual buffering; the two-shot form
+  (reduce-scatter of shares, then all-gather) for more GPUs;
+* flash-comm abstract again -- the same transfers carry a standalone
+  all-gather.
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against
 something other than itself (exhaustive sweeps against torch and numpy, an
@@ -77,6 +81,15 @@ def _load():
     lib.o_allreduce.argtypes = [ctypes.c_int, u16p, i64, ctypes.c_int,
                                 ctypes.c_uint32, i32p, u16p]
     lib.o_allreduce.restype = ctypes.c_int
+    lib.o_shard_bounds.argtypes = [i64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.o_shard_bounds.restype = None
+    lib.o_allgather.argtypes = [ctypes.c_int, u16p, i64, ctypes.c_int,
+                                ctypes.c_uint32, i32p, u16p]
+    lib.o_allgather.restype = ctypes.c_int
+    lib.o_twoshot.argtypes = [ctypes.c_int, u16p, i64, ctypes.c_int,
+                              ctypes.c_uint32, u16p]
+    lib.o_twoshot.restype = ctypes.c_int
     lib.o_bf16_rne_array.argtypes = [f32p, i64, u16p]
     lib.o_bf16_rne_array.restype = None
     lib.o_canon_in_array.argtypes = [u16p, i64, u16p]
@@ -202,6 +215,69 @@ def allreduce_ops(x: np.ndarray, proto="ll", seq0: int = 1) -> np.ndarray:
         st, out[i] = allreduce(x[i], proto, seq)
         if st != READY:
             raise RuntimeError(f"oracle op {i} not ready: status {st}")
+        seq = epoch_next(seq)
+    return out
+
+
+def shard_bounds(count: int, n: int, k: int):
+    """[lo, hi) of the share rank k owns in a two-shot all-reduce."""
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    _load().o_shard_bounds(count, n, k, ctypes.byref(lo), ctypes.byref(hi))
+    return lo.value, hi.value
+
+
+def allgather(x: np.ndarray, proto="ll", seq: int = 1, perm=None):
+    """Encode, deliver in `perm` order, validate and decode every rank's
+    payload.  x: uint16 [n, count].  Returns (status, uint16 [n, count])."""
+    x = _u16(x)
+    n, count = x.shape
+    out = np.zeros((n, max(count, 1)), dtype=np.uint16)
+    pp = None
+    if perm is not None:
+        perm = np.ascontiguousarray(perm, dtype=np.int32)
+        if perm.shape != (n,):
+            raise ValueError("perm must be a permutation of range(n)")
+        pp = _ptr(perm, ctypes.c_int32)
+    st = _load().o_allgather(n, _ptr(x, ctypes.c_uint16), count, proto_id(proto),
+                             seq, pp, _ptr(out, ctypes.c_uint16))
+    return int(st), out[:, :count]
+
+
+def allgather_ops(x: np.ndarray, proto="ll", seq0: int = 1) -> np.ndarray:
+    """Expected outputs of K back-to-back all-gathers: [K, n, count] -> [K, n, count]."""
+    x = _u16(x)
+    K = x.shape[0]
+    out = np.empty_like(x)
+    seq = seq0
+    for i in range(K):
+        st, out[i] = allgather(x[i], proto, seq)
+        if st != READY:
+            raise RuntimeError(f"oracle all-gather {i} not ready: status {st}")
+        seq = epoch_next(seq)
+    return out
+
+
+def twoshot(x: np.ndarray, proto="ll", seq: int = 1):
+    """Two-shot all-reduce: reduce-scatter of shares, then all-gather of the
+    reduced shares.  x: uint16 [n, count].  Returns (status, uint16 [count])."""
+    x = _u16(x)
+    n, count = x.shape
+    out = np.zeros(max(count, 1), dtype=np.uint16)
+    st = _load().o_twoshot(n, _ptr(x, ctypes.c_uint16), count, proto_id(proto), seq,
+                           _ptr(out, ctypes.c_uint16))
+    return int(st), out[:count]
+
+
+def twoshot_ops(x: np.ndarray, proto="ll", seq0: int = 1) -> np.ndarray:
+    """Expected outputs of K back-to-back two-shot all-reduces: [K, n, count] -> [K, count]."""
+    x = _u16(x)
+    K, n, count = x.shape
+    out = np.empty((K, count), dtype=np.uint16)
+    seq = seq0
+    for i in range(K):
+        st, out[i] = twoshot(x[i], proto, seq)
+        if st != READY:
+            raise RuntimeError(f"oracle two-shot {i} not ready: status {st}")
         seq = epoch_next(seq)
     return out
 

@@ -389,3 +389,120 @@ void o_canon_in_array(const uint16_t* b, int64_t n, uint16_t* out)
     for (int64_t i = 0; i < n; ++i)
         out[i] = o_canon_in(b[i]);
 }
+
+/* ------------------------------------------------ all-gather, two-shot --- */
+/*
+ * [FC] abstract: the same self-synchronizing transfer also carries a
+ * standalone all-gather.  [SiFAR] abstract: the two-shot all-reduce (a
+ * reduce-scatter, each rank reducing one share, then an all-gather of the
+ * reduced shares) is the form that scales to more GPUs.
+ *
+ * Readings (listed in the design doc):
+ *  - shares: rank k owns elements [lo_k, hi_k) with width C = ceil(count/n)
+ *    rounded up to a multiple of 8 elements (16 bytes), lo_k = min(k*C,
+ *    count), hi_k = min(lo_k + C, count); trailing shares may be empty.
+ *  - each share travels with the same encodings as a whole payload, encoded
+ *    on its own (element 0 of the share is element 0 of the encoding).
+ *  - all-gather output: n rows, row r = rank r's payload as decoded (the
+ *    sentinel protocol delivers canon_in(x)).
+ */
+void o_shard_bounds(int64_t count, int n, int k, int64_t* lo, int64_t* hi)
+{
+    int64_t w = (count + n - 1) / n;
+    w = (w + 7) / 8 * 8;
+    int64_t a = (int64_t)k * w;
+    if (a > count)
+        a = count;
+    int64_t b = a + w;
+    if (b > count)
+        b = count;
+    *lo = a;
+    *hi = b;
+}
+
+/*
+ * All-gather as seen by one receiving rank: every rank's payload is encoded
+ * for epoch seq, delivered in perm order (NULL = rank order), validated and
+ * decoded into row r of out (n rows of `count`).  Returns the worst status.
+ */
+int o_allgather(int n, const uint16_t* x, int64_t count, int proto,
+                uint32_t seq, const int32_t* perm, uint16_t* out)
+{
+    if (n < 1 || count < 0)
+        return O_CORRUPT;
+    int64_t E = o_encoded_bytes(proto, count);
+    if (E < 0)
+        return O_CORRUPT;
+    uint8_t* wire = (uint8_t*)malloc((size_t)(E > 0 ? E : 1));
+    int* seen = (int*)calloc((size_t)n, sizeof(int));
+    if (!wire || !seen) {
+        free(wire); free(seen);
+        return O_CORRUPT;
+    }
+    int status = O_READY;
+    for (int i = 0; i < n; ++i) {
+        int r = perm ? perm[i] : i;
+        if (r < 0 || r >= n || seen[r]) {
+            status = O_CORRUPT;
+            break;
+        }
+        seen[r] = 1;
+        o_encode(proto, x + (int64_t)r * count, count, seq, wire);
+        int c = o_decode(proto, wire, count, seq, out + (int64_t)r * count);
+        if (c > status)
+            status = c;
+    }
+    free(wire);
+    free(seen);
+    return status;
+}
+
+/*
+ * Two-shot all-reduce, every step in order:
+ *  1. reduce-scatter: for each share k, every rank r's elements [lo_k, hi_k)
+ *     are encoded for epoch seq, delivered to rank k, validated and decoded;
+ *     rank k reduces them in rank order (o_reduce) into its reduced share;
+ *  2. all-gather: each reduced share is encoded for epoch seq, delivered to
+ *     every rank, validated, decoded and written to out[lo_k, hi_k).
+ * x: n rows of `count`; out: `count`.  Returns the worst status.
+ */
+int o_twoshot(int n, const uint16_t* x, int64_t count, int proto,
+              uint32_t seq, uint16_t* out)
+{
+    if (n < 1 || count < 0)
+        return O_CORRUPT;
+    int64_t lo0, w;
+    o_shard_bounds(count, n, 0, &lo0, &w);          /* w = width of share 0 */
+    w -= lo0;
+    int64_t Emax = o_encoded_bytes(proto, w > 0 ? w : 1);
+    uint8_t* wire = (uint8_t*)malloc((size_t)(Emax > 0 ? Emax : 1));
+    uint16_t* y = (uint16_t*)malloc((size_t)(n * (w > 0 ? w : 1)) * 2);
+    uint16_t* red = (uint16_t*)malloc((size_t)(w > 0 ? w : 1) * 2);
+    if (!wire || !y || !red) {
+        free(wire); free(y); free(red);
+        return O_CORRUPT;
+    }
+    int status = O_READY;
+    for (int k = 0; k < n; ++k) {
+        int64_t lo, hi;
+        o_shard_bounds(count, n, k, &lo, &hi);
+        int64_t m = hi - lo;
+        if (m == 0)
+            continue;
+        for (int r = 0; r < n; ++r) {                /* step 1 */
+            o_encode(proto, x + (int64_t)r * count + lo, m, seq, wire);
+            int c = o_decode(proto, wire, m, seq, y + (int64_t)r * m);
+            if (c > status)
+                status = c;
+        }
+        o_reduce(n, y, m, red);
+        o_encode(proto, red, m, seq, wire);           /* step 2 */
+        int c = o_decode(proto, wire, m, seq, out + lo);
+        if (c > status)
+            status = c;
+    }
+    free(wire);
+    free(y);
+    free(red);
+    return status;
+}
