@@ -26,6 +26,9 @@ AR_SIM_COOPERATIVE = 1
 AR_SIM_NARROW = 2
 AR_SIM_WIDE = 4
 AR_MAX_RANKS = 16
+AR_ALLREDUCE, AR_ALLGATHER, AR_TWOSHOT = 0, 1, 2
+COLLECTIVE_IDS = {"allreduce": AR_ALLREDUCE, "allgather": AR_ALLGATHER,
+                  "twoshot": AR_TWOSHOT}
 PROTO_IDS = {"ll": AR_LL, "ll128": AR_LL128, "sentinel": AR_SENTINEL,
              "barrier": AR_BARRIER}
 PROTO_NAMES = {v: k for k, v in PROTO_IDS.items()}
@@ -34,7 +37,7 @@ PROTO_NAMES = {v: k for k, v in PROTO_IDS.items()}
 class ar_desc(ctypes.Structure):
     _fields_ = [("nranks", ctypes.c_int32), ("nconsumers", ctypes.c_int32),
                 ("count", ctypes.c_int64), ("proto", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("collective", ctypes.c_int32)]
 
 
 class ar_epoch(ctypes.Structure):
@@ -93,6 +96,9 @@ _SIGS = {
     "ar_encoded_bytes": ([_i32, _i64], _i64),
     "ar_slot_bytes": ([_i32, _i64], _i64),
     "ar_scratch_bytes": ([ctypes.POINTER(ar_desc)], _i64),
+    "ar_desc_slot_bytes": ([ctypes.POINTER(ar_desc)], _i64),
+    "ar_shard_bounds": ([_i64, _i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)],
+                        ctypes.c_int),
     "ar_ctrl_bytes": ([], _i64),
     "ar_ctrl_reset": ([_vp, _vp], ctypes.c_int),
     "ar_epoch_init": ([ctypes.POINTER(ar_epoch)], ctypes.c_int),
@@ -104,6 +110,8 @@ _SIGS = {
     "ar_pack_plain": ([ctypes.POINTER(ar_desc), _vp, _i64, _vp, ar_epoch, _vp], ctypes.c_int),
     "ar_arm_sentinel": ([ctypes.POINTER(ar_desc), _vp, _i32, _vp], ctypes.c_int),
     "ar_reduce_validate": ([ctypes.POINTER(ar_desc), _vp, _vp, _i64, ar_epoch, _vp,
+                            _u64, _i32, _vp], ctypes.c_int),
+    "ar_gather_validate": ([ctypes.POINTER(ar_desc), _vp, _vp, _i64, ar_epoch, _vp,
                             _u64, _i32, _vp], ctypes.c_int),
     "ar_sim_run": ([ctypes.POINTER(ar_sim_params), _vp], ctypes.c_int),
     "ar_sim_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
@@ -165,8 +173,13 @@ def proto_id(p) -> int:
     return PROTO_IDS[p] if isinstance(p, str) else int(p)
 
 
-def make_desc(nranks: int, count: int, proto, nconsumers: int = 1) -> ar_desc:
-    return ar_desc(nranks, nconsumers, count, proto_id(proto), 0)
+def collective_id(c) -> int:
+    return COLLECTIVE_IDS[c] if isinstance(c, str) else int(c)
+
+
+def make_desc(nranks: int, count: int, proto, nconsumers: int = 1,
+              collective=AR_ALLREDUCE) -> ar_desc:
+    return ar_desc(nranks, nconsumers, count, proto_id(proto), collective_id(collective))
 
 
 # ---------------------------------------------------------------- sizes ---
@@ -181,6 +194,17 @@ def ar_slot_bytes(proto, count: int) -> int:
 
 def ar_scratch_bytes(desc: ar_desc) -> int:
     return _check(_lib.ar_scratch_bytes(ctypes.byref(desc)), "ar_scratch_bytes")
+
+
+def ar_desc_slot_bytes(desc: ar_desc) -> int:
+    return _check(_lib.ar_desc_slot_bytes(ctypes.byref(desc)), "ar_desc_slot_bytes")
+
+
+def ar_shard_bounds(count: int, nranks: int, k: int):
+    lo, hi = _i64(), _i64()
+    _check(_lib.ar_shard_bounds(count, nranks, k, ctypes.byref(lo), ctypes.byref(hi)),
+           "ar_shard_bounds")
+    return lo.value, hi.value
 
 
 def ar_ctrl_bytes() -> int:
@@ -247,6 +271,13 @@ def ar_reduce_validate(desc, scratch, out, out_stride, epoch, ctrl,
     _check(_lib.ar_reduce_validate(ctypes.byref(desc), _ptr(scratch), _ptr(out),
                                    out_stride, epoch, _ptr(ctrl), timeout_ns, flags,
                                    _stream(stream)), "ar_reduce_validate")
+
+
+def ar_gather_validate(desc, scratch, out, out_stride, epoch, ctrl,
+                       timeout_ns: int = 0, flags: int = 0, stream=None) -> None:
+    _check(_lib.ar_gather_validate(ctypes.byref(desc), _ptr(scratch), _ptr(out),
+                                   out_stride, epoch, _ptr(ctrl), timeout_ns, flags,
+                                   _stream(stream)), "ar_gather_validate")
 
 
 def sim_params(desc, nops, inp, in_stride, out, out_stride, scratch, ctrl, epoch,

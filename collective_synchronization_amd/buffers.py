@@ -54,8 +54,8 @@ class Workspace:
     """
 
     def __init__(self, nranks: int, count: int, proto, nconsumers: int = 1,
-                 device="cuda"):
-        self.desc = abi.make_desc(nranks, count, proto, nconsumers)
+                 device="cuda", collective=abi.AR_ALLREDUCE):
+        self.desc = abi.make_desc(nranks, count, proto, nconsumers, collective)
         self.device = device
         self.scratch_bytes = abi.ar_scratch_bytes(self.desc)
         self.scratch = device_bytes(self.scratch_bytes, device)
@@ -68,6 +68,15 @@ class Workspace:
     def proto(self) -> int:
         return self.desc.proto
 
+    @property
+    def collective(self) -> int:
+        return self.desc.collective
+
+    def gather_stride(self) -> int:
+        """Output row stride of one all-gather consumer: nranks rows of
+        count rounded up to 8 elements."""
+        return self.desc.nranks * row_stride(self.desc.count)
+
     def status(self) -> int:
         return int(self.ctrl[:4].view(torch.int32).item())
 
@@ -75,10 +84,14 @@ class Workspace:
         abi.ar_ctrl_reset(self.ctrl, stream)
 
     def slot_view(self) -> np.ndarray:
-        """Host copy of the receive buffers: uint8 [nconsumers, 2, nranks, slot]."""
+        """Host copy of the receive buffers: uint8 [nconsumers, 2, nranks, slot]
+        ([2 regions, nconsumers, 2, nranks, slot] for the two-shot all-reduce:
+        reduce-scatter, then all-gather)."""
         d = self.desc
-        slot = abi.ar_slot_bytes(d.proto, d.count)
+        slot = abi.ar_desc_slot_bytes(d)
         raw = self.scratch[: self.scratch_bytes].cpu().numpy()
+        if d.collective == abi.AR_TWOSHOT:
+            return raw.reshape(2, d.nconsumers, 2, d.nranks, slot)
         return raw.reshape(d.nconsumers, 2, d.nranks, slot)
 
     # -------------------------------------------------- stream-ordered op --
@@ -89,6 +102,11 @@ class Workspace:
     def reduce(self, out_dev, out_stride, timeout_ns=0, rearm=True, stream=None) -> None:
         flags = abi.AR_FLAG_REARM if (rearm and self.desc.proto == abi.AR_SENTINEL) else 0
         abi.ar_reduce_validate(self.desc, self.scratch, out_dev, out_stride, self.epoch,
+                               self.ctrl, timeout_ns, flags, stream)
+
+    def gather(self, out_dev, out_stride, timeout_ns=0, rearm=True, stream=None) -> None:
+        flags = abi.AR_FLAG_REARM if (rearm and self.desc.proto == abi.AR_SENTINEL) else 0
+        abi.ar_gather_validate(self.desc, self.scratch, out_dev, out_stride, self.epoch,
                                self.ctrl, timeout_ns, flags, stream)
 
     def flip(self, nops: int = 1) -> None:

@@ -1,0 +1,682 @@
+// ar_collectives.hip -- the standalone all-gather and the two-shot
+// all-reduce on the same self-synchronizing transfers (gfx950).
+//
+// "flash-comm: Self-Synchronizing Collective Communication for LLM
+// Decoding", abstract: the transfers that carry their own readiness evidence
+// also serve a standalone all-gather.  "SiFAR: Synchronization-Free
+// All-Reduce for Low-Latency LLM Inference", abstract: the two-shot form
+// (reduce-scatter of shares, then all-gather of the reduced shares) is the
+// one that scales to more GPUs.  Here each share and each reduced share
+// travels with the one-shot encodings (LL, LL128, sentinel) and the same
+// dual-buffered epochs; the two exchanges use two receive regions.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/ar.h"
+#include "ar_host.h"
+#include "ar_protocols.h"
+
+namespace ar {
+
+// =========================================================== stream-ordered
+
+struct GatherArgs {
+  uint16_t* out;
+  int64_t out_stride, row_stride, count;
+  const uint8_t* scratch;
+  uint32_t scratch_bytes;
+  uint32_t E, slot_bytes;
+  int32_t nranks, nconsumers, tiles;
+  uint32_t seq, parity;
+  int* ctrl;
+  uint64_t timeout_ticks;
+  int32_t rearm;
+};
+
+// One wave per (consumer, source rank, tile): poll, validate, decode into
+// the source's output row.
+template <int P>
+__global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int per_c = a.nranks * a.tiles;
+  const int c = gw / per_c;
+  if (c >= a.nconsumers) return;
+  const int rem = gw - c * per_c;
+  const int r = rem / a.tiles;
+  const int tile = rem - r * a.tiles;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+  const uint32_t at =
+      (((uint32_t)c * 2u + a.parity) * (uint32_t)a.nranks + (uint32_t)r) * a.slot_bytes + loff;
+  u32x4 v;
+  if (poll_chunk<P>(rs, at, loff < a.E, a.seq, seq_prev(seq_prev(a.seq)), a.rearm != 0,
+                    a.ctrl, a.timeout_ticks, lane, v) != 0)
+    return;
+  store_chunk_elems<P>(a.out + (int64_t)c * a.out_stride + (int64_t)r * a.row_stride,
+                       a.count, tile, a.E, lane, v);
+}
+
+struct TsArgs {
+  const uint16_t* in;      // pack only
+  int64_t in_stride;
+  uint16_t* out;           // reduce / gather
+  int64_t out_stride, count, width;
+  const uint8_t* scratch;
+  uint32_t scratch_bytes, slot_bytes, ag0;   // ag0: byte offset of the all-gather region
+  int32_t nranks, tiles;                     // tiles of one full share
+  uint32_t seq, parity;
+  int* ctrl;
+  uint64_t timeout_ticks;
+  int32_t rearm;
+};
+
+__device__ __forceinline__ void share_of(int64_t count, int64_t width, int k, int64_t& lo,
+                                         int64_t& m) {
+  int64_t a = (int64_t)k * width;
+  if (a > count) a = count;
+  int64_t b = a + width;
+  if (b > count) b = count;
+  lo = a;
+  m = b - a;
+}
+
+// One wave per (rank r, consumer c, tile of share c): encode rank r's share c
+// into the reduce-scatter slot r of consumer c.
+template <int P>
+__global__ __launch_bounds__(kBlock) void k_ts_pack(TsArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int per_r = a.nranks * a.tiles;
+  const int r = gw / per_r;
+  if (r >= a.nranks) return;
+  const int rem = gw - r * per_r;
+  const int c = rem / a.tiles;
+  const int tile = rem - c * a.tiles;
+  int64_t lo, m;
+  share_of(a.count, a.width, c, lo, m);
+  const uint32_t E = enc_bytes<P>(m);
+  if ((uint32_t)tile * kTileBytes >= E) return;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t dst0 =
+      (((uint32_t)c * 2u + a.parity) * (uint32_t)a.nranks + (uint32_t)r) * a.slot_bytes;
+  const uint16_t* row = a.in + (int64_t)r * a.in_stride + lo;
+  produce_data<P>(rs, dst0, 0u, 1, -1, row, (uint32_t)((m * 2 + 15) & ~int64_t(15)), m,
+                  tile, E, a.seq, lane);
+  if (P == kLL128) {
+    fence_release();
+    produce_flags(rs, dst0, 0u, 1, -1, tile, E, a.seq, lane);
+  }
+}
+
+// One wave per (consumer c, tile of share c): poll and validate share c of
+// every rank, reduce in rank order, write it to consumer c's output and send
+// it to every other consumer's all-gather slot c.
+template <int P, int NMAX>
+__global__ __launch_bounds__(kBlock) void k_ts_reduce(TsArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int c = gw / a.tiles;
+  if (c >= a.nranks) return;
+  const int tile = gw - c * a.tiles;
+  int64_t lo, m;
+  share_of(a.count, a.width, c, lo, m);
+  const uint32_t E = enc_bytes<P>(m);
+  if ((uint32_t)tile * kTileBytes >= E) return;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t N = (uint32_t)a.nranks;
+  const uint32_t src0 = ((uint32_t)c * 2u + a.parity) * N * a.slot_bytes;
+  u32x4 v[NMAX];
+  if (poll_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, tile, E, a.seq,
+                         seq_prev(seq_prev(a.seq)), a.rearm != 0, -1,
+                         u32x4{0u, 0u, 0u, 0u}, a.ctrl, a.timeout_ticks, lane, v) != 0)
+    return;
+  uint32_t o[4];
+  reduce_words<P, NMAX>(v, a.nranks, o);
+  mask_words(o, chunk_keep<P>(m, tile, lane));
+  int64_t first;
+  int n;
+  lane_elems<P>(tile, lane, first, n);
+  if ((uint32_t)tile * kTileBytes + (uint32_t)lane * 16u < E)
+    store_elems(a.out + (int64_t)c * a.out_stride + lo, m, first, n, o);
+  const u32x4 enc = encode_words<P>(o, lane, a.seq);
+  const uint32_t dst0 = a.ag0 + (a.parity * N + (uint32_t)c) * a.slot_bytes;
+  const uint32_t cstride = 2u * N * a.slot_bytes;
+  store_chunk<P>(rs, dst0, cstride, a.nranks, c, tile, E, lane, enc);
+  if (P == kLL128) {
+    fence_release();
+    produce_flags(rs, dst0, cstride, a.nranks, c, tile, E, a.seq, lane);
+  }
+}
+
+// One wave per (consumer c, share k != c, tile of share k): poll, validate
+// and decode the reduced share k into consumer c's output.
+template <int P>
+__global__ __launch_bounds__(kBlock) void k_ts_gather(TsArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int per_c = a.nranks * a.tiles;
+  const int c = gw / per_c;
+  if (c >= a.nranks) return;
+  const int rem = gw - c * per_c;
+  const int k = rem / a.tiles;
+  const int tile = rem - k * a.tiles;
+  if (k == c) return;
+  int64_t lo, m;
+  share_of(a.count, a.width, k, lo, m);
+  const uint32_t E = enc_bytes<P>(m);
+  if ((uint32_t)tile * kTileBytes >= E) return;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+  const uint32_t at =
+      a.ag0 + (((uint32_t)c * 2u + a.parity) * (uint32_t)a.nranks + (uint32_t)k) * a.slot_bytes +
+      loff;
+  u32x4 v;
+  if (poll_chunk<P>(rs, at, loff < E, a.seq, seq_prev(seq_prev(a.seq)), a.rearm != 0,
+                    a.ctrl, a.timeout_ticks, lane, v) != 0)
+    return;
+  store_chunk_elems<P>(a.out + (int64_t)c * a.out_stride + lo, m, tile, E, lane, v);
+}
+
+// ================================================================ simulator
+
+struct CollSimArgs {
+  const uint16_t* in;
+  int64_t in_stride;
+  uint16_t* out;
+  int64_t out_stride, row_stride, count, width;
+  const uint8_t* scratch;
+  uint32_t scratch_bytes, slot_bytes, ag0, E;
+  int* ctrl;
+  int32_t nranks, nops;
+  int32_t W, Q, T, TPW;
+  uint32_t seq0, parity0;
+  uint64_t timeout_ticks;
+  const uint32_t* delay;
+  uint64_t* trace;
+};
+
+__device__ __forceinline__ void sim_delay(const CollSimArgs& a, int op, int g) {
+  if (!a.delay) return;
+  const uint32_t d = a.delay[(int64_t)op * a.nranks + g];
+  if (d) {
+    const uint64_t t0 = now_ticks();
+    while (now_ticks() - t0 < (uint64_t)d) __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+__device__ __forceinline__ void trace_max(const CollSimArgs& a, int64_t idx) {
+  __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(a.trace) + idx,
+                         (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup b -> (rank g, tile group tg) with the all-reduce simulator's
+// XCD-aware placement: workgroup b runs on XCD b mod 8 and rank g's groups
+// are rotated by g, so a producer and the consumer reading it sit on
+// different XCDs.  Returns false for workgroups without work.
+__device__ __forceinline__ bool sim_place(const CollSimArgs& a, int& g, int& tg) {
+  const int b = blockIdx.x;
+  const int x = b & 7;
+  const int q = b >> 3;
+  g = q / a.Q;
+  const int qq = q - g * a.Q;
+  if (g >= a.nranks) return false;
+  tg = qq * 8 + ((x - (g & 7)) & 7);
+  return tg < a.T;
+}
+
+// All-gather simulator: a workgroup of nranks waves per (rank g, tile group
+// tg), wave w paired with peer w.  Per op, wave w sends rank g's tiles to
+// consumer w, then polls peer w's tiles and decodes them straight into row
+// w of rank g's output (no staging: nothing is reduced); the rank's own
+// wave writes its own row.  One workgroup barrier per op: a rank starts op
+// i+1 once it holds all of op i.
+template <int P, int NMAX>
+__global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
+  __shared__ int lds_err;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  int g, tg;
+  if (!sim_place(a, g, tg)) return;                // whole workgroup
+  const int G = a.W;
+  const int mine = (a.T - 1 - tg) / G + 1;
+  const bool own = w == g;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t N = (uint32_t)a.nranks;
+  const int tstride = 2 * a.nranks;
+  const uint32_t row_bytes = (uint32_t)(((a.count * 2) + 15) & ~int64_t(15));
+  if (threadIdx.x == 0) lds_err = 0;
+  __syncthreads();
+  if (a.trace && lane == 0 && w == 0) {
+    __hip_atomic_fetch_min(reinterpret_cast<unsigned long long*>(a.trace) +
+                               (int64_t)a.nops * tstride,
+                           (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+  uint32_t seq = a.seq0;
+  uint32_t par = a.parity0;
+  for (int op = 0; op < a.nops; ++op) {
+    const uint32_t stale = seq_prev(seq_prev(seq));
+    const uint16_t* row = a.in + ((int64_t)op * a.nranks + g) * a.in_stride;
+    uint16_t* orow = a.out + ((int64_t)op * a.nranks + g) * a.out_stride;
+    if (!own) {
+      sim_delay(a, op, g);
+      // this wave's earlier stores (sentinel re-arms) complete before it sends
+      if (P == kSentinel) fence_release();
+      const uint32_t dst0 = (((uint32_t)w * 2u + par) * N + (uint32_t)g) * a.slot_bytes;
+      for (int k = 0; k < mine; ++k)
+        produce_data<P>(rs, dst0, 0u, 1, -1, row, row_bytes, a.count, tg + k * G, a.E, seq,
+                        lane);
+      if (P == kLL128) {
+        fence_release();
+        for (int k = 0; k < mine; ++k)
+          produce_flags(rs, dst0, 0u, 1, -1, tg + k * G, a.E, seq, lane);
+      }
+      if (a.trace) {
+        fence_release();
+        if (lane == 0) trace_max(a, (int64_t)op * tstride + g);
+      }
+      const uint32_t src0 = (((uint32_t)g * 2u + par) * N + (uint32_t)w) * a.slot_bytes;
+      for (int k = 0; k < mine; ++k) {
+        const int tile = tg + k * G;
+        const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+        u32x4 v;
+        if (poll_chunk<P>(rs, src0 + loff, loff < a.E, seq, stale, true, a.ctrl,
+                          a.timeout_ticks, lane, v) != 0) {
+          if (lane == 0) lds_err = 1;
+          break;
+        }
+        store_chunk_elems<P>(orow + (int64_t)w * a.row_stride, a.count, tile, a.E, lane, v);
+      }
+    } else {
+      for (int k = 0; k < mine; ++k) {
+        const int tile = tg + k * G;
+        store_chunk_elems<P>(orow + (int64_t)g * a.row_stride, a.count, tile, a.E, lane,
+                             encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq));
+      }
+    }
+    __syncthreads();
+    if (lds_err) return;                           // whole workgroup
+    if (a.trace && own && lane == 0) trace_max(a, (int64_t)op * tstride + a.nranks + g);
+    seq = seq_next(seq);
+    par ^= 1u;
+  }
+}
+
+// Two-shot simulator: a workgroup of nranks waves per (rank g, tile group tg
+// of the share tiles), wave w paired with peer w.  Per op and tile t:
+//  1. reduce-scatter: wave w sends tile t of rank g's share w to rank w;
+//     it then polls tile t of rank w's share g, staging it in LDS row w (the
+//     own wave stages its own share-g chunk);
+//  2. after a barrier the own wave reduces the staged rows in rank order,
+//     writes the reduced tile to rank g's output and stages it;
+//  3. all-gather: after a second barrier wave w sends the reduced tile to
+//     rank w and polls tile t of rank w's reduced share w, decoding it into
+//     rank g's output.
+// Every sending wave first waits for its own earlier stores, so the
+// sentinel re-arm of a slot completes before the exchange that licenses the
+// slot's next write (reduce-scatter: the all-gather two steps later;
+// all-gather: the next reduce-scatter).
+template <int P, int NMAX>
+__global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
+  __shared__ u32x4 lds[NMAX][kWave];
+  __shared__ u32x4 red[kWave];
+  __shared__ int lds_err;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  int g, tg;
+  if (!sim_place(a, g, tg)) return;                // whole workgroup
+  const int G = a.W;
+  const int mine = (a.T - 1 - tg) / G + 1;
+  const bool own = w == g;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t N = (uint32_t)a.nranks;
+  const int tstride = 2 * a.nranks;
+  int64_t lo_g, m_g, lo_w, m_w;
+  share_of(a.count, a.width, g, lo_g, m_g);
+  share_of(a.count, a.width, w, lo_w, m_w);
+  const uint32_t E_g = enc_bytes<P>(m_g);
+  const uint32_t E_w = enc_bytes<P>(m_w);
+  const uint32_t rb_w = (uint32_t)((m_w * 2 + 15) & ~int64_t(15));
+  const uint32_t rb_g = (uint32_t)((m_g * 2 + 15) & ~int64_t(15));
+  if (threadIdx.x == 0) lds_err = 0;
+  __syncthreads();
+  if (a.trace && lane == 0 && w == 0) {
+    __hip_atomic_fetch_min(reinterpret_cast<unsigned long long*>(a.trace) +
+                               (int64_t)a.nops * tstride,
+                           (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+  uint32_t seq = a.seq0;
+  uint32_t par = a.parity0;
+  for (int op = 0; op < a.nops; ++op) {
+    const uint32_t stale = seq_prev(seq_prev(seq));
+    const uint16_t* row = a.in + ((int64_t)op * a.nranks + g) * a.in_stride;
+    uint16_t* orow = a.out + ((int64_t)op * a.nranks + g) * a.out_stride;
+    // reduce-scatter slots: to consumer w from g, and here (g) from w
+    const uint32_t rs_dst = (((uint32_t)w * 2u + par) * N + (uint32_t)g) * a.slot_bytes;
+    const uint32_t rs_src = (((uint32_t)g * 2u + par) * N + (uint32_t)w) * a.slot_bytes;
+    const uint32_t ag_dst = a.ag0 + rs_dst;
+    const uint32_t ag_src = a.ag0 + rs_src;
+    if (!own) sim_delay(a, op, g);
+    for (int k = 0; k < mine; ++k) {
+      const int tile = tg + k * G;
+      const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+      // ---- 1. reduce-scatter ----
+      if (!own) {
+        if (P == kSentinel) fence_release();
+        produce_data<P>(rs, rs_dst, 0u, 1, -1, row + lo_w, rb_w, m_w, tile, E_w, seq, lane);
+        if (P == kLL128) {
+          fence_release();
+          produce_flags(rs, rs_dst, 0u, 1, -1, tile, E_w, seq, lane);
+        }
+        if (a.trace && k == mine - 1) {
+          fence_release();
+          if (lane == 0) trace_max(a, (int64_t)op * tstride + g);
+        }
+        u32x4 got;
+        if (poll_chunk<P>(rs, rs_src + loff, loff < E_g, seq, stale, true, a.ctrl,
+                          a.timeout_ticks, lane, got) != 0) {
+          if (lane == 0) lds_err = 1;
+        } else {
+          lds[w][lane] = got;
+        }
+      } else {
+        lds[g][lane] = encode_chunk<P>(row + lo_g, rb_g, m_g, tile, lane, seq);
+      }
+      __syncthreads();
+      if (lds_err) return;                         // whole workgroup
+      // ---- 2. fixed-order reduce of share g, tile t (own wave) ----
+      if (own) {
+        u32x4 v[NMAX];
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r)
+          v[r] = (r < a.nranks) ? lds[r][lane] : u32x4{0u, 0u, 0u, 0u};
+        uint32_t o[4];
+        reduce_words<P, NMAX>(v, a.nranks, o);
+        mask_words(o, chunk_keep<P>(m_g, tile, lane));
+        int64_t first;
+        int n;
+        lane_elems<P>(tile, lane, first, n);
+        if (loff < E_g) store_elems(orow + lo_g, m_g, first, n, o);
+        red[lane] = u32x4{o[0], o[1], o[2], o[3]};
+      }
+      __syncthreads();
+      // ---- 3. all-gather of the reduced tile ----
+      if (!own) {
+        const u32x4 r4 = red[lane];
+        const uint32_t o[4] = {r4.x, r4.y, r4.z, r4.w};
+        if (P == kSentinel) fence_release();
+        store_chunk<P>(rs, ag_dst, 0u, 1, -1, tile, E_g, lane, encode_words<P>(o, lane, seq));
+        if (P == kLL128) {
+          fence_release();
+          produce_flags(rs, ag_dst, 0u, 1, -1, tile, E_g, seq, lane);
+        }
+        u32x4 got;
+        if (poll_chunk<P>(rs, ag_src + loff, loff < E_w, seq, stale, true, a.ctrl,
+                          a.timeout_ticks, lane, got) != 0) {
+          if (lane == 0) lds_err = 1;
+        } else {
+          store_chunk_elems<P>(orow + lo_w, m_w, tile, E_w, lane, got);
+        }
+      }
+    }
+    __syncthreads();
+    if (lds_err) return;
+    if (a.trace && own && lane == 0) trace_max(a, (int64_t)op * tstride + a.nranks + g);
+    seq = seq_next(seq);
+    par ^= 1u;
+  }
+}
+
+// ================================================================ host side
+
+template <int P, int NMAX>
+static const void* sim_fn(int collective) {
+  return collective == AR_ALLGATHER ? reinterpret_cast<const void*>(&k_sim_gather<P, NMAX>)
+                                    : reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX>);
+}
+
+template <int P>
+static const void* sim_fn_n(int collective, int nranks) {
+  if (nranks <= 4) return sim_fn<P, 4>(collective);
+  if (nranks <= 8) return sim_fn<P, 8>(collective);
+  return sim_fn<P, 16>(collective);
+}
+
+static const void* coll_sim_fn(int proto, int collective, int nranks) {
+  switch (proto) {
+    case kLL: return sim_fn_n<kLL>(collective, nranks);
+    case kLL128: return sim_fn_n<kLL128>(collective, nranks);
+    default: return sim_fn_n<kSentinel>(collective, nranks);
+  }
+}
+
+struct CollGeom {
+  int32_t W, Q, T, TPW, blocks;
+};
+
+static int coll_check(const ar_sim_params* p) {
+  const ar_desc* d = &p->desc;
+  if (d->nconsumers != d->nranks) return AR_EINVAL;
+  if (d->proto == kBarrier) return AR_EINVAL;
+  if (p->flags != 0 || p->tile_order) return AR_EINVAL;
+  return AR_OK;
+}
+
+// Tiles of one rank's transfer: the whole payload (all-gather) or one full
+// share (two-shot).  Grid: the all-reduce simulator's rule (half of the
+// occupancy query's residency, tile groups in multiples of 8 per rank).
+static int coll_geometry(const ar_sim_params* p, const DeviceInfo& di, CollGeom* g) {
+  const ar_desc* d = &p->desc;
+  const int64_t n_el =
+      d->collective == AR_TWOSHOT ? share_width(d->count, d->nranks) : d->count;
+  const int64_t T = ceil_div64(encoded_bytes(d->proto, n_el), kTileBytes);
+  if (T <= 0) {
+    *g = CollGeom{0, 0, 0, 0, 0};
+    return AR_OK;
+  }
+  if (T > (int64_t(1) << 24)) return AR_ESIZE;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &occ, coll_sim_fn(d->proto, d->collective, d->nranks), kWave * d->nranks, 0) !=
+          hipSuccess ||
+      occ <= 0)
+    return AR_ELAUNCH;
+  const int64_t capacity = (int64_t)occ * di.cus / 2;
+  const int64_t qmax = capacity / (8 * (int64_t)d->nranks);
+  if (qmax < 1) return AR_ECAPACITY;
+  int64_t Q;
+  if (p->waves_per_rank > 0) {
+    if (p->waves_per_rank % 8) return AR_EINVAL;
+    Q = p->waves_per_rank / 8;
+    if (Q > qmax) return AR_ECAPACITY;
+  } else {
+    Q = ceil_div64(T, 8);
+    if (Q > qmax) Q = qmax;
+  }
+  g->W = (int32_t)(8 * Q);
+  g->Q = (int32_t)Q;
+  g->T = (int32_t)T;
+  g->TPW = (int32_t)ceil_div64(T, 8 * Q);
+  g->blocks = (int32_t)(8 * Q * d->nranks);
+  return AR_OK;
+}
+
+int coll_sim_geometry(const ar_sim_params* p, int32_t* groups, int32_t* tiles,
+                      int32_t* tiles_per_group, int32_t* blocks) {
+  int rc = coll_check(p);
+  if (rc) return rc;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  CollGeom g;
+  rc = coll_geometry(p, di, &g);
+  if (rc) return rc;
+  if (groups) *groups = g.W;
+  if (tiles) *tiles = g.T;
+  if (tiles_per_group) *tiles_per_group = g.TPW;
+  if (blocks) *blocks = g.blocks;
+  return AR_OK;
+}
+
+int coll_sim_run(const ar_sim_params* p, hipStream_t s) {
+  int rc = coll_check(p);
+  if (rc) return rc;
+  const ar_desc* d = &p->desc;
+  const int64_t R = (d->count + 7) / 8 * 8;
+  if (d->collective == AR_ALLGATHER && p->out_stride < (int64_t)d->nranks * R)
+    return AR_EINVAL;
+  if (d->count == 0) return AR_OK;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  CollGeom g;
+  rc = coll_geometry(p, di, &g);
+  if (rc) return rc;
+  CollSimArgs a;
+  a.in = static_cast<const uint16_t*>(p->in);
+  a.in_stride = p->in_stride;
+  a.out = static_cast<uint16_t*>(p->out);
+  a.out_stride = p->out_stride;
+  a.row_stride = R;
+  a.count = d->count;
+  a.width = share_width(d->count, d->nranks);
+  a.scratch = static_cast<const uint8_t*>(p->scratch);
+  a.scratch_bytes = (uint32_t)desc_scratch_bytes(d);
+  a.slot_bytes = (uint32_t)desc_slot_bytes(d);
+  a.ag0 = (uint32_t)desc_region_bytes(d);
+  a.E = (uint32_t)encoded_bytes(d->proto, d->count);
+  a.ctrl = static_cast<int*>(p->ctrl);
+  a.nranks = d->nranks;
+  a.nops = p->nops;
+  a.W = g.W;
+  a.Q = g.Q;
+  a.T = g.T;
+  a.TPW = g.TPW;
+  a.seq0 = p->epoch.seq;
+  a.parity0 = p->epoch.parity;
+  a.timeout_ticks = ns_to_ticks(p->timeout_ns, di.wallclock_hz);
+  a.delay = p->delay_ticks;
+  a.trace = p->trace;
+  void* args[] = {&a};
+  return map_hip(hipLaunchKernel(coll_sim_fn(d->proto, d->collective, d->nranks),
+                                 dim3(g.blocks), dim3(kWave * d->nranks), args, 0, s));
+}
+
+// ----------------------------------------------------- stream-ordered host
+
+static TsArgs ts_args(const ar_desc* d, void* scratch, ar_epoch e) {
+  TsArgs a{};
+  a.count = d->count;
+  a.width = share_width(d->count, d->nranks);
+  a.scratch = static_cast<const uint8_t*>(scratch);
+  a.scratch_bytes = (uint32_t)desc_scratch_bytes(d);
+  a.slot_bytes = (uint32_t)desc_slot_bytes(d);
+  a.ag0 = (uint32_t)desc_region_bytes(d);
+  a.nranks = d->nranks;
+  a.tiles = (int32_t)ceil_div64(encoded_bytes(d->proto, a.width), kTileBytes);
+  a.seq = e.seq;
+  a.parity = e.parity;
+  return a;
+}
+
+int twoshot_pack(int32_t proto, const ar_desc* d, const void* in, int64_t in_stride,
+                 void* scratch, ar_epoch e, hipStream_t s) {
+  TsArgs a = ts_args(d, scratch, e);
+  a.in = static_cast<const uint16_t*>(in);
+  a.in_stride = in_stride;
+  const int64_t waves = (int64_t)d->nranks * d->nranks * a.tiles;
+  const dim3 grid((unsigned)ceil_div64(waves, kWavesPerBlock));
+  switch (proto) {
+    case kLL: return map_hip(launch(k_ts_pack<kLL>, grid, dim3(kBlock), s, a));
+    case kLL128: return map_hip(launch(k_ts_pack<kLL128>, grid, dim3(kBlock), s, a));
+    default: return map_hip(launch(k_ts_pack<kSentinel>, grid, dim3(kBlock), s, a));
+  }
+}
+
+template <int P>
+static hipError_t ts_reduce_p(const TsArgs& a, hipStream_t s) {
+  const dim3 g1((unsigned)ceil_div64((int64_t)a.nranks * a.tiles, kWavesPerBlock));
+  hipError_t e;
+  if (a.nranks <= 4) e = launch(k_ts_reduce<P, 4>, g1, dim3(kBlock), s, a);
+  else if (a.nranks <= 8) e = launch(k_ts_reduce<P, 8>, g1, dim3(kBlock), s, a);
+  else e = launch(k_ts_reduce<P, 16>, g1, dim3(kBlock), s, a);
+  if (e != hipSuccess) return e;
+  const dim3 g2(
+      (unsigned)ceil_div64((int64_t)a.nranks * a.nranks * a.tiles, kWavesPerBlock));
+  return launch(k_ts_gather<P>, g2, dim3(kBlock), s, a);
+}
+
+int twoshot_reduce(const ar_desc* d, void* scratch, void* out, int64_t out_stride,
+                   ar_epoch e, void* ctrl, uint64_t timeout_ns, int32_t flags,
+                   hipStream_t s) {
+  DeviceInfo di;
+  int rc = device_info(&di);
+  if (rc) return rc;
+  TsArgs a = ts_args(d, scratch, e);
+  a.out = static_cast<uint16_t*>(out);
+  a.out_stride = out_stride;
+  a.ctrl = static_cast<int*>(ctrl);
+  a.timeout_ticks = ns_to_ticks(timeout_ns, di.wallclock_hz);
+  a.rearm = (flags & AR_FLAG_REARM) && d->proto == kSentinel;
+  switch (d->proto) {
+    case kLL: return map_hip(ts_reduce_p<kLL>(a, s));
+    case kLL128: return map_hip(ts_reduce_p<kLL128>(a, s));
+    default: return map_hip(ts_reduce_p<kSentinel>(a, s));
+  }
+}
+
+}  // namespace ar
+
+// ================================================================== C ABI
+
+using namespace ar;
+
+extern "C" int ar_gather_validate(const ar_desc* d, void* scratch, void* out,
+                                  int64_t out_stride, ar_epoch e, void* ctrl,
+                                  uint64_t timeout_ns, int32_t flags, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->collective != AR_ALLGATHER) return AR_EINVAL;
+  if (e.parity > 1u || e.seq == 0u) return AR_EINVAL;
+  if (flags & ~AR_FLAG_REARM) return AR_EINVAL;
+  const int64_t R = (d->count + 7) / 8 * 8;
+  rc = check_rows(out, out_stride, (int64_t)d->nranks * R);
+  if (rc) return rc;
+  if (d->count == 0) return AR_OK;
+  if (!scratch || !ctrl) return AR_EINVAL;
+  if (!aligned(scratch, 256) || !aligned(ctrl, 256)) return AR_EALIGN;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  GatherArgs a;
+  a.out = static_cast<uint16_t*>(out);
+  a.out_stride = out_stride;
+  a.row_stride = R;
+  a.count = d->count;
+  a.scratch = static_cast<const uint8_t*>(scratch);
+  a.scratch_bytes = (uint32_t)desc_scratch_bytes(d);
+  a.slot_bytes = (uint32_t)desc_slot_bytes(d);
+  a.E = (uint32_t)encoded_bytes(d->proto, d->count);
+  a.nranks = d->nranks;
+  a.nconsumers = d->nconsumers;
+  a.tiles = (int32_t)ceil_div64(a.E, kTileBytes);
+  a.seq = e.seq;
+  a.parity = e.parity;
+  a.ctrl = static_cast<int*>(ctrl);
+  a.timeout_ticks = ns_to_ticks(timeout_ns, di.wallclock_hz);
+  a.rearm = (flags & AR_FLAG_REARM) && d->proto == kSentinel;
+  const int64_t waves = (int64_t)a.tiles * d->nranks * d->nconsumers;
+  if (waves >= (int64_t(1) << 31)) return AR_ESIZE;
+  const dim3 grid((unsigned)ceil_div64(waves, kWavesPerBlock));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d->proto) {
+    case kLL: return map_hip(launch(k_gather<kLL>, grid, dim3(kBlock), s, a));
+    case kLL128: return map_hip(launch(k_gather<kLL128>, grid, dim3(kBlock), s, a));
+    case kSentinel: return map_hip(launch(k_gather<kSentinel>, grid, dim3(kBlock), s, a));
+    default: return map_hip(launch(k_gather<kBarrier>, grid, dim3(kBlock), s, a));
+  }
+}

@@ -9,15 +9,11 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "../../include/ar.h"
+#include "ar_host.h"
 #include "ar_protocols.h"
 
 namespace ar {
-
-constexpr int kBlock = 256;              // 4 waves
-constexpr int kWavesPerBlock = kBlock / kWave;
 
 // Waves per workgroup of the simulator.  One wave per workgroup spreads a
 // rank's waves over as many CUs as possible: each CU's path to the L2 then
@@ -703,116 +699,6 @@ __global__ void k_empty() {}
 
 // ============================================================ host side ==
 
-struct DeviceInfo {
-  bool ok = false;
-  int cus = 0;
-  double wallclock_hz = 0.0;
-  int coop = 0;
-};
-
-static std::mutex g_mu;
-static DeviceInfo g_info[64];
-
-static int device_info(DeviceInfo* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return AR_ENODEV;
-  std::lock_guard<std::mutex> lk(g_mu);
-  DeviceInfo& d = g_info[dev];
-  if (!d.ok) {
-    int cus = 0, khz = 0, coop = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return AR_ENODEV;
-    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
-      return AR_ENODEV;
-    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
-      coop = 0;
-    d.cus = cus;
-    d.wallclock_hz = (double)khz * 1000.0;
-    d.coop = coop;
-    d.ok = true;
-  }
-  *out = d;
-  return AR_OK;
-}
-
-static uint64_t ns_to_ticks(uint64_t ns, double hz) {
-  if (ns == 0) ns = 1000000000ull;
-  const double t = (double)ns * hz * 1e-9;
-  return t < 1.0 ? 1ull : (uint64_t)t;
-}
-
-static int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-static int64_t encoded_bytes(int32_t proto, int64_t count) {
-  if (count < 0) return AR_EINVAL;
-  switch (proto) {
-    case kLL: return 16 * ceil_div64(count, 4);
-    case kLL128: return 128 * ceil_div64(count, 60);
-    case kSentinel:
-    case kBarrier: return 16 * ceil_div64(count, 8);
-    default: return AR_EINVAL;
-  }
-}
-
-static int64_t slot_bytes_of(int32_t proto, int64_t count) {
-  const int64_t E = encoded_bytes(proto, count);
-  if (E < 0) return E;
-  return ceil_div64(E, 128) * 128;
-}
-
-static bool aligned(const void* p, uintptr_t a) {
-  return ((uintptr_t)p & (a - 1)) == 0;
-}
-
-static int check_desc(const ar_desc* d) {
-  if (!d) return AR_EINVAL;
-  if (d->nranks < 1 || d->nranks > AR_MAX_RANKS) return AR_EINVAL;
-  if (d->nconsumers != 1 && d->nconsumers != d->nranks) return AR_EINVAL;
-  if (d->count < 0) return AR_EINVAL;
-  if (d->proto < 0 || d->proto > kBarrier) return AR_EINVAL;
-  if (d->reserved != 0) return AR_EINVAL;
-  const int64_t slot = slot_bytes_of(d->proto, d->count);
-  if (slot > (int64_t(1) << 30)) return AR_ESIZE;
-  const int64_t total = (int64_t)d->nconsumers * 2 * d->nranks * slot;
-  if (total >= (int64_t(1) << 32)) return AR_ESIZE;
-  return AR_OK;
-}
-
-static int check_rows(const void* p, int64_t stride, int64_t count) {
-  if (count == 0) return AR_OK;
-  if (!p) return AR_EINVAL;
-  if (stride < count) return AR_EINVAL;
-  if (!aligned(p, 16) || (stride % 8) != 0) return AR_EALIGN;
-  if (stride >= (int64_t(1) << 30)) return AR_ESIZE;   // row byte offsets stay 32-bit
-  return AR_OK;
-}
-
-static thread_local int g_last_hip_error = 0;
-
-static int map_hip(hipError_t e) {
-  if (e == hipSuccess) return AR_OK;
-  g_last_hip_error = (int)e;
-  return AR_ELAUNCH;
-}
-
-// Launch with the runtime's own return code (not the sticky last error,
-// which may hold an unrelated earlier failure of the calling thread).
-template <typename... KArgs>
-static hipError_t launch_typed(void (*kernel)(KArgs...), dim3 grid, dim3 block,
-                               hipStream_t s, KArgs... args) {
-  void* argv[sizeof...(KArgs) + 1] = {static_cast<void*>(&args)..., nullptr};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
-                         argv, 0, s);
-}
-
-// Every argument is converted to the kernel's own parameter type first.
-template <typename... KArgs, typename... Args>
-static hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block,
-                         hipStream_t s, Args... args) {
-  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel arity");
-  return launch_typed<KArgs...>(kernel, grid, block, s, static_cast<KArgs>(args)...);
-}
-
 template <int P>
 static hipError_t launch_pack(PackArgs a, int blocks, hipStream_t s) {
   return launch(k_pack<P>, dim3(blocks), dim3(kBlock), s, a);
@@ -830,6 +716,9 @@ static int pack_common(int32_t want_proto, const ar_desc* d, const void* in,
   if (d->count == 0) return AR_OK;
   if (!scratch) return AR_EINVAL;
   if (!aligned(scratch, 256)) return AR_EALIGN;
+  if (d->collective == AR_TWOSHOT)
+    return twoshot_pack(want_proto, d, in, in_stride, scratch, e,
+                        static_cast<hipStream_t>(stream));
   PackArgs a;
   a.in = static_cast<const uint16_t*>(in);
   a.in_stride = in_stride;
@@ -1054,7 +943,7 @@ const char* ar_status_string(int code) {
   }
 }
 
-int ar_abi_version(void) { return 2; }
+int ar_abi_version(void) { return 3; }
 
 int64_t ar_encoded_bytes(int32_t proto, int64_t count) {
   return encoded_bytes(proto, count);
@@ -1067,7 +956,22 @@ int64_t ar_slot_bytes(int32_t proto, int64_t count) {
 int64_t ar_scratch_bytes(const ar_desc* d) {
   const int rc = check_desc(d);
   if (rc) return rc;
-  return (int64_t)d->nconsumers * 2 * d->nranks * slot_bytes_of(d->proto, d->count);
+  return desc_scratch_bytes(d);
+}
+
+int64_t ar_desc_slot_bytes(const ar_desc* d) {
+  const int rc = check_desc(d);
+  if (rc) return rc;
+  return desc_slot_bytes(d);
+}
+
+int ar_shard_bounds(int64_t count, int32_t nranks, int32_t k, int64_t* lo,
+                    int64_t* hi) {
+  if (!lo || !hi || count < 0 || nranks < 1 || nranks > AR_MAX_RANKS || k < 0 ||
+      k >= nranks)
+    return AR_EINVAL;
+  share_bounds(count, nranks, k, lo, hi);
+  return AR_OK;
 }
 
 int64_t ar_ctrl_bytes(void) {
@@ -1136,19 +1040,22 @@ int ar_arm_sentinel(const ar_desc* d, void* scratch, int32_t parity,
   if (d->count == 0) return AR_OK;
   if (!scratch) return AR_EINVAL;
   if (!aligned(scratch, 256)) return AR_EALIGN;
-  const uint32_t slot = (uint32_t)slot_bytes_of(d->proto, d->count);
-  const uint32_t total = (uint32_t)((int64_t)d->nconsumers * 2 * d->nranks * slot);
+  const uint32_t slot = (uint32_t)desc_slot_bytes(d);
+  const uint32_t total = (uint32_t)desc_scratch_bytes(d);
   const uint32_t region = (uint32_t)d->nranks * slot;   // one parity of one consumer
+  // consumer buffers in the scratch: one per consumer, twice for two-shot
+  // (reduce-scatter region, then all-gather region, same layout)
+  const int32_t nbuf = d->nconsumers * (d->collective == AR_TWOSHOT ? 2 : 1);
   uint32_t region0, stride;
   int32_t nregions;
   if (parity < 0) {
     region0 = 0;
     stride = region;
-    nregions = 2 * d->nconsumers;
+    nregions = 2 * nbuf;
   } else {
     region0 = (uint32_t)parity * region;
     stride = 2u * region;
-    nregions = d->nconsumers;
+    nregions = nbuf;
   }
   const uint64_t chunks = (uint64_t)(region / 16u) * (uint64_t)nregions;
   uint64_t blocks = (chunks + kBlock - 1) / kBlock;
@@ -1166,11 +1073,15 @@ int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
   if (rc) return rc;
   if (e.parity > 1u || e.seq == 0u) return AR_EINVAL;
   if (flags & ~AR_FLAG_REARM) return AR_EINVAL;
+  if (d->collective == AR_ALLGATHER) return AR_EINVAL;
   rc = check_rows(out, out_stride, d->count);
   if (rc) return rc;
   if (d->count == 0) return AR_OK;
   if (!scratch || !ctrl) return AR_EINVAL;
   if (!aligned(scratch, 256) || !aligned(ctrl, 256)) return AR_EALIGN;
+  if (d->collective == AR_TWOSHOT)
+    return twoshot_reduce(d, scratch, out, out_stride, e, ctrl, timeout_ns, flags,
+                          static_cast<hipStream_t>(stream));
   DeviceInfo di;
   rc = device_info(&di);
   if (rc) return rc;
@@ -1209,6 +1120,10 @@ int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
   if (!p) return AR_EINVAL;
   int rc = check_desc(&p->desc);
   if (rc) return rc;
+  if (p->desc.collective != AR_ALLREDUCE) {
+    if (wide) *wide = 1;
+    return coll_sim_geometry(p, waves_per_rank, tiles_per_rank, tiles_per_wave, blocks);
+  }
   DeviceInfo di;
   rc = device_info(&di);
   if (rc) return rc;
@@ -1227,6 +1142,8 @@ int ar_sim_run(const ar_sim_params* p, void* stream) {
   int rc = check_sim(p);
   if (rc) return rc;
   const ar_desc* d = &p->desc;
+  if (d->collective != AR_ALLREDUCE)
+    return coll_sim_run(p, static_cast<hipStream_t>(stream));
   if (d->count == 0) return AR_OK;
   DeviceInfo di;
   rc = device_info(&di);

@@ -492,13 +492,8 @@ __device__ __forceinline__ int poll_chunks(rsrc_t rs, const uint32_t (&at)[B],
 // addition at a time, round to bf16 (NaN -> 0x7FC0), store the lane's
 // elements of tile `tile` below `count`.
 template <int P, int NMAX>
-__device__ __forceinline__ void reduce_store_tile(const u32x4 (&v)[NMAX],
-                                                  int nranks, int tile,
-                                                  uint32_t E, int lane,
-                                                  uint16_t* __restrict__ out_row,
-                                                  int64_t count) {
-  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
-  if (loff >= E) return;
+__device__ __forceinline__ void reduce_words(const u32x4 (&v)[NMAX], int nranks,
+                                             uint32_t o[4]) {
   float acc[8];
   {
     const u32x4 d = v[0];
@@ -527,7 +522,6 @@ __device__ __forceinline__ void reduce_store_tile(const u32x4 (&v)[NMAX],
       }
     }
   }
-  uint32_t o[4];
   if (P == kLL) {
     o[0] = pack2(to_bf16(acc[0]), to_bf16(acc[1]));
     o[1] = pack2(to_bf16(acc[2]), to_bf16(acc[3]));
@@ -538,10 +532,57 @@ __device__ __forceinline__ void reduce_store_tile(const u32x4 (&v)[NMAX],
     o[2] = pack2(to_bf16(acc[4]), to_bf16(acc[5]));
     o[3] = pack2(to_bf16(acc[6]), to_bf16(acc[7]));
   }
+}
+
+template <int P, int NMAX>
+__device__ __forceinline__ void reduce_store_tile(const u32x4 (&v)[NMAX],
+                                                  int nranks, int tile,
+                                                  uint32_t E, int lane,
+                                                  uint16_t* __restrict__ out_row,
+                                                  int64_t count) {
+  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+  if (loff >= E) return;
+  uint32_t o[4];
+  reduce_words<P, NMAX>(v, nranks, o);
   int64_t first;
   int n;
   lane_elems<P>(tile, lane, first, n);
   store_elems(out_row, count, first, n, o);
+}
+
+// The data words of one validated 16-byte chunk (the inverse of
+// encode_words up to the NaN canonicalization of SENTINEL).
+template <int P>
+__device__ __forceinline__ void chunk_words(const u32x4 v, uint32_t w[4]) {
+  if (P == kLL) {
+    w[0] = v.x; w[1] = v.z; w[2] = 0u; w[3] = 0u;
+  } else {
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;   // LL128 lane 7: 4 elements
+  }
+}
+
+// Decode one validated chunk of tile `tile` and store its elements below
+// `count` into out_row (element 0 of the encoding at out_row[0]).
+template <int P>
+__device__ __forceinline__ void store_chunk_elems(uint16_t* __restrict__ out_row,
+                                                  int64_t count, int tile,
+                                                  uint32_t E, int lane, u32x4 v) {
+  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+  if (loff >= E) return;
+  uint32_t w[4];
+  chunk_words<P>(v, w);
+  int64_t first;
+  int n;
+  lane_elems<P>(tile, lane, first, n);
+  store_elems(out_row, count, first, n, w);
+}
+
+// Encoded bytes of `count` elements (the slot layout of ar_encoded_bytes).
+template <int P>
+__device__ __forceinline__ uint32_t enc_bytes(int64_t count) {
+  if (P == kLL) return (uint32_t)(16 * ((count + 3) / 4));
+  if (P == kLL128) return (uint32_t)(128 * ((count + 59) / 60));
+  return (uint32_t)(16 * ((count + 7) / 8));
 }
 
 // Poll, validate and reduce one tile for one consumer (all ranks polled).

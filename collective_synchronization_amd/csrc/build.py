@@ -13,8 +13,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 LIB = os.path.join(PKG, "libcsync_ar.so")
-SOURCES = [os.path.join(HERE, "ar_kernels.hip"), os.path.join(HERE, "ar_select.cpp")]
+SOURCES = [os.path.join(HERE, "ar_kernels.hip"), os.path.join(HERE, "ar_collectives.hip"),
+           os.path.join(HERE, "ar_select.cpp")]
 HEADERS = [os.path.join(HERE, "ar_device.h"), os.path.join(HERE, "ar_protocols.h"),
+           os.path.join(HERE, "ar_host.h"),
            os.path.join(os.path.dirname(PKG), "include", "ar.h")]
 ARCH = os.environ.get("AR_OFFLOAD_ARCH", "gfx950")
 

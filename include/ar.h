@@ -110,20 +110,61 @@ int ar_epoch_flip(ar_epoch* e);
 int ar_epoch_advance(ar_epoch* e, uint64_t nops);    /* nops flips */
 
 /* -------------------------------------------------------- descriptors --- */
+/*
+ * Collectives carried by the same self-synchronizing transfers:
+ *   AR_ALLREDUCE  one-shot all-reduce: every rank sends its whole payload to
+ *                 every consumer, which reduces all of them ("SiFAR" and
+ *                 "flash-comm" abstracts; "Why Microseconds Matter in AI
+ *                 Infrastructure", "Latency can matter more than bandwidth");
+ *   AR_ALLGATHER  standalone all-gather: every consumer receives every
+ *                 rank's payload unreduced ("flash-comm", abstract);
+ *   AR_TWOSHOT    two-shot all-reduce ("SiFAR", abstract): rank k owns share
+ *                 k of the elements (ar_shard_bounds); a reduce-scatter sends
+ *                 share k of every payload to rank k, which reduces it in
+ *                 rank order, and an all-gather sends each reduced share to
+ *                 every rank.  Every rank is a consumer (nconsumers ==
+ *                 nranks); LL, LL128 and SENTINEL only.
+ * All three give bit-identical results on every consumer, and the two
+ * all-reduces give the same bits.
+ */
+typedef enum {
+    AR_ALLREDUCE = 0,
+    AR_ALLGATHER = 1,
+    AR_TWOSHOT = 2
+} ar_collective;
+
 typedef struct {
     int32_t nranks;      /* N simulated ranks, 1..AR_MAX_RANKS              */
     int32_t nconsumers;  /* receive buffers: 1 (rank 0's share) or nranks    */
     int64_t count;       /* bf16 elements per rank payload, >= 0             */
     int32_t proto;       /* AR_LL, AR_LL128, AR_SENTINEL or AR_BARRIER       */
-    int32_t reserved;    /* must be 0                                        */
+    int32_t collective;  /* ar_collective (0 = one-shot all-reduce)          */
 } ar_desc;
+
+/*
+ * Share k of a two-shot all-reduce: elements [lo, hi) with width
+ * C = ceil(count / nranks) rounded up to a multiple of 8, lo = min(k*C,
+ * count), hi = min(lo + C, count); trailing shares may be empty.  Host only.
+ */
+int ar_shard_bounds(int64_t count, int32_t nranks, int32_t k, int64_t* lo,
+                    int64_t* hi);
+
+/*
+ * Slot bytes of a descriptor: ar_slot_bytes(proto, count) for AR_ALLREDUCE
+ * and AR_ALLGATHER, ar_slot_bytes(proto, C) for AR_TWOSHOT (one share).
+ */
+int64_t ar_desc_slot_bytes(const ar_desc* d);
 
 /*
  * Receive-buffer ("scratch") layout, caller-owned, 256-byte aligned:
  *   scratch[consumer c][parity p][source rank r][slot_bytes]
- * at byte offset ((c*2 + p)*nranks + r) * slot_bytes.  LL and LL128 scratch
- * must be zero-filled once before first use (a zero flag is "never
- * written"); SENTINEL scratch must be armed with ar_arm_sentinel.
+ * at byte offset ((c*2 + p)*nranks + r) * slot_bytes.  AR_TWOSHOT has two
+ * such regions, each slot holding one share: the reduce-scatter region
+ * first (slot r of consumer c: share c of rank r's payload), then, at byte
+ * nconsumers*2*nranks*slot_bytes, the all-gather region (slot k of consumer
+ * c: share k reduced by rank k).  LL and LL128 scratch must be zero-filled
+ * once before first use (a zero flag is "never written"); SENTINEL scratch
+ * must be armed with ar_arm_sentinel.
  */
 int64_t ar_scratch_bytes(const ar_desc* d);
 
@@ -140,7 +181,9 @@ int ar_ctrl_reset(void* ctrl, void* stream);
 /* ------------------------------------------------------------ producer --- */
 /*
  * Producers: encode every simulated rank's payload for epoch `e` into slot r
- * of parity e.parity of every consumer's receive buffer.
+ * of parity e.parity of every consumer's receive buffer.  AR_TWOSHOT: rank
+ * r's share c (encoded on its own, element lo_c first) into the
+ * reduce-scatter slot r of consumer c.
  *   in:   device, rank r's payload at in + r*in_stride (elements), bf16.
  *         16-byte aligned, in_stride a multiple of 8 and >= count.  Each
  *         row is read up to the 16-byte boundary after element count-1
@@ -183,6 +226,7 @@ int ar_pack_plain(const ar_desc* d, const void* in, int64_t in_stride,
  * both) of every consumer with 0xFFFF ("Why Microseconds Matter in AI
  * Infrastructure", "Latency can matter more than bandwidth": the receive
  * buffer is initialized to a negative NaN).  A fill kernel, not a memset.
+ * AR_TWOSHOT: both regions.
  */
 int ar_arm_sentinel(const ar_desc* d, void* scratch, int32_t parity,
                     void* stream);
@@ -207,6 +251,32 @@ int ar_arm_sentinel(const ar_desc* d, void* scratch, int32_t parity,
  * (the kernel boundary after ar_pack_plain is the barrier).
  */
 int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
+                       int64_t out_stride, ar_epoch e, void* ctrl,
+                       uint64_t timeout_ns, int32_t flags, void* stream);
+/*
+ * With d->collective == AR_TWOSHOT, ar_reduce_validate runs both steps after
+ * the ar_pack_* of the shares: consumer c polls and validates share c of
+ * every rank, reduces it in rank order, writes it to its output and sends it
+ * (encoded for epoch e) to every other consumer's all-gather slot c; then
+ * every consumer polls, validates and decodes the other shares into its
+ * output.  Same arguments and errors; AR_FLAG_REARM re-arms both regions.
+ * AR_ALLGATHER descriptors are rejected (AR_EINVAL): use ar_gather_validate.
+ */
+
+/*
+ * ar_gather_validate -- standalone all-gather ("flash-comm", abstract: the
+ * same self-synchronizing transfers support all-gather).  d->collective must
+ * be AR_ALLGATHER.  After ar_pack_* (which is the same as for the one-shot
+ * all-reduce), every consumer c polls and validates slot r of every rank in
+ * any arrival order and writes the decoded payload (SENTINEL: negative NaNs
+ * arrive as 0x7FC0) to row r of its output:
+ *   out: device, consumer c's row r at out + c*out_stride + r*R elements,
+ *        R = count rounded up to a multiple of 8; 16-byte aligned,
+ *        out_stride a multiple of 8 and >= nranks*R.  Elements of a row at
+ *        or past count are not written.
+ * ctrl, timeout_ns, flags and errors as for ar_reduce_validate.
+ */
+int ar_gather_validate(const ar_desc* d, void* scratch, void* out,
                        int64_t out_stride, ar_epoch e, void* ctrl,
                        uint64_t timeout_ns, int32_t flags, void* stream);
 
@@ -248,6 +318,21 @@ int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
  *        = latest completion of op i at consumer c, last element = earliest
  *        start.  Must be zero-filled, and the last element set to all ones,
  *        by the caller.
+ *
+ * Other collectives (desc.collective), system mode only (nconsumers ==
+ * nranks), LL / LL128 / SENTINEL, no tile_order and no AR_SIM_NARROW /
+ * AR_SIM_WIDE (one kernel each, a workgroup of one wave per peer):
+ *   AR_ALLGATHER: op i's output at consumer c is the all-gather layout of
+ *        ar_gather_validate at out + (i*nranks + c)*out_stride.  A rank
+ *        starts op i+1 once it holds all of op i (one workgroup barrier per
+ *        op), as a rank whose next payload depends on this result would.
+ *   AR_TWOSHOT: per op and tile of a share, the reduce-scatter exchange, the
+ *        share owner's fixed-order reduce, then the all-gather exchange of
+ *        the reduced share; output as for AR_ALLREDUCE.  The trace's
+ *        "last store" is that of the reduce-scatter.
+ * Every wave waits for its own earlier stores (the sentinel re-arms among
+ * them) before it sends, so a slot is re-armed before the exchange that
+ * licenses its next write, in both regions.
  */
 #define AR_SIM_COOPERATIVE 1   /* launch with hipLaunchCooperativeKernel */
 #define AR_SIM_NARROW 2        /* one wave per tile serving every peer, instead

@@ -36,7 +36,7 @@ def test_header_symbols_all_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert abi.raw().ar_abi_version() == 2
+    assert abi.raw().ar_abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert abi.status_string(code).startswith("AR_")
     assert abi.status_string(-99) == "AR_UNKNOWN"
@@ -87,7 +87,8 @@ def _code(fn, *args):
 @pytest.mark.parametrize("field,value,code", [
     ("nranks", 0, abi.AR_EINVAL), ("nranks", 17, abi.AR_EINVAL),
     ("nconsumers", 3, abi.AR_EINVAL), ("count", -1, abi.AR_EINVAL),
-    ("proto", 7, abi.AR_EINVAL), ("reserved", 1, abi.AR_EINVAL),
+    ("proto", 7, abi.AR_EINVAL), ("collective", 3, abi.AR_EINVAL),
+    ("collective", -1, abi.AR_EINVAL),
 ])
 def test_desc_checks(field, value, code):
     d = abi.make_desc(4, 4096, "ll")
@@ -183,3 +184,74 @@ def test_selector_ties_nearest_and_unavailable():
         abi.ar_select_protocol(t, -1, 4)
     with pytest.raises(abi.ArError):
         abi.ar_select_protocol(t, 100, 17)
+
+
+# ------------------------------------------------- all-gather and two-shot --
+
+def test_shard_bounds_match_oracle():
+    import oracle
+    for n in (1, 2, 3, 4, 7, 8, 16):
+        for count in (0, 1, 5, 8, 9, 61, 1000, 4096, 4099, 32768):
+            for k in range(n):
+                assert abi.ar_shard_bounds(count, n, k) == oracle.shard_bounds(count, n, k)
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    for args in ((-1, 4, 0), (100, 0, 0), (100, 17, 0), (100, 4, 4), (100, 4, -1)):
+        assert _code("ar_shard_bounds", *args, ctypes.byref(lo), ctypes.byref(hi)) == abi.AR_EINVAL
+    assert _code("ar_shard_bounds", 100, 4, 0, None, ctypes.byref(hi)) == abi.AR_EINVAL
+
+
+def test_collective_sizes():
+    import oracle
+    for proto in ("ll", "ll128", "sentinel"):
+        for n, count in ((8, 4096), (16, 32768), (3, 1000), (4, 5)):
+            d = abi.make_desc(n, count, proto, n, "twoshot")
+            lo, hi = oracle.shard_bounds(count, n, 0)
+            slot = -(-oracle.encoded_bytes(proto, hi - lo) // 128) * 128
+            assert abi.ar_desc_slot_bytes(d) == slot
+            assert abi.ar_scratch_bytes(d) == 2 * n * 2 * n * slot      # two regions
+            g = abi.make_desc(n, count, proto, n, "allgather")
+            assert abi.ar_desc_slot_bytes(g) == abi.ar_slot_bytes(proto, count)
+            assert abi.ar_scratch_bytes(g) == n * 2 * n * abi.ar_slot_bytes(proto, count)
+    # two-shot: every rank consumes; no barrier baseline
+    for d in (abi.make_desc(8, 4096, "ll", 1, "twoshot"),
+              abi.make_desc(8, 4096, "barrier", 8, "twoshot")):
+        assert _code("ar_scratch_bytes", ctypes.byref(d)) == abi.AR_EINVAL
+
+
+def test_gather_and_twoshot_argument_checks():
+    ep = abi.ar_epoch(1, 0)
+    g = abi.make_desc(4, 100, "ll", 4, "allgather")
+    gv = lambda d, *a: _code("ar_gather_validate", ctypes.byref(d), *a)
+    # output rows: 4 ranks x 104 elements per consumer
+    assert gv(g, FAKE, FAKE, 4 * 104 - 8, ep, FAKE, 0, 0, None) == abi.AR_EINVAL
+    assert gv(g, FAKE, FAKE + 8, 4 * 104, ep, FAKE, 0, 0, None) == abi.AR_EALIGN
+    assert gv(g, FAKE, FAKE, 4 * 104, ep, None, 0, 0, None) == abi.AR_EINVAL
+    assert gv(g, FAKE, FAKE, 4 * 104, ep, FAKE, 0, 2, None) == abi.AR_EINVAL
+    # ar_gather_validate needs an all-gather descriptor, ar_reduce_validate the others
+    a = abi.make_desc(4, 100, "ll", 4)
+    assert gv(a, FAKE, FAKE, 4 * 104, ep, FAKE, 0, 0, None) == abi.AR_EINVAL
+    assert _code("ar_reduce_validate", ctypes.byref(g), FAKE, FAKE, 104, ep, FAKE, 0, 0,
+                 None) == abi.AR_EINVAL
+    # count 0 succeeds without touching the device
+    g0 = abi.make_desc(4, 0, "ll", 4, "allgather")
+    assert gv(g0, None, None, 0, ep, None, 0, 0, None) == abi.AR_OK
+
+
+def test_collective_sim_argument_checks():
+    base = dict(nops=4, inp=FAKE, in_stride=4096, out=FAKE, out_stride=8 * 4096,
+                scratch=FAKE, ctrl=FAKE, epoch=abi.ar_epoch(1, 0))
+
+    def run(d, flags=0, tile_order=None, out_stride=None):
+        p = abi.sim_params(d, base["nops"], base["inp"], base["in_stride"], base["out"],
+                           out_stride or base["out_stride"], base["scratch"], base["ctrl"],
+                           base["epoch"], tile_order=tile_order, flags=flags)
+        return _code("ar_sim_run", ctypes.byref(p), None)
+
+    g8 = abi.make_desc(8, 4096, "ll", 8, "allgather")
+    assert run(abi.make_desc(8, 4096, "ll", 1, "allgather")) == abi.AR_EINVAL   # system only
+    assert run(abi.make_desc(8, 4096, "barrier", 8, "allgather")) == abi.AR_EINVAL
+    assert run(g8, flags=abi.AR_SIM_NARROW) == abi.AR_EINVAL
+    assert run(g8, tile_order=FAKE) == abi.AR_EINVAL
+    assert run(g8, out_stride=4096) == abi.AR_EINVAL          # needs 8 rows of 4096
+    t8 = abi.make_desc(8, 4096, "sentinel", 8, "twoshot")
+    assert run(t8, flags=abi.AR_SIM_WIDE) == abi.AR_EINVAL
