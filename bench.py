@@ -11,6 +11,9 @@ so each op carries the real cross-rank dependency.  Share mode (one receive
 buffer, rank 0's share of the traffic) is reported beside it.  Inputs are
 resident in HBM before the timed region.
 
+`--collective allgather|twoshot` times the standalone all-gather or the
+two-shot all-reduce (system mode) on the same transfers instead.
+
 Prints ONE JSON line: value = microseconds per all-reduce (lower is better),
 with the roofline of the simulator kernel (algorithmic HBM bytes per launch /
 HIP-event duration of the launch), the measured one-chip floor, and the CPU
@@ -48,17 +51,36 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(proto: str, nranks: int, count: int, nconsumers: int) -> int:
-    """HBM bytes one op must move (re-polls not counted).  Every rank reads
-    its payload (N*S); every consumer receives E from each of the N-1 other
-    ranks (written once, read once) and writes S of output; sentinel slots
-    are re-armed after reading (another (N-1)*E per consumer).  A rank's own
-    contribution stays in registers."""
+def algorithmic_bytes(proto: str, nranks: int, count: int, nconsumers: int,
+                      collective: str = "allreduce") -> int:
+    """HBM bytes one op must move (re-polls not counted).
+
+    allreduce: every rank reads its payload (N*S); every consumer receives E
+    from each of the N-1 other ranks (written once, read once) and writes S
+    of output; sentinel slots are re-armed after reading (another (N-1)*E
+    per consumer).  A rank's own contribution stays in registers.
+    allgather: the same exchange, but every consumer writes N*S of output.
+    twoshot: every rank reads its payload (N*S); each share k's encoding E_k
+    is received by its owner from the N-1 others (reduce-scatter) and the
+    reduced share is received by the N-1 others (all-gather), each written
+    once and read once; every rank writes S of output; sentinel slots of
+    both exchanges are re-armed."""
     from collective_synchronization_amd import abi
     S = 2 * count
+    if collective == "twoshot":
+        sumE = 0
+        for k in range(nranks):
+            lo, hi = abi.ar_shard_bounds(count, nranks, k)
+            sumE += abi.ar_encoded_bytes(proto, hi - lo)
+        recv = 2 * (nranks - 1) * sumE
+        b = nranks * S + 2 * recv + nranks * S
+        if proto == "sentinel":
+            b += recv
+        return b
     E = abi.ar_encoded_bytes(proto, count)
     recv = nconsumers * (nranks - 1) * E
-    b = nranks * S + 2 * recv + nconsumers * S
+    out = nconsumers * S * (nranks if collective == "allgather" else 1)
+    b = nranks * S + 2 * recv + out
     if proto == "sentinel":
         b += recv
     return b
@@ -91,9 +113,9 @@ def measure_floor(torch, abi, iters=2000):
             "pingpong_pairs": len(oneway)}
 
 
-def cpu_baseline(x, proto, seconds):
+def cpu_baseline(x, proto, seconds, collective="allreduce"):
     import oracle
-    us, ops = oracle.time_allreduce(x, proto, seconds=seconds)
+    us, ops = oracle.time_collective(x, proto, collective, seconds=seconds)
     return us, ops
 
 
@@ -112,19 +134,20 @@ def load_traffic(kernel_name: str):
 
 
 def measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, warmup,
-            waves_per_rank=0, flags=0):
+            waves_per_rank=0, flags=0, collective="allreduce"):
     """Time `steps` launches of the simulator (one step = nops ops).
 
     Returns per-launch HIP-event durations (ms, on the launch stream), the
     wall-clock duration of the timed region (s), geometry and status."""
     nconsumers = nranks if mode == "system" else 1
     xd, stride = buffers.rows_to_device(x)
-    outd = torch.zeros((nops * nconsumers, stride), dtype=torch.int16, device="cuda")
-    ws = buffers.Workspace(nranks, count, proto, nconsumers)
+    ws = buffers.Workspace(nranks, count, proto, nconsumers, collective=collective)
+    ostride = ws.gather_stride() if collective == "allgather" else stride
+    outd = torch.zeros((nops * nconsumers, ostride), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
     kw = dict(timeout_ns=2_000_000_000, waves_per_rank=waves_per_rank, flags=flags)
     for _ in range(warmup):
-        ws.sim(nops, xd, stride, outd, stride, **kw)
+        ws.sim(nops, xd, stride, outd, ostride, **kw)
     torch.cuda.synchronize()
     if ws.status() != 0:
         raise RuntimeError(f"device status {abi.status_string(ws.status())}")
@@ -136,7 +159,7 @@ def measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, war
     for k in range(steps):
         if proto == "barrier":
             ws.reset_ctrl()
-        p = ws.sim_params(nops, xd, stride, outd, stride, **kw)
+        p = ws.sim_params(nops, xd, stride, outd, ostride, **kw)
         params.append(p)
         starts[k].record(stream)
         abi.ar_sim_run(p, stream)
@@ -151,10 +174,10 @@ def measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, war
     return dict(launch_ms=launch_ms, wall=wall, geo=geo, nconsumers=nconsumers)
 
 
-def summarize(res, proto, nranks, count, nops, steps):
+def summarize(res, proto, nranks, count, nops, steps, collective="allreduce"):
     import numpy as np
     launch_ms = res["launch_ms"]
-    b_op = algorithmic_bytes(proto, nranks, count, res["nconsumers"])
+    b_op = algorithmic_bytes(proto, nranks, count, res["nconsumers"], collective)
     avg = statistics.mean(launch_ms)
     return dict(
         us_per_op=res["wall"] * 1e6 / (steps * nops),
@@ -176,6 +199,10 @@ def main() -> int:
     ap.add_argument("--proto", default="sentinel",
                     choices=["ll", "ll128", "sentinel", "barrier"])
     ap.add_argument("--mode", default="system", choices=["share", "system"])
+    ap.add_argument("--collective", default="allreduce",
+                    choices=["allreduce", "allgather", "twoshot"],
+                    help="one-shot all-reduce (default), standalone all-gather or "
+                         "two-shot all-reduce (the last two: system mode)")
     ap.add_argument("--nranks", type=int, default=8)
     ap.add_argument("--rows", type=int, default=1)
     ap.add_argument("--hidden", type=int, default=4096)
@@ -205,10 +232,16 @@ def main() -> int:
     torch.cuda.set_device(0)
     cfg = CONFIGS[2]
     nranks, count, nops, proto = args.nranks, args.rows * args.hidden, args.nops, args.proto
-    default_workload = (nranks, args.rows, args.hidden, nops, proto, args.mode) == \
-        (cfg["nranks"], 1, cfg["hidden"], cfg["nops"], "sentinel", "system")
+    coll = args.collective
+    if coll != "allreduce" and (args.mode != "system" or proto == "barrier"):
+        print("bench.py: --collective allgather/twoshot run in system mode with "
+              "ll, ll128 or sentinel", file=sys.stderr)
+        return 2
+    default_workload = (nranks, args.rows, args.hidden, nops, proto, args.mode, coll) == \
+        (cfg["nranks"], 1, cfg["hidden"], cfg["nops"], "sentinel", "system", "allreduce")
     workload = cfg["name"] if default_workload else \
-        f"n{nranks}_{proto}_{args.rows}x{args.hidden}_{nops}ops_{args.mode}"
+        f"n{nranks}_{proto}_{args.rows}x{args.hidden}_{nops}ops_{args.mode}" + \
+        ("" if coll == "allreduce" else f"_{coll}")
     flags = abi.AR_SIM_COOPERATIVE if args.cooperative else 0
 
     x = inputs.payload(cfg["seed"], (nops, nranks, count), "normal")
@@ -222,18 +255,23 @@ def main() -> int:
         del src, dst
     try:
         res = measure(torch, abi, buffers, x, proto, nranks, count, nops, args.mode,
-                      args.steps, args.warmup, args.waves_per_rank, flags)
+                      args.steps, args.warmup, args.waves_per_rank, flags, coll)
     except RuntimeError as e:
         print(f"bench.py: {e}", file=sys.stderr)
         return 1
-    m = summarize(res, proto, nranks, count, nops, args.steps)
-    kname = ("k_sim_wide" if res["geo"]["kernel"] == "wide" else "k_sim") + \
-        f"<{abi.proto_id(proto)}>"
+    m = summarize(res, proto, nranks, count, nops, args.steps, coll)
+    if coll == "allreduce":
+        kname = ("k_sim_wide" if res["geo"]["kernel"] == "wide" else "k_sim") + \
+            f"<{abi.proto_id(proto)}>"
+    else:
+        kname = ("k_sim_gather" if coll == "allgather" else "k_sim_twoshot") + \
+            f"<{abi.proto_id(proto)}>"
+    unit = "us per all-gather" if coll == "allgather" else "us per all-reduce"
 
     line = {
         "metric": METRIC,
         "value": round(m["us_per_op"], 4),
-        "unit": "us per all-reduce",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -245,7 +283,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": workload, "nranks": nranks, "shape": [args.rows, args.hidden],
-            "protocol": proto, "ops_per_step": nops, "mode": args.mode,
+            "protocol": proto, "collective": coll, "ops_per_step": nops, "mode": args.mode,
             "nconsumers": res["nconsumers"], "values": "N(0,1) seed %d" % cfg["seed"],
             "tile_groups_per_rank": res["geo"]["waves_per_rank"],
             "blocks": res["geo"]["blocks"], "kernel": res["geo"]["kernel"],
@@ -264,7 +302,7 @@ def main() -> int:
         },
     }
 
-    if not args.no_share and args.mode == "system":
+    if not args.no_share and args.mode == "system" and coll == "allreduce":
         try:
             rs = measure(torch, abi, buffers, x, proto, nranks, count, nops, "share",
                          args.steps, args.warmup, args.waves_per_rank, flags)
@@ -285,14 +323,17 @@ def main() -> int:
         line["floor"] = fl
 
     if not args.no_cpu_baseline:
-        us, ops = cpu_baseline(x, proto, args.cpu_seconds)
+        us, ops = cpu_baseline(x, proto, args.cpu_seconds, coll)
+        what = {"allreduce": "encode N + validate/decode N + fixed-order reduce",
+                "allgather": "encode N + validate/decode N",
+                "twoshot": "per share: encode N + validate/decode N + fixed-order "
+                           "reduce + encode/decode of the reduced share"}[coll]
         line["cpu_baseline"] = {
-            "value": round(us, 3), "unit": "us per all-reduce", "cores": 1,
+            "value": round(us, 3), "unit": unit, "cores": 1,
             "kind": "oracle",
             "sample": (f"{ops} ops of the same workload (N={nranks}, [{args.rows},"
-                       f"{args.hidden}], {proto}: encode N + validate/decode N + "
-                       f"fixed-order reduce for one receiving rank, single thread, "
-                       f"~{args.cpu_seconds:g} s)"),
+                       f"{args.hidden}], {proto}: {what} for one receiving rank, "
+                       f"single thread, ~{args.cpu_seconds:g} s)"),
         }
 
     print(json.dumps(line), flush=True)

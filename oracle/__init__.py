@@ -282,6 +282,45 @@ def twoshot_ops(x: np.ndarray, proto="ll", seq0: int = 1) -> np.ndarray:
     return out
 
 
+def time_collective(x: np.ndarray, proto="sentinel", collective="allreduce",
+                    seconds: float = 10.0, seq0: int = 1):
+    """Time the oracle (single thread) on x uint16 [K, n, count] for ~seconds,
+    as seen by one receiving rank: "allreduce" (o_allreduce), "allgather"
+    (o_allgather) or "twoshot" (o_twoshot: every share's reduce-scatter,
+    reduce and all-gather).  Returns (microseconds per op, ops run)."""
+    if collective == "allreduce":
+        return time_allreduce(x, proto, seconds, seq0)
+    x = _u16(x)
+    K, n, count = x.shape
+    lib = _load()
+    p = proto_id(proto)
+    if collective == "allgather":
+        out = np.zeros((n, max(count, 1)), dtype=np.uint16)
+    elif collective == "twoshot":
+        out = np.zeros(max(count, 1), dtype=np.uint16)
+    else:
+        raise ValueError(f"unknown collective {collective!r}")
+    optr = _ptr(out, ctypes.c_uint16)
+    rows = [np.ascontiguousarray(x[i]) for i in range(K)]
+    ptrs = [_ptr(r, ctypes.c_uint16) for r in rows]
+    seq = seq0
+    ops = 0
+    t0 = time.perf_counter()
+    deadline = t0 + seconds
+    while True:
+        for i in range(K):
+            if collective == "allgather":
+                lib.o_allgather(n, ptrs[i], count, p, seq, None, optr)
+            else:
+                lib.o_twoshot(n, ptrs[i], count, p, seq, optr)
+            seq = seq + 1 if seq != 0xFFFFFFFF else 1
+            ops += 1
+        if time.perf_counter() >= deadline:
+            break
+    dt = time.perf_counter() - t0
+    return dt * 1e6 / ops, ops
+
+
 def time_allreduce(x: np.ndarray, proto="sentinel", seconds: float = 10.0,
                    seq0: int = 1):
     """Time the oracle (single thread) on x uint16 [K, n, count] for ~seconds.
