@@ -382,6 +382,13 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
   const int dst_c = SHARE ? 0 : w;
   const bool own = consumer && w == g;
   const bool poller = consumer && w != g;
+  // The rank's own chunk is staged in LDS by the sender wave g+1, which
+  // holds the same encoded chunk in registers, so that the own wave only
+  // reduces and stays off the critical path.  Share mode and a single rank
+  // have no sender wave in the consumer workgroup: there the own wave
+  // stages it.
+  const bool own_stages = SHARE || a.nranks == 1;
+  const bool stager = own_stages ? own : (w == (g + 1) % a.nranks);
 
   const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
   const uint32_t N = (uint32_t)a.nranks;
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
                            __HIP_MEMORY_SCOPE_AGENT);
 
   uint32_t wnext[4] = {0u, 0u, 0u, 0u};
-  const bool needs_input = sender || own;
+  const bool needs_input = sender || (own && own_stages);
   const uint32_t row_bytes = (uint32_t)(((a.count * 2) + 15) & ~int64_t(15));
   const int keep = chunk_keep<P>(a.count, tg, lane);
   if (pipelined && needs_input)
@@ -438,16 +445,12 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
     const uint32_t dst0 = ((uint32_t)dst_c * 2u * N + pp * N + (uint32_t)g) * a.slot_bytes;
     const uint32_t src0 = ((uint32_t)cself * 2u * N + pp * N) * a.slot_bytes;
     // ---- send every tile of this op first ----
-    u32x4 own_v = u32x4{0u, 0u, 0u, 0u};       // single-tile case: own chunk
-    if (sender || (own && pipelined)) {
-      // senders take their tiles in the caller's order, if one is given
-      const uint16_t* ord = (sender && a.order)
-                                ? a.order + ((int64_t)op * a.nranks + g) * a.TPW
-                                : nullptr;
-      const int nsteps = ord ? a.TPW : mine;
-      for (int j = 0; j < nsteps; ++j) {
-        const int k = ord ? (int)ord[j] : j;
-        if (k >= mine) continue;
+    // own0 / own1: the encoded own chunks of the group's first two tiles,
+    // kept by the stager for its LDS writes
+    u32x4 own0 = u32x4{0u, 0u, 0u, 0u};
+    u32x4 own1 = u32x4{0u, 0u, 0u, 0u};
+    if (sender || (own && own_stages)) {
+      auto send_tile = [&](int k) -> u32x4 {
         const int tile = tg + k * G;
         u32x4 mine_v;
         if (pipelined) {
@@ -455,11 +458,30 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
           mine_v = encode_words<P>(wnext, lane, seq);
           if (op + 1 < a.nops)
             load_chunk<P>(row + op_rows * a.in_stride, row_bytes, tile, lane, wnext);
-          own_v = mine_v;
         } else {
           mine_v = encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq);
         }
         if (sender) store_chunk<P>(rs, dst0, 0u, 1, -1, tile, a.E, lane, mine_v);
+        return mine_v;
+      };
+      // senders take their tiles in the caller's order, if one is given (a
+      // separate loop: the order's loads would otherwise make every send
+      // wait for all of the wave's outstanding memory operations)
+      if (sender && a.order) {
+        const uint16_t* ord = a.order + ((int64_t)op * a.nranks + g) * a.TPW;
+        for (int j = 0; j < a.TPW; ++j) {
+          const int k = (int)ord[j];
+          if (k < mine) {
+            const u32x4 v = send_tile(k);
+            if (k == 0) own0 = v;
+            if (BATCH > 1 && k == 1) own1 = v;
+          }
+        }
+      } else {
+        // (one tile per group whenever BATCH is 1)
+        own0 = send_tile(0);
+        if (BATCH > 1 && mine > 1) own1 = send_tile(1);
+        for (int k = BATCH > 1 ? 2 : 1; k < mine; ++k) send_tile(k);
       }
       if (sender && P == kLL128) {
         fence_release();
@@ -508,13 +530,18 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
           for (int j = 0; j < BATCH; ++j)
             if (j < nb) lds[buf][j][w][lane] = got[j];
         }
-      } else {
+      }
+      if (stager) {
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j)
+        for (int j = 0; j < BATCH; ++j) {
+          const int k = k0 + j;
           if (j < nb)
-            lds[buf][j][w][lane] =
-                pipelined ? own_v
-                          : encode_chunk<P>(row, row_bytes, a.count, tg + (k0 + j) * G, lane, seq);
+            lds[buf][j][g][lane] =
+                k == 0 ? own0
+                       : (BATCH > 1 && k == 1)
+                             ? own1
+                             : encode_chunk<P>(row, row_bytes, a.count, tg + k * G, lane, seq);
+        }
       }
       __syncthreads();
       if (lds_err) return;                         // whole workgroup
