@@ -19,7 +19,10 @@ arithmetic is in the C file, which cites the pages it follows:
   abstract -- one-shot all-reduce with dual buffering; the two-shot form
   (reduce-scatter of shares, then all-gather) for more GPUs;
 * flash-comm abstract again -- the same transfers carry a standalone
-  all-gather.
+  all-gather;
+* "Why Microseconds Matter in AI Infrastructure", section "Communication is
+  becoming part of GPU execution" -- send/receive/reduce called from inside
+  the producing kernel (the producer epilogue used for it: a per-rank scale).
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against
 something other than itself (exhaustive sweeps against torch and numpy, an
@@ -90,6 +93,8 @@ def _load():
     lib.o_twoshot.argtypes = [ctypes.c_int, u16p, i64, ctypes.c_int,
                               ctypes.c_uint32, u16p]
     lib.o_twoshot.restype = ctypes.c_int
+    lib.o_scale.argtypes = [u16p, i64, ctypes.c_float, u16p]
+    lib.o_scale.restype = None
     lib.o_bf16_rne_array.argtypes = [f32p, i64, u16p]
     lib.o_bf16_rne_array.restype = None
     lib.o_canon_in_array.argtypes = [u16p, i64, u16p]
@@ -217,6 +222,16 @@ def allreduce_ops(x: np.ndarray, proto="ll", seq0: int = 1) -> np.ndarray:
             raise RuntimeError(f"oracle op {i} not ready: status {st}")
         seq = epoch_next(seq)
     return out
+
+
+def scale(x: np.ndarray, s: float) -> np.ndarray:
+    """Producer epilogue: bf16_rne(f32(x) * s), one binary32 multiply per
+    element.  x: uint16 [count] -> uint16 [count]."""
+    x = _u16(x).reshape(-1)
+    out = np.zeros(max(x.size, 1), dtype=np.uint16)
+    _load().o_scale(_ptr(x, ctypes.c_uint16), x.size, ctypes.c_float(s),
+                    _ptr(out, ctypes.c_uint16))
+    return out[:x.size]
 
 
 def shard_bounds(count: int, n: int, k: int):

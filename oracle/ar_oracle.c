@@ -506,3 +506,22 @@ int o_twoshot(int n, const uint16_t* x, int64_t count, int proto,
     free(red);
     return status;
 }
+
+/* ------------------------------------------------ producer epilogue --- */
+/*
+ * "Why Microseconds Matter in AI Infrastructure", section "Communication is
+ * becoming part of GPU execution": send, receive and reduce become callable
+ * from inside the kernels that produce the data.  The producer used to
+ * exercise that path is a per-rank scaling epilogue (a reading: the pages
+ * name no producer):
+ *     y[j] = bf16_rne( f32(x[j]) * s )
+ * one binary32 multiplication, round to nearest even, then the bf16
+ * rounding of o_bf16_rne (NaN -> 0x7FC0).
+ */
+void o_scale(const uint16_t* x, int64_t count, float s, uint16_t* out)
+{
+    for (int64_t j = 0; j < count; ++j) {
+        float p = o_bf16_to_f32(x[j]) * s;
+        out[j] = o_bf16_rne(p);
+    }
+}
