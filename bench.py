@@ -174,6 +174,47 @@ def measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, war
     return dict(launch_ms=launch_ms, wall=wall, geo=geo, nconsumers=nconsumers)
 
 
+def measure_epilogue(torch, abi, buffers, x, proto, nranks, count, steps, warmup):
+    """Stream-ordered ops whose producer is a per-rank scale, two ways:
+    fused (ar_scale_pack sends from the producer's epilogue) and unfused
+    (ar_scale_rows writes the result, ar_pack_* encodes it).  Both end with
+    ar_reduce_validate (system mode).  HIP events around the producer part
+    and around the whole op, median over `steps` ops."""
+    stride = buffers.row_stride(count)
+    xd, _ = buffers.rows_to_device(x)
+    scales = torch.linspace(0.5, 1.5, nranks, dtype=torch.float32, device="cuda")
+    yd = torch.zeros((nranks, stride), dtype=torch.int16, device="cuda")
+    outd = torch.zeros((nranks, stride), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for mode in ("fused", "unfused"):
+        ws = buffers.Workspace(nranks, count, proto, nranks)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for k in range(warmup + steps):
+            e = ev[k - warmup] if k >= warmup else None
+            if e:
+                e[0].record(stream)
+            if mode == "fused":
+                abi.ar_scale_pack(ws.desc, xd, stride, scales, ws.scratch, ws.epoch, stream)
+            else:
+                abi.ar_scale_rows(nranks, count, xd, stride, scales, yd, stride, stream)
+                ws.pack(yd, stride, stream)
+            if e:
+                e[1].record(stream)
+            ws.reduce(outd, stride, timeout_ns=2_000_000_000, stream=stream)
+            if e:
+                e[2].record(stream)
+            ws.flip()
+        torch.cuda.synchronize()
+        if ws.status() != 0:
+            raise RuntimeError(f"device status {abi.status_string(ws.status())}")
+        out[mode] = {
+            "producer_us": round(statistics.median(a.elapsed_time(b) for a, b, _ in ev) * 1e3, 3),
+            "op_us": round(statistics.median(a.elapsed_time(c) for a, _, c in ev) * 1e3, 3),
+        }
+    return out
+
+
 def summarize(res, proto, nranks, count, nops, steps, collective="allreduce"):
     import numpy as np
     launch_ms = res["launch_ms"]
@@ -213,6 +254,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-floor", action="store_true")
     ap.add_argument("--no-share", action="store_true")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="also time stream-ordered ops whose producer (a per-rank "
+                         "scale) sends from its epilogue, against a separate pack")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run ar_probe_copy over BYTES, 3 times (reference "
                          "dispatches for hardware byte counters)")
@@ -316,6 +360,13 @@ def main() -> int:
             }
         except RuntimeError as e:
             line["share_mode"] = {"error": str(e)}
+
+    if args.epilogue:
+        try:
+            line["epilogue"] = measure_epilogue(torch, abi, buffers, x[0], proto, nranks,
+                                                count, args.steps, args.warmup)
+        except RuntimeError as e:
+            line["epilogue"] = {"error": str(e)}
 
     if not args.no_floor:
         fl = measure_floor(torch, abi)

@@ -113,6 +113,9 @@ _SIGS = {
                             _u64, _i32, _vp], ctypes.c_int),
     "ar_gather_validate": ([ctypes.POINTER(ar_desc), _vp, _vp, _i64, ar_epoch, _vp,
                             _u64, _i32, _vp], ctypes.c_int),
+    "ar_scale_pack": ([ctypes.POINTER(ar_desc), _vp, _i64, _vp, _vp, ar_epoch, _vp],
+                      ctypes.c_int),
+    "ar_scale_rows": ([_i32, _i64, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "ar_sim_run": ([ctypes.POINTER(ar_sim_params), _vp], ctypes.c_int),
     "ar_sim_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
                          ctypes.POINTER(_i32), ctypes.POINTER(_i32),
@@ -278,6 +281,17 @@ def ar_gather_validate(desc, scratch, out, out_stride, epoch, ctrl,
     _check(_lib.ar_gather_validate(ctypes.byref(desc), _ptr(scratch), _ptr(out),
                                    out_stride, epoch, _ptr(ctrl), timeout_ns, flags,
                                    _stream(stream)), "ar_gather_validate")
+
+
+def ar_scale_pack(desc, inp, in_stride, scales, scratch, epoch, stream=None) -> None:
+    _check(_lib.ar_scale_pack(ctypes.byref(desc), _ptr(inp), in_stride, _ptr(scales),
+                              _ptr(scratch), epoch, _stream(stream)), "ar_scale_pack")
+
+
+def ar_scale_rows(nranks, count, inp, in_stride, scales, out, out_stride,
+                  stream=None) -> None:
+    _check(_lib.ar_scale_rows(nranks, count, _ptr(inp), in_stride, _ptr(scales), _ptr(out),
+                              out_stride, _stream(stream)), "ar_scale_rows")
 
 
 def sim_params(desc, nops, inp, in_stride, out, out_stride, scratch, ctrl, epoch,

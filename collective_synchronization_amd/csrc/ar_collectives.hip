@@ -14,6 +14,7 @@
 #include <stdint.h>
 
 #include "../../include/ar.h"
+#include "../../include/ar_dev.h"
 #include "ar_host.h"
 #include "ar_protocols.h"
 
@@ -46,16 +47,69 @@ __global__ __launch_bounds__(kBlock) void k_gather(GatherArgs a) {
   const int rem = gw - c * per_c;
   const int r = rem / a.tiles;
   const int tile = rem - r * a.tiles;
-  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
-  const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
-  const uint32_t at =
-      (((uint32_t)c * 2u + a.parity) * (uint32_t)a.nranks + (uint32_t)r) * a.slot_bytes + loff;
-  u32x4 v;
-  if (poll_chunk<P>(rs, at, loff < a.E, a.seq, seq_prev(seq_prev(a.seq)), a.rearm != 0,
-                    a.ctrl, a.timeout_ticks, lane, v) != 0)
+  const ar_dev::buffer b = ar_dev::make(a.scratch, a.scratch_bytes, a.slot_bytes, a.E,
+                                        a.nranks, a.nconsumers, a.count, a.seq, a.parity);
+  uint32_t w[4];
+  if (ar_dev::recv<P>(b, c, r, tile, lane, a.rearm != 0, a.ctrl, a.timeout_ticks, w) != 0)
     return;
-  store_chunk_elems<P>(a.out + (int64_t)c * a.out_stride + (int64_t)r * a.row_stride,
-                       a.count, tile, a.E, lane, v);
+  ar_dev::store_row<P>(a.out + (int64_t)c * a.out_stride + (int64_t)r * a.row_stride,
+                       a.count, tile, lane, w);
+}
+
+// --------------------------------------------------- producer epilogue --
+
+// y = bf16_rne(f32(x) * s) on the lane's data words (the producer whose
+// epilogue sends; one binary32 multiplication per element).
+__device__ __forceinline__ void scale_words(uint32_t w[4], float s) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    w[d] = pack2(to_bf16(bf_lo(w[d]) * s), to_bf16(bf_hi(w[d]) * s));
+}
+
+struct ScaleArgs {
+  const uint16_t* in;
+  int64_t in_stride;
+  const float* scales;
+  uint16_t* out;              // unfused producer only
+  int64_t out_stride;
+  ar_dev::buffer b;           // fused producer only
+  int32_t nranks, tiles;
+  int64_t count;
+};
+
+// Fused: one wave per (rank, tile) computes its scaled payload chunk and
+// broadcasts it from registers with the device-callable interface.
+template <int P>
+__global__ __launch_bounds__(kBlock) void k_scale_send(ScaleArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int r = gw / a.tiles;
+  if (r >= a.nranks) return;
+  const int tile = gw - r * a.tiles;
+  uint32_t w[4];
+  load_chunk<P>(a.in + (int64_t)r * a.in_stride,
+                (uint32_t)(((a.count * 2) + 15) & ~int64_t(15)), tile, lane, w);
+  scale_words(w, a.scales[r]);
+  mask_words(w, chunk_keep<P>(a.count, tile, lane));
+  ar_dev::broadcast<P>(a.b, r, tile, lane, w);
+  if (P == kLL128) {
+    ar_dev::fence();
+    ar_dev::broadcast_flags(a.b, r, tile, lane);
+  }
+}
+
+// Unfused: the same producer writing its result to HBM (8 elements a lane).
+__global__ __launch_bounds__(kBlock) void k_scale_rows(ScaleArgs a) {
+  const int64_t per_row = (a.count + 7) / 8;
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t r = i / per_row;
+  if (r >= a.nranks) return;
+  const int64_t first = (i - r * per_row) * 8;
+  uint32_t w[4];
+  // 8 elements from a 16-byte aligned start; both helpers stop at count
+  load_elems(a.in + r * a.in_stride, a.count, first, 8, w);
+  scale_words(w, a.scales[r]);
+  store_elems(a.out + r * a.out_stride, a.count, first, 8, w);
 }
 
 struct TsArgs {
@@ -679,4 +733,60 @@ extern "C" int ar_gather_validate(const ar_desc* d, void* scratch, void* out,
     case kSentinel: return map_hip(launch(k_gather<kSentinel>, grid, dim3(kBlock), s, a));
     default: return map_hip(launch(k_gather<kBarrier>, grid, dim3(kBlock), s, a));
   }
+}
+
+extern "C" int ar_scale_pack(const ar_desc* d, const void* in, int64_t in_stride,
+                             const float* scales, void* scratch, ar_epoch e,
+                             void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->collective == AR_TWOSHOT) return AR_EINVAL;
+  if (e.parity > 1u || e.seq == 0u) return AR_EINVAL;
+  rc = check_rows(in, in_stride, d->count);
+  if (rc) return rc;
+  if (d->count == 0) return AR_OK;
+  if (!scratch || !scales) return AR_EINVAL;
+  if (!aligned(scratch, 256) || !aligned(scales, 4)) return AR_EALIGN;
+  ScaleArgs a{};
+  a.in = static_cast<const uint16_t*>(in);
+  a.in_stride = in_stride;
+  a.scales = scales;
+  a.count = d->count;
+  a.nranks = d->nranks;
+  const int64_t E = encoded_bytes(d->proto, d->count);
+  a.tiles = (int32_t)ceil_div64(E, kTileBytes);
+  a.b = ar_dev::make(scratch, (uint32_t)desc_scratch_bytes(d), (uint32_t)desc_slot_bytes(d),
+                     (uint32_t)E, d->nranks, d->nconsumers, d->count, e.seq, e.parity);
+  const dim3 grid((unsigned)ceil_div64((int64_t)a.tiles * d->nranks, kWavesPerBlock));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d->proto) {
+    case kLL: return map_hip(launch(k_scale_send<kLL>, grid, dim3(kBlock), s, a));
+    case kLL128: return map_hip(launch(k_scale_send<kLL128>, grid, dim3(kBlock), s, a));
+    case kSentinel: return map_hip(launch(k_scale_send<kSentinel>, grid, dim3(kBlock), s, a));
+    default: return map_hip(launch(k_scale_send<kBarrier>, grid, dim3(kBlock), s, a));
+  }
+}
+
+extern "C" int ar_scale_rows(int32_t nranks, int64_t count, const void* in,
+                             int64_t in_stride, const float* scales, void* out,
+                             int64_t out_stride, void* stream) {
+  if (nranks < 1 || nranks > AR_MAX_RANKS || count < 0) return AR_EINVAL;
+  int rc = check_rows(in, in_stride, count);
+  if (rc) return rc;
+  rc = check_rows(out, out_stride, count);
+  if (rc) return rc;
+  if (count == 0) return AR_OK;
+  if (!scales) return AR_EINVAL;
+  if (!aligned(scales, 4)) return AR_EALIGN;
+  ScaleArgs a{};
+  a.in = static_cast<const uint16_t*>(in);
+  a.in_stride = in_stride;
+  a.scales = scales;
+  a.out = static_cast<uint16_t*>(out);
+  a.out_stride = out_stride;
+  a.nranks = nranks;
+  a.count = count;
+  const int64_t threads = (int64_t)nranks * ((count + 7) / 8);
+  return map_hip(launch(k_scale_rows, dim3((unsigned)ceil_div64(threads, kBlock)),
+                        dim3(kBlock), static_cast<hipStream_t>(stream), a));
 }

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "../../include/ar.h"
+#include "../../include/ar_dev.h"
 #include "ar_host.h"
 #include "ar_protocols.h"
 
@@ -38,7 +39,8 @@ struct PackArgs {
   uint32_t seq, parity;
 };
 
-// One wave per (rank, tile): encode and store into every consumer's buffer.
+// One wave per (rank, tile): encode and broadcast to every consumer's buffer
+// (the device-callable interface of ar_dev.h).
 template <int P>
 __global__ __launch_bounds__(kBlock) void k_pack(PackArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -46,16 +48,16 @@ __global__ __launch_bounds__(kBlock) void k_pack(PackArgs a) {
   const int r = gw / a.tiles;
   const int tile = gw - r * a.tiles;
   if (r >= a.nranks) return;
-  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
-  const uint32_t cstride = 2u * (uint32_t)a.nranks * a.slot_bytes;
-  const uint32_t dst0 = (a.parity * (uint32_t)a.nranks + (uint32_t)r) * a.slot_bytes;
-  const uint16_t* row = a.in + (int64_t)r * a.in_stride;
-  produce_data<P>(rs, dst0, cstride, a.nconsumers, -1, row,
-                  (uint32_t)(((a.count * 2) + 15) & ~int64_t(15)), a.count, tile, a.E,
-                  a.seq, lane);
+  const ar_dev::buffer b = ar_dev::make(a.scratch, a.scratch_bytes, a.slot_bytes, a.E,
+                                      a.nranks, a.nconsumers, a.count, a.seq, a.parity);
+  uint32_t w[4];
+  load_chunk<P>(a.in + (int64_t)r * a.in_stride,
+                (uint32_t)(((a.count * 2) + 15) & ~int64_t(15)), tile, lane, w);
+  mask_words(w, chunk_keep<P>(a.count, tile, lane));
+  ar_dev::broadcast<P>(b, r, tile, lane, w);
   if (P == kLL128) {
-    fence_release();
-    produce_flags(rs, dst0, cstride, a.nconsumers, -1, tile, a.E, a.seq, lane);
+    ar_dev::fence();
+    ar_dev::broadcast_flags(b, r, tile, lane);
   }
 }
 
@@ -81,14 +83,10 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
   const int c = gw / a.tiles;
   const int tile = gw - c * a.tiles;
   if (c >= a.nconsumers) return;
-  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
-  const uint32_t src0 =
-      ((uint32_t)c * 2u + a.parity) * (uint32_t)a.nranks * a.slot_bytes;
-  const uint32_t stale = seq_prev(seq_prev(a.seq));
-  consume_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, tile, a.E, a.seq,
-                        stale, a.rearm != 0,
-                        a.out + (int64_t)c * a.out_stride, a.count, a.ctrl,
-                        a.timeout_ticks, lane);
+  const ar_dev::buffer b = ar_dev::make(a.scratch, a.scratch_bytes, a.slot_bytes, a.E,
+                                      a.nranks, a.nconsumers, a.count, a.seq, a.parity);
+  ar_dev::recv_reduce<P, NMAX>(b, c, tile, lane, a.rearm != 0, a.ctrl, a.timeout_ticks,
+                               a.out + (int64_t)c * a.out_stride);
 }
 
 // Fill byte range [begin, begin+bytes) of the buffer with 0xFF, 16 bytes a

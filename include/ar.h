@@ -280,6 +280,31 @@ int ar_gather_validate(const ar_desc* d, void* scratch, void* out,
                        int64_t out_stride, ar_epoch e, void* ctrl,
                        uint64_t timeout_ns, int32_t flags, void* stream);
 
+/* ------------------------------------------------- producer epilogue --- */
+/*
+ * In-kernel sending ("Why Microseconds Matter in AI Infrastructure",
+ * "Communication is becoming part of GPU execution": send, receive, reduce
+ * and broadcast called from inside kernels).  The device-callable interface
+ * is include/ar_dev.h; these two entry points compare a producer that sends
+ * from its epilogue with one that writes its result for a separate pack.
+ * The producer is a per-rank scale: y_r = bf16_rne(f32(x_r) * scales[r]),
+ * one binary32 multiplication per element (NaN -> 0x7FC0).
+ *
+ * ar_scale_pack -- fused: computes y_r and encodes it for epoch e straight
+ * into slot r of every consumer (the ar_pack_* layout and encoding of
+ * d->proto; AR_ALLREDUCE and AR_ALLGATHER descriptors).  in as for ar_pack_*;
+ * scales: device float[nranks], 4-byte aligned.
+ */
+int ar_scale_pack(const ar_desc* d, const void* in, int64_t in_stride,
+                  const float* scales, void* scratch, ar_epoch e, void* stream);
+
+/*
+ * ar_scale_rows -- unfused: writes y_r to out + r*out_stride (elements below
+ * count only; rows as for ar_pack_*), for a later ar_pack_*.
+ */
+int ar_scale_rows(int32_t nranks, int64_t count, const void* in, int64_t in_stride,
+                  const float* scales, void* out, int64_t out_stride, void* stream);
+
 /* ------------------------------------------------------------ simulator --- */
 /*
  * ar_sim_run -- `nops` back-to-back one-shot all-reduces in one persistent

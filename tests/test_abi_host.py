@@ -255,3 +255,26 @@ def test_collective_sim_argument_checks():
     assert run(g8, out_stride=4096) == abi.AR_EINVAL          # needs 8 rows of 4096
     t8 = abi.make_desc(8, 4096, "sentinel", 8, "twoshot")
     assert run(t8, flags=abi.AR_SIM_WIDE) == abi.AR_EINVAL
+
+
+def test_epilogue_argument_checks():
+    ep = abi.ar_epoch(1, 0)
+    d = abi.make_desc(4, 100, "ll", 4)
+    sp = lambda dd, *a: _code("ar_scale_pack", ctypes.byref(dd), *a)
+    assert sp(d, FAKE, 104, None, FAKE, ep, None) == abi.AR_EINVAL          # null scales
+    assert sp(d, FAKE, 104, FAKE + 2, FAKE, ep, None) == abi.AR_EALIGN      # scales align
+    assert sp(d, FAKE + 8, 104, FAKE, FAKE, ep, None) == abi.AR_EALIGN      # in align
+    assert sp(d, FAKE, 104, FAKE, FAKE + 64, ep, None) == abi.AR_EALIGN     # scratch align
+    assert sp(d, FAKE, 104, FAKE, FAKE, abi.ar_epoch(0, 0), None) == abi.AR_EINVAL
+    t = abi.make_desc(4, 100, "ll", 4, "twoshot")
+    assert sp(t, FAKE, 104, FAKE, FAKE, ep, None) == abi.AR_EINVAL          # not for two-shot
+    d0 = abi.make_desc(4, 0, "ll", 4)
+    assert sp(d0, None, 0, None, None, ep, None) == abi.AR_OK
+    sr = lambda *a: _code("ar_scale_rows", *a)
+    assert sr(0, 100, FAKE, 104, FAKE, FAKE, 104, None) == abi.AR_EINVAL
+    assert sr(17, 100, FAKE, 104, FAKE, FAKE, 104, None) == abi.AR_EINVAL
+    assert sr(4, -1, FAKE, 104, FAKE, FAKE, 104, None) == abi.AR_EINVAL
+    assert sr(4, 100, FAKE, 104, None, FAKE, 104, None) == abi.AR_EINVAL
+    assert sr(4, 100, FAKE, 96, FAKE, FAKE, 104, None) == abi.AR_EINVAL     # in stride < count
+    assert sr(4, 100, FAKE, 104, FAKE, FAKE + 4, 104, None) == abi.AR_EALIGN
+    assert sr(4, 0, None, 0, None, None, 0, None) == abi.AR_OK
