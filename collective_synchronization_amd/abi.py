@@ -60,7 +60,7 @@ class ar_sim_params(ctypes.Structure):
 
 
 class ar_cost_entry(ctypes.Structure):
-    _fields_ = [("nranks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("nranks", ctypes.c_int32), ("collective", ctypes.c_int32),
                 ("max_bytes", ctypes.c_int64),
                 ("alpha_us", ctypes.c_double * 4),
                 ("beta_us_per_byte", ctypes.c_double * 4)]
@@ -124,6 +124,12 @@ _SIGS = {
     "ar_select_protocol": ([ctypes.POINTER(ar_cost_entry), _i32, _i64, _i32,
                             ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)],
                            ctypes.c_int),
+    "ar_select_collective": ([ctypes.POINTER(ar_cost_entry), _i32, _i32, _i64, _i32,
+                              ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)],
+                             ctypes.c_int),
+    "ar_select_allreduce": ([ctypes.POINTER(ar_cost_entry), _i32, _i64, _i32,
+                             ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                             ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     "ar_probe_pingpong": ([_vp, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
     "ar_probe_loadchain": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
     "ar_probe_litmus": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
@@ -325,11 +331,12 @@ def ar_wallclock_hz() -> float:
 def cost_table(entries) -> "ctypes.Array":
     """entries: iterable of dicts {nranks, alpha_us[4], beta_us_per_byte[4]}
     and optionally max_bytes (upper end of the size range; absent or <= 0:
-    no upper end)."""
+    no upper end) and collective (name or id; absent: one-shot all-reduce)."""
     entries = list(entries)
     arr = (ar_cost_entry * len(entries))()
     for i, e in enumerate(entries):
         arr[i].nranks = int(e["nranks"])
+        arr[i].collective = collective_id(e.get("collective", AR_ALLREDUCE))
         arr[i].max_bytes = int(e.get("max_bytes", 0))
         for p in range(4):
             arr[i].alpha_us[p] = float(e["alpha_us"][p])
@@ -345,6 +352,26 @@ def ar_select_protocol(table, payload_bytes: int, nranks: int):
                                    ctypes.byref(out), ctypes.byref(pred)),
            "ar_select_protocol")
     return out.value, pred.value
+
+
+def ar_select_collective(table, collective, payload_bytes: int, nranks: int):
+    """Returns (protocol id, predicted microseconds) for one collective."""
+    out = _i32()
+    pred = ctypes.c_double()
+    _check(_lib.ar_select_collective(table, len(table), collective_id(collective),
+                                     payload_bytes, nranks, ctypes.byref(out),
+                                     ctypes.byref(pred)), "ar_select_collective")
+    return out.value, pred.value
+
+
+def ar_select_allreduce(table, payload_bytes: int, nranks: int):
+    """Returns (collective id, protocol id, predicted microseconds)."""
+    coll, out = _i32(), _i32()
+    pred = ctypes.c_double()
+    _check(_lib.ar_select_allreduce(table, len(table), payload_bytes, nranks,
+                                    ctypes.byref(coll), ctypes.byref(out),
+                                    ctypes.byref(pred)), "ar_select_allreduce")
+    return coll.value, out.value, pred.value
 
 
 def ar_probe_pingpong(work, iters, xcd_a, xcd_b, result, stream=None) -> None:

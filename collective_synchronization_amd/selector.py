@@ -1,4 +1,4 @@
-"""Cost-guided protocol selector: measurement sweep, fit and table.
+"""Cost-guided selector: measurement sweep, fit and table.
 
 "flash-comm: Self-Synchronizing Collective Communication for LLM Decoding",
 abstract: the readiness encoding is chosen by message size and the number of
@@ -6,17 +6,23 @@ GPUs, trading synchronization overhead against the extra bytes an encoding
 moves.  "Why Microseconds Matter in AI Infrastructure", sections "What I
 learned from it" and "Where I think this is heading": the choice is made from
 measurements of the kernels, with a performance model as the next step.
+"SiFAR: Synchronization-Free All-Reduce for Low-Latency LLM Inference",
+abstract: one-shot scales poorly with the number of GPUs and two-shot does
+better at higher degrees -- so the same model also chooses the all-reduce
+algorithm.
 
-Model per protocol p, rank count N and size range: T_p(S) = alpha_p +
-beta_p * S, with S the payload bytes per rank.  alpha and beta are fitted to
-per-op times measured with the persistent simulator on this GPU (system mode,
-every rank running the full program), minimising relative error so that the
+Model per collective (one-shot all-reduce, two-shot all-reduce, all-gather),
+protocol p, rank count N and size range: T_p(S) = alpha_p + beta_p * S, with
+S the payload bytes per rank.  alpha and beta are fitted to per-op times
+measured with the persistent simulator on this GPU (system mode, every rank
+running the full program), minimising relative error so that the
 latency-bound small sizes count as much as the large ones.  The simulator
 changes kernel and geometry with size (a workgroup per peer at the smallest
-sizes, a wave per tile beyond), so each rank count may get two ranges, split
-where that lowers the worst-case regret on the measured points.  The argmin itself
-runs in the library (``ar_select_protocol``); this module measures, fits,
-stores and loads the table.
+sizes, a wave per tile beyond), so each (collective, rank count) may get two
+ranges, split where that lowers the worst-case protocol regret on the
+measured points.  The argmin itself runs in the library
+(``ar_select_protocol``, ``ar_select_collective``, ``ar_select_allreduce``);
+this module measures, fits, stores and loads the table.
 
     python -m collective_synchronization_amd.selector --out cost_table.json
 
@@ -36,7 +42,13 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 TABLE_PATH = os.path.join(HERE, "cost_table.json")
 PROTOS = ("ll", "ll128", "sentinel", "barrier")
+COLLECTIVES = ("allreduce", "allgather", "twoshot")     # ids 0, 1, 2 of ar.h
 SIZES = tuple(2 ** k for k in range(11, 23))          # 2 KiB .. 4 MiB per rank
+GATHER_MAX = 1 << 20                                  # all-gather sweep: up to 1 MiB
+
+
+def _coll(p) -> str:
+    return p.get("collective", "allreduce")
 
 
 def fit_alpha_beta(sizes, times):
@@ -55,38 +67,42 @@ def fit_alpha_beta(sizes, times):
     return alpha, beta
 
 
-def _fit_range(points, n, sizes):
+def _pts(points, coll, n):
+    return [p for p in points if _coll(p) == coll and p["nranks"] == n]
+
+
+def _fit_range(pts, sizes):
     alpha = [-1.0] * 4
     beta = [0.0] * 4
     for pi, proto in enumerate(PROTOS):
-        pts = [p for p in points
-               if p["nranks"] == n and p["proto"] == proto and p["bytes"] in sizes]
-        if len(pts) >= 2:
-            alpha[pi], beta[pi] = fit_alpha_beta([p["bytes"] for p in pts],
-                                                 [p["us"] for p in pts])
+        q = [p for p in pts if p["proto"] == proto and p["bytes"] in sizes]
+        if len(q) >= 2:
+            alpha[pi], beta[pi] = fit_alpha_beta([p["bytes"] for p in q],
+                                                 [p["us"] for p in q])
     return alpha, beta
 
 
-def _fit_ranges(points, n, cuts):
+def _fit_ranges(pts, coll, n, cuts):
     """One entry per size range; cuts are the inclusive upper ends of all
     ranges but the last (which has no upper end)."""
-    sizes = sorted({p["bytes"] for p in points if p["nranks"] == n})
+    sizes = sorted({p["bytes"] for p in pts})
     entries, lo = [], -1
     for hi in list(cuts) + [None]:
         rng = {s for s in sizes if s > lo and (hi is None or s <= hi)}
-        alpha, beta = _fit_range(points, n, rng)
-        entries.append({"nranks": n, "max_bytes": 0 if hi is None else int(hi),
+        alpha, beta = _fit_range(pts, rng)
+        entries.append({"nranks": n, "collective": coll,
+                        "max_bytes": 0 if hi is None else int(hi),
                         "alpha_us": alpha, "beta_us_per_byte": beta})
         lo = hi if hi is not None else lo
     return entries
 
 
-def _score(points, n, entries):
-    """(max regret, sum of squared relative model errors) on the measured
-    points of rank count n."""
+def _score(pts, entries):
+    """(max protocol regret, sum of squared relative model errors) on the
+    measured points of one collective and rank count."""
     worst, sq = 1.0, 0.0
-    for s in sorted({p["bytes"] for p in points if p["nranks"] == n}):
-        meas = {p["proto"]: p["us"] for p in points if p["nranks"] == n and p["bytes"] == s}
+    for s in sorted({p["bytes"] for p in pts}):
+        meas = {p["proto"]: p["us"] for p in pts if p["bytes"] == s}
         e = _range_entry(entries, s)
         pick, _ = argmin_py(e, s)
         if pick >= 0 and PROTOS[pick] in meas:
@@ -99,33 +115,36 @@ def _score(points, n, entries):
 
 
 def fit_table(points, max_ranges=2):
-    """points: list of {nranks, proto, bytes, us}.  Returns table entries.
+    """points: list of {collective?, nranks, proto, bytes, us} (collective
+    defaults to the one-shot all-reduce).  Returns table entries.
 
-    Per rank count, one alpha-beta line per protocol over the whole sweep,
-    or, with max_ranges=2, two lines split at the measured size that gives
-    the lowest worst-case regret on the measured points (ties: one range,
-    then the smaller squared relative error).  Each range holds at least two
-    measured sizes."""
+    Per collective and rank count, one alpha-beta line per protocol over the
+    whole sweep, or, with max_ranges=2, two lines split at the measured size
+    that gives the lowest worst-case regret on the measured points (ties: one
+    range, then the smaller squared relative error).  Each range holds at
+    least two measured sizes."""
     entries = []
-    for n in sorted({p["nranks"] for p in points}):
-        sizes = sorted({p["bytes"] for p in points if p["nranks"] == n})
-        best = None
-        cands = [()]
-        if max_ranges >= 2:
-            cands += [(c,) for c in sizes[1:-2]]
-        for cuts in cands:
-            ent = _fit_ranges(points, n, cuts)
-            worst, sq = _score(points, n, ent)
-            key = (round(worst, 9), len(cuts), sq)
-            if best is None or key < best[0]:
-                best = (key, ent)
-        entries.extend(best[1])
+    for coll in COLLECTIVES:
+        for n in sorted({p["nranks"] for p in points if _coll(p) == coll}):
+            pts = _pts(points, coll, n)
+            sizes = sorted({p["bytes"] for p in pts})
+            best = None
+            cands = [()]
+            if max_ranges >= 2:
+                cands += [(c,) for c in sizes[1:-2]]
+            for cuts in cands:
+                ent = _fit_ranges(pts, coll, n, cuts)
+                worst, sq = _score(pts, ent)
+                key = (round(worst, 9), len(cuts), sq)
+                if best is None or key < best[0]:
+                    best = (key, ent)
+            entries.extend(best[1])
     return entries
 
 
 def _range_entry(entries, nbytes):
-    """The entry of one rank count whose size range holds nbytes (the same
-    rule as the library)."""
+    """The entry of one (collective, rank count) whose size range holds
+    nbytes (the same rule as the library)."""
     def upper(e):
         m = e.get("max_bytes", 0)
         return m if m > 0 else float("inf")
@@ -147,32 +166,70 @@ def argmin_py(entry, nbytes):
     return best, tbest
 
 
-def select_py(entries, nbytes, nranks):
-    """Plain-Python statement of the library's choice: nearest rank count
-    (ties: smaller), then the size range, then the argmin."""
-    ns = sorted({e["nranks"] for e in entries})
+def select_py(entries, nbytes, nranks, collective="allreduce"):
+    """Plain-Python statement of the library's choice within one collective:
+    nearest rank count (ties: smaller), then the size range, then the
+    argmin.  Returns (-1, 0.0) when the collective has no entries."""
+    mine = [e for e in entries if _coll(e) == collective]
+    if not mine:
+        return -1, 0.0
+    ns = sorted({e["nranks"] for e in mine})
     n_use = min(ns, key=lambda n: (abs(n - nranks), n))
-    return argmin_py(_range_entry([e for e in entries if e["nranks"] == n_use], nbytes),
+    return argmin_py(_range_entry([e for e in mine if e["nranks"] == n_use], nbytes),
                      nbytes)
 
 
+def select_allreduce_py(entries, nbytes, nranks):
+    """(collective, protocol id, predicted us): the one-shot choice unless the
+    two-shot one predicts strictly less."""
+    p1, t1 = select_py(entries, nbytes, nranks, "allreduce")
+    p2, t2 = select_py(entries, nbytes, nranks, "twoshot")
+    if p2 >= 0 and t2 < t1:
+        return "twoshot", p2, t2
+    return "allreduce", p1, t1
+
+
 def regret(points, entries):
-    """Measured time of the selected protocol over the best measured time."""
+    """Measured time of the library's choice over the best measured time.
+
+    kind "protocol": the protocol choice within each collective;
+    kind "allreduce": the algorithm-and-protocol choice of the all-reduce,
+    over the best one-shot or two-shot measurement at that point."""
     from . import abi
     table = abi.cost_table(entries)
     out = []
-    for n in sorted({p["nranks"] for p in points}):
-        for s in sorted({p["bytes"] for p in points if p["nranks"] == n}):
-            meas = {p["proto"]: p["us"] for p in points
-                    if p["nranks"] == n and p["bytes"] == s}
-            if len(meas) < 2:
-                continue
-            pick, _ = abi.ar_select_protocol(table, s, n)
-            chosen = meas.get(PROTOS[pick])
-            best = min(meas.values())
-            out.append({"nranks": n, "bytes": s, "pick": PROTOS[pick],
-                        "best": min(meas, key=meas.get),
-                        "regret": (chosen / best) if chosen else None})
+    for coll in COLLECTIVES:
+        if not any(_coll(e) == coll for e in entries):
+            continue
+        for n in sorted({p["nranks"] for p in points if _coll(p) == coll}):
+            for s in sorted({p["bytes"] for p in points if _coll(p) == coll and
+                             p["nranks"] == n}):
+                meas = {p["proto"]: p["us"] for p in points
+                        if _coll(p) == coll and p["nranks"] == n and p["bytes"] == s}
+                if len(meas) < 2:
+                    continue
+                pick, _ = abi.ar_select_collective(table, coll, s, n)
+                chosen = meas.get(PROTOS[pick])
+                out.append({"kind": "protocol", "collective": coll, "nranks": n,
+                            "bytes": s, "pick": PROTOS[pick],
+                            "best": min(meas, key=meas.get),
+                            "regret": (chosen / min(meas.values())) if chosen else None})
+    if any(_coll(e) == "twoshot" for e in entries):
+        for n in sorted({p["nranks"] for p in points if _coll(p) == "twoshot"}):
+            for s in sorted({p["bytes"] for p in points if _coll(p) == "twoshot" and
+                             p["nranks"] == n}):
+                meas = {(_coll(p), p["proto"]): p["us"] for p in points
+                        if _coll(p) in ("allreduce", "twoshot") and p["nranks"] == n and
+                        p["bytes"] == s}
+                if not any(k[0] == "allreduce" for k in meas):
+                    continue
+                cid, pick, _ = abi.ar_select_allreduce(table, s, n)
+                key = (COLLECTIVES[cid], PROTOS[pick])
+                chosen = meas.get(key)
+                best = min(meas, key=meas.get)
+                out.append({"kind": "allreduce", "nranks": n, "bytes": s,
+                            "pick": "/".join(key), "best": "/".join(best),
+                            "regret": (chosen / meas[best]) if chosen else None})
     return out
 
 
@@ -182,27 +239,37 @@ def load_table(path: str = TABLE_PATH):
 
 
 def select(nbytes: int, nranks: int, path: str = TABLE_PATH):
-    """Protocol name chosen by the library for a payload of nbytes per rank."""
+    """One-shot protocol chosen by the library for a payload of nbytes per rank."""
     from . import abi
     t = load_table(path)
     pick, pred = abi.ar_select_protocol(abi.cost_table(t["entries"]), nbytes, nranks)
     return PROTOS[pick], pred
 
 
+def select_allreduce(nbytes: int, nranks: int, path: str = TABLE_PATH):
+    """(algorithm, protocol, predicted us) chosen by the library."""
+    from . import abi
+    t = load_table(path)
+    cid, pick, pred = abi.ar_select_allreduce(abi.cost_table(t["entries"]), nbytes, nranks)
+    return COLLECTIVES[cid], PROTOS[pick], pred
+
+
 # ------------------------------------------------------------------ sweep --
 
 def measure_point(torch, abi, buffers, inputs, proto, nranks, nbytes, nops, reps,
-                  seed=1004):
+                  seed=1004, collective="allreduce"):
     count = nbytes // 2
     x = inputs.payload(seed + nbytes, (nops, nranks, count), "uniform")
-    ws = buffers.Workspace(nranks, count, proto, nranks)
+    ws = buffers.Workspace(nranks, count, proto, nranks, collective=collective)
     xd, stride = buffers.rows_to_device(x)
-    outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    ostride = ws.gather_stride() if collective == "allgather" else stride
+    outd = torch.zeros((nops * nranks, ostride), dtype=torch.int16, device="cuda")
     for _ in range(2):
-        ws.sim(nops, xd, stride, outd, stride, timeout_ns=2_000_000_000)
+        ws.sim(nops, xd, stride, outd, ostride, timeout_ns=2_000_000_000)
     torch.cuda.synchronize()
     if ws.status() != 0:
-        raise RuntimeError(f"{proto} N={nranks} S={nbytes}: {abi.status_string(ws.status())}")
+        raise RuntimeError(f"{collective} {proto} N={nranks} S={nbytes}: "
+                           f"{abi.status_string(ws.status())}")
     st = torch.cuda.current_stream()
     ms = []
     for _ in range(reps):
@@ -210,7 +277,7 @@ def measure_point(torch, abi, buffers, inputs, proto, nranks, nbytes, nops, reps
         b = torch.cuda.Event(enable_timing=True)
         if proto == "barrier":
             ws.reset_ctrl()
-        p = ws.sim_params(nops, xd, stride, outd, stride, timeout_ns=2_000_000_000)
+        p = ws.sim_params(nops, xd, stride, outd, ostride, timeout_ns=2_000_000_000)
         a.record(st)
         abi.ar_sim_run(p, st)
         b.record(st)
@@ -218,26 +285,34 @@ def measure_point(torch, abi, buffers, inputs, proto, nranks, nbytes, nops, reps
         torch.cuda.synchronize()
         ms.append(a.elapsed_time(b))
     if ws.status() != 0:
-        raise RuntimeError(f"{proto} N={nranks} S={nbytes}: {abi.status_string(ws.status())}")
+        raise RuntimeError(f"{collective} {proto} N={nranks} S={nbytes}: "
+                           f"{abi.status_string(ws.status())}")
     return statistics.median(ms) * 1e3 / nops
 
 
-def sweep(ranks=(4, 8, 16), sizes=SIZES, protos=PROTOS, reps=7):
+def sweep(ranks=(4, 8, 16), sizes=SIZES, protos=PROTOS, reps=7, collectives=COLLECTIVES):
     import torch
     from . import abi, buffers, inputs
     torch.cuda.set_device(0)
     points = []
-    for n in ranks:
-        for s in sizes:
-            # system-mode receive buffers must stay below 4 GiB in total
-            E_max = 2 * s
-            if n * 2 * n * E_max >= (1 << 32):
-                continue
-            nops = 64 if s <= (256 << 10) else 16
-            for proto in protos:
-                us = measure_point(torch, abi, buffers, inputs, proto, n, s, nops, reps)
-                points.append({"nranks": n, "proto": proto, "bytes": s, "us": round(us, 4)})
-                print(json.dumps(points[-1]), flush=True)
+    for coll in collectives:
+        for n in ranks:
+            for s in sizes:
+                if coll == "allgather" and s > GATHER_MAX:
+                    continue
+                # system-mode receive buffers must stay below 4 GiB in total
+                E_max = 2 * s
+                if n * 2 * n * E_max >= (1 << 32):
+                    continue
+                nops = 64 if s <= (256 << 10) else 16
+                for proto in protos:
+                    if coll != "allreduce" and proto == "barrier":
+                        continue
+                    us = measure_point(torch, abi, buffers, inputs, proto, n, s, nops, reps,
+                                       collective=coll)
+                    points.append({"collective": coll, "nranks": n, "proto": proto,
+                                   "bytes": s, "us": round(us, 4)})
+                    print(json.dumps(points[-1]), flush=True)
     return points
 
 
@@ -263,21 +338,29 @@ def main() -> int:
     entries = fit_table(points)
     reg = regret(points, entries)
     worst = max(r["regret"] for r in reg if r["regret"])
+    worst_by = {}
+    for r in reg:
+        k = r["kind"] if r["kind"] == "allreduce" else f"protocol/{r['collective']}"
+        if r["regret"]:
+            worst_by[k] = max(worst_by.get(k, 1.0), r["regret"])
     table = {
         "model": "T_p(S) = alpha_us[p] + beta_us_per_byte[p] * S for S <= max_bytes "
-                 "(0: no upper end); S = payload bytes per rank",
+                 "(0: no upper end), per collective and rank count; "
+                 "S = payload bytes per rank",
         "protocols": list(PROTOS),
+        "collectives": list(COLLECTIVES),
         "measured_with": measured_with,
         "entries": entries,
         "points": points,
         "regret": reg,
         "max_regret": worst,
+        "max_regret_by_kind": worst_by,
         "sweep_seconds": (old.get("sweep_seconds") if old
                           else round(time.time() - t0, 1)),
     }
     with open(args.out, "w") as fh:
         json.dump(table, fh, indent=1)
-    print(json.dumps({"max_regret": worst, "entries": entries}), flush=True)
+    print(json.dumps({"max_regret": worst, "by_kind": worst_by}), flush=True)
     return 0
 
 

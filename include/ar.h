@@ -420,10 +420,14 @@ int ar_wallclock_hz(double* hz);
  * chosen id and, if non-NULL, its predicted time.  AR_EINVAL for a NULL
  * table or proto_out, nentries < 1, S < 0, nranks outside 1..16, or no
  * available protocol in the chosen entry.
+ *
+ * Each entry models one collective (ar_collective): the one-shot all-reduce
+ * (0), the all-gather or the two-shot all-reduce.  ar_select_protocol uses
+ * the one-shot entries only.
  */
 typedef struct {
     int32_t nranks;
-    int32_t reserved;           /* 0 */
+    int32_t collective;         /* ar_collective the entry models */
     int64_t max_bytes;          /* inclusive upper end of the range; <= 0: none */
     double alpha_us[4];
     double beta_us_per_byte[4];
@@ -432,6 +436,25 @@ typedef struct {
 int ar_select_protocol(const ar_cost_entry* table, int32_t nentries,
                        int64_t payload_bytes, int32_t nranks,
                        int32_t* proto_out, double* predicted_us);
+
+/* The same choice among the entries of one collective; AR_EINVAL when the
+ * table has none for it. */
+int ar_select_collective(const ar_cost_entry* table, int32_t nentries,
+                         int32_t collective, int64_t payload_bytes, int32_t nranks,
+                         int32_t* proto_out, double* predicted_us);
+
+/*
+ * All-reduce algorithm and protocol: the one-shot choice and the two-shot
+ * choice are each made as above from their own entries, and the one with the
+ * lower predicted time wins (ties: one-shot; no two-shot entries: one-shot).
+ * The pages' reason for both forms ("SiFAR", abstract): one-shot scales
+ * poorly with the number of GPUs, two-shot does better at higher degrees.
+ * Writes AR_ALLREDUCE or AR_TWOSHOT and the protocol.
+ */
+int ar_select_allreduce(const ar_cost_entry* table, int32_t nentries,
+                        int64_t payload_bytes, int32_t nranks,
+                        int32_t* collective_out, int32_t* proto_out,
+                        double* predicted_us);
 
 /* -------------------------------------------------------- floor probes --- */
 /*

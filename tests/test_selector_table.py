@@ -116,3 +116,73 @@ def test_fit_finds_regime_change():
     assert sorted(e["max_bytes"] for e in two) == [0, 16384]
     assert max(r["regret"] for r in selector.regret(pts, one)) > 1.05
     assert max(r["regret"] for r in selector.regret(pts, two)) == pytest.approx(1.0)
+
+
+def _random_entries(rng, colls=("allreduce", "twoshot", "allgather")):
+    entries = []
+    for coll in colls:
+        for n in (4, 8, 16):
+            cuts = sorted(rng.choice([2 ** k for k in range(10, 22)], size=1, replace=False))
+            for hi in list(cuts) + [0]:
+                a = list(rng.uniform(1, 6, 4))
+                if coll != "allreduce":
+                    a[3] = -1.0                      # no barrier form
+                entries.append({"nranks": n, "collective": coll, "max_bytes": int(hi),
+                                "alpha_us": a,
+                                "beta_us_per_byte": list(rng.uniform(5e-5, 3e-4, 4))})
+    rng.shuffle(entries)
+    return entries
+
+
+def test_library_collective_and_algorithm_choice_match_python():
+    rng = np.random.default_rng(21)
+    entries = _random_entries(rng)
+    table = abi.cost_table(entries)
+    for n in (1, 4, 6, 8, 12, 16):
+        for s in [0, 3000, 70000] + [2 ** k for k in range(8, 24)]:
+            for coll in ("allreduce", "twoshot", "allgather"):
+                pick, pred = abi.ar_select_collective(table, coll, s, n)
+                ref, tref = selector.select_py(entries, s, n, coll)
+                assert pick == ref and pred == pytest.approx(tref), (coll, n, s)
+            cid, pick, pred = abi.ar_select_allreduce(table, s, n)
+            rc, rp, rt = selector.select_allreduce_py(entries, s, n)
+            assert (selector.COLLECTIVES[cid], pick) == (rc, rp) and pred == pytest.approx(rt)
+    # one-shot entries only drive ar_select_protocol
+    for n in (4, 8):
+        for s in (2048, 1 << 20):
+            assert abi.ar_select_protocol(table, s, n)[0] == selector.select_py(entries, s, n)[0]
+
+
+def test_selection_without_entries_for_a_collective():
+    rng = np.random.default_rng(22)
+    one = _random_entries(rng, colls=("allreduce",))
+    table = abi.cost_table(one)
+    with pytest.raises(abi.ArError):
+        abi.ar_select_collective(table, "twoshot", 4096, 8)
+    cid, pick, _ = abi.ar_select_allreduce(table, 4096, 8)      # no two-shot: one-shot
+    assert cid == abi.AR_ALLREDUCE
+    only_two = _random_entries(rng, colls=("twoshot",))
+    with pytest.raises(abi.ArError):                             # needs one-shot entries
+        abi.ar_select_allreduce(abi.cost_table(only_two), 4096, 8)
+
+
+def test_fit_chooses_two_shot_past_the_crossover():
+    """One-shot: low latency, steep per-byte cost; two-shot: one more
+    exchange, N/2 times fewer bytes.  The fitted table picks one-shot below
+    the crossover and two-shot above it, with no regret."""
+    pts = []
+    for s in selector.SIZES:
+        for proto, k in (("ll", 1.0), ("ll128", 1.3), ("sentinel", 1.1)):
+            pts.append({"collective": "allreduce", "nranks": 16, "proto": proto,
+                        "bytes": s, "us": k * (2.0 + 8e-4 * s)})
+            pts.append({"collective": "twoshot", "nranks": 16, "proto": proto,
+                        "bytes": s, "us": k * (4.0 + 1e-4 * s)})
+        pts.append({"collective": "allreduce", "nranks": 16, "proto": "barrier",
+                    "bytes": s, "us": 9.0 + 9e-4 * s})
+    entries = selector.fit_table(pts)
+    reg = selector.regret(pts, entries)
+    assert {r["kind"] for r in reg} == {"protocol", "allreduce"}
+    assert max(r["regret"] for r in reg) == pytest.approx(1.0)
+    table = abi.cost_table(entries)
+    assert abi.ar_select_allreduce(table, 2048, 16)[:2] == (abi.AR_ALLREDUCE, abi.AR_LL)
+    assert abi.ar_select_allreduce(table, 1 << 20, 16)[:2] == (abi.AR_TWOSHOT, abi.AR_LL)
