@@ -485,61 +485,284 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
   }
 }
 
-// ================================================================ host side
-
+// Poll tile `tile` of the all-gather slots of every source but `skip`, each
+// holding the reduced share of its source (so each source has its own
+// encoded length), in whatever order they arrive; validate from the
+// evidence and re-arm (SENTINEL).  LL128 first probes every source's last
+// line flag (lane r watches source r), then reads after an acquire, as
+// poll_tile does.  Returns 0, kEtimeout or kEcorrupt; chunks end in v.
 template <int P, int NMAX>
-static const void* sim_fn(int collective) {
-  return collective == AR_ALLGATHER ? reinterpret_cast<const void*>(&k_sim_gather<P, NMAX>)
-                                    : reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX>);
+__device__ __forceinline__ int poll_shares(rsrc_t rs, uint32_t src0, uint32_t slot_bytes,
+                                           int nranks, int skip, int tile, int64_t count,
+                                           int64_t width, uint32_t seq, uint32_t stale,
+                                           int* ctrl, uint64_t timeout_ticks, int lane,
+                                           u32x4 (&v)[NMAX]) {
+  const uint32_t tile0 = (uint32_t)tile * kTileBytes;
+  const uint32_t loff = tile0 + (uint32_t)lane * 16u;
+  uint32_t pending = 0u;                           // wave-uniform
+  uint32_t E[NMAX];
+#pragma unroll
+  for (int r = 0; r < NMAX; ++r) {
+    v[r] = u32x4{0u, 0u, 0u, 0u};
+    int64_t lo, m;
+    share_of(count, width, r, lo, m);
+    E[r] = enc_bytes<P>(m);
+    if (r < nranks && r != skip && tile0 < E[r]) pending |= 1u << r;
+  }
+  if (pending == 0u) return 0;
+  Waiter wt(timeout_ticks, ctrl);
+  if (P == kLL128) {
+    int64_t lo, m;
+    share_of(count, width, lane, lo, m);
+    const uint32_t El = enc_bytes<P>(m);
+    const uint32_t tile_end = (tile0 + kTileBytes < El) ? tile0 + kTileBytes : El;
+    uint32_t waiting = pending;
+    while (true) {
+      const bool mine = lane < nranks && ((waiting >> lane) & 1u);
+      bool ok = true, bad = false;
+      if (mine) {
+        const u32x2 f = ld8(rs, src0 + (uint32_t)lane * slot_bytes + tile_end - 8u);
+        ok = (f.x == seq) && (f.y == 0u);
+        bad = !ok && !(f.y == 0u && (f.x == 0u || f.x == stale));
+      }
+      if (__ballot(bad) != 0ull) {
+        if (lane == 0) report_error(ctrl, kEcorrupt);
+        return kEcorrupt;
+      }
+      waiting &= ~(uint32_t)__ballot(mine && ok);
+      if (waiting == 0u) break;
+      if (!wt.again(lane)) return kEtimeout;
+    }
+    fence_acquire();
+  }
+  while (true) {
+#pragma unroll
+    for (int r = 0; r < NMAX; ++r)
+      if (((pending >> r) & 1u) && loff < E[r]) v[r] = ld16(rs, src0 + r * slot_bytes + loff);
+    uint32_t fresh = 0u;
+    bool corrupt = false;
+#pragma unroll
+    for (int r = 0; r < NMAX; ++r) {
+      if ((pending >> r) & 1u) {
+        bool ok = true, bad = false;
+        if (loff < E[r]) {
+          if (P == kLL128) {
+            if ((lane & 7) == 7) {
+              ok = (v[r].z == seq) && (v[r].w == 0u);
+              bad = !ok && !(v[r].w == 0u && (v[r].z == 0u || v[r].z == stale));
+            }
+          } else {
+            classify<P>(v[r], seq, stale, ok, bad);
+          }
+        }
+        if (__ballot(bad) != 0ull) corrupt = true;
+        if (__ballot(!ok) == 0ull) fresh |= 1u << r;
+      }
+    }
+    if (corrupt) {
+      if (lane == 0) report_error(ctrl, kEcorrupt);
+      return kEcorrupt;
+    }
+    if (P == kSentinel && fresh != 0u) {
+      const u32x4 armed = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r)
+        if (((fresh >> r) & 1u) && loff < E[r]) st16(rs, src0 + r * slot_bytes + loff, armed);
+    }
+    pending &= ~fresh;
+    if (pending == 0u) break;
+    if (!wt.again(lane)) return kEtimeout;
+  }
+  return 0;
 }
 
-template <int P>
-static const void* sim_fn_n(int collective, int nranks) {
-  if (nranks <= 4) return sim_fn<P, 4>(collective);
-  if (nranks <= 8) return sim_fn<P, 8>(collective);
-  return sim_fn<P, 16>(collective);
-}
-
-static const void* coll_sim_fn(int proto, int collective, int nranks) {
-  switch (proto) {
-    case kLL: return sim_fn_n<kLL>(collective, nranks);
-    case kLL128: return sim_fn_n<kLL128>(collective, nranks);
-    default: return sim_fn_n<kSentinel>(collective, nranks);
+// Two-shot simulator for larger shares: one wave per (rank g, share tile
+// group), no workgroup barrier.  Per op and tile t the wave
+//  1. sends tile t of each share w of rank g's payload to rank w;
+//  2. polls tile t of share g from every other rank at once (its own share-g
+//     chunk stays in registers), reduces in rank order and writes the
+//     reduced tile to rank g's output;
+//  3. sends the reduced tile to every other rank's all-gather slot g;
+//  4. polls tile t of every other rank's reduced share at once and decodes
+//     each into rank g's output.
+// A wave talks only to the waves of the same tile group of the other ranks,
+// so the dual-buffer licences of the wide two-shot kernel hold pairwise:
+// every send is preceded by a wait for the wave's own earlier stores (the
+// sentinel re-arms among them).
+template <int P, int NMAX>
+__global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
+  const int lane = threadIdx.x;
+  int g, tg;
+  if (!sim_place(a, g, tg)) return;
+  const int G = a.W;
+  const int mine = (a.T - 1 - tg) / G + 1;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t N = (uint32_t)a.nranks;
+  const int tstride = 2 * a.nranks;
+  int64_t lo_g, m_g;
+  share_of(a.count, a.width, g, lo_g, m_g);
+  const uint32_t E_g = enc_bytes<P>(m_g);
+  const uint32_t rb_g = (uint32_t)((m_g * 2 + 15) & ~int64_t(15));
+  if (a.trace && lane == 0 && tg == 0)
+    __hip_atomic_fetch_min(reinterpret_cast<unsigned long long*>(a.trace) +
+                               (int64_t)a.nops * tstride,
+                           (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t seq = a.seq0;
+  uint32_t par = a.parity0;
+  for (int op = 0; op < a.nops; ++op) {
+    const uint32_t stale = seq_prev(seq_prev(seq));
+    const uint16_t* row = a.in + ((int64_t)op * a.nranks + g) * a.in_stride;
+    uint16_t* orow = a.out + ((int64_t)op * a.nranks + g) * a.out_stride;
+    const uint32_t rs_src = (((uint32_t)g * 2u + par) * N) * a.slot_bytes;   // slot 0 of g
+    const uint32_t ag_src = a.ag0 + rs_src;
+    sim_delay(a, op, g);
+    for (int k = 0; k < mine; ++k) {
+      const int tile = tg + k * G;
+      const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+      // ---- 1. reduce-scatter sends ----
+      if (P == kSentinel) fence_release();
+      for (int w = 0; w < a.nranks; ++w) {
+        if (w == g) continue;
+        int64_t lo_w, m_w;
+        share_of(a.count, a.width, w, lo_w, m_w);
+        const uint32_t dst = (((uint32_t)w * 2u + par) * N + (uint32_t)g) * a.slot_bytes;
+        produce_data<P>(rs, dst, 0u, 1, -1, row + lo_w,
+                        (uint32_t)((m_w * 2 + 15) & ~int64_t(15)), m_w, tile,
+                        enc_bytes<P>(m_w), seq, lane);
+      }
+      if (P == kLL128) {
+        fence_release();
+        for (int w = 0; w < a.nranks; ++w) {
+          if (w == g) continue;
+          int64_t lo_w, m_w;
+          share_of(a.count, a.width, w, lo_w, m_w);
+          produce_flags(rs, (((uint32_t)w * 2u + par) * N + (uint32_t)g) * a.slot_bytes, 0u, 1,
+                        -1, tile, enc_bytes<P>(m_w), seq, lane);
+        }
+      }
+      if (a.trace && k == mine - 1) {
+        fence_release();
+        if (lane == 0) trace_max(a, (int64_t)op * tstride + g);
+      }
+      // ---- 2.-3. share g: receive, reduce, all-gather send ----
+      if ((uint32_t)tile * kTileBytes < E_g) {
+        u32x4 v[NMAX];
+        const u32x4 own_v = encode_chunk<P>(row + lo_g, rb_g, m_g, tile, lane, seq);
+        if (poll_tile<P, NMAX>(rs, rs_src, a.slot_bytes, a.nranks, tile, E_g, seq, stale, true,
+                               g, own_v, a.ctrl, a.timeout_ticks, lane, v) != 0)
+          return;
+        uint32_t o[4];
+        reduce_words<P, NMAX>(v, a.nranks, o);
+        mask_words(o, chunk_keep<P>(m_g, tile, lane));
+        int64_t first;
+        int n;
+        lane_elems<P>(tile, lane, first, n);
+        if (loff < E_g) store_elems(orow + lo_g, m_g, first, n, o);
+        const u32x4 enc = encode_words<P>(o, lane, seq);
+        if (P == kSentinel) fence_release();
+        store_chunk<P>(rs, a.ag0 + (par * N + (uint32_t)g) * a.slot_bytes,
+                       2u * N * a.slot_bytes, a.nranks, g, tile, E_g, lane, enc);
+        if (P == kLL128) {
+          fence_release();
+          produce_flags(rs, a.ag0 + (par * N + (uint32_t)g) * a.slot_bytes,
+                        2u * N * a.slot_bytes, a.nranks, g, tile, E_g, seq, lane);
+        }
+      }
+      // ---- 4. all-gather receive ----
+      {
+        u32x4 v[NMAX];
+        if (poll_shares<P, NMAX>(rs, ag_src, a.slot_bytes, a.nranks, g, tile, a.count,
+                                 a.width, seq, stale, a.ctrl, a.timeout_ticks, lane, v) != 0)
+          return;
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r) {
+          if (r >= a.nranks || r == g) continue;
+          int64_t lo_r, m_r;
+          share_of(a.count, a.width, r, lo_r, m_r);
+          store_chunk_elems<P>(orow + lo_r, m_r, tile, enc_bytes<P>(m_r), lane, v[r]);
+        }
+      }
+    }
+    if (a.trace && lane == 0 && tg == 0) trace_max(a, (int64_t)op * tstride + a.nranks + g);
+    seq = seq_next(seq);
+    par ^= 1u;
   }
 }
 
+// ================================================================ host side
+
+template <int P, int NMAX>
+static const void* sim_fn(int collective, bool narrow) {
+  if (collective == AR_ALLGATHER) return reinterpret_cast<const void*>(&k_sim_gather<P, NMAX>);
+  return narrow ? reinterpret_cast<const void*>(&k_sim_twoshot_narrow<P, NMAX>)
+                : reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX>);
+}
+
+template <int P>
+static const void* sim_fn_n(int collective, int nranks, bool narrow) {
+  if (nranks <= 4) return sim_fn<P, 4>(collective, narrow);
+  if (nranks <= 8) return sim_fn<P, 8>(collective, narrow);
+  return sim_fn<P, 16>(collective, narrow);
+}
+
+static const void* coll_sim_fn(int proto, int collective, int nranks, bool narrow) {
+  switch (proto) {
+    case kLL: return sim_fn_n<kLL>(collective, nranks, narrow);
+    case kLL128: return sim_fn_n<kLL128>(collective, nranks, narrow);
+    default: return sim_fn_n<kSentinel>(collective, nranks, narrow);
+  }
+}
+
+// Measured on MI355X (4, 8 and 16 ranks, 4 KiB .. 4 MiB per rank): the
+// workgroup kernel wins while each workgroup walks at most two share tiles
+// (the one-wave kernel serializes its N-1 sends and polls: 2-4x slower at
+// small shares); from three tiles on, the one-wave kernel's wider grid wins
+// by up to 1.6x (8 ranks, 1 MiB: 22.1 -> 13.9 us per op, LL).
+static constexpr int kTwoShotWideMaxTiles = 2;
+
 struct CollGeom {
   int32_t W, Q, T, TPW, blocks;
+  bool narrow;                 // two-shot: one wave per tile group
 };
 
 static int coll_check(const ar_sim_params* p) {
   const ar_desc* d = &p->desc;
   if (d->nconsumers != d->nranks) return AR_EINVAL;
   if (d->proto == kBarrier) return AR_EINVAL;
-  if (p->flags != 0 || p->tile_order) return AR_EINVAL;
+  if (p->tile_order) return AR_EINVAL;
+  const int kernel_flags = AR_SIM_NARROW | AR_SIM_WIDE;
+  if (p->flags & ~kernel_flags) return AR_EINVAL;
+  if ((p->flags & kernel_flags) &&
+      (d->collective != AR_TWOSHOT || (p->flags & kernel_flags) == kernel_flags))
+    return AR_EINVAL;
   return AR_OK;
 }
 
 // Tiles of one rank's transfer: the whole payload (all-gather) or one full
 // share (two-shot).  Grid: the all-reduce simulator's rule (half of the
 // occupancy query's residency, tile groups in multiples of 8 per rank).
-static int coll_geometry(const ar_sim_params* p, const DeviceInfo& di, CollGeom* g) {
+static int coll_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool narrow,
+                            CollGeom* g) {
   const ar_desc* d = &p->desc;
   const int64_t n_el =
       d->collective == AR_TWOSHOT ? share_width(d->count, d->nranks) : d->count;
   const int64_t T = ceil_div64(encoded_bytes(d->proto, n_el), kTileBytes);
   if (T <= 0) {
-    *g = CollGeom{0, 0, 0, 0, 0};
+    *g = CollGeom{0, 0, 0, 0, 0, narrow};
     return AR_OK;
   }
   if (T > (int64_t(1) << 24)) return AR_ESIZE;
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &occ, coll_sim_fn(d->proto, d->collective, d->nranks), kWave * d->nranks, 0) !=
-          hipSuccess ||
+          &occ, coll_sim_fn(d->proto, d->collective, d->nranks, narrow),
+          narrow ? kWave : kWave * d->nranks, 0) != hipSuccess ||
       occ <= 0)
     return AR_ELAUNCH;
-  const int64_t capacity = (int64_t)occ * di.cus / 2;
+  // whole grid resident: half the occupancy query's figure, and one-wave
+  // workgroups at most 8 per CU (as for the all-reduce simulator)
+  int64_t capacity = (int64_t)occ * di.cus / 2;
+  if (narrow && capacity > 8 * (int64_t)di.cus) capacity = 8 * (int64_t)di.cus;
   const int64_t qmax = capacity / (8 * (int64_t)d->nranks);
   if (qmax < 1) return AR_ECAPACITY;
   int64_t Q;
@@ -556,11 +779,24 @@ static int coll_geometry(const ar_sim_params* p, const DeviceInfo& di, CollGeom*
   g->T = (int32_t)T;
   g->TPW = (int32_t)ceil_div64(T, 8 * Q);
   g->blocks = (int32_t)(8 * Q * d->nranks);
+  g->narrow = narrow;
   return AR_OK;
 }
 
+// Two-shot kernel choice: a workgroup of one wave per peer while each
+// workgroup owns one share tile, else (or with AR_SIM_NARROW) one wave per
+// share tile group; AR_SIM_WIDE forces the former.
+static int coll_geometry(const ar_sim_params* p, const DeviceInfo& di, CollGeom* g) {
+  if (p->desc.collective != AR_TWOSHOT) return coll_geometry_as(p, di, false, g);
+  if (p->flags & AR_SIM_NARROW) return coll_geometry_as(p, di, true, g);
+  const int rc = coll_geometry_as(p, di, false, g);
+  if (p->flags & AR_SIM_WIDE) return rc;
+  if (rc == AR_OK && g->TPW <= kTwoShotWideMaxTiles) return AR_OK;
+  return coll_geometry_as(p, di, true, g);
+}
+
 int coll_sim_geometry(const ar_sim_params* p, int32_t* groups, int32_t* tiles,
-                      int32_t* tiles_per_group, int32_t* blocks) {
+                      int32_t* tiles_per_group, int32_t* blocks, int32_t* wide) {
   int rc = coll_check(p);
   if (rc) return rc;
   DeviceInfo di;
@@ -573,6 +809,7 @@ int coll_sim_geometry(const ar_sim_params* p, int32_t* groups, int32_t* tiles,
   if (tiles) *tiles = g.T;
   if (tiles_per_group) *tiles_per_group = g.TPW;
   if (blocks) *blocks = g.blocks;
+  if (wide) *wide = g.narrow ? 0 : 1;
   return AR_OK;
 }
 
@@ -616,8 +853,9 @@ int coll_sim_run(const ar_sim_params* p, hipStream_t s) {
   a.delay = p->delay_ticks;
   a.trace = p->trace;
   void* args[] = {&a};
-  return map_hip(hipLaunchKernel(coll_sim_fn(d->proto, d->collective, d->nranks),
-                                 dim3(g.blocks), dim3(kWave * d->nranks), args, 0, s));
+  return map_hip(hipLaunchKernel(coll_sim_fn(d->proto, d->collective, d->nranks, g.narrow),
+                                 dim3(g.blocks), dim3(g.narrow ? kWave : kWave * d->nranks),
+                                 args, 0, s));
 }
 
 // ----------------------------------------------------- stream-ordered host

@@ -167,7 +167,7 @@ int twoshot_reduce(const ar_desc* d, void* scratch, void* out, int64_t out_strid
                    ar_epoch e, void* ctrl, uint64_t timeout_ns, int32_t flags,
                    hipStream_t s);
 int coll_sim_geometry(const ar_sim_params* p, int32_t* groups, int32_t* tiles,
-                      int32_t* tiles_per_group, int32_t* blocks);
+                      int32_t* tiles_per_group, int32_t* blocks, int32_t* wide);
 int coll_sim_run(const ar_sim_params* p, hipStream_t s);
 
 }  // namespace ar

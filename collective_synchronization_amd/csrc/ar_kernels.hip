@@ -1145,10 +1145,9 @@ int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
   if (!p) return AR_EINVAL;
   int rc = check_desc(&p->desc);
   if (rc) return rc;
-  if (p->desc.collective != AR_ALLREDUCE) {
-    if (wide) *wide = 1;
-    return coll_sim_geometry(p, waves_per_rank, tiles_per_rank, tiles_per_wave, blocks);
-  }
+  if (p->desc.collective != AR_ALLREDUCE)
+    return coll_sim_geometry(p, waves_per_rank, tiles_per_rank, tiles_per_wave, blocks,
+                             wide);
   DeviceInfo di;
   rc = device_info(&di);
   if (rc) return rc;

@@ -253,8 +253,10 @@ def test_collective_sim_argument_checks():
     assert run(g8, flags=abi.AR_SIM_NARROW) == abi.AR_EINVAL
     assert run(g8, tile_order=FAKE) == abi.AR_EINVAL
     assert run(g8, out_stride=4096) == abi.AR_EINVAL          # needs 8 rows of 4096
+    assert run(g8, flags=abi.AR_SIM_WIDE) == abi.AR_EINVAL      # kernel flags: two-shot only
     t8 = abi.make_desc(8, 4096, "sentinel", 8, "twoshot")
-    assert run(t8, flags=abi.AR_SIM_WIDE) == abi.AR_EINVAL
+    assert run(t8, flags=abi.AR_SIM_WIDE | abi.AR_SIM_NARROW) == abi.AR_EINVAL
+    assert run(t8, flags=abi.AR_SIM_COOPERATIVE) == abi.AR_EINVAL
 
 
 def test_epilogue_argument_checks():

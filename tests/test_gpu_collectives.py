@@ -121,21 +121,26 @@ def test_twoshot_missing_producer_times_out():
 
 
 SIM_CASES = [(8, 4096, 8), (4, 8192, 6), (16, 32768, 3), (3, 1000, 5), (2, 60, 7),
-             (1, 100, 3), (16, 100, 4), (8, 131072, 2)]
+             (1, 100, 3), (16, 100, 4), (8, 131072, 2), (16, 262144 + 13, 2)]
 
 
+@pytest.mark.parametrize("kernel", ["auto", "narrow", "wide"])
 @pytest.mark.parametrize("proto", PROTOS)
 @pytest.mark.parametrize("nranks,count,nops", SIM_CASES)
-def test_sim_twoshot(proto, nranks, count, nops):
-    print(f"[sim-twoshot] {proto} N={nranks} count={count} ops={nops}", flush=True)
+def test_sim_twoshot(proto, nranks, count, nops, kernel):
+    print(f"[sim-twoshot] {kernel} {proto} N={nranks} count={count} ops={nops}", flush=True)
+    flags = {"auto": 0, "narrow": abi.AR_SIM_NARROW, "wide": abi.AR_SIM_WIDE}[kernel]
     ws = buffers.Workspace(nranks, count, proto, nranks, collective="twoshot")
     x = _x(3 * count + nops + nranks, (nops, nranks, count))
     xd, stride = buffers.rows_to_device(x)
     outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
     seq0 = ws.epoch.seq
     want = oracle.twoshot_ops(x, proto, seq0)
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride, flags=flags))
+    if kernel != "auto":
+        assert geo["kernel"] == kernel
     for run in range(2):                                 # the epoch carries over
-        ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS)
+        ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS, flags=flags)
         torch.cuda.synchronize()
         assert ws.status() == 0, abi.status_string(ws.status())
         got = buffers.rows_from_device(outd, count, (nops, nranks))
