@@ -174,6 +174,65 @@ def measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, war
     return dict(launch_ms=launch_ms, wall=wall, geo=geo, nconsumers=nconsumers)
 
 
+def measure_placement(torch, abi, blocks, threads):
+    """Where the workgroups of the timed grid ran: the XCC_ID of each,
+    against round-robin dispatch (workgroup b on XCD (s + b) mod 8, s the
+    XCD of workgroup 0), which the simulators' placement relies on."""
+    import numpy as np
+    work = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    res = torch.full((blocks,), -2, dtype=torch.int32, device="cuda")
+    abi.ar_probe_placement(blocks, threads, work, res)
+    torch.cuda.synchronize()
+    x = res.cpu().numpy()
+    props = torch.cuda.get_device_properties(0)
+    return {"blocks": blocks, "threads": threads,
+            "round_robin_start": int(x[0]),
+            "on_expected_xcd": round(float(np.mean(x == (x[0] + np.arange(blocks)) % 8)), 4),
+            "xcds_seen": int(len(set(x[x >= 0].tolist()))),
+            "cus": int(props.multi_processor_count)}
+
+
+def measure_skew(torch, abi, buffers, inputs, x, proto, nranks, count, nops, steps,
+                 warmup, skew_us, seed, collective):
+    """Ops with a seeded producer delay U[0, skew_us) per (op, producer) and
+    the wall-clock trace: per-op time and the post-arrival latency (op done
+    at the last consumer minus the last producer's last store).  The trace
+    makes every sender wait for its stores before its timestamp, so these
+    runs are slower than the untraced ones."""
+    import numpy as np
+    xd, stride = buffers.rows_to_device(x)
+    ws = buffers.Workspace(nranks, count, proto, nranks, collective=collective)
+    ostride = ws.gather_stride() if collective == "allgather" else stride
+    outd = torch.zeros((nops * nranks, ostride), dtype=torch.int16, device="cuda")
+    hz = abi.ar_wallclock_hz()
+    d_us = inputs.delays_us(seed + 1, nops, nranks, skew_us)
+    ticks = torch.from_numpy(np.round(d_us * hz * 1e-6).astype(np.int32)).to("cuda")
+    trace = torch.zeros(nops * 2 * nranks + 1, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    post, per_op = [], []
+    for k in range(warmup + steps):
+        trace.zero_()
+        trace[-1] = -1
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        ws.sim(nops, xd, stride, outd, ostride, timeout_ns=2_000_000_000,
+               delay_ticks=ticks, trace=trace)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if ws.status() != 0:
+            raise RuntimeError(f"device status {abi.status_string(ws.status())}")
+        if k < warmup:
+            continue
+        t = trace.cpu().numpy()[:-1].reshape(nops, 2, nranks).astype(np.float64)
+        post.extend(((t[:, 1, :].max(axis=1) - t[:, 0, :].max(axis=1)) / hz * 1e6).tolist())
+        per_op.append(a.elapsed_time(b) * 1e3 / nops)
+    return {"skew_us": skew_us, "mean_delay_us": round(float(d_us.mean()), 3),
+            "us_per_op": round(statistics.median(per_op), 3),
+            "post_arrival_us_median": round(float(np.median(post)), 3),
+            "post_arrival_us_p90": round(float(np.percentile(post, 90)), 3)}
+
+
 def measure_epilogue(torch, abi, buffers, x, proto, nranks, count, steps, warmup):
     """Stream-ordered ops whose producer is a per-rank scale, two ways:
     fused (ar_scale_pack sends from the producer's epilogue) and unfused
@@ -238,10 +297,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--proto", default="sentinel",
-                    choices=["ll", "ll128", "sentinel", "barrier"])
+                    choices=["ll", "ll128", "sentinel", "barrier", "auto"],
+                    help="auto: the protocol the committed cost table chooses")
     ap.add_argument("--mode", default="system", choices=["share", "system"])
     ap.add_argument("--collective", default="allreduce",
-                    choices=["allreduce", "allgather", "twoshot"],
+                    choices=["allreduce", "allgather", "twoshot", "auto"],
                     help="one-shot all-reduce (default), standalone all-gather or "
                          "two-shot all-reduce (the last two: system mode)")
     ap.add_argument("--nranks", type=int, default=8)
@@ -254,6 +314,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-floor", action="store_true")
     ap.add_argument("--no-share", action="store_true")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="input seed (default: that of the 8-rank [1,4096] workload)")
+    ap.add_argument("--skew-us", type=float, default=0.0,
+                    help="also run with a seeded producer delay U[0, D) us per (op, "
+                         "producer) and report the post-arrival latency")
     ap.add_argument("--epilogue", action="store_true",
                     help="also time stream-ordered ops whose producer (a per-rank "
                          "scale) sends from its epilogue, against a separate pack")
@@ -277,18 +342,36 @@ def main() -> int:
     cfg = CONFIGS[2]
     nranks, count, nops, proto = args.nranks, args.rows * args.hidden, args.nops, args.proto
     coll = args.collective
+    selected = None
+    if proto == "auto" or coll == "auto":
+        # the library's choice from the committed cost table
+        from collective_synchronization_amd import selector
+        table = abi.cost_table(selector.load_table()["entries"])
+        if coll == "auto":
+            cid, pid, pred = abi.ar_select_allreduce(table, 2 * count, nranks)
+            coll = selector.COLLECTIVES[cid]
+            if proto == "auto":
+                proto = selector.PROTOS[pid]
+            else:
+                pid, pred = abi.ar_select_collective(table, coll, 2 * count, nranks)
+        else:
+            pid, pred = abi.ar_select_collective(table, coll, 2 * count, nranks)
+            proto = selector.PROTOS[pid]
+        selected = {"collective": coll, "protocol": proto, "predicted_us": round(pred, 3)}
     if coll != "allreduce" and (args.mode != "system" or proto == "barrier"):
         print("bench.py: --collective allgather/twoshot run in system mode with "
               "ll, ll128 or sentinel", file=sys.stderr)
         return 2
-    default_workload = (nranks, args.rows, args.hidden, nops, proto, args.mode, coll) == \
-        (cfg["nranks"], 1, cfg["hidden"], cfg["nops"], "sentinel", "system", "allreduce")
+    default_workload = (nranks, args.rows, args.hidden, nops, proto, args.mode, coll,
+                        args.seed in (None, cfg["seed"])) == \
+        (cfg["nranks"], 1, cfg["hidden"], cfg["nops"], "sentinel", "system", "allreduce", True)
     workload = cfg["name"] if default_workload else \
         f"n{nranks}_{proto}_{args.rows}x{args.hidden}_{nops}ops_{args.mode}" + \
         ("" if coll == "allreduce" else f"_{coll}")
     flags = abi.AR_SIM_COOPERATIVE if args.cooperative else 0
 
-    x = inputs.payload(cfg["seed"], (nops, nranks, count), "normal")
+    seed = cfg["seed"] if args.seed is None else args.seed
+    x = inputs.payload(seed, (nops, nranks, count), "normal")
     if args.calibrate_copy > 0:
         n = args.calibrate_copy // 16 * 16
         src = torch.ones(n // 2, dtype=torch.int16, device="cuda")
@@ -328,11 +411,12 @@ def main() -> int:
         "config": {
             "workload": workload, "nranks": nranks, "shape": [args.rows, args.hidden],
             "protocol": proto, "collective": coll, "ops_per_step": nops, "mode": args.mode,
-            "nconsumers": res["nconsumers"], "values": "N(0,1) seed %d" % cfg["seed"],
+            "nconsumers": res["nconsumers"], "values": "N(0,1) seed %d" % seed,
             "tile_groups_per_rank": res["geo"]["waves_per_rank"],
             "blocks": res["geo"]["blocks"], "kernel": res["geo"]["kernel"],
             "launch": "cooperative" if args.cooperative else "ordinary",
             "input_sha256": inputs.sha256(x)[:16],
+            "selected_by_cost_table": selected,
         },
         "kernel_us_per_op": round(m["kernel_us_per_op"], 4),
         "kernel_us_per_op_p10_p90": [round(m["p10"], 4), round(m["p90"], 4)],
@@ -361,6 +445,14 @@ def main() -> int:
         except RuntimeError as e:
             line["share_mode"] = {"error": str(e)}
 
+    if args.skew_us > 0 and args.mode == "system":
+        try:
+            line["skew"] = measure_skew(torch, abi, buffers, inputs, x, proto, nranks, count,
+                                        nops, min(args.steps, 10), 2, args.skew_us,
+                                        seed, coll)
+        except RuntimeError as e:
+            line["skew"] = {"error": str(e)}
+
     if args.epilogue:
         try:
             line["epilogue"] = measure_epilogue(torch, abi, buffers, x[0], proto, nranks,
@@ -369,6 +461,8 @@ def main() -> int:
             line["epilogue"] = {"error": str(e)}
 
     if not args.no_floor:
+        threads = 64 * nranks if res["geo"]["kernel"] == "wide" else 64
+        line["placement"] = measure_placement(torch, abi, res["geo"]["blocks"], threads)
         fl = measure_floor(torch, abi)
         fl["frac_of_op"] = round(fl["sol_us"] / m["kernel_us_per_op"], 4)
         line["floor"] = fl

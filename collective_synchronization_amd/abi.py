@@ -135,6 +135,7 @@ _SIGS = {
     "ar_probe_litmus": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
     "ar_probe_copy": ([_vp, _vp, _i64, _vp], ctypes.c_int),
     "ar_probe_empty": ([_vp], ctypes.c_int),
+    "ar_probe_placement": ([_i32, _i32, _vp, _vp, _vp], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -396,3 +397,8 @@ def ar_probe_copy(src, dst, nbytes, stream=None) -> None:
 
 def ar_probe_empty(stream=None) -> None:
     _check(_lib.ar_probe_empty(_stream(stream)), "ar_probe_empty")
+
+
+def ar_probe_placement(blocks: int, threads: int, work, result, stream=None) -> None:
+    _check(_lib.ar_probe_placement(blocks, threads, _ptr(work), _ptr(result), _stream(stream)),
+           "ar_probe_placement")

@@ -267,9 +267,10 @@ __device__ __forceinline__ void trace_max(const CollSimArgs& a, int64_t idx) {
 }
 
 // Workgroup b -> (rank g, tile group tg) with the all-reduce simulator's
-// XCD-aware placement: workgroup b runs on XCD b mod 8 and rank g's groups
-// are rotated by g, so a producer and the consumer reading it sit on
-// different XCDs.  Returns false for workgroups without work.
+// XCD-aware placement: workgroup b runs on XCD (s + b) mod 8 (round-robin
+// dispatch from a start s) and rank g's groups are rotated by g, so a
+// producer and the consumer reading it sit on different XCDs.  Returns
+// false for workgroups without work.
 __device__ __forceinline__ bool sim_place(const CollSimArgs& a, int& g, int& tg) {
   const int b = blockIdx.x;
   const int x = b & 7;

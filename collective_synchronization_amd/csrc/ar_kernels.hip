@@ -144,8 +144,10 @@ __device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
   return true;
 }
 
-// Persistent role-split kernel.  Workgroup b sits on XCD b % 8 (round-robin
-// dispatch).  Rank g owns Q workgroups per XCD; its wave index wr (0..W-1)
+// Persistent role-split kernel.  Workgroups are dispatched round robin over
+// the eight XCDs: workgroup b sits on XCD (s + b) % 8, with a start s that
+// depends on earlier dispatches, so only b % 8 matters for which workgroups
+// share an XCD.  Rank g owns Q workgroups per XCD; its wave index wr (0..W-1)
 // is rotated by g so that the producer of a tile and the consumer that
 // reads it sit on different XCDs, and the same wr owns the same tiles
 // {wr, wr + W, ...} in every rank.
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
 // to peer w, so waiting for its own stores orders re-arm before refill.
 // Share mode: only rank 0 consumes; a producer rank's workgroup keeps its
 // wave 0, which takes the dual-buffer licence from rank 0's progress word.
-// Placement: workgroup (g, tg) sits on XCD (tg + rot(g)) mod 8 as in k_sim.
+// Placement: workgroup (g, tg) sits on XCD (s + tg + rot(g)) mod 8 as in k_sim.
 // BATCH: tiles received per workgroup barrier (1 when every workgroup owns a
 // single tile, 2 otherwise; the two chunks of a peer are polled together).
 template <int P, int NMAX, bool SHARE, int BATCH>
@@ -721,6 +723,24 @@ __global__ __launch_bounds__(kBlock) void k_copy(const u32x4* __restrict__ src,
 }
 
 __global__ void k_empty() {}
+
+// Each workgroup records the XCD it runs on and holds its slot until every
+// workgroup of the grid has arrived (a bounded wait), so that the recorded
+// placement is that of a fully resident grid, as in the simulators.
+__global__ void k_placement(int32_t* res, uint32_t* count, uint32_t blocks,
+                            uint64_t timeout_ticks) {
+  if (threadIdx.x != 0) return;
+  res[blockIdx.x] = (int32_t)xcc_id();
+  __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t deadline = now_ticks() + timeout_ticks;
+  while (ld_agent_u32(count) < blocks) {
+    if (now_ticks() > deadline) {
+      res[blockIdx.x] = -1;
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
 
 // ============================================================ host side ==
 
@@ -1287,6 +1307,22 @@ int ar_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
 
 int ar_probe_empty(void* stream) {
   return map_hip(launch(k_empty, dim3(1), dim3(64), static_cast<hipStream_t>(stream)));
+}
+
+int ar_probe_placement(int32_t blocks, int32_t threads, void* work, void* result,
+                       void* stream) {
+  if (!work || !result || blocks < 1 || threads < 1 || threads > 1024) return AR_EINVAL;
+  if (!aligned(work, 256) || !aligned(result, 4)) return AR_EALIGN;
+  DeviceInfo di;
+  int rc = device_info(&di);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = map_hip(launch(k_fill_zero, dim3(1), dim3(kBlock), s, static_cast<uint32_t*>(work),
+                      1u));
+  if (rc) return rc;
+  return map_hip(launch(k_placement, dim3((unsigned)blocks), dim3((unsigned)threads), s,
+                        static_cast<int32_t*>(result), static_cast<uint32_t*>(work),
+                        (uint32_t)blocks, ns_to_ticks(1000000000ull, di.wallclock_hz)));
 }
 
 int ar_last_hip_error(void) { return g_last_hip_error; }

@@ -482,6 +482,19 @@ int ar_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
 int ar_probe_empty(void* stream);
 
 /*
+ * ar_probe_placement: the XCD each workgroup of a `blocks` x `threads` grid
+ * runs on (the XCC_ID hardware register), taken while the whole grid is
+ * resident (each workgroup waits, bounded to 1 s, for all to arrive; one
+ * that gives up records -1).  The simulators assume round-robin dispatch
+ * over the eight XCDs of one partition: workgroup b on XCD (s + b) mod 8,
+ * s depending on earlier dispatches; this checks it.  work: device,
+ * 256-byte aligned, >= 4 bytes (zeroed by the call); result: device
+ * int32[blocks].
+ */
+int ar_probe_placement(int32_t blocks, int32_t threads, void* work, void* result,
+                       void* stream);
+
+/*
  * ar_probe_litmus: ordering evidence for the coherent accesses the protocols
  * rely on, between one writer wave on XCD `xcd_a` and one reader wave on XCD
  * `xcd_b`, `iters` rounds (work: >= 4096 bytes, zeroed; result: device

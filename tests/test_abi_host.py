@@ -280,3 +280,13 @@ def test_epilogue_argument_checks():
     assert sr(4, 100, FAKE, 96, FAKE, FAKE, 104, None) == abi.AR_EINVAL     # in stride < count
     assert sr(4, 100, FAKE, 104, FAKE, FAKE + 4, 104, None) == abi.AR_EALIGN
     assert sr(4, 0, None, 0, None, None, 0, None) == abi.AR_OK
+
+
+def test_placement_probe_argument_checks():
+    pp = lambda *a: _code("ar_probe_placement", *a)
+    assert pp(0, 64, FAKE, FAKE, None) == abi.AR_EINVAL
+    assert pp(8, 0, FAKE, FAKE, None) == abi.AR_EINVAL
+    assert pp(8, 1025, FAKE, FAKE, None) == abi.AR_EINVAL
+    assert pp(8, 64, None, FAKE, None) == abi.AR_EINVAL
+    assert pp(8, 64, FAKE + 4, FAKE, None) == abi.AR_EALIGN
+    assert pp(8, 64, FAKE, FAKE + 2, None) == abi.AR_EALIGN

@@ -89,3 +89,21 @@ def test_sim_cooperative_launch(proto):
     for i in range(nops):
         for c in range(nranks):
             assert np.array_equal(got[i, c], want[i])
+
+
+@pytest.mark.parametrize("blocks,threads", [(64, 512), (128, 1024), (2048, 64), (384, 512)])
+def test_workgroup_xcd_placement(blocks, threads):
+    """The simulators place the producer and the consumers of a tile on
+    different XCDs by assuming that consecutive workgroups are dispatched to
+    consecutive XCDs (round robin over the eight XCDs of one partition).  The
+    round robin continues from earlier dispatches, so workgroup b runs on XCD
+    (s + b) mod 8 for a start s of the launch; the XCC_ID register confirms
+    it."""
+    work = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    res = torch.full((blocks,), -2, dtype=torch.int32, device="cuda")
+    abi.ar_probe_placement(blocks, threads, work, res)
+    torch.cuda.synchronize()
+    x = res.cpu().numpy()
+    print(f"[placement] {blocks}x{threads}: xcds {sorted(set(x.tolist()))}", flush=True)
+    assert np.all(x >= 0)
+    assert np.array_equal(x, (x[0] + np.arange(blocks)) % 8)
