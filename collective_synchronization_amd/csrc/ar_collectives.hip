@@ -302,6 +302,12 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
   const uint32_t N = (uint32_t)a.nranks;
   const int tstride = 2 * a.nranks;
   const uint32_t row_bytes = (uint32_t)(((a.count * 2) + 15) & ~int64_t(15));
+  // one tile per group: the next op's payload chunk is loaded while this op
+  // is exchanged, so no input load sits between two ops' sends
+  const bool pipelined = mine == 1;
+  const int keep = chunk_keep<P>(a.count, tg, lane);
+  uint32_t wnext[4] = {0u, 0u, 0u, 0u};
+  if (pipelined) load_chunk<P>(a.in + (int64_t)g * a.in_stride, row_bytes, tg, lane, wnext);
   if (threadIdx.x == 0) lds_err = 0;
   __syncthreads();
   if (a.trace && lane == 0 && w == 0) {
@@ -316,14 +322,22 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
     const uint32_t stale = seq_prev(seq_prev(seq));
     const uint16_t* row = a.in + ((int64_t)op * a.nranks + g) * a.in_stride;
     uint16_t* orow = a.out + ((int64_t)op * a.nranks + g) * a.out_stride;
+    u32x4 mine_v = u32x4{0u, 0u, 0u, 0u};
+    if (pipelined) {
+      mask_words(wnext, keep);
+      mine_v = encode_words<P>(wnext, lane, seq);
+    }
     if (!own) {
       sim_delay(a, op, g);
       // this wave's earlier stores (sentinel re-arms) complete before it sends
       if (P == kSentinel) fence_release();
       const uint32_t dst0 = (((uint32_t)w * 2u + par) * N + (uint32_t)g) * a.slot_bytes;
-      for (int k = 0; k < mine; ++k)
-        produce_data<P>(rs, dst0, 0u, 1, -1, row, row_bytes, a.count, tg + k * G, a.E, seq,
-                        lane);
+      if (pipelined)
+        store_chunk<P>(rs, dst0, 0u, 1, -1, tg, a.E, lane, mine_v);
+      else
+        for (int k = 0; k < mine; ++k)
+          produce_data<P>(rs, dst0, 0u, 1, -1, row, row_bytes, a.count, tg + k * G, a.E, seq,
+                          lane);
       if (P == kLL128) {
         fence_release();
         for (int k = 0; k < mine; ++k)
@@ -333,6 +347,10 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
         fence_release();
         if (lane == 0) trace_max(a, (int64_t)op * tstride + g);
       }
+      // the next op's load goes out after this op's sends, so that no wait
+      // for this wave's stores (the fences above) also waits for it
+      if (pipelined && op + 1 < a.nops)
+        load_chunk<P>(row + (int64_t)a.nranks * a.in_stride, row_bytes, tg, lane, wnext);
       const uint32_t src0 = (((uint32_t)g * 2u + par) * N + (uint32_t)w) * a.slot_bytes;
       for (int k = 0; k < mine; ++k) {
         const int tile = tg + k * G;
@@ -346,10 +364,14 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
         store_chunk_elems<P>(orow + (int64_t)w * a.row_stride, a.count, tile, a.E, lane, v);
       }
     } else {
+      if (pipelined && op + 1 < a.nops)
+        load_chunk<P>(row + (int64_t)a.nranks * a.in_stride, row_bytes, tg, lane, wnext);
       for (int k = 0; k < mine; ++k) {
         const int tile = tg + k * G;
         store_chunk_elems<P>(orow + (int64_t)g * a.row_stride, a.count, tile, a.E, lane,
-                             encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq));
+                             pipelined ? mine_v
+                                       : encode_chunk<P>(row, row_bytes, a.count, tile, lane,
+                                                         seq));
       }
     }
     __syncthreads();
@@ -396,6 +418,15 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
   const uint32_t E_w = enc_bytes<P>(m_w);
   const uint32_t rb_w = (uint32_t)((m_w * 2 + 15) & ~int64_t(15));
   const uint32_t rb_g = (uint32_t)((m_g * 2 + 15) & ~int64_t(15));
+  // one share tile per group: the next op's chunk (share w for a sender,
+  // share g for the own wave) is loaded while this op is exchanged
+  const bool pipelined = mine == 1;
+  const int64_t lo_mine = own ? lo_g : lo_w;
+  const uint32_t rb_mine = own ? rb_g : rb_w;
+  const int keep = chunk_keep<P>(own ? m_g : m_w, tg, lane);
+  uint32_t wnext[4] = {0u, 0u, 0u, 0u};
+  if (pipelined)
+    load_chunk<P>(a.in + (int64_t)g * a.in_stride + lo_mine, rb_mine, tg, lane, wnext);
   if (threadIdx.x == 0) lds_err = 0;
   __syncthreads();
   if (a.trace && lane == 0 && w == 0) {
@@ -419,10 +450,18 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
     for (int k = 0; k < mine; ++k) {
       const int tile = tg + k * G;
       const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+      u32x4 mine_v = u32x4{0u, 0u, 0u, 0u};
+      if (pipelined) {
+        mask_words(wnext, keep);
+        mine_v = encode_words<P>(wnext, lane, seq);
+      }
       // ---- 1. reduce-scatter ----
       if (!own) {
         if (P == kSentinel) fence_release();
-        produce_data<P>(rs, rs_dst, 0u, 1, -1, row + lo_w, rb_w, m_w, tile, E_w, seq, lane);
+        if (pipelined)
+          store_chunk<P>(rs, rs_dst, 0u, 1, -1, tile, E_w, lane, mine_v);
+        else
+          produce_data<P>(rs, rs_dst, 0u, 1, -1, row + lo_w, rb_w, m_w, tile, E_w, seq, lane);
         if (P == kLL128) {
           fence_release();
           produce_flags(rs, rs_dst, 0u, 1, -1, tile, E_w, seq, lane);
@@ -431,6 +470,11 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
           fence_release();
           if (lane == 0) trace_max(a, (int64_t)op * tstride + g);
         }
+        // the next op's load goes out after this op's sends, so that no wait
+        // for this wave's stores (the fences above) also waits for it
+        if (pipelined && op + 1 < a.nops)
+          load_chunk<P>(row + (int64_t)a.nranks * a.in_stride + lo_mine, rb_mine, tile, lane,
+                        wnext);
         u32x4 got;
         if (poll_chunk<P>(rs, rs_src + loff, loff < E_g, seq, stale, true, a.ctrl,
                           a.timeout_ticks, lane, got) != 0) {
@@ -439,7 +483,11 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
           lds[w][lane] = got;
         }
       } else {
-        lds[g][lane] = encode_chunk<P>(row + lo_g, rb_g, m_g, tile, lane, seq);
+        lds[g][lane] = pipelined ? mine_v
+                                 : encode_chunk<P>(row + lo_g, rb_g, m_g, tile, lane, seq);
+        if (pipelined && op + 1 < a.nops)
+          load_chunk<P>(row + (int64_t)a.nranks * a.in_stride + lo_mine, rb_mine, tile, lane,
+                        wnext);
       }
       __syncthreads();
       if (lds_err) return;                         // whole workgroup

@@ -456,8 +456,6 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
         if (pipelined) {
           mask_words(wnext, keep);
           mine_v = encode_words<P>(wnext, lane, seq);
-          if (op + 1 < a.nops)
-            load_chunk<P>(row + op_rows * a.in_stride, row_bytes, tile, lane, wnext);
         } else {
           mine_v = encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq);
         }
@@ -496,6 +494,10 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
               (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
               __HIP_MEMORY_SCOPE_AGENT);
       }
+      // the next op's payload is loaded after this op's sends, so that no
+      // wait for this wave's stores (the fences above) also waits for it
+      if (pipelined && op + 1 < a.nops)
+        load_chunk<P>(row + op_rows * a.in_stride, row_bytes, tg, lane, wnext);
     }
     if (!consumer) {
       seq = seq_next(seq);
