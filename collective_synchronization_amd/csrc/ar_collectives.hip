@@ -651,7 +651,6 @@ __global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
   int64_t lo_g, m_g;
   share_of(a.count, a.width, g, lo_g, m_g);
   const uint32_t E_g = enc_bytes<P>(m_g);
-  const uint32_t rb_g = (uint32_t)((m_g * 2 + 15) & ~int64_t(15));
   if (a.trace && lane == 0 && tg == 0)
     __hip_atomic_fetch_min(reinterpret_cast<unsigned long long*>(a.trace) +
                                (int64_t)a.nops * tstride,
@@ -670,15 +669,37 @@ __global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
       const int tile = tg + k * G;
       const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
       // ---- 1. reduce-scatter sends ----
+      // the tiles of up to 8 shares (the own one included) are loaded first,
+      // all the loads in flight together, then encoded and sent share by
+      // share; the own share's chunk stays in own_v
+      constexpr int GB = NMAX < 8 ? NMAX : 8;
       if (P == kSentinel) fence_release();
-      for (int w = 0; w < a.nranks; ++w) {
-        if (w == g) continue;
-        int64_t lo_w, m_w;
-        share_of(a.count, a.width, w, lo_w, m_w);
-        const uint32_t dst = (((uint32_t)w * 2u + par) * N + (uint32_t)g) * a.slot_bytes;
-        produce_data<P>(rs, dst, 0u, 1, -1, row + lo_w,
-                        (uint32_t)((m_w * 2 + 15) & ~int64_t(15)), m_w, tile,
-                        enc_bytes<P>(m_w), seq, lane);
+      u32x4 own_v = u32x4{0u, 0u, 0u, 0u};
+      for (int w0 = 0; w0 < (NMAX <= GB ? 1 : a.nranks); w0 += GB) {
+        uint32_t wv[GB][4];
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+          // shares past nranks are empty: their loads read nothing and give 0
+          int64_t lo_w, m_w;
+          share_of(a.count, a.width, w0 + j, lo_w, m_w);
+          load_chunk<P>(row + lo_w, (uint32_t)((m_w * 2 + 15) & ~int64_t(15)), tile, lane,
+                        wv[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+          const int w = w0 + j;
+          if (w >= a.nranks) break;
+          int64_t lo_w, m_w;
+          share_of(a.count, a.width, w, lo_w, m_w);
+          mask_words(wv[j], chunk_keep<P>(m_w, tile, lane));
+          const u32x4 enc = encode_words<P>(wv[j], lane, seq);
+          if (w == g) {
+            own_v = enc;
+            continue;
+          }
+          store_chunk<P>(rs, (((uint32_t)w * 2u + par) * N + (uint32_t)g) * a.slot_bytes, 0u,
+                         1, -1, tile, enc_bytes<P>(m_w), lane, enc);
+        }
       }
       if (P == kLL128) {
         fence_release();
@@ -697,7 +718,6 @@ __global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
       // ---- 2.-3. share g: receive, reduce, all-gather send ----
       if ((uint32_t)tile * kTileBytes < E_g) {
         u32x4 v[NMAX];
-        const u32x4 own_v = encode_chunk<P>(row + lo_g, rb_g, m_g, tile, lane, seq);
         if (poll_tile<P, NMAX>(rs, rs_src, a.slot_bytes, a.nranks, tile, E_g, seq, stale, true,
                                g, own_v, a.ctrl, a.timeout_ticks, lane, v) != 0)
           return;
