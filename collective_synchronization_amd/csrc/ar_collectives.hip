@@ -392,10 +392,11 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
 //  3. all-gather: after a second barrier wave w sends the reduced tile to
 //     rank w and polls tile t of rank w's reduced share w, decoding it into
 //     rank g's output.
-// Every sending wave first waits for its own earlier stores, so the
-// sentinel re-arm of a slot completes before the exchange that licenses the
-// slot's next write (reduce-scatter: the all-gather two steps later;
-// all-gather: the next reduce-scatter).
+// A wave waits for its own earlier stores before each reduce-scatter send.
+// Both slots of a parity are written again two ops later, and a peer gets
+// there only after it has received this wave's reduce-scatter chunk of the
+// op in between; so the sentinel re-arms of an op (the wave's own, of the
+// slots it polled) complete before that licence is sent.
 template <int P, int NMAX>
 __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
   __shared__ u32x4 lds[NMAX][kWave];
@@ -511,7 +512,6 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
       if (!own) {
         const u32x4 r4 = red[lane];
         const uint32_t o[4] = {r4.x, r4.y, r4.z, r4.w};
-        if (P == kSentinel) fence_release();
         store_chunk<P>(rs, ag_dst, 0u, 1, -1, tile, E_g, lane, encode_words<P>(o, lane, seq));
         if (P == kLL128) {
           fence_release();
@@ -636,8 +636,8 @@ __device__ __forceinline__ int poll_shares(rsrc_t rs, uint32_t src0, uint32_t sl
 //     each into rank g's output.
 // A wave talks only to the waves of the same tile group of the other ranks,
 // so the dual-buffer licences of the wide two-shot kernel hold pairwise:
-// every send is preceded by a wait for the wave's own earlier stores (the
-// sentinel re-arms among them).
+// each reduce-scatter send is preceded by a wait for the wave's own earlier
+// stores (the sentinel re-arms among them).
 template <int P, int NMAX>
 __global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
   const int lane = threadIdx.x;
@@ -729,7 +729,6 @@ __global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
         lane_elems<P>(tile, lane, first, n);
         if (loff < E_g) store_elems(orow + lo_g, m_g, first, n, o);
         const u32x4 enc = encode_words<P>(o, lane, seq);
-        if (P == kSentinel) fence_release();
         store_chunk<P>(rs, a.ag0 + (par * N + (uint32_t)g) * a.slot_bytes,
                        2u * N * a.slot_bytes, a.nranks, g, tile, E_g, lane, enc);
         if (P == kLL128) {
@@ -783,12 +782,23 @@ static const void* coll_sim_fn(int proto, int collective, int nranks, bool narro
   }
 }
 
-// Measured on MI355X (4, 8 and 16 ranks, 4 KiB .. 4 MiB per rank): the
-// workgroup kernel wins while each workgroup walks at most two share tiles
-// (the one-wave kernel serializes its N-1 sends and polls: 2-4x slower at
-// small shares); from three tiles on, the one-wave kernel's wider grid wins
-// by up to 1.6x (8 ranks, 1 MiB: 22.1 -> 13.9 us per op, LL).
-static constexpr int kTwoShotWideMaxTiles = 2;
+// Two-shot kernel choice, from a sweep of both kernels on MI355X (4, 8 and 16
+// ranks, 16 KiB .. 2 MiB per rank, every protocol).  The one-wave kernel
+// serializes its N-1 sends and polls, which costs it a roughly fixed 6 / 9 /
+// 16-22 us per op at 4 / 8 / 16 ranks, while the workgroup kernel's time
+// grows with the share tiles each workgroup walks.  The workgroup kernel
+// wins up to this many tiles:
+//   4 ranks: 1 (2 tiles: 8.2 vs 7.1 us, LL, 512 KiB);
+//   8 ranks: 3 (3 tiles: 17.4 vs 19.3 us, LL128, 512 KiB; 4 tiles:
+//     15.3 vs 10.7 us, LL, 512 KiB);
+//   16 ranks: 5 for LL128 and SENTINEL (4 tiles: 21.6 vs 24.5 us, SENTINEL,
+//     512 KiB; 5 tiles: 36.3 vs 38.5 us, LL128, 512 KiB), 3 for LL (4 tiles:
+//     18.6 vs 16.5 us, 256 KiB).
+static int twoshot_wide_max_tiles(int proto, int nranks) {
+  if (nranks <= 4) return 1;
+  if (nranks <= 8) return 3;
+  return proto == kLL ? 3 : 5;
+}
 
 struct CollGeom {
   int32_t W, Q, T, TPW, blocks;
@@ -853,14 +863,16 @@ static int coll_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool n
 }
 
 // Two-shot kernel choice: a workgroup of one wave per peer while each
-// workgroup owns one share tile, else (or with AR_SIM_NARROW) one wave per
-// share tile group; AR_SIM_WIDE forces the former.
+// workgroup walks at most twoshot_wide_max_tiles share tiles, else (or with
+// AR_SIM_NARROW) one wave per share tile group; AR_SIM_WIDE forces the
+// former.
 static int coll_geometry(const ar_sim_params* p, const DeviceInfo& di, CollGeom* g) {
   if (p->desc.collective != AR_TWOSHOT) return coll_geometry_as(p, di, false, g);
   if (p->flags & AR_SIM_NARROW) return coll_geometry_as(p, di, true, g);
   const int rc = coll_geometry_as(p, di, false, g);
   if (p->flags & AR_SIM_WIDE) return rc;
-  if (rc == AR_OK && g->TPW <= kTwoShotWideMaxTiles) return AR_OK;
+  if (rc == AR_OK && g->TPW <= twoshot_wide_max_tiles(p->desc.proto, p->desc.nranks))
+    return AR_OK;
   return coll_geometry_as(p, di, true, g);
 }
 

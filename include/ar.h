@@ -345,19 +345,24 @@ int ar_scale_rows(int32_t nranks, int64_t count, const void* in, int64_t in_stri
  *        by the caller.
  *
  * Other collectives (desc.collective), system mode only (nconsumers ==
- * nranks), LL / LL128 / SENTINEL, no tile_order and no AR_SIM_NARROW /
- * AR_SIM_WIDE (one kernel each, a workgroup of one wave per peer):
+ * nranks), LL / LL128 / SENTINEL, no tile_order:
  *   AR_ALLGATHER: op i's output at consumer c is the all-gather layout of
  *        ar_gather_validate at out + (i*nranks + c)*out_stride.  A rank
  *        starts op i+1 once it holds all of op i (one workgroup barrier per
  *        op), as a rank whose next payload depends on this result would.
+ *        One kernel (a workgroup of one wave per peer); AR_SIM_NARROW and
+ *        AR_SIM_WIDE are rejected.
  *   AR_TWOSHOT: per op and tile of a share, the reduce-scatter exchange, the
  *        share owner's fixed-order reduce, then the all-gather exchange of
  *        the reduced share; output as for AR_ALLREDUCE.  The trace's
- *        "last store" is that of the reduce-scatter.
+ *        "last store" is that of the reduce-scatter.  Two kernels: a
+ *        workgroup of one wave per peer (AR_SIM_WIDE) or one wave per share
+ *        tile group serving every peer (AR_SIM_NARROW); without either flag
+ *        the library picks by rank count, protocol and share tiles per
+ *        workgroup.
  * Every wave waits for its own earlier stores (the sentinel re-arms among
- * them) before it sends, so a slot is re-armed before the exchange that
- * licenses its next write, in both regions.
+ * them) before the first send of each op, so every slot this wave re-armed
+ * in op i is armed again before any peer can get to op i+2 and write it.
  */
 #define AR_SIM_COOPERATIVE 1   /* launch with hipLaunchCooperativeKernel */
 #define AR_SIM_NARROW 2        /* one wave per tile serving every peer, instead
