@@ -113,6 +113,49 @@ def measure_floor(torch, abi, iters=2000):
             "pingpong_pairs": len(oneway)}
 
 
+def measure_launch_and_copy(torch, abi, launches=200, copy_bytes=256 << 20, copies=5):
+    """Empty-kernel launch time (HIP events around a burst of launches, per
+    launch) and the streaming-copy ceiling (bytes read + written per second,
+    best of `copies` copies of copy_bytes)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(10):
+        abi.ar_probe_empty(stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(launches):
+        abi.ar_probe_empty(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    empty_us = a.elapsed_time(b) * 1e3 / launches
+    src = torch.ones(copy_bytes // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    abi.ar_probe_copy(src, dst, copy_bytes, stream)
+    best = float("inf")
+    for _ in range(copies):
+        a.record(stream)
+        abi.ar_probe_copy(src, dst, copy_bytes, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e-3)
+    ok = bool(torch.equal(src, dst))
+    del src, dst
+    return {"empty_kernel_us": round(empty_us, 3),
+            "copy_gbs": round(2 * copy_bytes / best / 1e9, 1) if ok else None,
+            "copy_bytes": copy_bytes}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(x, proto, seconds, collective="allreduce"):
     import oracle
     us, ops = oracle.time_collective(x, proto, collective, seconds=seconds)
@@ -189,7 +232,9 @@ def measure_placement(torch, abi, blocks, threads):
             "round_robin_start": int(x[0]),
             "on_expected_xcd": round(float(np.mean(x == (x[0] + np.arange(blocks)) % 8)), 4),
             "xcds_seen": int(len(set(x[x >= 0].tolist()))),
-            "cus": int(props.multi_processor_count)}
+            "cus": int(props.multi_processor_count),
+            # one device spanning all eight XCDs (256 CUs) is the SPX partition
+            "partition": "SPX" if len(set(x[x >= 0].tolist())) == 8 else "other"}
 
 
 def measure_skew(torch, abi, buffers, inputs, x, proto, nranks, count, nops, steps,
@@ -465,7 +510,21 @@ def main() -> int:
         line["placement"] = measure_placement(torch, abi, res["geo"]["blocks"], threads)
         fl = measure_floor(torch, abi)
         fl["frac_of_op"] = round(fl["sol_us"] / m["kernel_us_per_op"], 4)
+        fl.update(measure_launch_and_copy(torch, abi))
+        if fl["copy_gbs"]:
+            line["roofline"]["frac_of_copy"] = round(m["gbs"] / fl["copy_gbs"], 6)
         line["floor"] = fl
+        if coll == "allreduce":
+            # the same workload one op per launch: what a stream-ordered
+            # caller that launches each op pays
+            try:
+                r1 = measure(torch, abi, buffers, x[:1], proto, nranks, count, 1, args.mode,
+                             min(args.steps, 50), 3, 0, flags, coll)
+                line["single_op_launch"] = {
+                    "kernel_us": round(statistics.median(r1["launch_ms"]) * 1e3, 3),
+                    "empty_kernel_us": fl["empty_kernel_us"]}
+            except RuntimeError as e:
+                line["single_op_launch"] = {"error": str(e)}
 
     if not args.no_cpu_baseline:
         us, ops = cpu_baseline(x, proto, args.cpu_seconds, coll)
@@ -475,7 +534,7 @@ def main() -> int:
                            "reduce + encode/decode of the reduced share"}[coll]
         line["cpu_baseline"] = {
             "value": round(us, 3), "unit": unit, "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": (f"{ops} ops of the same workload (N={nranks}, [{args.rows},"
                        f"{args.hidden}], {proto}: {what} for one receiving rank, "
                        f"single thread, ~{args.cpu_seconds:g} s)"),
