@@ -383,15 +383,19 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
 }
 
 // Two-shot simulator: a workgroup of nranks waves per (rank g, tile group tg
-// of the share tiles), wave w paired with peer w.  Per op and tile t:
-//  1. reduce-scatter: wave w sends tile t of rank g's share w to rank w;
-//     it then polls tile t of rank w's share g, staging it in LDS row w (the
-//     own wave stages its own share-g chunk);
-//  2. after a barrier the own wave reduces the staged rows in rank order,
-//     writes the reduced tile to rank g's output and stages it;
-//  3. all-gather: after a second barrier wave w sends the reduced tile to
-//     rank w and polls tile t of rank w's reduced share w, decoding it into
-//     rank g's output.
+// of the share tiles), wave w paired with peer w.  Per op:
+//  1. reduce-scatter: wave w sends every tile of the group of rank g's share
+//     w to rank w;
+//  2. per tile t: wave w polls tile t of rank w's share g and stages it in
+//     LDS row w (the own wave stages its own share-g chunk); after a barrier
+//     the own wave reduces the staged rows in rank order, writes the reduced
+//     tile to rank g's output and stages it; after a second barrier wave w
+//     sends the reduced tile to rank w (all-gather);
+//  3. wave w polls every tile of rank w's reduced share w and decodes it
+//     into rank g's output.
+// No step waits on a peer's progress in the same op beyond the data it
+// needs: every reduce-scatter chunk is out before any wave polls, and every
+// reduced tile is sent before any wave polls the all-gather.
 // A wave waits for its own earlier stores before each reduce-scatter send.
 // Both slots of a parity are written again two ops later, and a peer gets
 // there only after it has received this wave's reduce-scatter chunk of the
@@ -448,34 +452,55 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
     const uint32_t ag_dst = a.ag0 + rs_dst;
     const uint32_t ag_src = a.ag0 + rs_src;
     if (!own) sim_delay(a, op, g);
+    u32x4 mine_v = u32x4{0u, 0u, 0u, 0u};        // pipelined: this op's chunk
+    if (pipelined) {
+      mask_words(wnext, keep);
+      mine_v = encode_words<P>(wnext, lane, seq);
+    }
+    // ---- 1. reduce-scatter sends: every tile of the group ----
+    if (!own) {
+      if (P == kSentinel) fence_release();
+      if (pipelined) {
+        store_chunk<P>(rs, rs_dst, 0u, 1, -1, tg, E_w, lane, mine_v);
+      } else {
+        // the loads of up to TB tiles in flight together, then their stores
+        // (a tile past the share reads nothing and stores nothing); 16-wave
+        // workgroups have 128 registers a lane, hence the smaller group
+        constexpr int TB = NMAX >= 16 ? 2 : 4;
+        for (int k0 = 0; k0 < mine; k0 += TB) {
+          uint32_t wv[TB][4];
+#pragma unroll
+          for (int j = 0; j < TB; ++j)
+            load_chunk<P>(row + lo_w, rb_w, tg + (k0 + j) * G, lane, wv[j]);
+#pragma unroll
+          for (int j = 0; j < TB; ++j) {
+            if (k0 + j >= mine) break;
+            const int tile = tg + (k0 + j) * G;
+            mask_words(wv[j], chunk_keep<P>(m_w, tile, lane));
+            store_chunk<P>(rs, rs_dst, 0u, 1, -1, tile, E_w, lane,
+                           encode_words<P>(wv[j], lane, seq));
+          }
+        }
+      }
+      if (P == kLL128) {
+        fence_release();
+        for (int k = 0; k < mine; ++k)
+          produce_flags(rs, rs_dst, 0u, 1, -1, tg + k * G, E_w, seq, lane);
+      }
+      if (a.trace) {
+        fence_release();
+        if (lane == 0) trace_max(a, (int64_t)op * tstride + g);
+      }
+    }
+    // the next op's load goes out after this op's sends, so that no wait for
+    // this wave's stores (the fences above) also waits for it
+    if (pipelined && op + 1 < a.nops)
+      load_chunk<P>(row + (int64_t)a.nranks * a.in_stride + lo_mine, rb_mine, tg, lane, wnext);
+    // ---- 2. per tile: receive share g, reduce, send the reduced tile ----
     for (int k = 0; k < mine; ++k) {
       const int tile = tg + k * G;
       const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
-      u32x4 mine_v = u32x4{0u, 0u, 0u, 0u};
-      if (pipelined) {
-        mask_words(wnext, keep);
-        mine_v = encode_words<P>(wnext, lane, seq);
-      }
-      // ---- 1. reduce-scatter ----
       if (!own) {
-        if (P == kSentinel) fence_release();
-        if (pipelined)
-          store_chunk<P>(rs, rs_dst, 0u, 1, -1, tile, E_w, lane, mine_v);
-        else
-          produce_data<P>(rs, rs_dst, 0u, 1, -1, row + lo_w, rb_w, m_w, tile, E_w, seq, lane);
-        if (P == kLL128) {
-          fence_release();
-          produce_flags(rs, rs_dst, 0u, 1, -1, tile, E_w, seq, lane);
-        }
-        if (a.trace && k == mine - 1) {
-          fence_release();
-          if (lane == 0) trace_max(a, (int64_t)op * tstride + g);
-        }
-        // the next op's load goes out after this op's sends, so that no wait
-        // for this wave's stores (the fences above) also waits for it
-        if (pipelined && op + 1 < a.nops)
-          load_chunk<P>(row + (int64_t)a.nranks * a.in_stride + lo_mine, rb_mine, tile, lane,
-                        wnext);
         u32x4 got;
         if (poll_chunk<P>(rs, rs_src + loff, loff < E_g, seq, stale, true, a.ctrl,
                           a.timeout_ticks, lane, got) != 0) {
@@ -486,13 +511,10 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
       } else {
         lds[g][lane] = pipelined ? mine_v
                                  : encode_chunk<P>(row + lo_g, rb_g, m_g, tile, lane, seq);
-        if (pipelined && op + 1 < a.nops)
-          load_chunk<P>(row + (int64_t)a.nranks * a.in_stride + lo_mine, rb_mine, tile, lane,
-                        wnext);
       }
       __syncthreads();
       if (lds_err) return;                         // whole workgroup
-      // ---- 2. fixed-order reduce of share g, tile t (own wave) ----
+      // fixed-order reduce of share g, tile t (own wave)
       if (own) {
         u32x4 v[NMAX];
 #pragma unroll
@@ -508,7 +530,6 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
         red[lane] = u32x4{o[0], o[1], o[2], o[3]};
       }
       __syncthreads();
-      // ---- 3. all-gather of the reduced tile ----
       if (!own) {
         const u32x4 r4 = red[lane];
         const uint32_t o[4] = {r4.x, r4.y, r4.z, r4.w};
@@ -517,13 +538,20 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
           fence_release();
           produce_flags(rs, ag_dst, 0u, 1, -1, tile, E_g, seq, lane);
         }
+      }
+    }
+    // ---- 3. all-gather receive: every tile of peer w's reduced share ----
+    if (!own) {
+      for (int k = 0; k < mine; ++k) {
+        const int tile = tg + k * G;
+        const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
         u32x4 got;
         if (poll_chunk<P>(rs, ag_src + loff, loff < E_w, seq, stale, true, a.ctrl,
                           a.timeout_ticks, lane, got) != 0) {
           if (lane == 0) lds_err = 1;
-        } else {
-          store_chunk_elems<P>(orow + lo_w, m_w, tile, E_w, lane, got);
+          break;
         }
+        store_chunk_elems<P>(orow + lo_w, m_w, tile, E_w, lane, got);
       }
     }
     __syncthreads();
@@ -785,19 +813,20 @@ static const void* coll_sim_fn(int proto, int collective, int nranks, bool narro
 // Two-shot kernel choice, from a sweep of both kernels on MI355X (4, 8 and 16
 // ranks, 16 KiB .. 2 MiB per rank, every protocol).  The one-wave kernel
 // serializes its N-1 sends and polls, which costs it a roughly fixed 6 / 9 /
-// 16-22 us per op at 4 / 8 / 16 ranks, while the workgroup kernel's time
-// grows with the share tiles each workgroup walks.  The workgroup kernel
-// wins up to this many tiles:
-//   4 ranks: 1 (2 tiles: 8.2 vs 7.1 us, LL, 512 KiB);
-//   8 ranks: 3 (3 tiles: 17.4 vs 19.3 us, LL128, 512 KiB; 4 tiles:
-//     15.3 vs 10.7 us, LL, 512 KiB);
-//   16 ranks: 5 for LL128 and SENTINEL (4 tiles: 21.6 vs 24.5 us, SENTINEL,
-//     512 KiB; 5 tiles: 36.3 vs 38.5 us, LL128, 512 KiB), 3 for LL (4 tiles:
-//     18.6 vs 16.5 us, 256 KiB).
+// 16-22 us per op at 4 / 8 / 16 ranks (LL128: 11 / 18 / 33 us), while the
+// workgroup kernel's time grows with the share tiles each workgroup walks.
+// The workgroup kernel wins up to this many tiles:
+//   4 ranks: 2 (2 tiles: 6.5 vs 7.1 us, LL, 512 KiB; 3 tiles: 9.0 vs
+//     7.7 us, LL, 1 MiB);
+//   8 ranks: 3 (3 tiles: 14.2 vs 19.1 us, LL128, 512 KiB; 4 tiles:
+//     12.6 vs 10.7 us, LL, 512 KiB);
+//   16 ranks: 5 (4 tiles: 18.3 vs 24.3 us, SENTINEL, 512 KiB; 8 tiles:
+//     41.5 vs 29.2 us, SENTINEL, 1 MiB), and 9 for LL128 (9 tiles: 62.0 vs
+//     70.9 us, 1 MiB; 18 tiles: 120 vs 109 us, 2 MiB).
 static int twoshot_wide_max_tiles(int proto, int nranks) {
-  if (nranks <= 4) return 1;
+  if (nranks <= 4) return 2;
   if (nranks <= 8) return 3;
-  return proto == kLL ? 3 : 5;
+  return proto == kLL128 ? 9 : 5;
 }
 
 struct CollGeom {
