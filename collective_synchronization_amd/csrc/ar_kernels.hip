@@ -261,11 +261,28 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
     } else {
       const uint16_t* ord =
           a.order ? a.order + ((int64_t)op * a.nranks + g) * a.TPW : nullptr;
-      for (int j = 0; j < a.TPW; ++j) {
-        const int k = ord ? (int)ord[j] : j;
-        if (k >= mine) continue;
-        produce_data<P>(rs, dst0, cstride, a.nconsumers, skip, row, row_bytes,
-                        a.count, wr + k * a.W, a.E, seq, lane);
+      // the loads of up to TB tiles in flight together, then their stores (a
+      // tile past the payload reads nothing and stores nothing).  Measured:
+      // 1-5% per op at 0.5-4 MiB for LL, LL128 and the sentinel; up to 8%
+      // slower for the barrier baseline, which keeps one tile at a time.
+      constexpr int TB = P == kBarrier ? 1 : 4;
+      for (int j0 = 0; j0 < a.TPW; j0 += TB) {
+        uint32_t wv[TB][4];
+        int kk[TB];
+#pragma unroll
+        for (int i = 0; i < TB; ++i) {
+          const int j = j0 + i;
+          kk[i] = j < a.TPW ? (ord ? (int)ord[j] : j) : mine;
+          load_chunk<P>(row, row_bytes, wr + kk[i] * a.W, lane, wv[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < TB; ++i) {
+          if (kk[i] >= mine) continue;
+          const int tile = wr + kk[i] * a.W;
+          mask_words(wv[i], chunk_keep<P>(a.count, tile, lane));
+          store_chunk<P>(rs, dst0, cstride, a.nconsumers, skip, tile, a.E, lane,
+                         encode_words<P>(wv[i], lane, seq));
+        }
       }
       if (P == kLL128) {
         fence_release();
