@@ -179,6 +179,39 @@ def test_sim_waves_per_rank_override(proto):
     assert np.array_equal(got[:, 0], want)
 
 
+@pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel", "barrier"])
+def test_sim_narrow_many_tiles_shuffled(proto):
+    """The one-wave kernel with 8 waves per rank, so that each wave walks many
+    tiles (a count of tiles per wave that is not a multiple of the 4 whose
+    loads the kernel overlaps), a ragged payload, a shuffled send order per
+    (op, producer) and seeded producer delays: every consumer bit-exact."""
+    n, count, nops = 8, 65536 + 5, 3
+    ws = buffers.Workspace(n, count, proto, n)
+    x = _x(700 + count, (nops, n, count), specials=True)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    kw = dict(waves_per_rank=8, flags=abi.AR_SIM_NARROW)
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride, **kw))
+    print(f"[narrow-order] {proto} N={n} count={count} geo={geo}", flush=True)
+    assert geo["kernel"] == "narrow" and geo["tiles_per_wave"] > 4
+    assert geo["tiles_per_wave"] % 4 != 0
+    order = inputs.tile_orders(19, nops, n, geo["tiles_per_wave"])
+    order_d = torch.from_numpy(order.view(np.int16)).to("cuda")
+    hz = abi.ar_wallclock_hz()
+    d_us = inputs.delays_us(20, nops, n, 5.0)
+    ticks = torch.from_numpy(np.round(d_us * hz * 1e-6).astype(np.int32)).to("cuda")
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS, delay_ticks=ticks,
+           tile_order=order_d, **kw)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    got = buffers.rows_from_device(outd, count, (nops, n))
+    want = oracle.allreduce_ops(x, proto, seq0)
+    for i in range(nops):
+        for c in range(n):
+            assert np.array_equal(got[i, c], want[i]), (i, c)
+
+
 @pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel"])
 def test_sim_wide_shuffled_and_skewed(proto):
     """The wide kernel with two tiles per workgroup, a shuffled send order
