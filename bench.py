@@ -354,7 +354,8 @@ def main() -> int:
     ap.add_argument("--hidden", type=int, default=4096)
     ap.add_argument("--nops", type=int, default=64)
     ap.add_argument("--waves-per-rank", type=int, default=0)
-    ap.add_argument("--cooperative", action="store_true")
+    ap.add_argument("--launch", default="auto", choices=["auto", "cooperative", "ordinary"],
+                    help="simulator launch: the library's choice, or forced")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-floor", action="store_true")
@@ -413,7 +414,8 @@ def main() -> int:
     workload = cfg["name"] if default_workload else \
         f"n{nranks}_{proto}_{args.rows}x{args.hidden}_{nops}ops_{args.mode}" + \
         ("" if coll == "allreduce" else f"_{coll}")
-    flags = abi.AR_SIM_COOPERATIVE if args.cooperative else 0
+    flags = {"auto": 0, "cooperative": abi.AR_SIM_COOPERATIVE,
+             "ordinary": abi.AR_SIM_ORDINARY}[args.launch]
 
     seed = cfg["seed"] if args.seed is None else args.seed
     x = inputs.payload(seed, (nops, nranks, count), "normal")
@@ -459,7 +461,7 @@ def main() -> int:
             "nconsumers": res["nconsumers"], "values": "N(0,1) seed %d" % seed,
             "tile_groups_per_rank": res["geo"]["waves_per_rank"],
             "blocks": res["geo"]["blocks"], "kernel": res["geo"]["kernel"],
-            "launch": "cooperative" if args.cooperative else "ordinary",
+            "launch": res["geo"]["launch"],
             "input_sha256": inputs.sha256(x)[:16],
             "selected_by_cost_table": selected,
         },

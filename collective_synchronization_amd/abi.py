@@ -25,6 +25,7 @@ AR_FLAG_REARM = 1
 AR_SIM_COOPERATIVE = 1
 AR_SIM_NARROW = 2
 AR_SIM_WIDE = 4
+AR_SIM_ORDINARY = 8
 AR_MAX_RANKS = 16
 AR_ALLREDUCE, AR_ALLGATHER, AR_TWOSHOT = 0, 1, 2
 COLLECTIVE_IDS = {"allreduce": AR_ALLREDUCE, "allgather": AR_ALLGATHER,
@@ -119,7 +120,8 @@ _SIGS = {
     "ar_sim_run": ([ctypes.POINTER(ar_sim_params), _vp], ctypes.c_int),
     "ar_sim_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
                          ctypes.POINTER(_i32), ctypes.POINTER(_i32),
-                         ctypes.POINTER(_i32), ctypes.POINTER(_i32)], ctypes.c_int),
+                         ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                         ctypes.POINTER(_i32)], ctypes.c_int),
     "ar_wallclock_hz": ([ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     "ar_select_protocol": ([ctypes.POINTER(ar_cost_entry), _i32, _i64, _i32,
                             ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)],
@@ -314,13 +316,15 @@ def ar_sim_run(params: ar_sim_params, stream=None) -> None:
 
 
 def ar_sim_geometry(params: ar_sim_params) -> dict:
-    w, t, tpw, b, wide = _i32(), _i32(), _i32(), _i32(), _i32()
+    w, t, tpw, b, wide, coop = _i32(), _i32(), _i32(), _i32(), _i32(), _i32()
     _check(_lib.ar_sim_geometry(ctypes.byref(params), ctypes.byref(w), ctypes.byref(t),
-                                ctypes.byref(tpw), ctypes.byref(b), ctypes.byref(wide)),
+                                ctypes.byref(tpw), ctypes.byref(b), ctypes.byref(wide),
+                                ctypes.byref(coop)),
            "ar_sim_geometry")
     return {"waves_per_rank": w.value, "tiles_per_rank": t.value,
             "tiles_per_wave": tpw.value, "blocks": b.value,
-            "kernel": "wide" if wide.value else "narrow"}
+            "kernel": "wide" if wide.value else "narrow",
+            "launch": "cooperative" if coop.value else "ordinary"}
 
 
 def ar_wallclock_hz() -> float:

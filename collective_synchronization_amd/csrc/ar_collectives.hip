@@ -876,6 +876,7 @@ static int twoshot_wide_max_tiles(int proto, int nranks) {
 struct CollGeom {
   int32_t W, Q, T, TPW, blocks;
   bool narrow;                 // two-shot: one wave per tile group
+  bool coop;                   // cooperative launch
 };
 
 static int coll_check(const ar_sim_params* p) {
@@ -884,7 +885,9 @@ static int coll_check(const ar_sim_params* p) {
   if (d->proto == kBarrier) return AR_EINVAL;
   if (p->tile_order) return AR_EINVAL;
   const int kernel_flags = AR_SIM_NARROW | AR_SIM_WIDE;
-  if (p->flags & ~kernel_flags) return AR_EINVAL;
+  const int launch_flags = AR_SIM_COOPERATIVE | AR_SIM_ORDINARY;
+  if (p->flags & ~(kernel_flags | launch_flags)) return AR_EINVAL;
+  if ((p->flags & launch_flags) == launch_flags) return AR_EINVAL;
   if ((p->flags & kernel_flags) &&
       (d->collective != AR_TWOSHOT || (p->flags & kernel_flags) == kernel_flags))
     return AR_EINVAL;
@@ -892,16 +895,17 @@ static int coll_check(const ar_sim_params* p) {
 }
 
 // Tiles of one rank's transfer: the whole payload (all-gather) or one full
-// share (two-shot).  Grid: the all-reduce simulator's rule (half of the
-// occupancy query's residency, tile groups in multiples of 8 per rank).
+// share (two-shot).  Grid: the all-reduce simulator's rule (the occupancy
+// query's residency, halved for an ordinary launch; tile groups in
+// multiples of 8 per rank).
 static int coll_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool narrow,
-                            CollGeom* g) {
+                            bool coop, CollGeom* g) {
   const ar_desc* d = &p->desc;
   const int64_t n_el =
       d->collective == AR_TWOSHOT ? share_width(d->count, d->nranks) : d->count;
   const int64_t T = ceil_div64(encoded_bytes(d->proto, n_el), kTileBytes);
   if (T <= 0) {
-    *g = CollGeom{0, 0, 0, 0, 0, narrow};
+    *g = CollGeom{0, 0, 0, 0, 0, narrow, coop};
     return AR_OK;
   }
   if (T > (int64_t(1) << 24)) return AR_ESIZE;
@@ -917,9 +921,10 @@ static int coll_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool n
       return AR_ELAUNCH;
     occ = (m == 0 || o < occ) ? o : occ;
   }
-  // whole grid resident: half the occupancy query's figure, and one-wave
-  // workgroups at most 8 per CU (as for the all-reduce simulator)
-  int64_t capacity = (int64_t)occ * di.cus / 2;
+  // whole grid resident: the occupancy query's figure (half of it for an
+  // ordinary launch), and one-wave workgroups at most 8 per CU (as for the
+  // all-reduce simulator)
+  int64_t capacity = (int64_t)occ * di.cus / (coop ? 1 : 2);
   if (narrow && capacity > 8 * (int64_t)di.cus) capacity = 8 * (int64_t)di.cus;
   const int64_t qmax = capacity / (8 * (int64_t)d->nranks);
   if (qmax < 1) return AR_ECAPACITY;
@@ -938,6 +943,7 @@ static int coll_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool n
   g->TPW = (int32_t)ceil_div64(T, 8 * Q);
   g->blocks = (int32_t)(8 * Q * d->nranks);
   g->narrow = narrow;
+  g->coop = coop;
   return AR_OK;
 }
 
@@ -945,18 +951,35 @@ static int coll_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool n
 // workgroup walks at most twoshot_wide_max_tiles share tiles, else (or with
 // AR_SIM_NARROW) one wave per share tile group; AR_SIM_WIDE forces the
 // former.
-static int coll_geometry(const ar_sim_params* p, const DeviceInfo& di, CollGeom* g) {
-  if (p->desc.collective != AR_TWOSHOT) return coll_geometry_as(p, di, false, g);
-  if (p->flags & AR_SIM_NARROW) return coll_geometry_as(p, di, true, g);
-  const int rc = coll_geometry_as(p, di, false, g);
+static int coll_kernel_choice(const ar_sim_params* p, const DeviceInfo& di, bool coop,
+                              CollGeom* g) {
+  if (p->desc.collective != AR_TWOSHOT) return coll_geometry_as(p, di, false, coop, g);
+  if (p->flags & AR_SIM_NARROW) return coll_geometry_as(p, di, true, coop, g);
+  const int rc = coll_geometry_as(p, di, false, coop, g);
   if (p->flags & AR_SIM_WIDE) return rc;
   if (rc == AR_OK && g->TPW <= twoshot_wide_max_tiles(p->desc.proto, p->desc.nranks))
     return AR_OK;
-  return coll_geometry_as(p, di, true, g);
+  return coll_geometry_as(p, di, true, coop, g);
+}
+
+// Launch choice: as for the all-reduce simulator (coop_pays).
+static int coll_geometry(const ar_sim_params* p, const DeviceInfo& di, CollGeom* g) {
+  if (p->flags & AR_SIM_COOPERATIVE) return coll_kernel_choice(p, di, true, g);
+  const int rc = coll_kernel_choice(p, di, false, g);
+  if ((p->flags & AR_SIM_ORDINARY) || !di.coop || p->nops < kCoopMinOps) return rc;
+  if (rc != AR_OK && rc != AR_ECAPACITY) return rc;
+  CollGeom gc;
+  if (coll_kernel_choice(p, di, true, &gc) == AR_OK &&
+      coop_pays(rc, g->TPW, !g->narrow, gc.TPW, !gc.narrow)) {
+    *g = gc;
+    return AR_OK;
+  }
+  return rc;
 }
 
 int coll_sim_geometry(const ar_sim_params* p, int32_t* groups, int32_t* tiles,
-                      int32_t* tiles_per_group, int32_t* blocks, int32_t* wide) {
+                      int32_t* tiles_per_group, int32_t* blocks, int32_t* wide,
+                      int32_t* cooperative) {
   int rc = coll_check(p);
   if (rc) return rc;
   DeviceInfo di;
@@ -970,6 +993,7 @@ int coll_sim_geometry(const ar_sim_params* p, int32_t* groups, int32_t* tiles,
   if (tiles_per_group) *tiles_per_group = g.TPW;
   if (blocks) *blocks = g.blocks;
   if (wide) *wide = g.narrow ? 0 : 1;
+  if (cooperative) *cooperative = g.coop ? 1 : 0;
   return AR_OK;
 }
 
@@ -984,6 +1008,7 @@ int coll_sim_run(const ar_sim_params* p, hipStream_t s) {
   DeviceInfo di;
   rc = device_info(&di);
   if (rc) return rc;
+  if ((p->flags & AR_SIM_COOPERATIVE) && !di.coop) return AR_ENODEV;
   CollGeom g;
   rc = coll_geometry(p, di, &g);
   if (rc) return rc;
@@ -1013,10 +1038,11 @@ int coll_sim_run(const ar_sim_params* p, hipStream_t s) {
   a.delay = p->delay_ticks;
   a.trace = p->trace;
   void* args[] = {&a};
-  return map_hip(hipLaunchKernel(coll_sim_fn(d->proto, d->collective, d->nranks, g.narrow,
-                                             g.TPW > 1),
-                                 dim3(g.blocks), dim3(g.narrow ? kWave : kWave * d->nranks),
-                                 args, 0, s));
+  const void* fn = coll_sim_fn(d->proto, d->collective, d->nranks, g.narrow, g.TPW > 1);
+  const dim3 block(g.narrow ? kWave : kWave * d->nranks);
+  if (g.coop)
+    return map_hip(hipLaunchCooperativeKernel(fn, dim3(g.blocks), block, args, 0, s));
+  return map_hip(hipLaunchKernel(fn, dim3(g.blocks), block, args, 0, s));
 }
 
 // ----------------------------------------------------- stream-ordered host

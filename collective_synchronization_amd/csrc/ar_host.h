@@ -133,6 +133,22 @@ inline int check_rows(const void* p, int64_t stride, int64_t count) {
   return AR_OK;
 }
 
+// Launch choice without a flag.  A cooperative launch may fill the
+// occupancy the runtime reports, an ordinary one keeps half; the
+// cooperative launch costs a fixed ~15 us more per launch on MI355X (8 ranks
+// [1,4096]: 23.4 against 6.8 us for one op, the same per-op time over 256
+// ops).  It is taken when the device supports it, the launch holds at least
+// kCoopMinOps ops, and its grid lets the waves walk fewer tiles in the same
+// kernel, or run the workgroup kernel where the ordinary grid needs the
+// one-wave kernel (or the ordinary grid does not fit at all).
+constexpr int kCoopMinOps = 32;
+
+inline bool coop_pays(int rc_ord, int tpw_ord, bool wide_ord, int tpw_co, bool wide_co) {
+  if (rc_ord != AR_OK) return true;
+  if (wide_co == wide_ord) return tpw_co < tpw_ord;
+  return wide_co;
+}
+
 inline thread_local int g_last_hip_error = 0;
 
 inline int map_hip(hipError_t e) {
@@ -167,7 +183,8 @@ int twoshot_reduce(const ar_desc* d, void* scratch, void* out, int64_t out_strid
                    ar_epoch e, void* ctrl, uint64_t timeout_ns, int32_t flags,
                    hipStream_t s);
 int coll_sim_geometry(const ar_sim_params* p, int32_t* groups, int32_t* tiles,
-                      int32_t* tiles_per_group, int32_t* blocks, int32_t* wide);
+                      int32_t* tiles_per_group, int32_t* blocks, int32_t* wide,
+                      int32_t* cooperative);
 int coll_sim_run(const ar_sim_params* p, hipStream_t s);
 
 }  // namespace ar

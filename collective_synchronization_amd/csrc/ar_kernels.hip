@@ -881,6 +881,7 @@ static int sim_occupancy(int proto, int nranks, bool share, bool wide) {
 struct SimGeom {
   int32_t W, Q, T, TPW, blocks;
   bool wide;
+  bool coop;                 // cooperative launch
 };
 
 // The wide kernel (a workgroup of one wave per peer) serves LL, LL128 and
@@ -894,12 +895,12 @@ static bool sim_force_wide(const ar_sim_params* p) {
 }
 
 static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wide,
-                           SimGeom* g) {
+                           bool coop, SimGeom* g) {
   const ar_desc* d = &p->desc;
   const int64_t E = encoded_bytes(d->proto, d->count);
   const int64_t T = ceil_div64(E, kTileBytes);
   if (T <= 0) {
-    *g = SimGeom{0, 0, 0, 0, 0, wide};
+    *g = SimGeom{0, 0, 0, 0, 0, wide, coop};
     return AR_OK;
   }
   if (T > (int64_t(1) << 24)) return AR_ESIZE;
@@ -907,11 +908,13 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
   const int occ = sim_occupancy(d->proto, d->nranks, share, wide);
   if (occ <= 0) return AR_ELAUNCH;
   // Every workgroup waits on others, so the whole grid must be resident at
-  // once.  The grid is kept to half of what the occupancy query reports (a
-  // margin for limits the query does not model) and, for the one-wave
-  // kernel, to 8 workgroups per CU: the large sizes that use it are bound by
-  // memory bandwidth, which that many waves already saturate.
-  int64_t capacity = (int64_t)occ * di.cus / 2;
+  // once.  An ordinary launch keeps the grid to half of what the occupancy
+  // query reports (a margin for limits the query does not model); a
+  // cooperative launch, whose residency the runtime checks, may fill it.
+  // The one-wave kernel is held to 8 workgroups per CU: the large sizes that
+  // use it are bound by memory bandwidth, which that many waves already
+  // saturate.
+  int64_t capacity = (int64_t)occ * di.cus / (coop ? 1 : 2);
   if (!wide && capacity > 8 * (int64_t)di.cus) capacity = 8 * (int64_t)di.cus;
   const int64_t qmax_dev = capacity / (8 * (int64_t)d->nranks);
   const int64_t per_q = wide ? 8 : kSimWavesPerQ;   // tile groups / waves per Q
@@ -935,6 +938,7 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
   g->TPW = (int32_t)ceil_div64(T, W);
   g->blocks = (int32_t)(8 * Q * d->nranks);
   g->wide = wide;
+  g->coop = coop;
   return AR_OK;
 }
 
@@ -945,10 +949,11 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
 // wins everywhere (up to 2.6x); with two it wins at 8 and 16 ranks (up to
 // 1.7x) but loses up to 13% at 4 ranks, where one wave serves few peers;
 // from three tiles on, the one-wave kernel's larger resident grid wins.
-static int sim_geometry(const ar_sim_params* p, const DeviceInfo& di, SimGeom* g) {
+static int sim_kernel_choice(const ar_sim_params* p, const DeviceInfo& di, bool coop,
+                             SimGeom* g) {
   if (sim_is_wide(p)) {
     SimGeom gw;
-    const int rc = sim_geometry_as(p, di, true, &gw);
+    const int rc = sim_geometry_as(p, di, true, coop, &gw);
     const int max_tiles = p->desc.nranks > 4 ? 2 : 1;
     if (rc == AR_OK && (gw.TPW <= max_tiles || sim_force_wide(p))) {
       *g = gw;
@@ -957,7 +962,25 @@ static int sim_geometry(const ar_sim_params* p, const DeviceInfo& di, SimGeom* g
     if (sim_force_wide(p)) return rc;
     if (rc != AR_OK && rc != AR_ECAPACITY && rc != AR_EINVAL) return rc;
   }
-  return sim_geometry_as(p, di, false, g);
+  return sim_geometry_as(p, di, false, coop, g);
+}
+
+// Launch choice (coop_pays): measured, 64 ops, 16 ranks [1,4096] LL 4.19 ->
+// 3.23 us per op (2 -> 1 tiles per workgroup), 16 ranks [8,4096] LL 15.8 ->
+// 10.0 us, 4 ranks [1,131072] sentinel 3.53 -> 2.23 us (the workgroup kernel
+// instead of the one-wave kernel).
+static int sim_geometry(const ar_sim_params* p, const DeviceInfo& di, SimGeom* g) {
+  if (p->flags & AR_SIM_COOPERATIVE) return sim_kernel_choice(p, di, true, g);
+  const int rc = sim_kernel_choice(p, di, false, g);
+  if ((p->flags & AR_SIM_ORDINARY) || !di.coop || p->nops < kCoopMinOps) return rc;
+  if (rc != AR_OK && rc != AR_ECAPACITY) return rc;
+  SimGeom gc;
+  if (sim_kernel_choice(p, di, true, &gc) == AR_OK &&
+      coop_pays(rc, g->TPW, g->wide, gc.TPW, gc.wide)) {
+    *g = gc;
+    return AR_OK;
+  }
+  return rc;
 }
 
 static int check_sim(const ar_sim_params* p) {
@@ -967,9 +990,11 @@ static int check_sim(const ar_sim_params* p) {
   const ar_desc* d = &p->desc;
   if (p->nops < 1) return AR_EINVAL;
   if (p->waves_per_rank < 0) return AR_EINVAL;
-  if ((p->flags & ~(AR_SIM_COOPERATIVE | AR_SIM_NARROW | AR_SIM_WIDE)) != 0 ||
+  if ((p->flags & ~(AR_SIM_COOPERATIVE | AR_SIM_ORDINARY | AR_SIM_NARROW | AR_SIM_WIDE)) !=
+          0 ||
       p->reserved != 0)
     return AR_EINVAL;
+  if ((p->flags & AR_SIM_COOPERATIVE) && (p->flags & AR_SIM_ORDINARY)) return AR_EINVAL;
   if ((p->flags & AR_SIM_NARROW) && (p->flags & AR_SIM_WIDE)) return AR_EINVAL;
   if (p->epoch.parity > 1u || p->epoch.seq == 0u) return AR_EINVAL;
   rc = check_rows(p->in, p->in_stride, d->count);
@@ -1007,7 +1032,7 @@ const char* ar_status_string(int code) {
   }
 }
 
-int ar_abi_version(void) { return 3; }
+int ar_abi_version(void) { return 4; }
 
 int64_t ar_encoded_bytes(int32_t proto, int64_t count) {
   return encoded_bytes(proto, count);
@@ -1180,13 +1205,13 @@ int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
 
 int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
                     int32_t* tiles_per_rank, int32_t* tiles_per_wave,
-                    int32_t* blocks, int32_t* wide) {
+                    int32_t* blocks, int32_t* wide, int32_t* cooperative) {
   if (!p) return AR_EINVAL;
   int rc = check_desc(&p->desc);
   if (rc) return rc;
   if (p->desc.collective != AR_ALLREDUCE)
     return coll_sim_geometry(p, waves_per_rank, tiles_per_rank, tiles_per_wave, blocks,
-                             wide);
+                             wide, cooperative);
   DeviceInfo di;
   rc = device_info(&di);
   if (rc) return rc;
@@ -1198,6 +1223,7 @@ int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
   if (tiles_per_wave) *tiles_per_wave = g.TPW;
   if (blocks) *blocks = g.blocks;
   if (wide) *wide = g.wide ? 1 : 0;
+  if (cooperative) *cooperative = g.coop ? 1 : 0;
   return AR_OK;
 }
 
@@ -1211,11 +1237,11 @@ int ar_sim_run(const ar_sim_params* p, void* stream) {
   DeviceInfo di;
   rc = device_info(&di);
   if (rc) return rc;
-  const bool coop = (p->flags & AR_SIM_COOPERATIVE) != 0;
-  if (coop && !di.coop) return AR_ENODEV;
+  if ((p->flags & AR_SIM_COOPERATIVE) && !di.coop) return AR_ENODEV;
   SimGeom g;
   rc = sim_geometry(p, di, &g);
   if (rc) return rc;
+  const bool coop = g.coop;
   const bool share = d->nconsumers == 1 && d->nranks > 1;
   SimArgs a;
   a.in = static_cast<const uint16_t*>(p->in);

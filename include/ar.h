@@ -321,11 +321,17 @@ int ar_scale_rows(int32_t nranks, int64_t count, const void* in, int64_t in_stri
  * barrier (completion counter) per op, both global.
  *
  * Every wave of the grid must be resident at once (waves wait on each
- * other).  With AR_SIM_COOPERATIVE the runtime guarantees it; otherwise the
- * library checks the grid against the kernel's occupancy on the whole
- * device and uses an ordinary launch, which needs the device to be free of
- * other work for the duration (otherwise waits end in AR_ETIMEOUT, never in
- * a hang).
+ * other).  A cooperative launch (hipLaunchCooperativeKernel) has the runtime
+ * guarantee it, and its grid may fill the occupancy the runtime reports for
+ * the kernel on the whole device.  An ordinary launch keeps the grid to half
+ * of that and needs the device to be free of other work for the duration
+ * (otherwise waits end in AR_ETIMEOUT, never in a hang).  A cooperative
+ * launch costs about 15 us more, once per launch, on MI355X.  Launch mode:
+ *   AR_SIM_COOPERATIVE: cooperative (AR_ENODEV where unsupported);
+ *   AR_SIM_ORDINARY: ordinary;
+ *   neither: cooperative where the device supports it, nops >= 32 and its
+ *        larger grid lets each wave or workgroup walk fewer tiles or run the
+ *        workgroup kernel; ordinary otherwise.
  *
  * Buffers (device):
  *   in:  op i, rank r at in + (i*nranks + r)*in_stride elements.
@@ -365,6 +371,7 @@ int ar_scale_rows(int32_t nranks, int64_t count, const void* in, int64_t in_stri
  * in op i is armed again before any peer can get to op i+2 and write it.
  */
 #define AR_SIM_COOPERATIVE 1   /* launch with hipLaunchCooperativeKernel */
+#define AR_SIM_ORDINARY 8      /* an ordinary launch (never cooperative) */
 #define AR_SIM_NARROW 2        /* one wave per tile serving every peer, instead
                                   of a workgroup of one wave per peer */
 #define AR_SIM_WIDE 4          /* the workgroup-of-one-wave-per-peer kernel even
@@ -375,8 +382,9 @@ typedef struct {
     int32_t nops;               /* >= 1 */
     int32_t waves_per_rank;     /* tile groups (wide) or waves (narrow) per
                                    rank, a multiple of 8; 0 = library choice */
-    int32_t flags;              /* AR_SIM_COOPERATIVE | AR_SIM_NARROW or
-                                   AR_SIM_WIDE, or 0 (library choice) */
+    int32_t flags;              /* AR_SIM_COOPERATIVE or AR_SIM_ORDINARY,
+                                   | AR_SIM_NARROW or AR_SIM_WIDE; 0 =
+                                   library choice of both */
     int32_t reserved;           /* must be 0 */
     const void* in;
     int64_t in_stride;
@@ -396,13 +404,14 @@ int ar_sim_run(const ar_sim_params* p, void* stream);
 /*
  * Geometry ar_sim_run will use for these parameters: tile groups per rank
  * (a wave each in the narrow kernel, a workgroup each in the wide kernel),
- * tiles per rank (1 KiB of slot each), tiles per group, total workgroups and
+ * tiles per rank (1 KiB of slot each), tiles per group, total workgroups,
  * the kernel (1 = wide: a workgroup of one wave per peer; 0 = narrow: one
- * wave per tile serving every peer).  Any output pointer may be NULL.
+ * wave per tile serving every peer) and the launch (1 = cooperative, 0 =
+ * ordinary).  Any output pointer may be NULL.
  */
 int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
                     int32_t* tiles_per_rank, int32_t* tiles_per_wave,
-                    int32_t* blocks, int32_t* wide);
+                    int32_t* blocks, int32_t* wide, int32_t* cooperative);
 
 /* Wall-clock counter frequency of the current device in Hz. */
 int ar_wallclock_hz(double* hz);

@@ -36,7 +36,7 @@ def test_header_symbols_all_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert abi.raw().ar_abi_version() == 3
+    assert abi.raw().ar_abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert abi.status_string(code).startswith("AR_")
     assert abi.status_string(-99) == "AR_UNKNOWN"
@@ -144,10 +144,15 @@ def test_sim_argument_checks():
         kw.update(over)
         p = abi.sim_params(kw["desc"], kw["nops"], kw["inp"], kw["in_stride"], kw["out"],
                            kw["out_stride"], kw["scratch"], kw["ctrl"], kw["epoch"],
-                           waves_per_rank=kw.get("waves_per_rank", 0))
+                           waves_per_rank=kw.get("waves_per_rank", 0),
+                           flags=kw.get("flags", 0))
         return _code("ar_sim_run", ctypes.byref(p), None)
 
     assert run(nops=0) == abi.AR_EINVAL
+    # a launch is cooperative or ordinary, not both; no unknown flag bits
+    assert run(flags=abi.AR_SIM_COOPERATIVE | abi.AR_SIM_ORDINARY) == abi.AR_EINVAL
+    assert run(flags=16) == abi.AR_EINVAL
+    assert run(flags=abi.AR_SIM_NARROW | abi.AR_SIM_WIDE) == abi.AR_EINVAL
     assert run(ctrl=None) == abi.AR_EINVAL
     assert run(scratch=FAKE + 16) == abi.AR_EALIGN
     assert run(out=FAKE + 8) == abi.AR_EALIGN
@@ -256,7 +261,9 @@ def test_collective_sim_argument_checks():
     assert run(g8, flags=abi.AR_SIM_WIDE) == abi.AR_EINVAL      # kernel flags: two-shot only
     t8 = abi.make_desc(8, 4096, "sentinel", 8, "twoshot")
     assert run(t8, flags=abi.AR_SIM_WIDE | abi.AR_SIM_NARROW) == abi.AR_EINVAL
-    assert run(t8, flags=abi.AR_SIM_COOPERATIVE) == abi.AR_EINVAL
+    assert run(t8, flags=abi.AR_SIM_COOPERATIVE | abi.AR_SIM_ORDINARY) == abi.AR_EINVAL
+    assert run(g8, flags=abi.AR_SIM_COOPERATIVE | abi.AR_SIM_ORDINARY) == abi.AR_EINVAL
+    assert run(g8, flags=16) == abi.AR_EINVAL
 
 
 def test_epilogue_argument_checks():

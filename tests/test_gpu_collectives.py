@@ -175,6 +175,43 @@ def test_sim_allgather(proto, nranks, count, nops):
         assert np.all(ws.slot_view() == 0xFF)
 
 
+@pytest.mark.parametrize("collective,nranks,count", [("twoshot", 16, 65536 + 9),
+                                                     ("allgather", 8, 16384 + 3)])
+@pytest.mark.parametrize("proto", PROTOS)
+def test_sim_cooperative_launches(collective, nranks, count, proto):
+    """Forced cooperative launches (whose grid may fill the occupancy) and the
+    library's own choice over 32 ops, bit-exact against the oracle."""
+    nops = 32
+    ws = buffers.Workspace(nranks, count, proto, nranks, collective=collective)
+    x = _x(11 * count + nranks, (nops, nranks, count), specials=True)
+    xd, stride = buffers.rows_to_device(x)
+    ostride = ws.gather_stride() if collective == "allgather" else stride
+    outd = torch.zeros((nops * nranks, ostride), dtype=torch.int16, device="cuda")
+    for flags in (abi.AR_SIM_COOPERATIVE, 0):
+        seq0 = ws.epoch.seq
+        geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, ostride, flags=flags))
+        print(f"[coll-coop] {collective} {proto} N={nranks} count={count} flags={flags} "
+              f"geo={geo}", flush=True)
+        if flags:
+            assert geo["launch"] == "cooperative"
+        ws.sim(nops, xd, stride, outd, ostride, timeout_ns=TIMEOUT_NS, flags=flags)
+        torch.cuda.synchronize()
+        assert ws.status() == 0, abi.status_string(ws.status())
+        if collective == "allgather":
+            want = oracle.allgather_ops(x, proto, seq0)
+            got = outd.cpu().numpy().view(np.uint16).reshape(nops, nranks, nranks, stride)
+            for i in range(nops):
+                for c in range(nranks):
+                    assert np.array_equal(got[i, c, :, :count], want[i]), (flags, i, c)
+        else:
+            want = oracle.twoshot_ops(x, proto, seq0)
+            got = buffers.rows_from_device(outd, count, (nops, nranks))
+            for i in range(nops):
+                for c in range(nranks):
+                    assert np.array_equal(got[i, c], want[i]), (flags, i, c)
+        outd.zero_()
+
+
 @pytest.mark.parametrize("proto", PROTOS)
 def test_twoshot_n16_8x4096_skewed(proto):
     """16 ranks, bf16 [8,4096], 64 ops, seeded 0-20 us producer delays: every

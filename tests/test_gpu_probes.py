@@ -74,12 +74,22 @@ def test_copy_probe():
 
 
 @pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel", "barrier"])
-def test_sim_cooperative_launch(proto):
-    nranks, count, nops = 8, 4096, 6
+@pytest.mark.parametrize("nranks,count", [(8, 4096), (16, 4096), (16, 32768 + 3)])
+def test_sim_cooperative_launch(proto, nranks, count):
+    """A cooperative launch may fill the occupancy the runtime reports (an
+    ordinary one keeps half), so its grid is at least as large."""
+    nops = 6
     ws = buffers.Workspace(nranks, count, proto, nranks)
-    x = inputs.payload(77, (nops, nranks, count), "normal")
+    x = inputs.payload(77 + count, (nops, nranks, count), "normal")
     xd, stride = buffers.rows_to_device(x)
     outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    coop = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride,
+                                             flags=abi.AR_SIM_COOPERATIVE))
+    plain = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride))
+    print(f"[coop] {proto} N={nranks} count={count} coop={coop} plain={plain}", flush=True)
+    if coop["kernel"] == plain["kernel"]:
+        assert coop["blocks"] >= plain["blocks"]
+        assert coop["tiles_per_wave"] <= plain["tiles_per_wave"]
     ws.sim(nops, xd, stride, outd, stride, timeout_ns=2_000_000_000,
            flags=abi.AR_SIM_COOPERATIVE)
     torch.cuda.synchronize()
@@ -88,7 +98,33 @@ def test_sim_cooperative_launch(proto):
     want = oracle.allreduce_ops(x, proto)
     for i in range(nops):
         for c in range(nranks):
-            assert np.array_equal(got[i, c], want[i])
+            assert np.array_equal(got[i, c], want[i]), (i, c)
+
+
+def test_sim_launch_choice():
+    """Without a launch flag the library launches cooperatively when the
+    launch holds at least 32 ops and the cooperative grid lets each workgroup
+    walk fewer tiles (16 ranks, LL, [1,4096]: 2 tiles at half the occupancy,
+    1 at all of it); otherwise, or with AR_SIM_ORDINARY, ordinarily."""
+    nranks, count = 16, 4096
+    ws = buffers.Workspace(nranks, count, "ll", nranks)
+    xd = torch.zeros((64 * nranks, count), dtype=torch.int16, device="cuda")
+    outd = torch.zeros_like(xd)
+
+    def geo(nops, flags=0):
+        return abi.ar_sim_geometry(ws.sim_params(nops, xd, count, outd, count, flags=flags))
+
+    long_auto, short_auto = geo(64), geo(8)
+    forced_ord, forced_coop = geo(64, abi.AR_SIM_ORDINARY), geo(8, abi.AR_SIM_COOPERATIVE)
+    print(f"[launch] {long_auto} {short_auto} {forced_ord} {forced_coop}", flush=True)
+    assert short_auto["launch"] == "ordinary" and forced_ord["launch"] == "ordinary"
+    assert forced_coop["launch"] == "cooperative"
+    assert forced_coop["tiles_per_wave"] <= short_auto["tiles_per_wave"]
+    if forced_coop["tiles_per_wave"] < short_auto["tiles_per_wave"]:
+        assert long_auto["launch"] == "cooperative"
+        assert long_auto["tiles_per_wave"] == forced_coop["tiles_per_wave"]
+    else:
+        assert long_auto["launch"] == "ordinary"
 
 
 @pytest.mark.parametrize("blocks,threads", [(64, 512), (128, 1024), (2048, 64), (384, 512)])
