@@ -304,7 +304,9 @@ def sweep(ranks=(4, 8, 16), sizes=SIZES, protos=PROTOS, reps=7, collectives=COLL
                 E_max = 2 * s
                 if n * 2 * n * E_max >= (1 << 32):
                     continue
-                nops = 64 if s <= (256 << 10) else 16
+                # launches long enough for the library's cooperative-launch
+                # choice (at least 32 ops), as in a decode step
+                nops = 64 if s <= (256 << 10) else 32
                 for proto in protos:
                     if coll != "allreduce" and proto == "barrier":
                         continue
