@@ -838,13 +838,23 @@ static hipError_t launch_sim(const SimArgs& a, int blocks, bool coop, bool wide,
 template <int P, int NMAX, bool SHARE>
 static int occupancy_of(bool wide, int nranks) {
   int nb = 0;
-  // the two-tile variant holds the larger LDS array: its residency bounds both
-  const void* fn = wide ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 2>)
-                        : reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>);
-  const int threads = wide ? kWave * nranks : kSimBlock;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, 0) != hipSuccess)
+  if (!wide) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>), kSimBlock, 0) !=
+        hipSuccess)
+      return 0;
+    return nb;
+  }
+  // the smaller of the one- and two-tile variants (the launch picks either)
+  int n1 = 0, n2 = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n1, reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 1>), kWave * nranks,
+          0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n2, reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 2>), kWave * nranks,
+          0) != hipSuccess)
     return 0;
-  return nb;
+  return n1 < n2 ? n1 : n2;
 }
 
 template <int P>
@@ -942,19 +952,23 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
   return AR_OK;
 }
 
-// Kernel choice: the wide kernel when each of its workgroups owns one tile,
-// or two tiles above 4 ranks, or when AR_SIM_WIDE asks for it; otherwise,
-// or with AR_SIM_NARROW, or for the barrier baseline, the one-wave-per-tile
-// kernel.  Measured on MI355X: with one tile per workgroup the wide kernel
-// wins everywhere (up to 2.6x); with two it wins at 8 and 16 ranks (up to
-// 1.7x) but loses up to 13% at 4 ranks, where one wave serves few peers;
-// from three tiles on, the one-wave kernel's larger resident grid wins.
+// Kernel choice: the wide kernel while each of its workgroups walks at most
+// 3 tiles (4 ranks) or 2 (8 and 16 ranks), or when AR_SIM_WIDE asks for it;
+// otherwise, or with AR_SIM_NARROW, or for the barrier baseline, the
+// one-wave-per-tile kernel.  From a sweep of both kernels on MI355X (4, 8
+// and 16 ranks, 8-256 KiB per rank, 64 ops, ordinary and cooperative
+// launches): with one tile the wide kernel wins everywhere (up to 3.2x);
+// with two it wins everywhere (4 ranks 256 KiB sentinel: 3.11 vs 3.54 us;
+// 16 ranks 8 KiB LL128: 4.71 vs 8.11 us); with three it still wins at 4
+// ranks (256 KiB LL: 4.62 vs 4.73 us) but loses at 8 and 16 (8 ranks 64 KiB
+// LL128: 6.13 vs 5.45 us); from four on, the one-wave kernel wins (8 ranks
+// 128 KiB sentinel: 6.64 vs 5.05 us).
 static int sim_kernel_choice(const ar_sim_params* p, const DeviceInfo& di, bool coop,
                              SimGeom* g) {
   if (sim_is_wide(p)) {
     SimGeom gw;
     const int rc = sim_geometry_as(p, di, true, coop, &gw);
-    const int max_tiles = p->desc.nranks > 4 ? 2 : 1;
+    const int max_tiles = p->desc.nranks > 4 ? 2 : 3;
     if (rc == AR_OK && (gw.TPW <= max_tiles || sim_force_wide(p))) {
       *g = gw;
       return AR_OK;
