@@ -435,10 +435,13 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
 // there only after it has received this wave's reduce-scatter chunk of the
 // op in between; so the sentinel re-arms of an op (the wave's own, of the
 // slots it polled) complete before that licence is sent.
-template <int P, int NMAX>
+// BATCH: share tiles received, reduced and all-gathered per pair of
+// workgroup barriers (1 when every workgroup owns one tile, 2 otherwise; a
+// wave polls its peer's two chunks together).
+template <int P, int NMAX, int BATCH>
 __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
-  __shared__ u32x4 lds[NMAX][kWave];
-  __shared__ u32x4 red[kWave];
+  __shared__ u32x4 lds[BATCH][NMAX][kWave];
+  __shared__ u32x4 red[BATCH][kWave];
   __shared__ int lds_err;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
@@ -530,47 +533,81 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
     // this wave's stores (the fences above) also waits for it
     if (pipelined && op + 1 < a.nops)
       load_chunk<P>(row + (int64_t)a.nranks * a.in_stride + lo_mine, rb_mine, tg, lane, wnext);
-    // ---- 2. per tile: receive share g, reduce, send the reduced tile ----
-    for (int k = 0; k < mine; ++k) {
-      const int tile = tg + k * G;
-      const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+    // ---- 2. per BATCH tiles: receive share g, reduce, send reduced ----
+    for (int k0 = 0; k0 < mine; k0 += BATCH) {
+      const int nb = (mine - k0) < BATCH ? (mine - k0) : BATCH;
       if (!own) {
-        u32x4 got;
-        if (poll_chunk<P>(rs, rs_src + loff, loff < E_g, seq, stale, true, a.ctrl,
-                          a.timeout_ticks, lane, got) != 0) {
+        u32x4 got[BATCH];
+        int st;
+        if constexpr (BATCH == 1) {
+          const uint32_t loff = (uint32_t)(tg + k0 * G) * kTileBytes + (uint32_t)lane * 16u;
+          st = poll_chunk<P>(rs, rs_src + loff, loff < E_g, seq, stale, true, a.ctrl,
+                             a.timeout_ticks, lane, got[0]);
+        } else {
+          uint32_t at[BATCH];
+          bool act[BATCH];
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j) {
+            const uint32_t loff =
+                (uint32_t)(tg + (k0 + j) * G) * kTileBytes + (uint32_t)lane * 16u;
+            at[j] = rs_src + loff;
+            act[j] = j < nb && loff < E_g;
+          }
+          st = poll_chunks<P, BATCH>(rs, at, act, nb, seq, stale, true, a.ctrl,
+                                     a.timeout_ticks, lane, got);
+        }
+        if (st != 0) {
           if (lane == 0) lds_err = 1;
         } else {
-          lds[w][lane] = got;
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j)
+            if (j < nb) lds[j][w][lane] = got[j];
         }
       } else {
-        lds[g][lane] = pipelined ? mine_v
-                                 : encode_chunk<P>(row + lo_g, rb_g, m_g, tile, lane, seq);
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j)
+          if (j < nb)
+            lds[j][g][lane] =
+                pipelined ? mine_v
+                          : encode_chunk<P>(row + lo_g, rb_g, m_g, tg + (k0 + j) * G, lane, seq);
       }
       __syncthreads();
       if (lds_err) return;                         // whole workgroup
-      // fixed-order reduce of share g, tile t (own wave)
+      // fixed-order reduce of share g, tiles k0.. (own wave)
       if (own) {
-        u32x4 v[NMAX];
 #pragma unroll
-        for (int r = 0; r < NMAX; ++r)
-          v[r] = (r < a.nranks) ? lds[r][lane] : u32x4{0u, 0u, 0u, 0u};
-        uint32_t o[4];
-        reduce_words<P, NMAX>(v, a.nranks, o);
-        mask_words(o, chunk_keep<P>(m_g, tile, lane));
-        int64_t first;
-        int n;
-        lane_elems<P>(tile, lane, first, n);
-        if (loff < E_g) store_elems(orow + lo_g, m_g, first, n, o);
-        red[lane] = u32x4{o[0], o[1], o[2], o[3]};
+        for (int j = 0; j < BATCH; ++j) {
+          if (j >= nb) break;
+          const int tile = tg + (k0 + j) * G;
+          const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
+          u32x4 v[NMAX];
+#pragma unroll
+          for (int r = 0; r < NMAX; ++r)
+            v[r] = (r < a.nranks) ? lds[j][r][lane] : u32x4{0u, 0u, 0u, 0u};
+          uint32_t o[4];
+          reduce_words<P, NMAX>(v, a.nranks, o);
+          mask_words(o, chunk_keep<P>(m_g, tile, lane));
+          int64_t first;
+          int n;
+          lane_elems<P>(tile, lane, first, n);
+          if (loff < E_g) store_elems(orow + lo_g, m_g, first, n, o);
+          red[j][lane] = u32x4{o[0], o[1], o[2], o[3]};
+        }
       }
       __syncthreads();
       if (!own) {
-        const u32x4 r4 = red[lane];
-        const uint32_t o[4] = {r4.x, r4.y, r4.z, r4.w};
-        store_chunk<P>(rs, ag_dst, 0u, 1, -1, tile, E_g, lane, encode_words<P>(o, lane, seq));
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          if (j >= nb) break;
+          const u32x4 r4 = red[j][lane];
+          const uint32_t o[4] = {r4.x, r4.y, r4.z, r4.w};
+          store_chunk<P>(rs, ag_dst, 0u, 1, -1, tg + (k0 + j) * G, E_g, lane,
+                         encode_words<P>(o, lane, seq));
+        }
         if (P == kLL128) {
           fence_release();
-          produce_flags(rs, ag_dst, 0u, 1, -1, tile, E_g, seq, lane);
+          for (int j = 0; j < nb; ++j)
+            produce_flags(rs, ag_dst, 0u, 1, -1, tg + (k0 + j) * G, E_g, seq, lane);
         }
       }
     }
@@ -834,8 +871,9 @@ static const void* sim_fn(int collective, bool narrow, bool multi) {
       if (multi) return reinterpret_cast<const void*>(&k_sim_gather<P, NMAX, 4>);
     return reinterpret_cast<const void*>(&k_sim_gather<P, NMAX, 1>);
   }
-  return narrow ? reinterpret_cast<const void*>(&k_sim_twoshot_narrow<P, NMAX>)
-                : reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX>);
+  if (narrow) return reinterpret_cast<const void*>(&k_sim_twoshot_narrow<P, NMAX>);
+  return multi ? reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX, 2>)
+               : reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX, 1>);
 }
 
 template <int P>
