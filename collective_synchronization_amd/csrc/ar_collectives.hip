@@ -1078,9 +1078,22 @@ int coll_sim_run(const ar_sim_params* p, hipStream_t s) {
   void* args[] = {&a};
   const void* fn = coll_sim_fn(d->proto, d->collective, d->nranks, g.narrow, g.TPW > 1);
   const dim3 block(g.narrow ? kWave : kWave * d->nranks);
-  if (g.coop)
-    return map_hip(hipLaunchCooperativeKernel(fn, dim3(g.blocks), block, args, 0, s));
-  return map_hip(hipLaunchKernel(fn, dim3(g.blocks), block, args, 0, s));
+  if (!g.coop) return map_hip(hipLaunchKernel(fn, dim3(g.blocks), block, args, 0, s));
+  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(g.blocks), block, args, 0, s);
+  if (e == hipSuccess || (p->flags & AR_SIM_COOPERATIVE)) return map_hip(e);
+  // a cooperative launch the library chose by itself that the runtime turns
+  // down is retried as an ordinary launch on the ordinary grid
+  (void)hipGetLastError();
+  CollGeom go;
+  rc = coll_kernel_choice(p, di, false, &go);
+  if (rc) return rc;
+  a.W = go.W;
+  a.Q = go.Q;
+  a.T = go.T;
+  a.TPW = go.TPW;
+  const void* fo = coll_sim_fn(d->proto, d->collective, d->nranks, go.narrow, go.TPW > 1);
+  return map_hip(hipLaunchKernel(fo, dim3(go.blocks), dim3(go.narrow ? kWave : kWave * d->nranks),
+                                 args, 0, s));
 }
 
 // ----------------------------------------------------- stream-ordered host

@@ -1241,21 +1241,9 @@ int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
   return AR_OK;
 }
 
-int ar_sim_run(const ar_sim_params* p, void* stream) {
-  int rc = check_sim(p);
-  if (rc) return rc;
+static int sim_launch(const ar_sim_params* p, const DeviceInfo& di, const SimGeom& g,
+                      hipStream_t s) {
   const ar_desc* d = &p->desc;
-  if (d->collective != AR_ALLREDUCE)
-    return coll_sim_run(p, static_cast<hipStream_t>(stream));
-  if (d->count == 0) return AR_OK;
-  DeviceInfo di;
-  rc = device_info(&di);
-  if (rc) return rc;
-  if ((p->flags & AR_SIM_COOPERATIVE) && !di.coop) return AR_ENODEV;
-  SimGeom g;
-  rc = sim_geometry(p, di, &g);
-  if (rc) return rc;
-  const bool coop = g.coop;
   const bool share = d->nconsumers == 1 && d->nranks > 1;
   SimArgs a;
   a.in = static_cast<const uint16_t*>(p->in);
@@ -1285,15 +1273,41 @@ int ar_sim_run(const ar_sim_params* p, void* stream) {
   a.p_total = wt * (uint32_t)d->nranks;
   a.c_total = wt * (uint32_t)d->nconsumers;
   if ((uint64_t)a.p_total * (uint64_t)(p->nops + 1) >= 0xFFFFFFFFull) return AR_ESIZE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (d->proto) {
-    case kLL: e = dispatch_sim_p<kLL>(a, share, g.blocks, coop, g.wide, s); break;
-    case kLL128: e = dispatch_sim_p<kLL128>(a, share, g.blocks, coop, g.wide, s); break;
-    case kSentinel: e = dispatch_sim_p<kSentinel>(a, share, g.blocks, coop, g.wide, s); break;
-    default: e = dispatch_sim_p<kBarrier>(a, share, g.blocks, coop, g.wide, s); break;
+    case kLL: e = dispatch_sim_p<kLL>(a, share, g.blocks, g.coop, g.wide, s); break;
+    case kLL128: e = dispatch_sim_p<kLL128>(a, share, g.blocks, g.coop, g.wide, s); break;
+    case kSentinel: e = dispatch_sim_p<kSentinel>(a, share, g.blocks, g.coop, g.wide, s); break;
+    default: e = dispatch_sim_p<kBarrier>(a, share, g.blocks, g.coop, g.wide, s); break;
   }
   return map_hip(e);
+}
+
+int ar_sim_run(const ar_sim_params* p, void* stream) {
+  int rc = check_sim(p);
+  if (rc) return rc;
+  const ar_desc* d = &p->desc;
+  if (d->collective != AR_ALLREDUCE)
+    return coll_sim_run(p, static_cast<hipStream_t>(stream));
+  if (d->count == 0) return AR_OK;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  if ((p->flags & AR_SIM_COOPERATIVE) && !di.coop) return AR_ENODEV;
+  SimGeom g;
+  rc = sim_geometry(p, di, &g);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = sim_launch(p, di, g, s);
+  // A cooperative launch the library chose by itself that the runtime turns
+  // down is retried as an ordinary launch (same kernel choice rule, half the
+  // occupancy).  Not with a tile order: its shape follows the first geometry.
+  if (rc == AR_ELAUNCH && g.coop && !(p->flags & AR_SIM_COOPERATIVE) && !p->tile_order) {
+    (void)hipGetLastError();
+    SimGeom go;
+    if (sim_kernel_choice(p, di, false, &go) == AR_OK) rc = sim_launch(p, di, go, s);
+  }
+  return rc;
 }
 
 int ar_wallclock_hz(double* hz) {

@@ -331,7 +331,10 @@ int ar_scale_rows(int32_t nranks, int64_t count, const void* in, int64_t in_stri
  *   AR_SIM_ORDINARY: ordinary;
  *   neither: cooperative where the device supports it, nops >= 32 and its
  *        larger grid lets each wave or workgroup walk fewer tiles or run the
- *        workgroup kernel; ordinary otherwise.
+ *        workgroup kernel; ordinary otherwise.  If the runtime refuses such
+ *        a cooperative launch, the op runs as an ordinary launch instead
+ *        (not with a tile_order, whose shape follows the first geometry:
+ *        then the error is returned).
  *
  * Buffers (device):
  *   in:  op i, rank r at in + (i*nranks + r)*in_stride elements.
