@@ -159,8 +159,17 @@ __device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
 // polled, and this op's output is stored after the next op's stores are
 // out, so neither input load nor output store sits between one op's
 // validation and the next op's transmission.
-template <int P, int NMAX, bool SHARE>
+// EXTRAS: the launch uses producer delays, a tile order or a trace.  The
+// variant without them drops those paths at compile time: less code and
+// fewer scalar registers in the op loop (8 ranks [1,4096]: 4.5% faster per
+// op in the workgroup kernel, 9% at 16 ranks).
+template <int P, int NMAX, bool SHARE, bool EXTRAS>
 __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
+  if constexpr (!EXTRAS) {
+    a.delay = nullptr;
+    a.order = nullptr;
+    a.trace = nullptr;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int b = blockIdx.x;
@@ -375,8 +384,14 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
 // Placement: workgroup (g, tg) sits on XCD (s + tg + rot(g)) mod 8 as in k_sim.
 // BATCH: tiles received per workgroup barrier (1 when every workgroup owns a
 // single tile, 2 otherwise; the two chunks of a peer are polled together).
-template <int P, int NMAX, bool SHARE, int BATCH>
+// EXTRAS: as for k_sim.
+template <int P, int NMAX, bool SHARE, int BATCH, bool EXTRAS>
 __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
+  if constexpr (!EXTRAS) {
+    a.delay = nullptr;
+    a.order = nullptr;
+    a.trace = nullptr;
+  }
   __shared__ u32x4 lds[2][BATCH][NMAX][kWave];
   __shared__ int lds_err;
   const int lane = threadIdx.x & (kWave - 1);
@@ -821,40 +836,43 @@ static hipError_t launch_reduce_n(const ReduceArgs& a, int blocks, hipStream_t s
   return launch_reduce<P, 16>(a, blocks, s);
 }
 
+template <int P, int NMAX, bool SHARE, bool EXTRAS>
+static const void* sim_kernel(bool wide, int tpw) {
+  if (!wide) return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS>);
+  return tpw <= 1 ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 1, EXTRAS>)
+                  : reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 2, EXTRAS>);
+}
+
 template <int P, int NMAX, bool SHARE>
 static hipError_t launch_sim(const SimArgs& a, int blocks, bool coop, bool wide,
                              hipStream_t s) {
   SimArgs copy = a;
   void* args[] = {&copy};
-  const void* fn =
-      !wide ? reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>)
-      : a.TPW <= 1 ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 1>)
-                   : reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 2>);
+  const bool extras = a.delay || a.order || a.trace;
+  const void* fn = extras ? sim_kernel<P, NMAX, SHARE, true>(wide, a.TPW)
+                          : sim_kernel<P, NMAX, SHARE, false>(wide, a.TPW);
   const dim3 block(wide ? kWave * a.nranks : kSimBlock);
   if (coop) return hipLaunchCooperativeKernel(fn, dim3(blocks), block, args, 0, s);
   return hipLaunchKernel(fn, dim3(blocks), block, args, 0, s);
 }
 
+// The smallest occupancy of the variants the launch may pick (one or two
+// tiles per workgroup, with or without the optional features).
 template <int P, int NMAX, bool SHARE>
 static int occupancy_of(bool wide, int nranks) {
-  int nb = 0;
-  if (!wide) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE>), kSimBlock, 0) !=
-        hipSuccess)
+  const void* fns[4] = {sim_kernel<P, NMAX, SHARE, false>(wide, 1),
+                        sim_kernel<P, NMAX, SHARE, false>(wide, 2),
+                        sim_kernel<P, NMAX, SHARE, true>(wide, 1),
+                        sim_kernel<P, NMAX, SHARE, true>(wide, 2)};
+  const int threads = wide ? kWave * nranks : kSimBlock;
+  int occ = 0;
+  for (int i = 0; i < 4; ++i) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fns[i], threads, 0) != hipSuccess)
       return 0;
-    return nb;
+    occ = (i == 0 || n < occ) ? n : occ;
   }
-  // the smaller of the one- and two-tile variants (the launch picks either)
-  int n1 = 0, n2 = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n1, reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 1>), kWave * nranks,
-          0) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n2, reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 2>), kWave * nranks,
-          0) != hipSuccess)
-    return 0;
-  return n1 < n2 ? n1 : n2;
+  return occ;
 }
 
 template <int P>
