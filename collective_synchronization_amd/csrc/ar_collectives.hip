@@ -289,8 +289,12 @@ __device__ __forceinline__ bool sim_place(const CollSimArgs& a, int& g, int& tg)
 // wave writes its own row.  One workgroup barrier per op: a rank starts op
 // i+1 once it holds all of op i.  TB: tiles whose input loads overlap when a
 // wave walks several (1: one load, then its stores, at a time).
-template <int P, int NMAX, int TB>
+template <int P, int NMAX, int TB, bool EXTRAS>
 __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
+  if constexpr (!EXTRAS) {
+    a.delay = nullptr;
+    a.trace = nullptr;
+  }
   __shared__ int lds_err;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
@@ -438,8 +442,12 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
 // BATCH: share tiles received, reduced and all-gathered per pair of
 // workgroup barriers (1 when every workgroup owns one tile, 2 otherwise; a
 // wave polls its peer's two chunks together).
-template <int P, int NMAX, int BATCH>
+template <int P, int NMAX, int BATCH, bool EXTRAS>
 __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
+  if constexpr (!EXTRAS) {
+    a.delay = nullptr;
+    a.trace = nullptr;
+  }
   __shared__ u32x4 lds[BATCH][NMAX][kWave];
   __shared__ u32x4 red[BATCH][kWave];
   __shared__ int lds_err;
@@ -737,8 +745,12 @@ __device__ __forceinline__ int poll_shares(rsrc_t rs, uint32_t src0, uint32_t sl
 // so the dual-buffer licences of the wide two-shot kernel hold pairwise:
 // each reduce-scatter send is preceded by a wait for the wave's own earlier
 // stores (the sentinel re-arms among them).
-template <int P, int NMAX>
+template <int P, int NMAX, bool EXTRAS>
 __global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
+  if constexpr (!EXTRAS) {
+    a.delay = nullptr;
+    a.trace = nullptr;
+  }
   const int lane = threadIdx.x;
   int g, tg;
   if (!sim_place(a, g, tg)) return;
@@ -864,31 +876,40 @@ __global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
 // ranks, 1 MiB: 56.7 -> 52.5 us); LL and LL128 measured no gain (LL: 8
 // ranks, 1 MiB, 93 -> 106 us).  With one tile per wave the plain kernel is
 // up to 7% faster.  The grid is sized by the smaller occupancy of the two.
-template <int P, int NMAX>
-static const void* sim_fn(int collective, bool narrow, bool multi) {
+// EXTRAS: the launch uses producer delays or a trace; the variant without
+// them drops those paths at compile time (as for the all-reduce simulators).
+template <int P, int NMAX, bool EXTRAS>
+static const void* sim_fn_x(int collective, bool narrow, bool multi) {
   if (collective == AR_ALLGATHER) {
     if constexpr (P == kSentinel)
-      if (multi) return reinterpret_cast<const void*>(&k_sim_gather<P, NMAX, 4>);
-    return reinterpret_cast<const void*>(&k_sim_gather<P, NMAX, 1>);
+      if (multi) return reinterpret_cast<const void*>(&k_sim_gather<P, NMAX, 4, EXTRAS>);
+    return reinterpret_cast<const void*>(&k_sim_gather<P, NMAX, 1, EXTRAS>);
   }
-  if (narrow) return reinterpret_cast<const void*>(&k_sim_twoshot_narrow<P, NMAX>);
-  return multi ? reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX, 2>)
-               : reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX, 1>);
+  if (narrow) return reinterpret_cast<const void*>(&k_sim_twoshot_narrow<P, NMAX, EXTRAS>);
+  return multi ? reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX, 2, EXTRAS>)
+               : reinterpret_cast<const void*>(&k_sim_twoshot<P, NMAX, 1, EXTRAS>);
+}
+
+template <int P, int NMAX>
+static const void* sim_fn(int collective, bool narrow, bool multi, bool extras) {
+  return extras ? sim_fn_x<P, NMAX, true>(collective, narrow, multi)
+                : sim_fn_x<P, NMAX, false>(collective, narrow, multi);
 }
 
 template <int P>
-static const void* sim_fn_n(int collective, int nranks, bool narrow, bool multi) {
-  if (nranks <= 4) return sim_fn<P, 4>(collective, narrow, multi);
-  if (nranks <= 8) return sim_fn<P, 8>(collective, narrow, multi);
-  return sim_fn<P, 16>(collective, narrow, multi);
+static const void* sim_fn_n(int collective, int nranks, bool narrow, bool multi,
+                            bool extras) {
+  if (nranks <= 4) return sim_fn<P, 4>(collective, narrow, multi, extras);
+  if (nranks <= 8) return sim_fn<P, 8>(collective, narrow, multi, extras);
+  return sim_fn<P, 16>(collective, narrow, multi, extras);
 }
 
 static const void* coll_sim_fn(int proto, int collective, int nranks, bool narrow,
-                               bool multi) {
+                               bool multi, bool extras) {
   switch (proto) {
-    case kLL: return sim_fn_n<kLL>(collective, nranks, narrow, multi);
-    case kLL128: return sim_fn_n<kLL128>(collective, nranks, narrow, multi);
-    default: return sim_fn_n<kSentinel>(collective, nranks, narrow, multi);
+    case kLL: return sim_fn_n<kLL>(collective, nranks, narrow, multi, extras);
+    case kLL128: return sim_fn_n<kLL128>(collective, nranks, narrow, multi, extras);
+    default: return sim_fn_n<kSentinel>(collective, nranks, narrow, multi, extras);
   }
 }
 
@@ -947,13 +968,15 @@ static int coll_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool n
     return AR_OK;
   }
   if (T > (int64_t(1) << 24)) return AR_ESIZE;
-  // the smaller occupancy of the two kernels the launch may pick (one tile
-  // per wave or several), so that either is resident on this grid
+  // the smallest occupancy of the kernels the launch may pick (one tile per
+  // wave or several, with or without delays and trace), so that any of them
+  // is resident on this grid
   int occ = 0;
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < 4; ++m) {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &o, coll_sim_fn(d->proto, d->collective, d->nranks, narrow, m == 1),
+            &o, coll_sim_fn(d->proto, d->collective, d->nranks, narrow, (m & 1) != 0,
+                            (m & 2) != 0),
             narrow ? kWave : kWave * d->nranks, 0) != hipSuccess ||
         o <= 0)
       return AR_ELAUNCH;
@@ -1076,7 +1099,9 @@ int coll_sim_run(const ar_sim_params* p, hipStream_t s) {
   a.delay = p->delay_ticks;
   a.trace = p->trace;
   void* args[] = {&a};
-  const void* fn = coll_sim_fn(d->proto, d->collective, d->nranks, g.narrow, g.TPW > 1);
+  const bool extras = a.delay || a.trace;
+  const void* fn =
+      coll_sim_fn(d->proto, d->collective, d->nranks, g.narrow, g.TPW > 1, extras);
   const dim3 block(g.narrow ? kWave : kWave * d->nranks);
   if (!g.coop) return map_hip(hipLaunchKernel(fn, dim3(g.blocks), block, args, 0, s));
   const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(g.blocks), block, args, 0, s);
@@ -1091,7 +1116,8 @@ int coll_sim_run(const ar_sim_params* p, hipStream_t s) {
   a.Q = go.Q;
   a.T = go.T;
   a.TPW = go.TPW;
-  const void* fo = coll_sim_fn(d->proto, d->collective, d->nranks, go.narrow, go.TPW > 1);
+  const void* fo =
+      coll_sim_fn(d->proto, d->collective, d->nranks, go.narrow, go.TPW > 1, extras);
   return map_hip(hipLaunchKernel(fo, dim3(go.blocks), dim3(go.narrow ? kWave : kWave * d->nranks),
                                  args, 0, s));
 }
