@@ -265,8 +265,10 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
             a.out + ((int64_t)(op - 1) * a.nconsumers + cself) * a.out_stride, a.count);
         out_pending = false;
       }
-      if (op + 1 < a.nops)
-        load_chunk<P>(row + op_rows * a.in_stride, row_bytes, wr, lane, wnext);
+      // unconditional: past the last op the range is empty and the load
+      // reads nothing, so the loaded registers need no merge (and no wait)
+      load_chunk<P>(row + op_rows * a.in_stride, op + 1 < a.nops ? row_bytes : 0u, wr, lane,
+                    wnext);
     } else {
       const uint16_t* ord =
           a.order ? a.order + ((int64_t)op * a.nranks + g) * a.TPW : nullptr;
@@ -406,7 +408,8 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
   const int tg = qq * 8 + ((x - rot) & 7);
   if (tg >= a.T) return;                           // whole workgroup
   const int G = a.W;
-  const int mine = (a.T - 1 - tg) / G + 1;
+  // the one-tile variant is launched only when every group owns one tile
+  const int mine = BATCH == 1 ? 1 : (a.T - 1 - tg) / G + 1;
   const bool consumer = SHARE ? (g == 0) : true;
   if (!consumer && w != 0) return;                 // producer-only rank: one wave
   const int cself = SHARE ? 0 : g;
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
   uint32_t* const progress = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlProgress;
   const int tstride = 2 * a.nranks;
   const int64_t op_rows = a.nranks;
-  const bool pipelined = mine == 1;
+  const bool pipelined = BATCH == 1 || mine == 1;
   if (threadIdx.x == 0) lds_err = 0;
   if (consumer) __syncthreads();
 
@@ -528,8 +531,11 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
       }
       // the next op's payload is loaded after this op's sends, so that no
       // wait for this wave's stores (the fences above) also waits for it
-      if (pipelined && op + 1 < a.nops)
-        load_chunk<P>(row + op_rows * a.in_stride, row_bytes, tg, lane, wnext);
+      // unconditional for the op: past the last op the range is empty and the
+      // load reads nothing, so the loaded registers need no merge (and no wait)
+      if (pipelined)
+        load_chunk<P>(row + op_rows * a.in_stride, op + 1 < a.nops ? row_bytes : 0u, tg, lane,
+                      wnext);
     }
     if (!consumer) {
       seq = seq_next(seq);
