@@ -378,7 +378,9 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
 // them tile by tile: validated chunks are staged in LDS (double-buffered by
 // tile iteration) and, after one workgroup barrier, the wave of the rank
 // itself (the "own" wave, whose contribution never leaves registers when
-// the group holds one tile) reduces in fixed rank order.
+// the group holds one tile) reduces in fixed rank order.  With one tile per
+// group in system mode, LL, a wave instead sends the next op right after its
+// own receive, before that barrier (the first loop below).
 // Sentinel: the wave that re-arms peer w's slot is the wave that next sends
 // to peer w, so waiting for its own stores orders re-arm before refill.
 // Share mode: only rank 0 consumes; a producer rank's workgroup keeps its
@@ -446,6 +448,88 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
   const int keep = chunk_keep<P>(a.count, tg, lane);
   if (pipelined && needs_input)
     load_chunk<P>(a.in + (int64_t)g * a.in_stride, row_bytes, tg, lane, wnext);
+
+  // One tile per group in system mode, LL: wave w sends op i+1 to peer w as
+  // soon as its own poll has validated peer w's op i, before the workgroup
+  // barrier of op i.  Peer w sent op i only after it had consumed this
+  // rank's op i-1, so the slot of op i+1's parity is free: the licence is
+  // pairwise and needs no barrier, and the send overlaps the wait for the
+  // other peers.  The sentinel and LL128 keep the general loop below: their
+  // waits before a send (re-arm stores, data before flags) would then hold
+  // every wave on its way to the barrier.  (A separate loop: folding this
+  // order into the general one made the compiler spill scalar registers.)
+  if constexpr (BATCH == 1 && !SHARE && P == kLL) {
+    uint32_t seq = a.seq0;
+    uint32_t par = a.parity0;
+    int buf = 0;
+    u32x4 own0 = u32x4{0u, 0u, 0u, 0u};   // encoded own chunk, for the stager
+    // the send of op `opn` (epoch sq, buffer parity pr), then the load of
+    // op opn+1's payload (an empty range past the last op)
+    auto send_op = [&](int opn, uint32_t sq, uint32_t pr) {
+      if (sender && a.delay) {
+        const uint32_t d = a.delay[(int64_t)opn * a.nranks + g];
+        if (d) {
+          const uint64_t t0 = now_ticks();
+          while (now_ticks() - t0 < (uint64_t)d) __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      if (!(sender || (own && own_stages))) return;
+      mask_words(wnext, keep);
+      own0 = encode_words<P>(wnext, lane, sq);
+      if (sender) {
+        const uint32_t dst0 = ((uint32_t)dst_c * 2u * N + pr * N + (uint32_t)g) * a.slot_bytes;
+        store_chunk<P>(rs, dst0, 0u, 1, -1, tg, a.E, lane, own0);
+        if (a.trace) {
+          fence_release();
+          if (lane == 0)
+            __hip_atomic_fetch_max(
+                reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)opn * tstride + g,
+                (unsigned long long)now_ticks(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      const uint16_t* next = a.in + ((int64_t)(opn + 1) * op_rows + g) * a.in_stride;
+      load_chunk<P>(next, opn + 1 < a.nops ? row_bytes : 0u, tg, lane, wnext);
+    };
+    send_op(0, seq, par);
+    for (int op = 0; op < a.nops; ++op) {
+      const uint32_t stale = seq_prev(seq_prev(seq));
+      const uint32_t src0 = ((uint32_t)cself * 2u * N + par * N) * a.slot_bytes;
+      int st = 0;
+      if (poller) {
+        const uint32_t loff = (uint32_t)tg * kTileBytes + (uint32_t)lane * 16u;
+        u32x4 got;
+        st = poll_chunk<P>(rs, src0 + (uint32_t)w * a.slot_bytes + loff, loff < a.E, seq, stale,
+                           true, a.ctrl, a.timeout_ticks, lane, got);
+        if (st != 0) {
+          if (lane == 0) lds_err = 1;
+        } else {
+          lds[buf][0][w][lane] = got;
+        }
+      }
+      if (stager) lds[buf][0][g][lane] = own0;
+      if (st == 0 && op + 1 < a.nops) send_op(op + 1, seq_next(seq), par ^ 1u);
+      __syncthreads();
+      if (lds_err) return;                         // whole workgroup
+      if (own) {
+        u32x4 v[NMAX];
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r)
+          v[r] = (r < a.nranks) ? lds[buf][0][r][lane] : u32x4{0u, 0u, 0u, 0u};
+        reduce_store_tile<P, NMAX>(v, a.nranks, tg, a.E, lane,
+                                   a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride,
+                                   a.count);
+        if (a.trace && lane == 0)
+          __hip_atomic_fetch_max(
+              reinterpret_cast<unsigned long long*>(a.trace) + (int64_t)op * tstride +
+                  a.nranks + cself,
+              (unsigned long long)now_ticks(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      buf ^= 1;
+      seq = seq_next(seq);
+      par ^= 1u;
+    }
+    return;
+  }
 
   uint32_t seq = a.seq0;
   uint32_t par = a.parity0;
