@@ -114,31 +114,72 @@ def _score(pts, entries):
     return worst, sq
 
 
+def _candidates(points, coll, n, max_ranges):
+    """Every admissible split of one (collective, rank count): a list of
+    (worst protocol regret, number of cuts, squared error, entries)."""
+    pts = _pts(points, coll, n)
+    sizes = sorted({p["bytes"] for p in pts})
+    cands = [()]
+    if max_ranges >= 2:
+        cands += [(c,) for c in sizes[1:-2]]
+    out = []
+    for cuts in cands:
+        ent = _fit_ranges(pts, coll, n, cuts)
+        worst, sq = _score(pts, ent)
+        out.append((worst, len(cuts), sq, ent))
+    return pts, out
+
+
+def _algorithm_regret(pts_one, pts_two, ent_one, ent_two):
+    """Worst measured regret of the one-shot / two-shot choice (the rule of
+    select_allreduce_py) over the sizes measured for both."""
+    worst = 1.0
+    sizes = sorted({p["bytes"] for p in pts_one} & {p["bytes"] for p in pts_two})
+    for s in sizes:
+        meas = {("allreduce", p["proto"]): p["us"] for p in pts_one if p["bytes"] == s}
+        meas.update({("twoshot", p["proto"]): p["us"] for p in pts_two if p["bytes"] == s})
+        p1, t1 = argmin_py(_range_entry(ent_one, s), s)
+        p2, t2 = argmin_py(_range_entry(ent_two, s), s)
+        key = ("twoshot", PROTOS[p2]) if (p2 >= 0 and t2 < t1) else ("allreduce", PROTOS[p1])
+        if key in meas:
+            worst = max(worst, meas[key] / min(meas.values()))
+    return worst
+
+
 def fit_table(points, max_ranges=2):
     """points: list of {collective?, nranks, proto, bytes, us} (collective
     defaults to the one-shot all-reduce).  Returns table entries.
 
     Per collective and rank count, one alpha-beta line per protocol over the
-    whole sweep, or, with max_ranges=2, two lines split at the measured size
-    that gives the lowest worst-case regret on the measured points (ties: one
-    range, then the smaller squared relative error).  Each range holds at
-    least two measured sizes."""
+    whole sweep, or, with max_ranges=2, two lines split at a measured size
+    (each range holds at least two measured sizes).  The split is the one
+    with the lowest worst-case regret on the measured points (ties: one
+    range, then the smaller squared relative error).  Where a rank count has
+    both one-shot and two-shot points, their two splits are chosen together,
+    and the regret also counts the choice between the two algorithms."""
+    def ranks(coll):
+        return sorted({p["nranks"] for p in points if _coll(p) == coll})
+
     entries = []
     for coll in COLLECTIVES:
-        for n in sorted({p["nranks"] for p in points if _coll(p) == coll}):
-            pts = _pts(points, coll, n)
-            sizes = sorted({p["bytes"] for p in pts})
-            best = None
-            cands = [()]
-            if max_ranges >= 2:
-                cands += [(c,) for c in sizes[1:-2]]
-            for cuts in cands:
-                ent = _fit_ranges(pts, coll, n, cuts)
-                worst, sq = _score(pts, ent)
-                key = (round(worst, 9), len(cuts), sq)
-                if best is None or key < best[0]:
-                    best = (key, ent)
-            entries.extend(best[1])
+        for n in ranks(coll):
+            joint = n in ranks("allreduce") and n in ranks("twoshot")
+            if coll == "twoshot" and joint:
+                continue                         # chosen with the one-shot
+            if coll == "allreduce" and joint:
+                p_one, c_one = _candidates(points, "allreduce", n, max_ranges)
+                p_two, c_two = _candidates(points, "twoshot", n, max_ranges)
+                best = None
+                for w1, k1, q1, e1 in c_one:
+                    for w2, k2, q2, e2 in c_two:
+                        worst = max(w1, w2, _algorithm_regret(p_one, p_two, e1, e2))
+                        key = (round(worst, 9), k1 + k2, q1 + q2)
+                        if best is None or key < best[0]:
+                            best = (key, e1 + e2)
+                entries.extend(best[1])
+            else:
+                _, c = _candidates(points, coll, n, max_ranges)
+                entries.extend(min(c, key=lambda t: (round(t[0], 9), t[1], t[2]))[3])
     return entries
 
 

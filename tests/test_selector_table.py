@@ -186,3 +186,45 @@ def test_fit_chooses_two_shot_past_the_crossover():
     table = abi.cost_table(entries)
     assert abi.ar_select_allreduce(table, 2048, 16)[:2] == (abi.AR_ALLREDUCE, abi.AR_LL)
     assert abi.ar_select_allreduce(table, 1 << 20, 16)[:2] == (abi.AR_TWOSHOT, abi.AR_LL)
+
+
+def _kinked_sweep(rng, n=8):
+    """One-shot: flat latency that turns steep past a random size; two-shot:
+    a higher floor with a gentler slope; LL, LL128 and sentinel scaled
+    copies with noise.  Random shapes, one rank count."""
+    pts = []
+    kink = 2 ** int(rng.integers(12, 18))
+    a1, b1, b1k = rng.uniform(1.0, 1.6), rng.uniform(1e-6, 5e-6), rng.uniform(2e-5, 8e-5)
+    a2, b2 = rng.uniform(2.5, 4.0), rng.uniform(5e-6, 1.2e-5)
+    for s in selector.SIZES:
+        one = a1 + b1 * s + (b1k * (s - kink) if s > kink else 0.0)
+        two = a2 + b2 * s
+        for proto, k in (("ll", rng.uniform(0.9, 1.2)), ("ll128", 1.4), ("sentinel", 1.0)):
+            pts.append({"collective": "allreduce", "nranks": n, "proto": proto, "bytes": s,
+                        "us": one * k * rng.uniform(0.97, 1.03)})
+            pts.append({"collective": "twoshot", "nranks": n, "proto": proto, "bytes": s,
+                        "us": two * k * rng.uniform(0.97, 1.03)})
+        pts.append({"collective": "allreduce", "nranks": n, "proto": "barrier", "bytes": s,
+                    "us": 3 * one})
+    return pts
+
+
+def test_joint_split_never_worse_than_separate_splits():
+    """The one-shot and two-shot size splits of a rank count are chosen
+    together: the worst regret over the protocol and algorithm choices is
+    never above that of splits chosen for each collective alone, and on some
+    sweeps it is strictly lower."""
+    rng = np.random.default_rng(31)
+    better = 0
+    for _ in range(12):
+        pts = _kinked_sweep(rng)
+        joint = selector.fit_table(pts)
+        sep = []
+        for coll in ("allreduce", "twoshot"):
+            _, cands = selector._candidates(pts, coll, 8, 2)
+            sep += min(cands, key=lambda t: (round(t[0], 9), t[1], t[2]))[3]
+        wj = max(r["regret"] for r in selector.regret(pts, joint))
+        ws = max(r["regret"] for r in selector.regret(pts, sep))
+        assert wj <= ws + 1e-12
+        better += wj < ws - 1e-9
+    assert better >= 1
