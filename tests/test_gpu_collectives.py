@@ -175,6 +175,53 @@ def test_sim_allgather(proto, nranks, count, nops):
         assert np.all(ws.slot_view() == 0xFF)
 
 
+LARGEST = [("twoshot", 8, 1 << 21), ("twoshot", 16, 1 << 20),
+           ("allgather", 8, 1 << 19), ("allgather", 16, 1 << 19)]
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("collective,nranks,count", LARGEST)
+def test_sim_largest_sweep_sizes(collective, proto, nranks, count):
+    """The two-shot and the all-gather at the largest sizes the selector
+    sweep measures (two-shot: 4 MiB per rank at 8 ranks, 2 MiB at 16;
+    all-gather: 1 MiB), with the sweep's 32 ops per launch, so in the
+    launch the library picks there: every consumer bit-exact on the first,
+    a middle and the last op (the other ops carry zero payloads)."""
+    nops = 32
+    sample = (0, nops // 2, nops - 1)
+    ws = buffers.Workspace(nranks, count, proto, nranks, collective=collective)
+    x = np.zeros((nops, nranks, count), dtype=np.uint16)
+    for i in sample:
+        x[i] = _x(11 * i + nranks + count, (nranks, count))
+    xd, stride = buffers.rows_to_device(x)
+    ostride = ws.gather_stride() if collective == "allgather" else stride
+    outd = torch.zeros((nops * nranks, ostride), dtype=torch.int16, device="cuda")
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, ostride))
+    print(f"[largest] {collective} {proto} N={nranks} count={count} geo={geo}", flush=True)
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, ostride, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    seqs = [seq0]
+    for _ in range(nops - 1):
+        seqs.append(oracle.epoch_next(seqs[-1]))
+    for i in sample:
+        rows = outd[i * nranks:(i + 1) * nranks].cpu().numpy().view(np.uint16)
+        if collective == "twoshot":
+            st, want = oracle.twoshot(x[i], proto, seqs[i])
+            assert st == oracle.READY
+            for c in range(nranks):
+                assert np.array_equal(rows[c, :count], want), (i, c)
+        else:
+            st, want = oracle.allgather(x[i], proto, seqs[i])
+            assert st == oracle.READY
+            got = rows.reshape(nranks, nranks, stride)
+            for c in range(nranks):
+                assert np.array_equal(got[c, :, :count], want), (i, c)
+    if proto == "sentinel":
+        assert np.all(ws.slot_view() == 0xFF)
+
+
 @pytest.mark.parametrize("collective,nranks,count", [("twoshot", 16, 65536 + 9),
                                                      ("allgather", 8, 16384 + 3)])
 @pytest.mark.parametrize("proto", PROTOS)
