@@ -369,9 +369,10 @@ int ar_scale_rows(int32_t nranks, int64_t count, const void* in, int64_t in_stri
  *        tile group serving every peer (AR_SIM_NARROW); without either flag
  *        the library picks by rank count, protocol and share tiles per
  *        workgroup.
- * Every wave waits for its own earlier stores (the sentinel re-arms among
+ * SENTINEL: every wave waits for its own earlier stores (its re-arms among
  * them) before the first send of each op, so every slot this wave re-armed
  * in op i is armed again before any peer can get to op i+2 and write it.
+ * LL and LL128 consumers only read their slots and need no such wait.
  */
 #define AR_SIM_COOPERATIVE 1   /* launch with hipLaunchCooperativeKernel */
 #define AR_SIM_ORDINARY 8      /* an ordinary launch (never cooperative) */
