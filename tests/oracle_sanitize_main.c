@@ -1,7 +1,7 @@
 /*
  * Host-side sanitizer driver for the C oracle (oracle/ar_oracle.c).
  *
- * Built by tests/test_oracle_sanitize.py with gcc's AddressSanitizer and
+ * Built by tests/test_host_sanitize.py with gcc's AddressSanitizer and
  * UndefinedBehaviorSanitizer (no recovery): every oracle entry point runs on
  * small, ragged and degenerate shapes, every protocol, with inputs that mix
  * random bf16 with the special values the protocols treat specially.  Every

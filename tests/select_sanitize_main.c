@@ -1,0 +1,177 @@
+/*
+ * Host-side sanitizer driver for the library's cost-table selector
+ * (collective_synchronization_amd/csrc/ar_select.cpp, declared in
+ * include/ar.h).  Built by tests/test_host_sanitize.py with gcc/g++ and
+ * AddressSanitizer + UndefinedBehaviorSanitizer.
+ *
+ * Every table is an exact-size heap block.  The driver checks the argument
+ * errors the header documents (NULL table or output, no entries, nranks
+ * outside 1..16, negative sizes, no available protocol) and compares every
+ * choice on random tables with a brute-force reading of the documented
+ * rule: nearest rank count (ties: the smaller), then the range holding S
+ * (the smallest max_bytes >= S, max_bytes <= 0 unbounded; if every range
+ * ends below S, the one that ends last), then the lowest predicted time
+ * (ties: the lower protocol id).
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <math.h>
+
+#include "../include/ar.h"
+
+static uint64_t rng_state = 0xD1B54A32D192ED03ull;
+static uint64_t next_u64(void)
+{
+    /* xorshift64* (Vigna, "An experimental exploration of Marsaglia's
+     * xorshift generators, scrambled") */
+    rng_state ^= rng_state >> 12;
+    rng_state ^= rng_state << 25;
+    rng_state ^= rng_state >> 27;
+    return rng_state * 0x2545F4914F6CDD1Dull;
+}
+static double uniform(double lo, double hi)
+{
+    return lo + (hi - lo) * (double)(next_u64() >> 11) / 9007199254740992.0;
+}
+
+static int failures = 0;
+#define CHECK(cond, ...)                                          \
+    do {                                                          \
+        if (!(cond)) {                                            \
+            fprintf(stderr, "FAIL %s:%d: ", __FILE__, __LINE__);  \
+            fprintf(stderr, __VA_ARGS__);                         \
+            fprintf(stderr, "\n");                                \
+            ++failures;                                           \
+        }                                                         \
+    } while (0)
+
+static double upper(const ar_cost_entry* e)
+{
+    return e->max_bytes > 0 ? (double)e->max_bytes : INFINITY;
+}
+
+/* the documented rule, written out; returns the protocol or -1 */
+static int brute(const ar_cost_entry* t, int m, int32_t coll, int64_t S, int32_t n,
+                 double* pred)
+{
+    int best_n = -1;
+    for (int i = 0; i < m; ++i) {
+        if (t[i].collective != coll)
+            continue;
+        int d = abs(t[i].nranks - n), bd = abs(best_n - n);
+        if (best_n < 0 || d < bd || (d == bd && t[i].nranks < best_n))
+            best_n = t[i].nranks;
+    }
+    if (best_n < 0)
+        return -1;
+    const ar_cost_entry* pick = NULL;
+    for (int i = 0; i < m; ++i) {      /* smallest range end >= S */
+        const ar_cost_entry* e = &t[i];
+        if (e->collective != coll || e->nranks != best_n || upper(e) < (double)S)
+            continue;
+        if (!pick || upper(e) < upper(pick))
+            pick = e;
+    }
+    if (!pick)
+        for (int i = 0; i < m; ++i) {  /* every range ends below S: the last */
+            const ar_cost_entry* e = &t[i];
+            if (e->collective != coll || e->nranks != best_n)
+                continue;
+            if (!pick || upper(e) > upper(pick))
+                pick = e;
+        }
+    int bp = -1;
+    double bt = 0.0;
+    for (int p = 0; p < 4; ++p) {
+        if (!(pick->alpha_us[p] >= 0.0))
+            continue;
+        double tp = pick->alpha_us[p] + pick->beta_us_per_byte[p] * (double)S;
+        if (bp < 0 || tp < bt) {
+            bp = p;
+            bt = tp;
+        }
+    }
+    *pred = bt;
+    return bp;
+}
+
+int main(void)
+{
+    int32_t proto = -7, coll = -7;
+    double pred = 0.0;
+    ar_cost_entry* one = (ar_cost_entry*)calloc(1, sizeof(ar_cost_entry));
+    one->nranks = 8;
+    one->collective = 0;
+    for (int p = 0; p < 4; ++p) {
+        one->alpha_us[p] = 1.0 + p;
+        one->beta_us_per_byte[p] = 1e-5;
+    }
+    CHECK(ar_select_protocol(NULL, 1, 4096, 8, &proto, &pred) == AR_EINVAL, "NULL table");
+    CHECK(ar_select_protocol(one, 1, 4096, 8, NULL, &pred) == AR_EINVAL, "NULL output");
+    CHECK(ar_select_protocol(one, 0, 4096, 8, &proto, &pred) == AR_EINVAL, "no entries");
+    CHECK(ar_select_protocol(one, 1, -1, 8, &proto, &pred) == AR_EINVAL, "negative size");
+    CHECK(ar_select_protocol(one, 1, 4096, 0, &proto, &pred) == AR_EINVAL, "nranks 0");
+    CHECK(ar_select_protocol(one, 1, 4096, 17, &proto, &pred) == AR_EINVAL, "nranks 17");
+    CHECK(ar_select_protocol(one, 1, 4096, 8, &proto, NULL) == AR_OK && proto == AR_LL,
+          "NULL prediction is allowed");
+    CHECK(ar_select_collective(one, 1, 2, 4096, 8, &proto, &pred) == AR_EINVAL,
+          "no entries for the collective");
+    CHECK(ar_select_allreduce(one, 1, 4096, 8, &coll, &proto, &pred) == AR_OK &&
+          coll == AR_ALLREDUCE, "no two-shot entries: one-shot");
+    for (int p = 0; p < 4; ++p)
+        one->alpha_us[p] = -1.0;
+    CHECK(ar_select_protocol(one, 1, 4096, 8, &proto, &pred) == AR_EINVAL,
+          "no available protocol");
+    free(one);
+
+    int checked = 0;
+    for (int trial = 0; trial < 2000; ++trial) {
+        const int m = 1 + (int)(next_u64() % 24);
+        ar_cost_entry* t = (ar_cost_entry*)malloc((size_t)m * sizeof(ar_cost_entry));
+        for (int i = 0; i < m; ++i) {
+            static const int32_t rk[] = {1, 2, 4, 8, 12, 16};
+            t[i].nranks = rk[next_u64() % 6];
+            t[i].collective = (int32_t)(next_u64() % 3);
+            t[i].max_bytes = (next_u64() % 3) == 0 ? 0 : (int64_t)(1u << (next_u64() % 23));
+            for (int p = 0; p < 4; ++p) {
+                /* a coarse grid of values makes exact ties common */
+                t[i].alpha_us[p] = (next_u64() % 5) == 0 ? -1.0
+                                                          : (double)(next_u64() % 4);
+                t[i].beta_us_per_byte[p] = (next_u64() % 2) ? 0.0 : uniform(0.0, 1e-4);
+            }
+        }
+        for (int q = 0; q < 8; ++q) {
+            const int32_t n = 1 + (int32_t)(next_u64() % 16);
+            const int64_t S = (next_u64() % 4) == 0 ? 0 : (int64_t)(next_u64() % (1u << 23));
+            for (int32_t c = 0; c < 3; ++c) {
+                double want_t = 0.0;
+                const int want = brute(t, m, c, S, n, &want_t);
+                const int rc = ar_select_collective(t, m, c, S, n, &proto, &pred);
+                if (want < 0) {
+                    CHECK(rc == AR_EINVAL, "expected EINVAL (trial %d)", trial);
+                } else {
+                    CHECK(rc == AR_OK && proto == want && pred == want_t,
+                          "choice (trial %d, coll %d, n %d, S %lld): %d %d vs %d", trial, c,
+                          n, (long long)S, rc, proto, want);
+                }
+                ++checked;
+            }
+            int32_t pa = -1;
+            double ta = 0.0, tb = 0.0;
+            pa = brute(t, m, 0, S, n, &ta);
+            const int pb = brute(t, m, 2, S, n, &tb);
+            const int rc = ar_select_allreduce(t, m, S, n, &coll, &proto, &pred);
+            if (pa < 0) {
+                CHECK(rc == AR_EINVAL, "allreduce needs one-shot entries");
+            } else if (pb >= 0 && tb < ta) {
+                CHECK(rc == AR_OK && coll == AR_TWOSHOT && proto == pb, "two-shot wins");
+            } else {
+                CHECK(rc == AR_OK && coll == AR_ALLREDUCE && proto == pa, "one-shot wins");
+            }
+        }
+        free(t);
+    }
+    printf("%d choices checked, %d failures\n", checked, failures);
+    return failures ? 1 : 0;
+}
