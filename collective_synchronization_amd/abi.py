@@ -118,6 +118,9 @@ _SIGS = {
                       ctypes.c_int),
     "ar_scale_rows": ([_i32, _i64, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "ar_sim_run": ([ctypes.POINTER(ar_sim_params), _vp], ctypes.c_int),
+    "ar_sim_chain_run": ([ctypes.POINTER(ar_sim_params), _vp, _vp], ctypes.c_int),
+    "ar_sim_chain_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
+                               ctypes.POINTER(_i32)], ctypes.c_int),
     "ar_sim_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
                          ctypes.POINTER(_i32), ctypes.POINTER(_i32),
                          ctypes.POINTER(_i32), ctypes.POINTER(_i32),
@@ -313,6 +316,19 @@ def sim_params(desc, nops, inp, in_stride, out, out_stride, scratch, ctrl, epoch
 
 def ar_sim_run(params: ar_sim_params, stream=None) -> None:
     _check(_lib.ar_sim_run(ctypes.byref(params), _stream(stream)), "ar_sim_run")
+
+
+def ar_sim_chain_run(params: ar_sim_params, scales, stream=None) -> None:
+    """scales: device float32 [nops, nranks] (op 0's row unused)."""
+    _check(_lib.ar_sim_chain_run(ctypes.byref(params), _ptr(scales), _stream(stream)),
+           "ar_sim_chain_run")
+
+
+def ar_sim_chain_geometry(params: ar_sim_params) -> dict:
+    b, coop = _i32(), _i32()
+    _check(_lib.ar_sim_chain_geometry(ctypes.byref(params), ctypes.byref(b), ctypes.byref(coop)),
+           "ar_sim_chain_geometry")
+    return {"blocks": b.value, "launch": "cooperative" if coop.value else "ordinary"}
 
 
 def ar_sim_geometry(params: ar_sim_params) -> dict:

@@ -127,3 +127,11 @@ class Workspace:
         p = self.sim_params(nops, x_dev, in_stride, out_dev, out_stride, **kw)
         abi.ar_sim_run(p, stream)
         self.flip(nops)
+
+    def sim_chain(self, nops, x_dev, in_stride, out_dev, out_stride, scales, stream=None,
+                  **kw) -> None:
+        """nops chained ops in one persistent launch (op i+1's payload is op
+        i's result scaled per rank by scales[i+1]); advances the epoch."""
+        p = self.sim_params(nops, x_dev, in_stride, out_dev, out_stride, **kw)
+        abi.ar_sim_chain_run(p, scales, stream)
+        self.flip(nops)

@@ -249,6 +249,7 @@ struct CollSimArgs {
   uint64_t timeout_ticks;
   const uint32_t* delay;
   uint64_t* trace;
+  const float* scales;        // chained simulator only
 };
 
 __device__ __forceinline__ void sim_delay(const CollSimArgs& a, int op, int g) {
@@ -869,6 +870,107 @@ __global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
   }
 }
 
+// ------------------------------------------------- chained simulator --
+
+// Chained all-reduce simulator: the decode pattern, in which each op's
+// result feeds the next op's producer ("Why Microseconds Matter in AI
+// Infrastructure", section "Communication is becoming part of GPU
+// execution": the producing computation and the communication in one
+// kernel).  Op 0's payload of rank r is its input row; op i+1's payload of
+// rank r is rank r's own copy of op i's result, scaled by
+// scales[(i+1)*nranks + r] (y = bf16_rne(f32(x) * s), the producer
+// epilogue's arithmetic).  So no op can start before the previous one has
+// been reduced, as in a decode step whose next layer consumes the sum.
+// One workgroup of nranks waves per (rank g, tile), wave w paired with peer
+// w, every workgroup holding one tile.  Per op: every wave but the own one
+// encodes the rank's payload chunk, sends it to peer w and polls peer w's
+// chunk into LDS; barrier; the own wave reduces in rank order, writes the
+// output tile and, unless the op is the last, scales the result into the
+// next payload chunk in LDS; barrier; every wave takes that chunk.  The
+// second barrier also covers both LDS buffers' reuse, and each op's sends
+// come after the op before it has been consumed (consume(i), then
+// produce(i+1)), which is the dual-buffer licence.
+template <int P, int NMAX>
+__global__ __launch_bounds__(1024) void k_sim_chain(CollSimArgs a) {
+  __shared__ u32x4 lds[NMAX][kWave];
+  __shared__ u32x4 next[kWave];
+  __shared__ int lds_err;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  int g, tg;
+  if (!sim_place(a, g, tg)) return;                // whole workgroup
+  const bool own = w == g;
+  // the rank's own chunk is staged by wave g+1 (by the own wave for one rank)
+  const int stager = a.nranks == 1 ? g : (g + 1) % a.nranks;
+  const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
+  const uint32_t N = (uint32_t)a.nranks;
+  const uint32_t row_bytes = (uint32_t)(((a.count * 2) + 15) & ~int64_t(15));
+  const int keep = chunk_keep<P>(a.count, tg, lane);
+  const uint32_t loff = (uint32_t)tg * kTileBytes + (uint32_t)lane * 16u;
+  uint32_t x[4];                                   // this op's payload chunk
+  load_chunk<P>(a.in + (int64_t)g * a.in_stride, row_bytes, tg, lane, x);
+  mask_words(x, keep);
+  if (threadIdx.x == 0) lds_err = 0;
+  __syncthreads();
+  uint32_t seq = a.seq0;
+  uint32_t par = a.parity0;
+  for (int op = 0; op < a.nops; ++op) {
+    const uint32_t stale = seq_prev(seq_prev(seq));
+    const u32x4 enc = encode_words<P>(x, lane, seq);
+    if (!own) {
+      // sentinel: this wave's re-arm stores of the previous op complete
+      // before its next store to the same peer
+      if (P == kSentinel) fence_release();
+      const uint32_t dst0 = (((uint32_t)w * 2u + par) * N + (uint32_t)g) * a.slot_bytes;
+      store_chunk<P>(rs, dst0, 0u, 1, -1, tg, a.E, lane, enc);
+      if (P == kLL128) {
+        fence_release();
+        produce_flags(rs, dst0, 0u, 1, -1, tg, a.E, seq, lane);
+      }
+      const uint32_t src = (((uint32_t)g * 2u + par) * N + (uint32_t)w) * a.slot_bytes + loff;
+      u32x4 got;
+      if (poll_chunk<P>(rs, src, loff < a.E, seq, stale, true, a.ctrl, a.timeout_ticks, lane,
+                        got) != 0) {
+        if (lane == 0) lds_err = 1;
+      } else {
+        lds[w][lane] = got;
+      }
+    }
+    if (w == stager) lds[g][lane] = enc;
+    __syncthreads();
+    if (lds_err) return;                           // whole workgroup
+    if (own) {
+      u32x4 v[NMAX];
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r)
+        v[r] = (r < a.nranks) ? lds[r][lane] : u32x4{0u, 0u, 0u, 0u};
+      uint32_t o[4];
+      reduce_words<P, NMAX>(v, a.nranks, o);
+      mask_words(o, keep);
+      int64_t first;
+      int n;
+      lane_elems<P>(tg, lane, first, n);
+      if (loff < a.E)
+        store_elems(a.out + ((int64_t)op * a.nranks + g) * a.out_stride, a.count, first, n, o);
+      if (op + 1 < a.nops) {
+        scale_words(o, a.scales[(int64_t)(op + 1) * a.nranks + g]);
+        mask_words(o, keep);
+        next[lane] = u32x4{o[0], o[1], o[2], o[3]};
+      }
+    }
+    __syncthreads();
+    if (op + 1 < a.nops) {
+      const u32x4 nx = next[lane];
+      x[0] = nx.x;
+      x[1] = nx.y;
+      x[2] = nx.z;
+      x[3] = nx.w;
+    }
+    seq = seq_next(seq);
+    par ^= 1u;
+  }
+}
+
 // ================================================================ host side
 
 // All-gather: with several tiles per wave, the sentinel kernel overlaps the
@@ -1098,6 +1200,7 @@ int coll_sim_run(const ar_sim_params* p, hipStream_t s) {
   a.timeout_ticks = ns_to_ticks(p->timeout_ns, di.wallclock_hz);
   a.delay = p->delay_ticks;
   a.trace = p->trace;
+  a.scales = nullptr;
   void* args[] = {&a};
   const bool extras = a.delay || a.trace;
   const void* fn =
@@ -1120,6 +1223,133 @@ int coll_sim_run(const ar_sim_params* p, hipStream_t s) {
       coll_sim_fn(d->proto, d->collective, d->nranks, go.narrow, go.TPW > 1, extras);
   return map_hip(hipLaunchKernel(fo, dim3(go.blocks), dim3(go.narrow ? kWave : kWave * d->nranks),
                                  args, 0, s));
+}
+
+// --------------------------------------------------- chained simulator host
+
+template <int P>
+static const void* chain_fn_n(int nranks) {
+  if (nranks <= 4) return reinterpret_cast<const void*>(&k_sim_chain<P, 4>);
+  if (nranks <= 8) return reinterpret_cast<const void*>(&k_sim_chain<P, 8>);
+  return reinterpret_cast<const void*>(&k_sim_chain<P, 16>);
+}
+
+static const void* chain_fn(int proto, int nranks) {
+  switch (proto) {
+    case kLL: return chain_fn_n<kLL>(nranks);
+    case kLL128: return chain_fn_n<kLL128>(nranks);
+    default: return chain_fn_n<kSentinel>(nranks);
+  }
+}
+
+// Beyond the simulator's own checks: the one-shot all-reduce in system mode,
+// LL / LL128 / SENTINEL, no tile order, delays or trace, and the library's
+// own grid (launch flags only).
+static int chain_check(const ar_sim_params* p) {
+  const ar_desc* d = &p->desc;
+  if (d->collective != AR_ALLREDUCE || d->nconsumers != d->nranks) return AR_EINVAL;
+  if (d->proto == kBarrier) return AR_EINVAL;
+  if (p->tile_order || p->delay_ticks || p->trace || p->waves_per_rank) return AR_EINVAL;
+  if (p->flags & (AR_SIM_NARROW | AR_SIM_WIDE)) return AR_EINVAL;
+  return AR_OK;
+}
+
+struct ChainGeom {
+  int32_t Q, T, blocks;
+  bool coop;
+};
+
+// One workgroup per (rank, tile) for every tile of the payload.  The grid
+// must be resident: at most the occupancy query's figure, halved for an
+// ordinary launch.  Without a launch flag: ordinary when the grid fits
+// that, else cooperative where the device supports it.
+static int chain_geometry(const ar_sim_params* p, const DeviceInfo& di, ChainGeom* g) {
+  const ar_desc* d = &p->desc;
+  const int64_t T = ceil_div64(encoded_bytes(d->proto, d->count), kTileBytes);
+  if (T > (int64_t(1) << 24)) return AR_ESIZE;
+  const int64_t Q = ceil_div64(T, 8);
+  const int64_t blocks = 8 * Q * d->nranks;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, chain_fn(d->proto, d->nranks),
+                                                   kWave * d->nranks, 0) != hipSuccess ||
+      occ <= 0)
+    return AR_ELAUNCH;
+  const int64_t full = (int64_t)occ * di.cus;
+  bool coop;
+  if (p->flags & AR_SIM_COOPERATIVE)
+    coop = true;
+  else if (p->flags & AR_SIM_ORDINARY)
+    coop = false;
+  else
+    coop = blocks > full / 2 && di.coop;
+  if (blocks > (coop ? full : full / 2)) return AR_ECAPACITY;
+  g->Q = (int32_t)Q;
+  g->T = (int32_t)T;
+  g->blocks = (int32_t)blocks;
+  g->coop = coop;
+  return AR_OK;
+}
+
+int chain_sim_geometry(const ar_sim_params* p, int32_t* blocks, int32_t* cooperative) {
+  int rc = chain_check(p);
+  if (rc) return rc;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  ChainGeom g;
+  rc = chain_geometry(p, di, &g);
+  if (rc) return rc;
+  if (blocks) *blocks = g.blocks;
+  if (cooperative) *cooperative = g.coop ? 1 : 0;
+  return AR_OK;
+}
+
+int chain_sim_run(const ar_sim_params* p, const float* scales, hipStream_t s) {
+  int rc = chain_check(p);
+  if (rc) return rc;
+  if (!scales) return AR_EINVAL;
+  if (!aligned(scales, 4)) return AR_EALIGN;
+  const ar_desc* d = &p->desc;
+  if (d->count == 0) return AR_OK;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  if ((p->flags & AR_SIM_COOPERATIVE) && !di.coop) return AR_ENODEV;
+  ChainGeom g;
+  rc = chain_geometry(p, di, &g);
+  if (rc) return rc;
+  CollSimArgs a{};
+  a.in = static_cast<const uint16_t*>(p->in);
+  a.in_stride = p->in_stride;
+  a.out = static_cast<uint16_t*>(p->out);
+  a.out_stride = p->out_stride;
+  a.row_stride = (d->count + 7) / 8 * 8;
+  a.count = d->count;
+  a.width = d->count;
+  a.scratch = static_cast<const uint8_t*>(p->scratch);
+  a.scratch_bytes = (uint32_t)desc_scratch_bytes(d);
+  a.slot_bytes = (uint32_t)desc_slot_bytes(d);
+  a.ag0 = 0u;
+  a.E = (uint32_t)encoded_bytes(d->proto, d->count);
+  a.ctrl = static_cast<int*>(p->ctrl);
+  a.nranks = d->nranks;
+  a.nops = p->nops;
+  a.W = 8 * g.Q;
+  a.Q = g.Q;
+  a.T = g.T;
+  a.TPW = 1;
+  a.seq0 = p->epoch.seq;
+  a.parity0 = p->epoch.parity;
+  a.timeout_ticks = ns_to_ticks(p->timeout_ns, di.wallclock_hz);
+  a.delay = nullptr;
+  a.trace = nullptr;
+  a.scales = scales;
+  void* args[] = {&a};
+  const void* fn = chain_fn(d->proto, d->nranks);
+  const dim3 block(kWave * d->nranks);
+  // no ordinary fallback: an ordinary grid could not hold every tile
+  if (g.coop) return map_hip(hipLaunchCooperativeKernel(fn, dim3(g.blocks), block, args, 0, s));
+  return map_hip(hipLaunchKernel(fn, dim3(g.blocks), block, args, 0, s));
 }
 
 // ----------------------------------------------------- stream-ordered host

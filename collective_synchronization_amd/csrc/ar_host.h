@@ -186,5 +186,7 @@ int coll_sim_geometry(const ar_sim_params* p, int32_t* groups, int32_t* tiles,
                       int32_t* tiles_per_group, int32_t* blocks, int32_t* wide,
                       int32_t* cooperative);
 int coll_sim_run(const ar_sim_params* p, hipStream_t s);
+int chain_sim_geometry(const ar_sim_params* p, int32_t* blocks, int32_t* cooperative);
+int chain_sim_run(const ar_sim_params* p, const float* scales, hipStream_t s);
 
 }  // namespace ar

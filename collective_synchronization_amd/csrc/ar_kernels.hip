@@ -1154,7 +1154,7 @@ const char* ar_status_string(int code) {
   }
 }
 
-int ar_abi_version(void) { return 4; }
+int ar_abi_version(void) { return 5; }
 
 int64_t ar_encoded_bytes(int32_t proto, int64_t count) {
   return encoded_bytes(proto, count);
@@ -1389,6 +1389,18 @@ static int sim_launch(const ar_sim_params* p, const DeviceInfo& di, const SimGeo
     default: e = dispatch_sim_p<kBarrier>(a, share, g.blocks, g.coop, g.wide, s); break;
   }
   return map_hip(e);
+}
+
+int ar_sim_chain_run(const ar_sim_params* p, const float* scales, void* stream) {
+  const int rc = check_sim(p);
+  if (rc) return rc;
+  return chain_sim_run(p, scales, static_cast<hipStream_t>(stream));
+}
+
+int ar_sim_chain_geometry(const ar_sim_params* p, int32_t* blocks, int32_t* cooperative) {
+  const int rc = check_sim(p);
+  if (rc) return rc;
+  return chain_sim_geometry(p, blocks, cooperative);
 }
 
 int ar_sim_run(const ar_sim_params* p, void* stream) {

@@ -417,6 +417,39 @@ int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
                     int32_t* tiles_per_rank, int32_t* tiles_per_wave,
                     int32_t* blocks, int32_t* wide, int32_t* cooperative);
 
+/*
+ * ar_sim_chain_run -- `nops` one-shot all-reduces in one persistent kernel
+ * where each op's result feeds the next op's producer, the dependency of a
+ * decode step whose next layer consumes the sum ("Why Microseconds Matter
+ * in AI Infrastructure", section "Communication is becoming part of GPU
+ * execution": the producing computation and the communication fused into
+ * one kernel).  Op 0's payload of rank r is row r of `in` (in +
+ * r*in_stride); op i+1's payload of rank r is rank r's own copy of op i's
+ * result scaled by scales[(i+1)*nranks + r]: y = bf16_rne(f32(x) * s), one
+ * binary32 multiplication per element (NaN -> 0x7FC0), the arithmetic of
+ * ar_scale_pack.  Every rank's output of op i at out + (i*nranks + r) *
+ * out_stride, as for ar_sim_run.
+ *   p: as for ar_sim_run, restricted to desc.collective = AR_ALLREDUCE,
+ *      nconsumers = nranks, proto AR_LL / AR_LL128 / AR_SENTINEL,
+ *      waves_per_rank = 0, no tile_order, delay_ticks or trace, flags
+ *      AR_SIM_COOPERATIVE or AR_SIM_ORDINARY or 0.  Only op 0's input rows
+ *      are read.
+ *   scales: device, float[nops * nranks], 4-byte aligned; entries of op 0
+ *      are not read.
+ * One workgroup per (rank, tile) holds every 1 KiB tile of a rank's slot,
+ * so the grid must be resident at once: without a launch flag the launch
+ * is ordinary when half the occupancy holds it, else cooperative.
+ * AR_ECAPACITY when no resident grid holds every tile (payloads above a
+ * few tens of KiB per rank at 16 ranks).  Per op: the sends, the polls,
+ * one workgroup barrier, the rank-order reduce and the scaling, a second
+ * barrier.  Errors as for ar_sim_run.
+ */
+int ar_sim_chain_run(const ar_sim_params* p, const float* scales, void* stream);
+
+/* Launch ar_sim_chain_run would make for these parameters: total
+ * workgroups and 1 for a cooperative launch.  Either output may be NULL. */
+int ar_sim_chain_geometry(const ar_sim_params* p, int32_t* blocks, int32_t* cooperative);
+
 /* Wall-clock counter frequency of the current device in Hz. */
 int ar_wallclock_hz(double* hz);
 

@@ -22,7 +22,9 @@ arithmetic is in the C file, which cites the pages it follows:
   all-gather;
 * "Why Microseconds Matter in AI Infrastructure", section "Communication is
   becoming part of GPU execution" -- send/receive/reduce called from inside
-  the producing kernel (the producer epilogue used for it: a per-rank scale).
+  the producing kernel (the producer epilogue used for it: a per-rank scale),
+  and the chain in which each all-reduce's result feeds that producer for
+  the next all-reduce (``chain_ops``).
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against
 something other than itself (exhaustive sweeps against torch and numpy, an
@@ -232,6 +234,32 @@ def scale(x: np.ndarray, s: float) -> np.ndarray:
     _load().o_scale(_ptr(x, ctypes.c_uint16), x.size, ctypes.c_float(s),
                     _ptr(out, ctypes.c_uint16))
     return out[:x.size]
+
+
+def chain_ops(x0: np.ndarray, scales: np.ndarray, proto="ll", seq0: int = 1) -> np.ndarray:
+    """Expected outputs of K chained all-reduces, each op's result feeding the
+    next op's producer ("Why Microseconds Matter in AI Infrastructure",
+    section "Communication is becoming part of GPU execution": the producing
+    computation and the communication in one kernel; the producer is the
+    per-rank scale above).  x0: uint16 [n, count], op 0's payloads; scales:
+    float32 [K, n], row 0 unused.  Op 0 all-reduces x0; op i+1's payload of
+    rank r is scale(out_i, scales[i+1, r]).  Returns uint16 [K, count]."""
+    x = _u16(x0)
+    n, count = x.shape
+    s = np.asarray(scales, dtype=np.float32)
+    if s.ndim != 2 or s.shape[1] != n:
+        raise ValueError("scales must be [K, n]")
+    K = s.shape[0]
+    out = np.empty((K, count), dtype=np.uint16)
+    seq = seq0
+    for i in range(K):
+        st, out[i] = allreduce(x, proto, seq)
+        if st != READY:
+            raise RuntimeError(f"oracle chained op {i} not ready: status {st}")
+        if i + 1 < K:
+            x = np.stack([scale(out[i], float(s[i + 1, r])) for r in range(n)])
+        seq = epoch_next(seq)
+    return out
 
 
 def shard_bounds(count: int, n: int, k: int):

@@ -36,7 +36,7 @@ def test_header_symbols_all_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert abi.raw().ar_abi_version() == 4
+    assert abi.raw().ar_abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert abi.status_string(code).startswith("AR_")
     assert abi.status_string(-99) == "AR_UNKNOWN"
