@@ -319,6 +319,47 @@ def measure_epilogue(torch, abi, buffers, x, proto, nranks, count, steps, warmup
     return out
 
 
+def measure_chain(torch, abi, buffers, x0, proto, nranks, count, nops, steps, warmup,
+                  seed=7):
+    """The chained simulator (ar_sim_chain_run): op i+1's payload of rank r
+    is op i's result times a per-rank factor s[i+1][r] ~ U[0.5, 1.5)/nranks,
+    in one persistent launch.  HIP events per launch, median over `steps`
+    launches, plus the wall clock of the timed launches."""
+    import numpy as np
+    ws = buffers.Workspace(nranks, count, proto, nranks)
+    xd, stride = buffers.rows_to_device(x0)
+    rng = np.random.default_rng(seed)
+    s = (rng.uniform(0.5, 1.5, size=(nops, nranks)) / nranks).astype(np.float32)
+    sd = torch.from_numpy(s).to("cuda")
+    outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    geo = abi.ar_sim_chain_geometry(ws.sim_params(nops, xd, stride, outd, stride))
+    kw = dict(timeout_ns=2_000_000_000)
+    for _ in range(warmup):
+        ws.sim_chain(nops, xd, stride, outd, stride, sd, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        ws.sim_chain(nops, xd, stride, outd, stride, sd, **kw)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ws.status() != 0:
+        raise RuntimeError(f"device status {abi.status_string(ws.status())}")
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return {
+        "us_per_op": round(wall * 1e6 / (steps * nops), 4),
+        "kernel_us_per_op": round(statistics.median(ms) * 1e3 / nops, 4),
+        "kernel_us_per_op_p10_p90": [round(float(np.percentile(ms, 10)) * 1e3 / nops, 4),
+                                     round(float(np.percentile(ms, 90)) * 1e3 / nops, 4)],
+        "launch": geo["launch"], "blocks": geo["blocks"],
+        "producer": "per-rank scale bf16_rne(f32(x)*s), s ~ U[0.5,1.5)/nranks",
+    }
+
+
 def summarize(res, proto, nranks, count, nops, steps, collective="allreduce"):
     import numpy as np
     launch_ms = res["launch_ms"]
@@ -368,6 +409,9 @@ def main() -> int:
     ap.add_argument("--epilogue", action="store_true",
                     help="also time stream-ordered ops whose producer (a per-rank "
                          "scale) sends from its epilogue, against a separate pack")
+    ap.add_argument("--chain", action="store_true",
+                    help="also time the chained simulator: each op's result, scaled "
+                         "per rank, is the next op's payload, in one launch")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run ar_probe_copy over BYTES, 3 times (reference "
                          "dispatches for hardware byte counters)")
@@ -506,6 +550,13 @@ def main() -> int:
                                                 count, args.steps, args.warmup)
         except RuntimeError as e:
             line["epilogue"] = {"error": str(e)}
+
+    if args.chain and args.mode == "system" and coll == "allreduce" and proto != "barrier":
+        try:
+            line["chain"] = measure_chain(torch, abi, buffers, x[0], proto, nranks, count,
+                                          nops, args.steps, args.warmup)
+        except RuntimeError as e:
+            line["chain"] = {"error": str(e)}
 
     if not args.no_floor:
         threads = 64 * nranks if res["geo"]["kernel"] == "wide" else 64

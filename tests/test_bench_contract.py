@@ -68,7 +68,7 @@ def test_twoshot_bytes(proto, nranks, count):
 @pytest.mark.gpu
 def test_bench_line_fields():
     cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "5",
-           "--warmup", "1", "--cpu-seconds", "0.5", "--no-share"]
+           "--warmup", "1", "--cpu-seconds", "0.5", "--no-share", "--chain"]
     print("[bench]", " ".join(cmd[1:]), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -95,3 +95,5 @@ def test_bench_line_fields():
     assert fl["empty_kernel_us"] > 0 and fl["copy_gbs"] > 100
     assert line["placement"]["on_expected_xcd"] == 1.0
     assert line["single_op_launch"]["kernel_us"] > 0
+    ch = line["chain"]
+    assert ch["kernel_us_per_op"] > 0 and ch["launch"] in ("ordinary", "cooperative")
