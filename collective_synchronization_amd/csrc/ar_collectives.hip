@@ -9,6 +9,10 @@
 // one that scales to more GPUs.  Here each share and each reduced share
 // travels with the one-shot encodings (LL, LL128, sentinel) and the same
 // dual-buffered epochs; the two exchanges use two receive regions.
+// "Why Microseconds Matter in AI Infrastructure", section "Communication is
+// becoming part of GPU execution": the producer that sends from its own
+// epilogue (a per-rank scale), and the chained simulator in which each
+// all-reduce's result feeds that producer for the next one, in one launch.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
