@@ -131,6 +131,31 @@ def test_sentinel_rearm_is_required():
             assert np.array_equal(got, oracle.allreduce(x0, "sentinel", 1)[1])
 
 
+@pytest.mark.parametrize("proto", ["ll", "sentinel"])
+def test_sim_producer_past_the_deadline_times_out(proto):
+    """One producer held past the poll deadline (a 20 ms delay before its
+    op-1 sends against a 2 ms timeout): the persistent launch ends with
+    AR_ETIMEOUT instead of waiting.  The wide kernel with one tile per
+    workgroup, through LL's per-peer send order and the sentinel's
+    barrier-first order; the other waves stop at the abort flag."""
+    n, count, nops = 8, 4096, 4
+    ws = buffers.Workspace(n, count, proto, n)
+    x = _x(61, (nops, n, count))
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    hz = abi.ar_wallclock_hz()
+    d = np.zeros((nops, n), dtype=np.int32)
+    d[1, 3] = int(0.02 * hz)
+    ticks = torch.from_numpy(d).to("cuda")
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride,
+                                            delay_ticks=ticks))
+    print(f"[sim-deadline] {proto} geo={geo}", flush=True)
+    assert geo["kernel"] == "wide" and geo["tiles_per_wave"] == 1
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=2_000_000, delay_ticks=ticks)
+    torch.cuda.synchronize()
+    assert ws.status() == abi.AR_ETIMEOUT
+
+
 SIM_CASES = [(4, 1, 4096, 4), (4, 4, 4096, 4), (8, 1, 4096, 8), (8, 8, 4099, 6),
              (16, 16, 32768, 3), (16, 1, 32768, 4), (3, 1, 1000, 5), (2, 2, 60, 7),
              (1, 1, 100, 3)]
