@@ -175,6 +175,30 @@ def test_sim_allgather(proto, nranks, count, nops):
         assert np.all(ws.slot_view() == 0xFF)
 
 
+@pytest.mark.parametrize("collective,nranks,count", [("twoshot", 8, 4096),
+                                                     ("twoshot", 16, 32768),
+                                                     ("allgather", 8, 4096)])
+@pytest.mark.parametrize("proto", PROTOS)
+def test_sim_producer_past_the_deadline_times_out(collective, proto, nranks, count):
+    """One producer held past the poll deadline (a 20 ms delay before its
+    op-1 sends against a 2 ms timeout): the persistent two-shot or all-gather
+    launch ends with AR_ETIMEOUT instead of waiting."""
+    nops = 4
+    ws = buffers.Workspace(nranks, count, proto, nranks, collective=collective)
+    x = _x(71 + count, (nops, nranks, count))
+    xd, stride = buffers.rows_to_device(x)
+    ostride = ws.gather_stride() if collective == "allgather" else stride
+    outd = torch.zeros((nops * nranks, ostride), dtype=torch.int16, device="cuda")
+    hz = abi.ar_wallclock_hz()
+    d = np.zeros((nops, nranks), dtype=np.int32)
+    d[1, nranks - 1] = int(0.02 * hz)
+    ticks = torch.from_numpy(d).to("cuda")
+    print(f"[coll-deadline] {collective} {proto} N={nranks} count={count}", flush=True)
+    ws.sim(nops, xd, stride, outd, ostride, timeout_ns=2_000_000, delay_ticks=ticks)
+    torch.cuda.synchronize()
+    assert ws.status() == abi.AR_ETIMEOUT
+
+
 LARGEST = [("twoshot", 8, 1 << 21), ("twoshot", 16, 1 << 20),
            ("allgather", 8, 1 << 19), ("allgather", 16, 1 << 19)]
 
