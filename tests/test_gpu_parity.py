@@ -131,27 +131,31 @@ def test_sentinel_rearm_is_required():
             assert np.array_equal(got, oracle.allreduce(x0, "sentinel", 1)[1])
 
 
-@pytest.mark.parametrize("proto", ["ll", "sentinel"])
-def test_sim_producer_past_the_deadline_times_out(proto):
+@pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel"])
+@pytest.mark.parametrize("kernel,ncons", [("wide", 8), ("narrow", 8), ("wide", 1)])
+def test_sim_producer_past_the_deadline_times_out(proto, kernel, ncons):
     """One producer held past the poll deadline (a 20 ms delay before its
     op-1 sends against a 2 ms timeout): the persistent launch ends with
     AR_ETIMEOUT instead of waiting.  The wide kernel with one tile per
-    workgroup, through LL's per-peer send order and the sentinel's
-    barrier-first order; the other waves stop at the abort flag."""
+    workgroup (LL's per-peer send order, the barrier-first order of the
+    others), the one-wave kernel, and share mode; the other waves stop at
+    the abort flag."""
     n, count, nops = 8, 4096, 4
-    ws = buffers.Workspace(n, count, proto, n)
+    ws = buffers.Workspace(n, count, proto, ncons)
     x = _x(61, (nops, n, count))
     xd, stride = buffers.rows_to_device(x)
-    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    outd = torch.zeros((nops * ncons, stride), dtype=torch.int16, device="cuda")
     hz = abi.ar_wallclock_hz()
     d = np.zeros((nops, n), dtype=np.int32)
     d[1, 3] = int(0.02 * hz)
     ticks = torch.from_numpy(d).to("cuda")
+    flags = abi.AR_SIM_NARROW if kernel == "narrow" else 0
     geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride,
-                                            delay_ticks=ticks))
-    print(f"[sim-deadline] {proto} geo={geo}", flush=True)
-    assert geo["kernel"] == "wide" and geo["tiles_per_wave"] == 1
-    ws.sim(nops, xd, stride, outd, stride, timeout_ns=2_000_000, delay_ticks=ticks)
+                                            delay_ticks=ticks, flags=flags))
+    print(f"[sim-deadline] {proto} C={ncons} geo={geo}", flush=True)
+    assert geo["kernel"] == kernel
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=2_000_000, delay_ticks=ticks,
+           flags=flags)
     torch.cuda.synchronize()
     assert ws.status() == abi.AR_ETIMEOUT
 
