@@ -233,6 +233,7 @@ def measure_placement(torch, abi, blocks, threads):
             "on_expected_xcd": round(float(np.mean(x == (x[0] + np.arange(blocks)) % 8)), 4),
             "xcds_seen": int(len(set(x[x >= 0].tolist()))),
             "cus": int(props.multi_processor_count),
+            "device": props.name, "arch": getattr(props, "gcnArchName", ""),
             # one device spanning all eight XCDs (256 CUs) is the SPX partition
             "partition": "SPX" if len(set(x[x >= 0].tolist())) == 8 else "other"}
 

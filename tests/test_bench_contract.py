@@ -94,6 +94,7 @@ def test_bench_line_fields():
     assert 0 < fl["oneway_us"] < 10 and 0 < fl["load_us"] < 10
     assert fl["empty_kernel_us"] > 0 and fl["copy_gbs"] > 100
     assert line["placement"]["on_expected_xcd"] == 1.0
+    assert line["placement"]["device"] and "gfx950" in line["placement"]["arch"]
     assert line["single_op_launch"]["kernel_us"] > 0
     ch = line["chain"]
     assert ch["kernel_us_per_op"] > 0 and ch["launch"] in ("ordinary", "cooperative")
