@@ -419,7 +419,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark measures "
               "N simulated ranks on ONE GPU; there is no multi-GPU path.",
               file=sys.stderr)
         return 2
@@ -427,10 +427,10 @@ def main() -> int:
     import torch
 
     from collective_synchronization_amd import abi, buffers, inputs
-    from collective_synchronization_amd.configs import CONFIGS
+    from collective_synchronization_amd.configs import BENCH_CONFIG, CONFIGS
 
     torch.cuda.set_device(0)
-    cfg = CONFIGS[2]
+    cfg = CONFIGS[BENCH_CONFIG]
     nranks, count, nops, proto = args.nranks, args.rows * args.hidden, args.nops, args.proto
     coll = args.collective
     selected = None

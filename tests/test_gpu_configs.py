@@ -48,8 +48,8 @@ def _check_all(got, want_ops, ops=None):
 
 
 @pytest.mark.parametrize("mode", ["share", "system"])
-def test_config1_ll_n4(mode):
-    cfg = CONFIGS[1]
+def test_ll_n4_1x4096(mode):
+    cfg = CONFIGS["n4_ll_1x4096"]
     n, count = cfg["nranks"], cfg["hidden"]
     x = inputs.payload(cfg["seed"], (1, n, count), cfg["dist"])
     ncons = n if mode == "system" else 1
@@ -66,8 +66,8 @@ def test_config1_ll_n4(mode):
 
 
 @pytest.mark.parametrize("inject", [False, True])
-def test_config2_sentinel_n8_64ops(inject):
-    cfg = CONFIGS[2]
+def test_sentinel_n8_1x4096_64ops(inject):
+    cfg = CONFIGS["n8_sentinel_1x4096_64ops"]
     n, count, nops = cfg["nranks"], cfg["hidden"], cfg["nops"]
     x = inputs.payload(cfg["seed"], (nops, n, count), cfg["dist"])
     if inject:
@@ -88,8 +88,8 @@ def test_config2_sentinel_n8_64ops(inject):
 
 
 @pytest.mark.parametrize("batch", [1, 4, 16])
-def test_config3_ll128_n4_160ops(batch):
-    cfg = CONFIGS[3]
+def test_ll128_n4_Bx8192_160ops(batch):
+    cfg = CONFIGS["n4_ll128_Bx8192_160ops"]
     n, nops = cfg["nranks"], cfg["nops"]
     count = batch * cfg["hidden"]
     x = inputs.payload(cfg["seed"] + batch, (nops, n, count), cfg["dist"])
@@ -97,8 +97,8 @@ def test_config3_ll128_n4_160ops(batch):
     _check_all(got, oracle.allreduce_ops(x, "ll128", seq0))
 
 
-def _config4_cases():
-    cfg = CONFIGS[4]
+def _sweep_cases():
+    cfg = CONFIGS["n8_sweep_2KiB_4MiB"]
     for size in cfg["sizes"]:
         if size not in (2048, 16384, 131072, 1 << 20, 4 << 20):
             continue
@@ -106,9 +106,9 @@ def _config4_cases():
             yield size, proto
 
 
-@pytest.mark.parametrize("size,proto", list(_config4_cases()))
-def test_config4_sweep_n8(size, proto):
-    cfg = CONFIGS[4]
+@pytest.mark.parametrize("size,proto", list(_sweep_cases()))
+def test_sweep_n8_2KiB_4MiB(size, proto):
+    cfg = CONFIGS["n8_sweep_2KiB_4MiB"]
     n = cfg["nranks"]
     count = size // 2
     nops = 64 if size <= 131072 else 8
@@ -126,8 +126,8 @@ def test_config4_sweep_n8(size, proto):
 
 
 @pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel"])
-def test_config5_skew_shuffle_n16(proto):
-    cfg = CONFIGS[5]
+def test_skew_shuffle_n16_8x4096_64ops(proto):
+    cfg = CONFIGS["n16_skew_8x4096_64ops"]
     n, nops = cfg["nranks"], cfg["nops"]
     count = cfg["batches"][0] * cfg["hidden"]
     x = inputs.payload(cfg["seed"], (nops, n, count), cfg["dist"])
@@ -156,6 +156,6 @@ def test_config5_skew_shuffle_n16(proto):
     last_store = t[:, 0, :].max(axis=1)
     done = t[:, 1, :].max(axis=1)
     post = (done - last_store) / hz * 1e6
-    print(f"[config5 {proto}] median post-arrival latency {np.median(post):.3f} us, "
+    print(f"[n16 skew {proto}] median post-arrival latency {np.median(post):.3f} us, "
           f"kernel {geo['kernel']}", flush=True)
     assert np.all(last_store > 0) and np.all(done >= last_store)
