@@ -310,7 +310,7 @@ def test_twoshot_n16_8x4096_skewed(proto):
     t = trace.cpu().numpy()[:-1].reshape(nops, 2, n).astype(np.float64)
     assert np.all(t[:, 0, :] > 0) and np.all(t[:, 1, :] > 0)
     post = (t[:, 1, :].max(axis=1) - t[:, 0, :].max(axis=1)) / hz * 1e6
-    print(f"[twoshot c5 {proto}] median post-arrival latency {np.median(post):.3f} us",
+    print(f"[twoshot n16 skew {proto}] median post-arrival latency {np.median(post):.3f} us",
           flush=True)
 
 
