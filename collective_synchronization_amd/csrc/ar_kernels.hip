@@ -549,7 +549,7 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
       }
       fence_acquire();
     }
-    if (SHARE && consumer && w == 0 && lane == 0) st_agent_u32(progress + tg, seq);
+    if (SHARE && consumer && w == 0 && lane == 0 && op == 0) st_agent_u32(progress + tg, seq);
     if (sender && a.delay) {
       const uint32_t d = a.delay[(int64_t)op * a.nranks + g];
       if (d) {
@@ -669,6 +669,12 @@ __global__ __launch_bounds__(1024) void k_sim_wide(SimArgs a) {
       }
       __syncthreads();
       if (lds_err) return;                         // whole workgroup
+      // share mode: every slot of this op has been read and re-armed (the
+      // pollers waited for their re-arm stores before the barrier), so rank
+      // 0 publishes the next op as started now, not after its reduce: the
+      // producers' licence for op+2 then reaches them one reduce earlier
+      if (SHARE && w == 0 && lane == 0 && k0 + nb == mine)
+        st_agent_u32(progress + tg, seq_next(seq));
       // ---- reduce in rank order (own wave) ----
       if (own) {
 #pragma unroll
