@@ -125,7 +125,7 @@ def test_sweep_n8_2KiB_4MiB(size, proto):
     _check_all(got, want, ops)
 
 
-@pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel"])
+@pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel", "barrier"])
 def test_skew_shuffle_n16_8x4096_64ops(proto):
     cfg = CONFIGS["n16_skew_8x4096_64ops"]
     n, nops = cfg["nranks"], cfg["nops"]
