@@ -37,6 +37,17 @@ METRIC = ("µs per all-reduce and achieved HBM GB/s vs roofline, "
           "N simulated ranks, 1 MI355X")
 HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _env(name, cast, fallback):
+    """An environment override (unset or empty: the fallback)."""
+    v = os.environ.get(name, "")
+    return fallback if v == "" else cast(v)
+
+
+# environment overrides: AR_TIMEOUT_US (poll deadline), AR_PROTO (default
+# protocol), AR_WG_PER_RANK (tile groups per rank; 0 = the library's choice)
+TIMEOUT_NS = int(_env("AR_TIMEOUT_US", float, 2e6) * 1e3)
 KERNEL_SOURCES = [
     os.path.join(ROOT, "collective_synchronization_amd", "csrc", n)
     for n in ("ar_kernels.hip", "ar_protocols.h", "ar_device.h")
@@ -188,7 +199,7 @@ def measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, war
     ostride = ws.gather_stride() if collective == "allgather" else stride
     outd = torch.zeros((nops * nconsumers, ostride), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
-    kw = dict(timeout_ns=2_000_000_000, waves_per_rank=waves_per_rank, flags=flags)
+    kw = dict(timeout_ns=TIMEOUT_NS, waves_per_rank=waves_per_rank, flags=flags)
     for _ in range(warmup):
         ws.sim(nops, xd, stride, outd, ostride, **kw)
     torch.cuda.synchronize()
@@ -262,7 +273,7 @@ def measure_skew(torch, abi, buffers, inputs, x, proto, nranks, count, nops, ste
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        ws.sim(nops, xd, stride, outd, ostride, timeout_ns=2_000_000_000,
+        ws.sim(nops, xd, stride, outd, ostride, timeout_ns=TIMEOUT_NS,
                delay_ticks=ticks, trace=trace)
         b.record(stream)
         torch.cuda.synchronize()
@@ -306,7 +317,7 @@ def measure_epilogue(torch, abi, buffers, x, proto, nranks, count, steps, warmup
                 ws.pack(yd, stride, stream)
             if e:
                 e[1].record(stream)
-            ws.reduce(outd, stride, timeout_ns=2_000_000_000, stream=stream)
+            ws.reduce(outd, stride, timeout_ns=TIMEOUT_NS, stream=stream)
             if e:
                 e[2].record(stream)
             ws.flip()
@@ -334,7 +345,7 @@ def measure_chain(torch, abi, buffers, x0, proto, nranks, count, nops, steps, wa
     sd = torch.from_numpy(s).to("cuda")
     outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
     geo = abi.ar_sim_chain_geometry(ws.sim_params(nops, xd, stride, outd, stride))
-    kw = dict(timeout_ns=2_000_000_000)
+    kw = dict(timeout_ns=TIMEOUT_NS)
     for _ in range(warmup):
         ws.sim_chain(nops, xd, stride, outd, stride, sd, **kw)
     torch.cuda.synchronize()
@@ -383,7 +394,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--proto", default="sentinel",
+    ap.add_argument("--proto", default=_env("AR_PROTO", str, "sentinel"),
                     choices=["ll", "ll128", "sentinel", "barrier", "auto"],
                     help="auto: the protocol the committed cost table chooses")
     ap.add_argument("--mode", default="system", choices=["share", "system"])
@@ -395,7 +406,7 @@ def main() -> int:
     ap.add_argument("--rows", type=int, default=1)
     ap.add_argument("--hidden", type=int, default=4096)
     ap.add_argument("--nops", type=int, default=64)
-    ap.add_argument("--waves-per-rank", type=int, default=0)
+    ap.add_argument("--waves-per-rank", type=int, default=_env("AR_WG_PER_RANK", int, 0))
     ap.add_argument("--launch", default="auto", choices=["auto", "cooperative", "ordinary"],
                     help="simulator launch: the library's choice, or forced")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -417,6 +428,11 @@ def main() -> int:
                     help="also run ar_probe_copy over BYTES, 3 times (reference "
                          "dispatches for hardware byte counters)")
     args = ap.parse_args()
+    protos = ("ll", "ll128", "sentinel", "barrier", "auto")
+    if args.proto not in protos:          # an AR_PROTO default is not checked by argparse
+        print(f"bench.py: protocol {args.proto!r} (AR_PROTO?) is not one of {protos}",
+              file=sys.stderr)
+        return 2
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark measures "

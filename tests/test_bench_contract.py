@@ -98,3 +98,17 @@ def test_bench_line_fields():
     assert line["single_op_launch"]["kernel_us"] > 0
     ch = line["chain"]
     assert ch["kernel_us_per_op"] > 0 and ch["launch"] in ("ordinary", "cooperative")
+
+
+def test_environment_overrides():
+    env = dict(os.environ, AR_TIMEOUT_US="5", AR_WG_PER_RANK="16", AR_PROTO="ll")
+    r = subprocess.run([sys.executable, "-c",
+                        "import bench, sys; sys.argv = ['bench.py']; "
+                        "print(bench.TIMEOUT_NS)"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT, env=env)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "5000"
+    bad = dict(os.environ, AR_PROTO="bogus")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT, env=bad)
+    assert r.returncode == 2 and "AR_PROTO" in r.stderr and r.stdout == ""
