@@ -7,14 +7,17 @@ geometry), against the CPU oracle.
 2. 8 ranks, bf16 [1,4096], sentinel, dual-buffered, 64 ops; and the same with
    negative NaNs (0xFFFF, 0xFFC0, 0xFF81) injected at 1/1024 of positions.
 3. 4 ranks, bf16 [B,8192], B in {1,4,16}, LL128, 160 ops.
-4. 8 ranks, 2 KiB .. 4 MiB payloads, U[-1,1), LL / LL128 / sentinel /
-   barrier (sampled ops at the largest sizes).
+4. 8 ranks, 2 KiB .. 4 MiB payloads (12 sizes), U[-1,1), LL / LL128 /
+   sentinel / barrier and the protocol the cost table picks, 64 ops per
+   launch (32 from 512 KiB), every op of every consumer.
 5. 16 ranks, bf16 [8,4096], seeded 0-20 us producer skew and shuffled tile
    order per (op, producer), every consumer bit-identical to the oracle.
 
 Every comparison is bit-exact (the method reaches the oracle's result
 exactly: integer encodings and one fixed-order binary32 sum per element).
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -97,32 +100,143 @@ def test_ll128_n4_Bx8192_160ops(batch):
     _check_all(got, oracle.allreduce_ops(x, "ll128", seq0))
 
 
+KIB = 1024
+SWEEP = CONFIGS["n8_sweep_2KiB_4MiB"]
+
+
+def sweep_nops(size):
+    """Ops per launch at one sweep size: 64, or 32 from 512 KiB per rank (the
+    selector sweep's counts, long enough for the library's launch choice)."""
+    return 64 if size < 512 * KIB else 32
+
+
+@functools.lru_cache(maxsize=1)
+def sweep_payload(size):
+    """The seeded U[-1,1) payloads of every op and rank at one sweep size."""
+    count = size // 2
+    return inputs.payload(SWEEP["seed"] + size, (sweep_nops(size), SWEEP["nranks"], count),
+                          SWEEP["dist"])
+
+
+@functools.lru_cache(maxsize=4)
+def sweep_expected(size, proto, collective, seq0):
+    """The oracle's result for every op of one sweep size."""
+    x = sweep_payload(size)
+    if collective == "twoshot":
+        return oracle.twoshot_ops(x, proto, seq0)
+    return oracle.allreduce_ops(x, proto, seq0)
+
+
+def check_ops_on_device(outd, want, ncons, count, label):
+    """Every op of every consumer against the oracle, bit for bit.  The
+    expected rows are uploaded one op at a time and compared on the device,
+    so that gigabytes of outputs need not come back to the host."""
+    nops = want.shape[0]
+    for i in range(nops):
+        w = torch.from_numpy(want[i].view(np.int16)).to(outd.device)
+        got = outd[i * ncons:(i + 1) * ncons, :count]
+        bad = (got != w[None, :])
+        if bool(bad.any()):
+            c, j = [int(v) for v in bad.nonzero()[0].tolist()]
+            g = int(got[c, j].item()) & 0xFFFF
+            raise AssertionError(f"{label}: op {i} consumer {c} element {j}: "
+                                 f"got {g:#06x}, oracle {int(want[i, j]):#06x}")
+
+
 def _sweep_cases():
-    cfg = CONFIGS["n8_sweep_2KiB_4MiB"]
-    for size in cfg["sizes"]:
-        if size not in (2048, 16384, 131072, 1 << 20, 4 << 20):
-            continue
-        for proto in cfg["protos"]:
+    for size in SWEEP["sizes"]:
+        for proto in SWEEP["protos"] + ("auto",):
             yield size, proto
 
 
 @pytest.mark.parametrize("size,proto", list(_sweep_cases()))
 def test_sweep_n8_2KiB_4MiB(size, proto):
-    cfg = CONFIGS["n8_sweep_2KiB_4MiB"]
-    n = cfg["nranks"]
+    """Config 4 at every size and protocol, plus the one-shot protocol
+    ar_select_protocol picks from the committed cost table ("auto"): the
+    sweep's op count with distinct payloads on every op, every op of every
+    consumer compared with the oracle."""
+    n = SWEEP["nranks"]
     count = size // 2
-    nops = 64 if size <= 131072 else 8
-    x = inputs.payload(cfg["seed"] + size, (nops, n, count), cfg["dist"])
-    _, got, seq0 = _run_sim(x, proto, n, n, nops)
-    ops = range(nops) if size <= 131072 else (0, nops // 2, nops - 1)
-    want = {}
-    seq = seq0
-    for i in range(nops):
-        if i in ops:
-            st, want[i] = oracle.allreduce(x[i], proto, seq)
-            assert st == oracle.READY
-        seq = oracle.epoch_next(seq)
-    _check_all(got, want, ops)
+    if proto == "auto":
+        from collective_synchronization_amd import selector
+        table = abi.cost_table(selector.load_table()["entries"])
+        pid, _ = abi.ar_select_protocol(table, size, n)
+        proto = abi.PROTO_NAMES[pid]
+    x = sweep_payload(size)
+    nops = x.shape[0]
+    ws = buffers.Workspace(n, count, proto, n)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride))
+    print(f"[sweep] {size} B {proto} ops={nops} geo={geo}", flush=True)
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    del xd, ws
+    check_ops_on_device(outd, sweep_expected(size, proto, "allreduce", seq0), n, count,
+                        f"{size} B {proto}")
+
+
+def _library_pick(size, nranks):
+    """ar_select_allreduce on the committed cost table: (collective, proto)."""
+    from collective_synchronization_amd import selector
+    table = abi.cost_table(selector.load_table()["entries"])
+    cid, pid, _ = abi.ar_select_allreduce(table, size, nranks)
+    return selector.COLLECTIVES[cid], abi.PROTO_NAMES[pid]
+
+
+@pytest.mark.parametrize("size", SWEEP["sizes"])
+def test_sweep_n8_library_pick(size):
+    """Config 4's selector column end to end: the all-reduce algorithm
+    (one-shot or two-shot) and protocol that ar_select_allreduce picks from
+    the committed cost table at each size, run in the persistent simulator
+    and checked on every op of every consumer against the oracle."""
+    n = SWEEP["nranks"]
+    count = size // 2
+    coll, proto = _library_pick(size, n)
+    x = sweep_payload(size)
+    nops = x.shape[0]
+    ws = buffers.Workspace(n, count, proto, n, collective=coll)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    print(f"[pick] {size} B -> {coll}/{proto} ops={nops}", flush=True)
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    del xd, ws
+    check_ops_on_device(outd, sweep_expected(size, proto, coll, seq0), n, count,
+                        f"{size} B {coll}/{proto}")
+
+
+def test_skew_n16_8x4096_library_pick():
+    """Config 5 with the algorithm and protocol the cost table picks, under
+    the seeded 0-20 us producer skew (and the shuffled tile order where the
+    pick is the one-shot): every consumer bit-identical to the oracle."""
+    cfg = CONFIGS["n16_skew_8x4096_64ops"]
+    n, nops = cfg["nranks"], cfg["nops"]
+    count = cfg["batches"][0] * cfg["hidden"]
+    coll, proto = _library_pick(2 * count, n)
+    x = inputs.payload(cfg["seed"], (nops, n, count), cfg["dist"])
+    hz = abi.ar_wallclock_hz()
+    d_us = inputs.delays_us(cfg["seed"] + 1, nops, n, cfg["delay_max_us"])
+    ticks = torch.from_numpy(np.round(d_us * hz * 1e-6).astype(np.int32)).to("cuda")
+    ws = buffers.Workspace(n, count, proto, n, collective=coll)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    kw = dict(timeout_ns=TIMEOUT_NS, delay_ticks=ticks)
+    if coll == "allreduce":
+        geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride))
+        order = inputs.tile_orders(cfg["seed"] + 2, nops, n, geo["tiles_per_wave"])
+        kw["tile_order"] = torch.from_numpy(order.view(np.int16)).to("cuda")
+    print(f"[pick n16] {coll}/{proto}", flush=True)
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, stride, **kw)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    want = (oracle.twoshot_ops if coll == "twoshot" else oracle.allreduce_ops)(x, proto, seq0)
+    check_ops_on_device(outd, want, n, count, f"n16 {coll}/{proto}")
 
 
 @pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel", "barrier"])
