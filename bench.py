@@ -47,7 +47,22 @@ def _env(name, cast, fallback):
 
 # environment overrides: AR_TIMEOUT_US (poll deadline), AR_PROTO (default
 # protocol), AR_WG_PER_RANK (tile groups per rank; 0 = the library's choice)
-TIMEOUT_NS = int(_env("AR_TIMEOUT_US", float, 2e6) * 1e3)
+MAX_TIMEOUT_US = 60e6          # the library's bound (AR_MAX_TIMEOUT_NS, 60 s)
+
+
+def _timeout_ns():
+    """AR_TIMEOUT_US as nanoseconds: (None, message) unless 0 < value <= 60 s."""
+    try:
+        us = _env("AR_TIMEOUT_US", float, 2e6)
+    except ValueError:
+        return None, f"AR_TIMEOUT_US={os.environ.get('AR_TIMEOUT_US')!r} is not a number"
+    if not (0.0 < us <= MAX_TIMEOUT_US) or int(us * 1e3) < 1:
+        return None, (f"AR_TIMEOUT_US={us:g} must be a poll deadline above 0 and at most "
+                      f"{MAX_TIMEOUT_US:g} us")
+    return int(us * 1e3), ""
+
+
+TIMEOUT_NS, TIMEOUT_ERROR = _timeout_ns()
 KERNEL_SOURCES = [
     os.path.join(ROOT, "collective_synchronization_amd", "csrc", n)
     for n in ("ar_kernels.hip", "ar_protocols.h", "ar_device.h")
@@ -428,6 +443,9 @@ def main() -> int:
                     help="also run ar_probe_copy over BYTES, 3 times (reference "
                          "dispatches for hardware byte counters)")
     args = ap.parse_args()
+    if TIMEOUT_NS is None:
+        print(f"bench.py: {TIMEOUT_ERROR}", file=sys.stderr)
+        return 2
     protos = ("ll", "ll128", "sentinel", "barrier", "auto")
     if args.proto not in protos:          # an AR_PROTO default is not checked by argparse
         print(f"bench.py: protocol {args.proto!r} (AR_PROTO?) is not one of {protos}",

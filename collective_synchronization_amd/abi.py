@@ -27,6 +27,7 @@ AR_SIM_NARROW = 2
 AR_SIM_WIDE = 4
 AR_SIM_ORDINARY = 8
 AR_MAX_RANKS = 16
+AR_MAX_TIMEOUT_NS = 60_000_000_000
 AR_ALLREDUCE, AR_ALLGATHER, AR_TWOSHOT = 0, 1, 2
 COLLECTIVE_IDS = {"allreduce": AR_ALLREDUCE, "allgather": AR_ALLGATHER,
                   "twoshot": AR_TWOSHOT}

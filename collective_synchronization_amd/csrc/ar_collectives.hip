@@ -1433,6 +1433,7 @@ extern "C" int ar_gather_validate(const ar_desc* d, void* scratch, void* out,
   if (d->collective != AR_ALLGATHER) return AR_EINVAL;
   if (e.parity > 1u || e.seq == 0u) return AR_EINVAL;
   if (flags & ~AR_FLAG_REARM) return AR_EINVAL;
+  if (!timeout_ok(timeout_ns)) return AR_EINVAL;
   const int64_t R = (d->count + 7) / 8 * 8;
   rc = check_rows(out, out_stride, (int64_t)d->nranks * R);
   if (rc) return rc;

@@ -48,6 +48,9 @@ inline int device_info(DeviceInfo* out) {
   return AR_OK;
 }
 
+// A poll deadline the library accepts (0 means the default of 1 s).
+inline bool timeout_ok(uint64_t ns) { return ns <= AR_MAX_TIMEOUT_NS; }
+
 inline uint64_t ns_to_ticks(uint64_t ns, double hz) {
   if (ns == 0) ns = 1000000000ull;
   const double t = (double)ns * hz * 1e-9;

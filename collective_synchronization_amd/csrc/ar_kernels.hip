@@ -1125,6 +1125,7 @@ static int check_sim(const ar_sim_params* p) {
   if ((p->flags & AR_SIM_COOPERATIVE) && (p->flags & AR_SIM_ORDINARY)) return AR_EINVAL;
   if ((p->flags & AR_SIM_NARROW) && (p->flags & AR_SIM_WIDE)) return AR_EINVAL;
   if (p->epoch.parity > 1u || p->epoch.seq == 0u) return AR_EINVAL;
+  if (!timeout_ok(p->timeout_ns)) return AR_EINVAL;
   rc = check_rows(p->in, p->in_stride, d->count);
   if (rc) return rc;
   rc = check_rows(p->out, p->out_stride, d->count);
@@ -1290,6 +1291,7 @@ int ar_reduce_validate(const ar_desc* d, void* scratch, void* out,
   if (rc) return rc;
   if (e.parity > 1u || e.seq == 0u) return AR_EINVAL;
   if (flags & ~AR_FLAG_REARM) return AR_EINVAL;
+  if (!timeout_ok(timeout_ns)) return AR_EINVAL;
   if (d->collective == AR_ALLGATHER) return AR_EINVAL;
   rc = check_rows(out, out_stride, d->count);
   if (rc) return rc;

@@ -77,6 +77,10 @@ typedef enum {
 
 #define AR_MAX_RANKS 16
 
+/* Largest poll deadline (timeout_ns) any call accepts: 60 s.  A larger value
+ * is rejected with AR_EINVAL, so that every wait stays bounded. */
+#define AR_MAX_TIMEOUT_NS 60000000000ull
+
 /*
  * Encoded bytes E of one rank's payload of `count` elements:
  *   LL 16*ceil(count/4), LL128 128*ceil(count/60), SENTINEL and BARRIER
@@ -244,7 +248,8 @@ int ar_arm_sentinel(const ar_desc* d, void* scratch, int32_t parity,
  *        out_stride a multiple of 8 and >= count.
  *   ctrl: device control block; a poll that passes timeout_ns writes
  *        AR_ETIMEOUT, an impossible LL/LL128 flag writes AR_ECORRUPT (the
- *        output of that tile is then not written).  timeout_ns 0 = 1 s.
+ *        output of that tile is then not written).  timeout_ns 0 = 1 s;
+ *        above AR_MAX_TIMEOUT_NS: AR_EINVAL.
  *   flags: AR_FLAG_REARM (SENTINEL only) re-arms what was read, so the same
  *        parity is ready for the op two epochs later.
  * BARRIER payloads carry no evidence: this call then trusts stream order
@@ -397,7 +402,8 @@ typedef struct {
     void* scratch;
     void* ctrl;
     ar_epoch epoch;             /* epoch of op 0 */
-    uint64_t timeout_ns;        /* per poll; 0 = 1 s */
+    uint64_t timeout_ns;        /* per poll; 0 = 1 s; at most
+                                   AR_MAX_TIMEOUT_NS (else AR_EINVAL) */
     const uint32_t* delay_ticks;
     const uint16_t* tile_order;
     uint64_t* trace;

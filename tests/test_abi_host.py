@@ -160,6 +160,33 @@ def test_sim_argument_checks():
     assert run(epoch=abi.ar_epoch(0, 1)) == abi.AR_EINVAL
 
 
+def test_timeout_bound():
+    """Every waiting call rejects a poll deadline above AR_MAX_TIMEOUT_NS
+    (60 s), before any device work, so waits stay bounded; 60 s itself and
+    0 (the 1 s default) pass the check."""
+    assert abi.AR_MAX_TIMEOUT_NS == 60_000_000_000
+    too_long = abi.AR_MAX_TIMEOUT_NS + 1
+    wrapped = ctypes.c_uint64(-5000).value          # what a negative value becomes
+    ep = abi.ar_epoch(1, 0)
+    d = abi.make_desc(8, 4096, "sentinel")
+    rv = lambda t: _code("ar_reduce_validate", ctypes.byref(d), FAKE, FAKE, 4096, ep, FAKE,
+                         ctypes.c_uint64(t), 0, None)
+    assert rv(too_long) == abi.AR_EINVAL
+    assert rv(wrapped) == abi.AR_EINVAL
+    g = abi.make_desc(4, 100, "ll", 4, "allgather")
+    assert _code("ar_gather_validate", ctypes.byref(g), FAKE, FAKE, 4 * 104, ep, FAKE,
+                 ctypes.c_uint64(too_long), 0, None) == abi.AR_EINVAL
+    for t in (too_long, wrapped):
+        p = abi.sim_params(abi.make_desc(8, 4096, "ll", 8), 4, FAKE, 4096, FAKE, 4096,
+                           FAKE, FAKE, ep, timeout_ns=t)
+        assert _code("ar_sim_run", ctypes.byref(p), None) == abi.AR_EINVAL
+        assert _code("ar_sim_chain_run", ctypes.byref(p), FAKE, None) == abi.AR_EINVAL
+    # the bound itself is accepted: the same call then fails later, on the
+    # misaligned control block, not on the deadline
+    assert _code("ar_reduce_validate", ctypes.byref(d), FAKE, FAKE, 4096, ep, FAKE + 4,
+                 ctypes.c_uint64(abi.AR_MAX_TIMEOUT_NS), 0, None) == abi.AR_EALIGN
+
+
 def _table(rows):
     return abi.cost_table(rows)
 

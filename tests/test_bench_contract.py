@@ -112,3 +112,9 @@ def test_environment_overrides():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")],
                        capture_output=True, text=True, timeout=120, cwd=ROOT, env=bad)
     assert r.returncode == 2 and "AR_PROTO" in r.stderr and r.stdout == ""
+    # the poll deadline must be positive and within the library's 60 s bound
+    for v in ("-5000", "0", "6.01e7", "1e9", "abc"):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")],
+                           capture_output=True, text=True, timeout=120, cwd=ROOT,
+                           env=dict(os.environ, AR_TIMEOUT_US=v))
+        assert r.returncode == 2 and "AR_TIMEOUT_US" in r.stderr and r.stdout == "", v
