@@ -28,21 +28,44 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = ["hipcc", *FLAGS, "-o", tmp, *SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _finish(proc):
+    _, stderr = proc.communicate()
     # hipcc's host pass does not know the packed-fp32 feature; that note is harmless
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
+    err = "\n".join(l for l in stderr.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
+    return err
+
+
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the sources in parallel (one object each), then link `out`.
+    `defines`: extra -D options (a variant build, e.g. AR_FORMAL_FENCES=1)."""
+    tag = os.path.splitext(os.path.basename(out))[0]
+    objdir = os.path.join(PKG, "_build", tag)
+    os.makedirs(objdir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
+    cflags = [f for f in FLAGS if f != "-shared"]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        procs.append(_run(["hipcc", *cflags, *dflags, "-c", "-o", obj, src], verbose))
+    errs = [_finish(p) for p in procs]
+    tmp = out + ".tmp"
+    errs.append(_finish(_run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC",
+                              "-o", tmp, *objs], verbose)))
+    err = "\n".join(e for e in errs if e.strip())
+    if verbose and err:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def device_asm(out_path: str) -> str:
