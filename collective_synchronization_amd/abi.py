@@ -28,6 +28,7 @@ AR_SIM_WIDE = 4
 AR_SIM_ORDINARY = 8
 AR_MAX_RANKS = 16
 AR_MAX_TIMEOUT_NS = 60_000_000_000
+AR_STATIC_SCRATCH_BYTES = 64 << 20
 AR_ALLREDUCE, AR_ALLGATHER, AR_TWOSHOT = 0, 1, 2
 COLLECTIVE_IDS = {"allreduce": AR_ALLREDUCE, "allgather": AR_ALLGATHER,
                   "twoshot": AR_TWOSHOT}
@@ -119,6 +120,7 @@ _SIGS = {
                       ctypes.c_int),
     "ar_scale_rows": ([_i32, _i64, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "ar_sim_run": ([ctypes.POINTER(ar_sim_params), _vp], ctypes.c_int),
+    "ar_sim_run_static": ([ctypes.POINTER(ar_sim_params), _vp, _vp], ctypes.c_int),
     "ar_sim_chain_run": ([ctypes.POINTER(ar_sim_params), _vp, _vp], ctypes.c_int),
     "ar_sim_chain_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
                                ctypes.POINTER(_i32)], ctypes.c_int),
@@ -317,6 +319,13 @@ def sim_params(desc, nops, inp, in_stride, out, out_stride, scratch, ctrl, epoch
 
 def ar_sim_run(params: ar_sim_params, stream=None) -> None:
     _check(_lib.ar_sim_run(ctypes.byref(params), _stream(stream)), "ar_sim_run")
+
+
+def ar_sim_run_static(params: ar_sim_params, status, stream=None) -> None:
+    """ar_sim_run on the library's own receive buffers (params.scratch and
+    params.ctrl must be None); status: device int32, written after the run."""
+    _check(_lib.ar_sim_run_static(ctypes.byref(params), _ptr(status), _stream(stream)),
+           "ar_sim_run_static")
 
 
 def ar_sim_chain_run(params: ar_sim_params, scales, stream=None) -> None:

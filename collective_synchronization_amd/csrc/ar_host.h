@@ -191,5 +191,8 @@ int coll_sim_geometry(const ar_sim_params* p, int32_t* groups, int32_t* tiles,
 int coll_sim_run(const ar_sim_params* p, hipStream_t s);
 int chain_sim_geometry(const ar_sim_params* p, int32_t* blocks, int32_t* cooperative);
 int chain_sim_run(const ar_sim_params* p, const float* scales, hipStream_t s);
+// Every host-side check ar_sim_run makes, including the grid it would launch,
+// without enqueuing anything (ar_kernels.hip).
+int sim_validate(const ar_sim_params* p);
 
 }  // namespace ar

@@ -1138,6 +1138,20 @@ static int check_sim(const ar_sim_params* p) {
   return AR_OK;
 }
 
+int sim_validate(const ar_sim_params* p) {
+  int rc = check_sim(p);
+  if (rc) return rc;
+  const ar_desc* d = &p->desc;
+  if (d->collective == AR_ALLGATHER && p->out_stride < (int64_t)d->nranks * ((d->count + 7) / 8 * 8))
+    return AR_EINVAL;
+  if (d->count == 0) return AR_OK;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc) return rc;
+  if ((p->flags & AR_SIM_COOPERATIVE) && !di.coop) return AR_ENODEV;
+  return ar_sim_geometry(p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+}
+
 }  // namespace ar
 
 // ============================================================ C ABI ======

@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 LIB = os.path.join(PKG, "libcsync_ar.so")
 SOURCES = [os.path.join(HERE, "ar_kernels.hip"), os.path.join(HERE, "ar_collectives.hip"),
+           os.path.join(HERE, "ar_static.hip"),
            os.path.join(HERE, "ar_select.cpp")]
 HEADERS = [os.path.join(HERE, "ar_device.h"), os.path.join(HERE, "ar_protocols.h"),
            os.path.join(HERE, "ar_host.h"),

@@ -412,6 +412,28 @@ typedef struct {
 int ar_sim_run(const ar_sim_params* p, void* stream);
 
 /*
+ * ar_sim_run_static -- ar_sim_run for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the receive buffers and the control block come from a
+ * library-owned device array of AR_STATIC_SCRATCH_BYTES (64 MiB) of receive
+ * buffers plus one control block, one copy per device, held until the
+ * process ends.  The call allocates nothing.
+ *   p: as for ar_sim_run, with p->scratch and p->ctrl NULL (else AR_EINVAL);
+ *      ar_scratch_bytes(&p->desc) above AR_STATIC_SCRATCH_BYTES: AR_ESIZE.
+ *      Every call clears the control block and the receive buffers it uses
+ *      (zero, or the sentinel for AR_SENTINEL) with fill kernels on
+ *      `stream` first, so p->epoch need not carry over between calls.
+ *   status: device int32, written after the simulator (stream-ordered)
+ *      with the control block's status word: 0, AR_ETIMEOUT or AR_ECORRUPT.
+ *      Not written when the call returns an error.
+ * All calls on one device share the array and leave their contents in it:
+ * calls that overlap in time on one device (streams not ordered against
+ * each other) race.  Errors otherwise as for ar_sim_run.
+ */
+#define AR_STATIC_SCRATCH_BYTES (64ll << 20)
+int ar_sim_run_static(const ar_sim_params* p, int32_t* status, void* stream);
+
+/*
  * Geometry ar_sim_run will use for these parameters: tile groups per rank
  * (a wave each in the narrow kernel, a workgroup each in the wide kernel),
  * tiles per rank (1 KiB of slot each), tiles per group, total workgroups,

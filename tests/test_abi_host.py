@@ -187,6 +187,24 @@ def test_timeout_bound():
                  ctypes.c_uint64(abi.AR_MAX_TIMEOUT_NS), 0, None) == abi.AR_EALIGN
 
 
+def test_static_sim_argument_checks():
+    """ar_sim_run_static: caller buffers, a missing status word and a
+    descriptor beyond the library's own array are refused before any device
+    work."""
+    ep = abi.ar_epoch(1, 0)
+    d = abi.make_desc(8, 4096, "sentinel", 8)
+    run = lambda p, st=FAKE: _code("ar_sim_run_static", ctypes.byref(p), st, None)
+    own = abi.sim_params(d, 4, FAKE, 4096, FAKE, 4096, None, None, ep)
+    assert run(own, None) == abi.AR_EINVAL
+    assert run(own, FAKE + 2) == abi.AR_EALIGN
+    assert run(abi.sim_params(d, 4, FAKE, 4096, FAKE, 4096, FAKE, None, ep)) == abi.AR_EINVAL
+    assert run(abi.sim_params(d, 4, FAKE, 4096, FAKE, 4096, None, FAKE, ep)) == abi.AR_EINVAL
+    big = abi.make_desc(16, 1 << 20, "ll", 16)
+    assert abi.ar_scratch_bytes(big) > abi.AR_STATIC_SCRATCH_BYTES
+    assert run(abi.sim_params(big, 1, FAKE, 1 << 20, FAKE, 1 << 20, None, None, ep)) == \
+        abi.AR_ESIZE
+
+
 def _table(rows):
     return abi.cost_table(rows)
 
