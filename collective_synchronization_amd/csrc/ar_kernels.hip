@@ -154,17 +154,25 @@ __device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
 //
 // A rank's own contribution never goes through memory: its consumer takes
 // the encoded chunk from registers and its producer skips its own buffer.
-// When a wave owns a single tile (the small-message case) the op loop is
-// software-pipelined: the next op's payload is loaded while this op is
-// polled, and this op's output is stored after the next op's stores are
-// out, so neither input load nor output store sits between one op's
-// validation and the next op's transmission.
+// ONE: every wave owns at most one tile (the small-message case; not the
+// barrier baseline).  The op loop is then software-pipelined: the next op's
+// payload is loaded while this op is polled, and this op's output is stored
+// after the next op's stores are out, so neither input load nor output store
+// sits between one op's validation and the next op's transmission.
+// Otherwise (many tiles per wave, the large-payload case) a wave sends all
+// its tiles, then receives them kReadBatch at a time: every chunk of a batch
+// is loaded in one round, so a batch whose data has arrived costs one memory
+// round trip (LL128: plus one flag probe per op, see probe_line_flags).  The
+// two variants are separate kernels so that neither carries the other's
+// registers.
 // EXTRAS: the launch uses producer delays, a tile order or a trace.  The
 // variant without them drops those paths at compile time: less code and
 // fewer scalar registers in the op loop (8 ranks [1,4096]: 4.5% faster per
 // op in the workgroup kernel, 9% at 16 ranks).
-template <int P, int NMAX, bool SHARE, bool EXTRAS>
+template <int P, int NMAX, bool SHARE, bool EXTRAS, bool ONE>
 __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
+  constexpr bool kFast = ONE && P != kBarrier;
+  constexpr int kReadBatch = NMAX <= 4 ? 4 : (NMAX <= 8 ? 2 : 1);
   if constexpr (!EXTRAS) {
     a.delay = nullptr;
     a.order = nullptr;
@@ -182,11 +190,11 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
   const int xr = (x - rot) & 7;
   const int wr = (qq * 8 + xr) * kSimWPB + wave;
   if (wr >= a.T) return;
-  const int mine = (a.T - 1 - wr) / a.W + 1;
+  // tiles of this wave (1 in the one-tile variant: T <= W there)
+  const int mine = kFast ? 1 : (a.T - 1 - wr) / a.W + 1;
   const bool consumer = SHARE ? (g == 0) : true;
   const int cself = SHARE ? 0 : g;
   const int skip = consumer ? cself : -1;       // own buffer, fed from registers
-  const bool fast = (mine == 1) && (P != kBarrier);
 
   const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
   const uint32_t N = (uint32_t)a.nranks;
@@ -203,12 +211,12 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
                            (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 
-  uint32_t wnext[4] = {0u, 0u, 0u, 0u};     // fast path: next op's payload
-  u32x4 v[NMAX];                            // fast path: last validated op
+  uint32_t wnext[4] = {0u, 0u, 0u, 0u};     // one-tile: next op's payload
+  u32x4 v[NMAX];                            // one-tile: last validated op
   bool out_pending = false;
   const uint32_t row_bytes = (uint32_t)(((a.count * 2) + 15) & ~int64_t(15));
   const int keep = chunk_keep<P>(a.count, wr, lane);
-  if (fast) load_chunk<P>(a.in + (int64_t)g * a.in_stride, row_bytes, wr, lane, wnext);
+  if (kFast) load_chunk<P>(a.in + (int64_t)g * a.in_stride, row_bytes, wr, lane, wnext);
 
   uint32_t seq = a.seq0;
   uint32_t par = a.parity0;
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
     const uint16_t* row = a.in + ((int64_t)op * op_rows + g) * a.in_stride;
     const uint32_t dst0 = (pp * N + (uint32_t)g) * a.slot_bytes;
     u32x4 own_v = u32x4{0u, 0u, 0u, 0u};
-    if (fast) {
+    if constexpr (kFast) {
       mask_words(wnext, keep);
       own_v = encode_words<P>(wnext, lane, seq);
       store_chunk<P>(rs, dst0, cstride, a.nconsumers, skip, wr, a.E, lane, own_v);
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
     // ---- consume(op) ----
     if (consumer) {
       const uint32_t src0 = ((uint32_t)cself * 2u + pp) * N * a.slot_bytes;
-      if (fast) {
+      if constexpr (kFast) {
         if (poll_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, wr, a.E, seq,
                                stale, true, g, own_v, a.ctrl, a.timeout_ticks,
                                lane, v) != 0)
@@ -333,15 +341,36 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
           fence_acquire();
         }
         uint16_t* orow = a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride;
-        u32x4 vt[NMAX];
-        for (int k = 0; k < mine; ++k) {
-          const int tile = wr + k * a.W;
-          const u32x4 mine_v = encode_chunk<P>(row, row_bytes, a.count, tile, lane, seq);
-          if (poll_tile<P, NMAX>(rs, src0, a.slot_bytes, a.nranks, tile, a.E, seq,
-                                 stale, true, g, mine_v, a.ctrl, a.timeout_ticks,
-                                 lane, vt) != 0)
+        // LL128: one flag per producer wave orders all of its data of the op
+        if (P == kLL128 &&
+            probe_line_flags(rs, src0, a.slot_bytes, a.nranks, wr, a.E, seq, stale, g,
+                             a.ctrl, a.timeout_ticks, lane) != 0)
+          return;
+        for (int k0 = 0; k0 < mine; k0 += kReadBatch) {
+          const int nb = (mine - k0) < kReadBatch ? (mine - k0) : kReadBatch;
+          int tl[kReadBatch];
+          uint32_t wv[kReadBatch][4];
+          u32x4 ov[kReadBatch];
+          // the rank's own chunks (input loads of the batch together)
+#pragma unroll
+          for (int j = 0; j < kReadBatch; ++j) {
+            tl[j] = wr + (k0 + j) * a.W;
+            load_chunk<P>(row, j < nb ? row_bytes : 0u, tl[j], lane, wv[j]);
+          }
+#pragma unroll
+          for (int j = 0; j < kReadBatch; ++j) {
+            mask_words(wv[j], chunk_keep<P>(a.count, tl[j], lane));
+            ov[j] = encode_words<P>(wv[j], lane, seq);
+          }
+          u32x4 vt[kReadBatch][NMAX];
+          if (read_tiles<P, NMAX, kReadBatch>(rs, src0, a.slot_bytes, a.nranks, tl, nb, a.E,
+                                              seq, stale, true, g, ov, a.ctrl,
+                                              a.timeout_ticks, lane, vt) != 0)
             return;
-          reduce_store_tile<P, NMAX>(vt, a.nranks, tile, a.E, lane, orow, a.count);
+#pragma unroll
+          for (int j = 0; j < kReadBatch; ++j)
+            if (j < nb)
+              reduce_store_tile<P, NMAX>(vt[j], a.nranks, tl[j], a.E, lane, orow, a.count);
         }
         if (P == kBarrier) {
           fence_release();
@@ -932,37 +961,43 @@ static hipError_t launch_reduce_n(const ReduceArgs& a, int blocks, hipStream_t s
   return launch_reduce<P, 16>(a, blocks, s);
 }
 
+// The kernel variant: `one` = every wave or workgroup owns at most one tile
+// (the narrow kernel's software-pipelined variant, the wide kernel's BATCH 1);
+// otherwise the variant for many tiles.  The barrier baseline has only the
+// latter.
 template <int P, int NMAX, bool SHARE, bool EXTRAS>
-static const void* sim_kernel(bool wide, int tpw) {
-  if (!wide) return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS>);
-  return tpw <= 1 ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 1, EXTRAS>)
-                  : reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 2, EXTRAS>);
+static const void* sim_kernel(bool wide, bool one) {
+  if (!wide) {
+    if constexpr (P != kBarrier)
+      if (one) return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS, true>);
+    return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS, false>);
+  }
+  return one ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 1, EXTRAS>)
+             : reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 2, EXTRAS>);
 }
 
 template <int P, int NMAX, bool SHARE>
-static hipError_t launch_sim(const SimArgs& a, int blocks, bool coop, bool wide,
+static hipError_t launch_sim(const SimArgs& a, int blocks, bool coop, bool wide, bool one,
                              hipStream_t s) {
   SimArgs copy = a;
   void* args[] = {&copy};
   const bool extras = a.delay || a.order || a.trace;
-  const void* fn = extras ? sim_kernel<P, NMAX, SHARE, true>(wide, a.TPW)
-                          : sim_kernel<P, NMAX, SHARE, false>(wide, a.TPW);
+  const void* fn = extras ? sim_kernel<P, NMAX, SHARE, true>(wide, one)
+                          : sim_kernel<P, NMAX, SHARE, false>(wide, one);
   const dim3 block(wide ? kWave * a.nranks : kSimBlock);
   if (coop) return hipLaunchCooperativeKernel(fn, dim3(blocks), block, args, 0, s);
   return hipLaunchKernel(fn, dim3(blocks), block, args, 0, s);
 }
 
-// The smallest occupancy of the variants the launch may pick (one or two
-// tiles per workgroup, with or without the optional features).
+// The smaller occupancy of the variant with and without the optional
+// features (a launch's grid is sized before it is known which it takes).
 template <int P, int NMAX, bool SHARE>
-static int occupancy_of(bool wide, int nranks) {
-  const void* fns[4] = {sim_kernel<P, NMAX, SHARE, false>(wide, 1),
-                        sim_kernel<P, NMAX, SHARE, false>(wide, 2),
-                        sim_kernel<P, NMAX, SHARE, true>(wide, 1),
-                        sim_kernel<P, NMAX, SHARE, true>(wide, 2)};
+static int occupancy_of(bool wide, bool one, int nranks) {
+  const void* fns[2] = {sim_kernel<P, NMAX, SHARE, false>(wide, one),
+                        sim_kernel<P, NMAX, SHARE, true>(wide, one)};
   const int threads = wide ? kWave * nranks : kSimBlock;
   int occ = 0;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fns[i], threads, 0) != hipSuccess)
       return 0;
@@ -973,32 +1008,35 @@ static int occupancy_of(bool wide, int nranks) {
 
 template <int P>
 static hipError_t dispatch_sim_p(const SimArgs& a, bool share, int blocks, bool coop,
-                                 bool wide, hipStream_t s) {
+                                 bool wide, bool one, hipStream_t s) {
   if (a.nranks <= 4)
-    return share ? launch_sim<P, 4, true>(a, blocks, coop, wide, s)
-                 : launch_sim<P, 4, false>(a, blocks, coop, wide, s);
+    return share ? launch_sim<P, 4, true>(a, blocks, coop, wide, one, s)
+                 : launch_sim<P, 4, false>(a, blocks, coop, wide, one, s);
   if (a.nranks <= 8)
-    return share ? launch_sim<P, 8, true>(a, blocks, coop, wide, s)
-                 : launch_sim<P, 8, false>(a, blocks, coop, wide, s);
-  return share ? launch_sim<P, 16, true>(a, blocks, coop, wide, s)
-               : launch_sim<P, 16, false>(a, blocks, coop, wide, s);
+    return share ? launch_sim<P, 8, true>(a, blocks, coop, wide, one, s)
+                 : launch_sim<P, 8, false>(a, blocks, coop, wide, one, s);
+  return share ? launch_sim<P, 16, true>(a, blocks, coop, wide, one, s)
+               : launch_sim<P, 16, false>(a, blocks, coop, wide, one, s);
 }
 
 template <int P>
-static int occupancy_p(int nranks, bool share, bool wide) {
+static int occupancy_p(int nranks, bool share, bool wide, bool one) {
   if (nranks <= 4)
-    return share ? occupancy_of<P, 4, true>(wide, nranks) : occupancy_of<P, 4, false>(wide, nranks);
+    return share ? occupancy_of<P, 4, true>(wide, one, nranks)
+                 : occupancy_of<P, 4, false>(wide, one, nranks);
   if (nranks <= 8)
-    return share ? occupancy_of<P, 8, true>(wide, nranks) : occupancy_of<P, 8, false>(wide, nranks);
-  return share ? occupancy_of<P, 16, true>(wide, nranks) : occupancy_of<P, 16, false>(wide, nranks);
+    return share ? occupancy_of<P, 8, true>(wide, one, nranks)
+                 : occupancy_of<P, 8, false>(wide, one, nranks);
+  return share ? occupancy_of<P, 16, true>(wide, one, nranks)
+               : occupancy_of<P, 16, false>(wide, one, nranks);
 }
 
-static int sim_occupancy(int proto, int nranks, bool share, bool wide) {
+static int sim_occupancy(int proto, int nranks, bool share, bool wide, bool one) {
   switch (proto) {
-    case kLL: return occupancy_p<kLL>(nranks, share, wide);
-    case kLL128: return occupancy_p<kLL128>(nranks, share, wide);
-    case kSentinel: return occupancy_p<kSentinel>(nranks, share, wide);
-    default: return occupancy_p<kBarrier>(nranks, share, wide);
+    case kLL: return occupancy_p<kLL>(nranks, share, wide, one);
+    case kLL128: return occupancy_p<kLL128>(nranks, share, wide, one);
+    case kSentinel: return occupancy_p<kSentinel>(nranks, share, wide, one);
+    default: return occupancy_p<kBarrier>(nranks, share, wide, one);
   }
 }
 
@@ -1006,6 +1044,7 @@ struct SimGeom {
   int32_t W, Q, T, TPW, blocks;
   bool wide;
   bool coop;                 // cooperative launch
+  bool one;                  // the one-tile kernel variant (TPW <= 1)
 };
 
 // The wide kernel (a workgroup of one wave per peer) serves LL, LL128 and
@@ -1018,18 +1057,13 @@ static bool sim_force_wide(const ar_sim_params* p) {
   return p->desc.proto != kBarrier && (p->flags & AR_SIM_WIDE) != 0;
 }
 
-static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wide,
-                           bool coop, SimGeom* g) {
+// Grid for one kernel variant: Q workgroups (or waves) per rank and XCD
+// within the residency the variant's occupancy allows.
+static int sim_plan(const ar_sim_params* p, const DeviceInfo& di, bool wide, bool coop,
+                    bool one, int64_t T, int64_t* Q_out) {
   const ar_desc* d = &p->desc;
-  const int64_t E = encoded_bytes(d->proto, d->count);
-  const int64_t T = ceil_div64(E, kTileBytes);
-  if (T <= 0) {
-    *g = SimGeom{0, 0, 0, 0, 0, wide, coop};
-    return AR_OK;
-  }
-  if (T > (int64_t(1) << 24)) return AR_ESIZE;
   const bool share = d->nconsumers == 1 && d->nranks > 1;
-  const int occ = sim_occupancy(d->proto, d->nranks, share, wide);
+  const int occ = sim_occupancy(d->proto, d->nranks, share, wide, one);
   if (occ <= 0) return AR_ELAUNCH;
   // Every workgroup waits on others, so the whole grid must be resident at
   // once.  An ordinary launch keeps the grid to half of what the occupancy
@@ -1055,6 +1089,33 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
     if (Q > qmax) Q = qmax;
     if (Q < 1) Q = 1;
   }
+  *Q_out = Q;
+  return AR_OK;
+}
+
+static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wide,
+                           bool coop, SimGeom* g) {
+  const ar_desc* d = &p->desc;
+  const int64_t E = encoded_bytes(d->proto, d->count);
+  const int64_t T = ceil_div64(E, kTileBytes);
+  if (T <= 0) {
+    *g = SimGeom{0, 0, 0, 0, 0, wide, coop, false};
+    return AR_OK;
+  }
+  if (T > (int64_t(1) << 24)) return AR_ESIZE;
+  const int64_t per_q = wide ? 8 : kSimWavesPerQ;
+  // the one-tile variant when its own residency gives every wave (or group)
+  // at most one tile; otherwise the many-tile variant, sized by its own
+  // (the variant launched is always the one whose occupancy sized the grid)
+  int64_t Q = 0;
+  bool one = false;
+  if (wide || d->proto != kBarrier) {
+    if (sim_plan(p, di, wide, coop, true, T, &Q) == AR_OK && T <= per_q * Q) one = true;
+  }
+  if (!one) {
+    const int rc = sim_plan(p, di, wide, coop, false, T, &Q);
+    if (rc) return rc;
+  }
   const int64_t W = per_q * Q;
   g->W = (int32_t)W;
   g->Q = (int32_t)Q;
@@ -1063,6 +1124,7 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
   g->blocks = (int32_t)(8 * Q * d->nranks);
   g->wide = wide;
   g->coop = coop;
+  g->one = one;
   return AR_OK;
 }
 
@@ -1405,10 +1467,12 @@ static int sim_launch(const ar_sim_params* p, const DeviceInfo& di, const SimGeo
   if ((uint64_t)a.p_total * (uint64_t)(p->nops + 1) >= 0xFFFFFFFFull) return AR_ESIZE;
   hipError_t e;
   switch (d->proto) {
-    case kLL: e = dispatch_sim_p<kLL>(a, share, g.blocks, g.coop, g.wide, s); break;
-    case kLL128: e = dispatch_sim_p<kLL128>(a, share, g.blocks, g.coop, g.wide, s); break;
-    case kSentinel: e = dispatch_sim_p<kSentinel>(a, share, g.blocks, g.coop, g.wide, s); break;
-    default: e = dispatch_sim_p<kBarrier>(a, share, g.blocks, g.coop, g.wide, s); break;
+    case kLL: e = dispatch_sim_p<kLL>(a, share, g.blocks, g.coop, g.wide, g.one, s); break;
+    case kLL128: e = dispatch_sim_p<kLL128>(a, share, g.blocks, g.coop, g.wide, g.one, s); break;
+    case kSentinel:
+      e = dispatch_sim_p<kSentinel>(a, share, g.blocks, g.coop, g.wide, g.one, s);
+      break;
+    default: e = dispatch_sim_p<kBarrier>(a, share, g.blocks, g.coop, g.wide, g.one, s); break;
   }
   return map_hip(e);
 }

@@ -175,7 +175,11 @@ __device__ __forceinline__ u32x4 encode_chunk(const uint16_t* __restrict__ row,
 // dst0, dst0 + cstride, ..., except buffer `skip` (the producer's own: its
 // consumer takes the value from registers; -1 = none).  For LL128 only the
 // data part is stored here; the flags follow an ordering point
-// (produce_flags).
+// (produce_flags).  The data store still covers the whole 128-byte line: the
+// flag field is written with the stale value of two ops before (seq - 2),
+// which a consumer reads as "not yet", so the line goes out as two full
+// 64-byte sectors; an 8-byte tail would be a second partial write of the
+// sector that the flag store writes again.
 template <int P>
 __device__ __forceinline__ void store_chunk(rsrc_t rs, uint32_t dst0,
                                             uint32_t cstride, int ncons,
@@ -184,10 +188,9 @@ __device__ __forceinline__ void store_chunk(rsrc_t rs, uint32_t dst0,
   const uint32_t loff = (uint32_t)tile * kTileBytes + (uint32_t)lane * 16u;
   if (loff >= E) return;
   if (P == kLL128 && (lane & 7) == 7) {
-    u32x2 d;
-    d.x = v.x; d.y = v.y;
+    const u32x4 d = u32x4{v.x, v.y, seq_prev(seq_prev(v.z)), 0u};   // v.z = seq
     for (int c = 0; c < ncons; ++c)
-      if (c != skip) st8(rs, dst0 + c * cstride + loff, d);
+      if (c != skip) st16(rs, dst0 + c * cstride + loff, d);
   } else {
     for (int c = 0; c < ncons; ++c)
       if (c != skip) st16(rs, dst0 + c * cstride + loff, v);
@@ -484,6 +487,124 @@ __device__ __forceinline__ int poll_chunks(rsrc_t rs, const uint32_t (&at)[B],
     for (int j = 0; j < B; ++j)
       if (j < nb && active[j])
         st16(rs, at[j], u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
+  }
+  return 0;
+}
+
+// LL128, many tiles per wave: every data store of a producer wave in an op
+// completes before the first of its flag stores, so one flag of that wave
+// seen for epoch `seq` makes all its data of the op readable.  Lane r (<
+// nranks, r != own) polls the last line flag of tile `tile` of rank r until
+// it holds seq; the caller then reads data with read_tiles.  Returns 0,
+// kEtimeout or kEcorrupt.
+__device__ __forceinline__ int probe_line_flags(rsrc_t rs, uint32_t src0,
+                                                uint32_t slot_bytes, int nranks,
+                                                int tile, uint32_t E, uint32_t seq,
+                                                uint32_t stale, int own, int* ctrl,
+                                                uint64_t timeout_ticks, int lane) {
+  const uint32_t tile0 = (uint32_t)tile * kTileBytes;
+  const uint32_t tile_end = (tile0 + kTileBytes < E) ? tile0 + kTileBytes : E;
+  const uint32_t flag_at = tile_end - 8u;      // u64 flag of the tile's last line
+  uint32_t waiting = ((1u << nranks) - 1u) & ~(own >= 0 ? 1u << own : 0u);
+  Waiter wt(timeout_ticks, ctrl);
+  while (waiting != 0u) {
+    const bool mine = lane < nranks && ((waiting >> lane) & 1u);
+    bool ok = true, bad = false;
+    if (mine) {
+      const u32x2 f = ld8(rs, src0 + (uint32_t)lane * slot_bytes + flag_at);
+      ok = (f.x == seq) && (f.y == 0u);
+      bad = !ok && !(f.y == 0u && (f.x == 0u || f.x == stale));
+    }
+    if (__ballot(bad) != 0ull) {
+      if (lane == 0) report_error(ctrl, kEcorrupt);
+      return kEcorrupt;
+    }
+    waiting &= ~(uint32_t)__ballot(mine && ok);
+    if (waiting == 0u) break;
+    if (!wt.again(lane)) return kEtimeout;
+  }
+  fence_acquire();
+  return 0;
+}
+
+// Read and validate tiles tile[0..nb) of every rank's slot at once, every
+// chunk checked from its own evidence, for a wave that owns many tiles (the
+// large-payload case).  All chunks of the batch are loaded in one round, so a
+// batch whose data has already arrived costs one memory round trip; chunks
+// not yet complete are read again.  Rank `own` (-1 = none) is not read: its
+// chunks are own_v[j].  SENTINEL with `rearm` stores the sentinel back over
+// every chunk once read.  LL128: call after probe_line_flags for the same
+// producers; the line flags are then checked here as the readiness evidence.
+// Returns 0, kEtimeout or kEcorrupt; chunk (j, r) ends in v[j][r].
+template <int P, int NMAX, int CB>
+__device__ __forceinline__ int read_tiles(rsrc_t rs, uint32_t src0, uint32_t slot_bytes,
+                                          int nranks, const int (&tile)[CB], int nb,
+                                          uint32_t E, uint32_t seq, uint32_t stale,
+                                          bool rearm, int own, const u32x4 (&own_v)[CB],
+                                          int* ctrl, uint64_t timeout_ticks, int lane,
+                                          u32x4 (&v)[CB][NMAX]) {
+  uint32_t pending[CB];
+  uint32_t loff[CB];
+  bool active[CB];
+  const uint32_t all = ((1u << nranks) - 1u) & ~(own >= 0 ? 1u << own : 0u);
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    loff[j] = (uint32_t)tile[j] * kTileBytes + (uint32_t)lane * 16u;
+    active[j] = j < nb && loff[j] < E;
+    pending[j] = j < nb ? all : 0u;
+    any = any || pending[j] != 0u;
+#pragma unroll
+    for (int r = 0; r < NMAX; ++r)
+      v[j][r] = (r == own) ? own_v[j] : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (!any) return 0;
+  Waiter wt(timeout_ticks, ctrl);
+  while (true) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r)
+        if (r < nranks && ((pending[j] >> r) & 1u) && active[j])
+          v[j][r] = ld16(rs, src0 + r * slot_bytes + loff[j]);
+    bool corrupt = false, left = false;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      uint32_t fresh = 0u;
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r) {
+        if (r < nranks && ((pending[j] >> r) & 1u)) {
+          bool ok = true, bad = false;
+          if (active[j]) {
+            if (P == kLL128) {
+              if ((lane & 7) == 7) {
+                ok = (v[j][r].z == seq) && (v[j][r].w == 0u);
+                bad = !ok && !(v[j][r].w == 0u && (v[j][r].z == 0u || v[j][r].z == stale));
+              }
+            } else {
+              classify<P>(v[j][r], seq, stale, ok, bad);
+            }
+          }
+          if (__ballot(bad) != 0ull) corrupt = true;
+          if (__ballot(!ok) == 0ull) fresh |= 1u << r;
+        }
+      }
+      if (P == kSentinel && rearm && fresh != 0u) {
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r)
+          if (r < nranks && ((fresh >> r) & 1u) && active[j])
+            st16(rs, src0 + r * slot_bytes + loff[j],
+                 u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
+      }
+      pending[j] &= ~fresh;
+      left = left || pending[j] != 0u;
+    }
+    if (corrupt) {
+      if (lane == 0) report_error(ctrl, kEcorrupt);
+      return kEcorrupt;
+    }
+    if (!left) break;
+    if (!wt.again(lane)) return kEtimeout;
   }
   return 0;
 }
