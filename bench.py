@@ -1,23 +1,34 @@
 #!/usr/bin/env python3
-"""Benchmark of the self-synchronizing one-shot bf16 all-reduce on one MI355X.
+"""Benchmark of the self-synchronizing bf16 all-reduce on one MI355X.
 
-One step = one decode token's worth of all-reduces for the workload: `nops`
-back-to-back one-shot all-reduces (2 per layer) run by one persistent launch
-of the simulator -- encode, poll + validate, fixed-order reduce, sentinel
+One step = `nops` back-to-back all-reduces run by one persistent launch of
+the simulator -- encode, poll + validate, fixed-order reduce, sentinel
 re-arm and epoch flip for every op.  The N simulated ranks are wave groups
-placed on different XCDs; by default (system mode) every rank runs the full
-per-rank program, consume(op) -> produce(op+1), into its own receive buffer,
-so each op carries the real cross-rank dependency.  Share mode (one receive
-buffer, rank 0's share of the traffic) is reported beside it.  Inputs are
-resident in HBM before the timed region.
+placed on different XCDs; in system mode every rank runs the full per-rank
+program, consume(op) -> produce(op+1), into its own receive buffer, so each
+op carries the real cross-rank dependency.  Inputs are resident in HBM
+before the timed region.
 
-`--collective allgather|twoshot` times the standalone all-gather or the
-two-shot all-reduce (system mode) on the same transfers instead.
+Headline (no arguments): the largest single-GPU workload, the top size of
+the 8-rank 2 KiB-4 MiB sweep -- 8 simulated ranks, 4 MiB bf16 payloads per
+rank drawn from U[-1,1), one-shot all-reduce in system mode with the
+protocol the committed cost table picks (ar_select_protocol), 64 ops per
+step.  Beside it, under "workloads", the other workloads at their own sizes
+(8 ranks [1,4096] with the sentinel and with the table's pick, 4 ranks
+[1,4096] LL one op per launch, 4 ranks [16,8192] LL128 over 160 ops,
+16 ranks [8,4096] with and without producer skew, and the two-shot pick at
+4 MiB), each with its fraction of the measured one-chip floor.
+
+Options select another workload for the headline line (--nranks, --rows,
+--hidden, --bytes, --proto, --collective, ...); `--collective
+allgather|twoshot` times the standalone all-gather or the two-shot
+all-reduce (system mode) on the same transfers.
 
 Prints ONE JSON line: value = microseconds per all-reduce (lower is better),
 with the roofline of the simulator kernel (algorithmic HBM bytes per launch /
 HIP-event duration of the launch), the measured one-chip floor, and the CPU
-oracle timed on the host as a baseline.
+oracle timed on the host as a baseline, whose results on the timed step's
+inputs are also compared with the GPU's outputs.
 """
 from __future__ import annotations
 
@@ -188,26 +199,70 @@ def cpu_baseline(x, proto, seconds, collective="allreduce"):
     return us, ops
 
 
-def load_traffic(kernel_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+def cpu_baseline_checked(torch, x, proto, collective, outd, nconsumers, seconds):
+    """The oracle on the timed step's inputs, one op at a time, single
+    thread, for about `seconds` (at least one op): microseconds per op, and
+    whether every consumer's GPU output of each op it ran equals the
+    oracle's bits (the comparison is not timed)."""
+    import numpy as np
+    import oracle
+    K, n, count = x.shape
+    run = oracle.twoshot if collective == "twoshot" else oracle.allreduce
+    spent, ops, bad = 0.0, 0, 0
+    for i in range(K):
+        t0 = time.perf_counter()
+        st, want = run(x[i], proto, 1)
+        spent += time.perf_counter() - t0
+        ops += 1
+        if st != oracle.READY:
+            raise RuntimeError(f"oracle op {i} not ready: status {st}")
+        w = torch.from_numpy(want.view(np.int16)).to(outd.device)
+        got = outd[i * nconsumers:(i + 1) * nconsumers, :count]
+        bad += int((got != w[None, :]).any(dim=1).sum().item())
+        if spent >= seconds:
+            break
+    return spent * 1e6 / ops, ops, bad
+
+
+def kernel_label(proto, nranks, geo, mode, collective):
+    """Name of the simulator kernel variant a launch ran (the key of its
+    counter summary in profiles/traffic.json)."""
+    from collective_synchronization_amd import abi
+    pid = abi.proto_id(proto)
+    nmax = 4 if nranks <= 4 else (8 if nranks <= 8 else 16)
+    if collective == "allgather":
+        return f"k_sim_gather<{pid},{nmax}>"
+    if collective == "twoshot":
+        return ("k_sim_twoshot" if geo["kernel"] == "wide" else "k_sim_twoshot_narrow") + \
+            f"<{pid},{nmax}>"
+    one = geo["tiles_per_wave"] <= 1 and (geo["kernel"] == "wide" or proto != "barrier")
+    if geo["kernel"] == "wide":
+        return f"k_sim_wide<{pid},{nmax},{mode},{1 if one else 2}>"
+    return f"k_sim<{pid},{nmax},{mode},{'one' if one else 'many'}>"
+
+
+def load_traffic(kernel_name: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel on this workload, if it was taken on the current kernel
+    source."""
     try:
         with open(PROFILE_TRAFFIC) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    ent = t.get(kernel_name)
+    ent = t.get(f"{kernel_name}@{workload}")
     if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
     return ent.get("bytes_per_launch")
 
 
 def measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, warmup,
-            waves_per_rank=0, flags=0, collective="allreduce"):
+            waves_per_rank=0, flags=0, collective="allreduce", keep=False):
     """Time `steps` launches of the simulator (one step = nops ops).
 
     Returns per-launch HIP-event durations (ms, on the launch stream), the
-    wall-clock duration of the timed region (s), geometry and status."""
+    wall-clock duration of the timed region (s), geometry and status; with
+    `keep`, also the output buffer, which then holds the last timed step."""
     nconsumers = nranks if mode == "system" else 1
     xd, stride = buffers.rows_to_device(x)
     ws = buffers.Workspace(nranks, count, proto, nconsumers, collective=collective)
@@ -240,7 +295,9 @@ def measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, war
         raise RuntimeError(f"device status {abi.status_string(ws.status())}")
     launch_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     geo = abi.ar_sim_geometry(params[0])
-    return dict(launch_ms=launch_ms, wall=wall, geo=geo, nconsumers=nconsumers)
+    del xd, ws
+    return dict(launch_ms=launch_ms, wall=wall, geo=geo, nconsumers=nconsumers,
+                out=outd if keep else None)
 
 
 def measure_placement(torch, abi, blocks, threads):
@@ -404,32 +461,138 @@ def summarize(res, proto, nranks, count, nops, steps, collective="allreduce"):
     )
 
 
+SWEEP_SEED = 1004                 # seed of the 2 KiB-4 MiB sweep: SWEEP_SEED + bytes
+HEADLINE = "n8_sweep_4MiB_oneshot_64ops"
+
+
+def named_workloads():
+    """The workloads of the default line: name -> (nranks, rows, hidden, dist,
+    seed, nops, proto, collective, mode).  proto "auto": the committed cost
+    table's one-shot pick (ar_select_protocol); collective "auto": its
+    all-reduce pick (ar_select_allreduce)."""
+    from collective_synchronization_amd.configs import CONFIGS
+    c1, c2 = CONFIGS["n4_ll_1x4096"], CONFIGS["n8_sentinel_1x4096_64ops"]
+    c3, c4 = CONFIGS["n4_ll128_Bx8192_160ops"], CONFIGS["n8_sweep_2KiB_4MiB"]
+    c5 = CONFIGS["n16_skew_8x4096_64ops"]
+    top = max(c4["sizes"])
+    return {
+        HEADLINE: (c4["nranks"], 1, top // 2, c4["dist"], c4["seed"] + top, 64, "auto",
+                   "allreduce", "system"),
+        "n8_sweep_4MiB_pick_64ops": (c4["nranks"], 1, top // 2, c4["dist"], c4["seed"] + top,
+                                     64, "auto", "auto", "system"),
+        c2["name"]: (c2["nranks"], 1, c2["hidden"], c2["dist"], c2["seed"], c2["nops"],
+                     "sentinel", "allreduce", "system"),
+        "n8_pick_1x4096_64ops": (c2["nranks"], 1, c2["hidden"], c2["dist"], c2["seed"],
+                                 c2["nops"], "auto", "auto", "system"),
+        "n4_ll_1x4096_1op_share": (c1["nranks"], 1, c1["hidden"], c1["dist"], c1["seed"], 1,
+                                   "ll", "allreduce", "share"),
+        "n4_ll128_16x8192_160ops": (c3["nranks"], 16, c3["hidden"], c3["dist"], c3["seed"] + 16,
+                                    c3["nops"], "ll128", "allreduce", "system"),
+        "n16_8x4096_64ops_oneshot": (c5["nranks"], 8, c5["hidden"], c5["dist"], c5["seed"],
+                                     c5["nops"], "auto", "allreduce", "system"),
+        "n16_8x4096_64ops_pick": (c5["nranks"], 8, c5["hidden"], c5["dist"], c5["seed"],
+                                  c5["nops"], "auto", "auto", "system"),
+    }
+
+
+def resolve(abi, proto, coll, count, nranks):
+    """The protocol and collective a workload runs; with "auto", the
+    committed cost table's choice.  Returns (proto, coll, selected or None)."""
+    if proto != "auto" and coll != "auto":
+        return proto, coll, None
+    from collective_synchronization_amd import selector
+    table = abi.cost_table(selector.load_table()["entries"])
+    if coll == "auto":
+        cid, pid, pred = abi.ar_select_allreduce(table, 2 * count, nranks)
+        coll = selector.COLLECTIVES[cid]
+        if proto == "auto":
+            proto = selector.PROTOS[pid]
+        else:
+            pid, pred = abi.ar_select_collective(table, coll, 2 * count, nranks)
+    else:
+        pid, pred = abi.ar_select_collective(table, coll, 2 * count, nranks)
+        proto = selector.PROTOS[pid]
+    return proto, coll, {"collective": coll, "protocol": proto, "predicted_us": round(pred, 3)}
+
+
+def side_workload(torch, abi, buffers, inputs, name, wl, steps, warmup, floor_us, skew_us=0.0):
+    """One extra workload of the default line: per-op time, algorithmic
+    GB/s, its fraction of 8 TB/s and of the one-chip floor."""
+    nranks, rows, hidden, dist, seed, nops, proto, coll, mode = wl
+    count = rows * hidden
+    proto, coll, selected = resolve(abi, proto, coll, count, nranks)
+    x = inputs.payload(seed, (nops, nranks, count), dist)
+    out = {"nranks": nranks, "shape": [rows, hidden], "protocol": proto, "collective": coll,
+           "mode": mode, "ops_per_launch": nops}
+    if selected:
+        out["selected_by_cost_table"] = selected
+    if nops == 1:
+        # one op per launch: what a stream-ordered caller pays per op
+        r = measure(torch, abi, buffers, x, proto, nranks, count, 1, mode, max(steps, 30),
+                    warmup, collective=coll)
+        us = statistics.median(r["launch_ms"]) * 1e3
+        out.update({"kernel_us_per_launch": round(us, 3),
+                    "kernel_us_per_launch_p10_p90": [
+                        round(float(statistics.quantiles(r["launch_ms"], n=10)[0]) * 1e3, 3),
+                        round(float(statistics.quantiles(r["launch_ms"], n=10)[-1]) * 1e3, 3)]})
+        return out
+    r = measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, warmup,
+                collective=coll)
+    m = summarize(r, proto, nranks, count, nops, steps, coll)
+    out.update({
+        "us_per_op": round(m["us_per_op"], 4),
+        "kernel_us_per_op": round(m["kernel_us_per_op"], 4),
+        "kernel_us_per_op_p10_p90": [round(m["p10"], 4), round(m["p90"], 4)],
+        "achieved_gbs": round(m["gbs"], 3), "frac": round(m["gbs"] / HBM_PEAK_GBS, 6),
+        "algorithmic_bytes_per_op": m["bytes_op"],
+        "floor_frac": round(floor_us / m["kernel_us_per_op"], 4) if floor_us else None,
+        "kernel": kernel_label(proto, nranks, r["geo"], mode, coll),
+        "launch": r["geo"]["launch"],
+    })
+    if skew_us > 0:
+        out["skew"] = measure_skew(torch, abi, buffers, inputs, x, proto, nranks, count, nops,
+                                   min(steps, 10), 2, skew_us, seed, coll)
+    return out
+
+
 def main() -> int:
+    if TIMEOUT_NS is None:
+        print(f"bench.py: {TIMEOUT_ERROR}", file=sys.stderr)
+        return 2
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--proto", default=_env("AR_PROTO", str, "sentinel"),
-                    choices=["ll", "ll128", "sentinel", "barrier", "auto"],
-                    help="auto: the protocol the committed cost table chooses")
+    ap.add_argument("--proto", default=_env("AR_PROTO", str, "auto"),
+                    help="ll, ll128, sentinel, barrier, or auto: the protocol the "
+                         "committed cost table chooses")
     ap.add_argument("--mode", default="system", choices=["share", "system"])
     ap.add_argument("--collective", default="allreduce",
                     choices=["allreduce", "allgather", "twoshot", "auto"],
                     help="one-shot all-reduce (default), standalone all-gather or "
-                         "two-shot all-reduce (the last two: system mode)")
+                         "two-shot all-reduce (the last two: system mode); auto: the "
+                         "cost table's all-reduce choice")
     ap.add_argument("--nranks", type=int, default=8)
-    ap.add_argument("--rows", type=int, default=1)
-    ap.add_argument("--hidden", type=int, default=4096)
+    ap.add_argument("--bytes", type=int, default=None,
+                    help="payload bytes per rank (a [1, bytes/2] payload), instead of "
+                         "--rows x --hidden")
+    ap.add_argument("--rows", type=int, default=None)
+    ap.add_argument("--hidden", type=int, default=None)
     ap.add_argument("--nops", type=int, default=64)
+    ap.add_argument("--dist", default=None, choices=["normal", "uniform"],
+                    help="payload values (default: U[-1,1) for --bytes payloads, N(0,1) "
+                         "for [rows, hidden] ones)")
     ap.add_argument("--waves-per-rank", type=int, default=_env("AR_WG_PER_RANK", int, 0))
     ap.add_argument("--launch", default="auto", choices=["auto", "cooperative", "ordinary"],
                     help="simulator launch: the library's choice, or forced")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-floor", action="store_true")
-    ap.add_argument("--no-share", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline line: no other workloads, share mode or "
+                         "single-op launches")
     ap.add_argument("--seed", type=int, default=None,
-                    help="input seed (default: that of the 8-rank [1,4096] workload)")
+                    help="input seed (default: that of the workload)")
     ap.add_argument("--skew-us", type=float, default=0.0,
                     help="also run with a seeded producer delay U[0, D) us per (op, "
                          "producer) and report the post-arrival latency")
@@ -443,9 +606,6 @@ def main() -> int:
                     help="also run ar_probe_copy over BYTES, 3 times (reference "
                          "dispatches for hardware byte counters)")
     args = ap.parse_args()
-    if TIMEOUT_NS is None:
-        print(f"bench.py: {TIMEOUT_ERROR}", file=sys.stderr)
-        return 2
     protos = ("ll", "ll128", "sentinel", "barrier", "auto")
     if args.proto not in protos:          # an AR_PROTO default is not checked by argparse
         print(f"bench.py: protocol {args.proto!r} (AR_PROTO?) is not one of {protos}",
@@ -461,43 +621,48 @@ def main() -> int:
     import torch
 
     from collective_synchronization_amd import abi, buffers, inputs
-    from collective_synchronization_amd.configs import BENCH_CONFIG, CONFIGS
 
     torch.cuda.set_device(0)
-    cfg = CONFIGS[BENCH_CONFIG]
-    nranks, count, nops, proto = args.nranks, args.rows * args.hidden, args.nops, args.proto
-    coll = args.collective
-    selected = None
-    if proto == "auto" or coll == "auto":
-        # the library's choice from the committed cost table
-        from collective_synchronization_amd import selector
-        table = abi.cost_table(selector.load_table()["entries"])
-        if coll == "auto":
-            cid, pid, pred = abi.ar_select_allreduce(table, 2 * count, nranks)
-            coll = selector.COLLECTIVES[cid]
-            if proto == "auto":
-                proto = selector.PROTOS[pid]
-            else:
-                pid, pred = abi.ar_select_collective(table, coll, 2 * count, nranks)
-        else:
-            pid, pred = abi.ar_select_collective(table, coll, 2 * count, nranks)
-            proto = selector.PROTOS[pid]
-        selected = {"collective": coll, "protocol": proto, "predicted_us": round(pred, 3)}
+    named = named_workloads()
+    h_nranks, _, h_hidden, h_dist, h_seed, _, _, _, _ = named[HEADLINE]
+    shaped = args.rows is not None or args.hidden is not None
+    if args.bytes is not None and shaped:
+        print("bench.py: give --bytes or --rows/--hidden, not both", file=sys.stderr)
+        return 2
+    if shaped:
+        rows, hidden = args.rows or 1, args.hidden or 4096
+        dist = args.dist or "normal"
+    else:
+        nbytes = args.bytes if args.bytes is not None else 2 * h_hidden
+        if nbytes <= 0 or nbytes % 2:
+            print("bench.py: --bytes must be a positive even number", file=sys.stderr)
+            return 2
+        rows, hidden = 1, nbytes // 2
+        dist = args.dist or "uniform"
+    nranks, count, nops = args.nranks, rows * hidden, args.nops
+    proto, coll, selected = resolve(abi, args.proto, args.collective, count, nranks)
     if coll != "allreduce" and (args.mode != "system" or proto == "barrier"):
         print("bench.py: --collective allgather/twoshot run in system mode with "
               "ll, ll128 or sentinel", file=sys.stderr)
         return 2
-    default_workload = (nranks, args.rows, args.hidden, nops, proto, args.mode, coll,
-                        args.seed in (None, cfg["seed"])) == \
-        (cfg["nranks"], 1, cfg["hidden"], cfg["nops"], "sentinel", "system", "allreduce", True)
-    workload = cfg["name"] if default_workload else \
-        f"n{nranks}_{proto}_{args.rows}x{args.hidden}_{nops}ops_{args.mode}" + \
-        ("" if coll == "allreduce" else f"_{coll}")
+    default_workload = (nranks, rows, hidden, nops, args.proto, args.mode, args.collective,
+                        dist, args.seed in (None, h_seed), args.waves_per_rank,
+                        args.launch) == (h_nranks, 1, h_hidden, 64, "auto", "system",
+                                         "allreduce", h_dist, True, 0, "auto")
+    if default_workload:
+        workload = HEADLINE
+        seed = h_seed
+    else:
+        seed = args.seed if args.seed is not None else (
+            SWEEP_SEED + 2 * count if not shaped else 1002)
+        workload = f"n{nranks}_{proto}_{rows}x{hidden}_{nops}ops_{args.mode}" + \
+            ("" if coll == "allreduce" else f"_{coll}") + \
+            ("" if args.waves_per_rank == 0 else f"_wpr{args.waves_per_rank}") + \
+            ("" if args.launch == "auto" else f"_{args.launch}")
     flags = {"auto": 0, "cooperative": abi.AR_SIM_COOPERATIVE,
              "ordinary": abi.AR_SIM_ORDINARY}[args.launch]
 
-    seed = cfg["seed"] if args.seed is None else args.seed
-    x = inputs.payload(seed, (nops, nranks, count), "normal")
+    x = inputs.payload(seed, (nops, nranks, count), dist)
     if args.calibrate_copy > 0:
         n = args.calibrate_copy // 16 * 16
         src = torch.ones(n // 2, dtype=torch.int16, device="cuda")
@@ -508,18 +673,24 @@ def main() -> int:
         del src, dst
     try:
         res = measure(torch, abi, buffers, x, proto, nranks, count, nops, args.mode,
-                      args.steps, args.warmup, args.waves_per_rank, flags, coll)
+                      args.steps, args.warmup, args.waves_per_rank, flags, coll,
+                      keep=not args.no_cpu_baseline)
     except RuntimeError as e:
         print(f"bench.py: {e}", file=sys.stderr)
         return 1
     m = summarize(res, proto, nranks, count, nops, args.steps, coll)
-    if coll == "allreduce":
-        kname = ("k_sim_wide" if res["geo"]["kernel"] == "wide" else "k_sim") + \
-            f"<{abi.proto_id(proto)}>"
-    else:
-        kname = ("k_sim_gather" if coll == "allgather" else "k_sim_twoshot") + \
-            f"<{abi.proto_id(proto)}>"
+    kname = kernel_label(proto, nranks, res["geo"], args.mode, coll)
     unit = "us per all-gather" if coll == "allgather" else "us per all-reduce"
+    # the survey's count of the same op: every rank's slot in every consumer's
+    # buffer, its own included (this build keeps a rank's own chunk in
+    # registers, so `achieved` counts N-1 slots per consumer)
+    n2_bytes = None
+    if coll == "allreduce":
+        E = abi.ar_encoded_bytes(proto, count)
+        nc = res["nconsumers"]
+        n2_bytes = 2 * nranks * 2 * count + 2 * nc * nranks * E + \
+            (nc * nranks * E if proto == "sentinel" else 0) - (nranks - nc) * 2 * count
+    avg_s = m["avg_launch_us"] * 1e-6
 
     line = {
         "metric": METRIC,
@@ -535,9 +706,11 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": workload, "nranks": nranks, "shape": [args.rows, args.hidden],
+            "workload": workload, "nranks": nranks, "shape": [rows, hidden],
+            "payload_bytes_per_rank": 2 * count,
             "protocol": proto, "collective": coll, "ops_per_step": nops, "mode": args.mode,
-            "nconsumers": res["nconsumers"], "values": "N(0,1) seed %d" % seed,
+            "nconsumers": res["nconsumers"],
+            "values": ("U[-1,1)" if dist == "uniform" else "N(0,1)") + f" seed {seed}",
             "tile_groups_per_rank": res["geo"]["waves_per_rank"],
             "blocks": res["geo"]["blocks"], "kernel": res["geo"]["kernel"],
             "launch": res["geo"]["launch"],
@@ -549,27 +722,57 @@ def main() -> int:
         "roofline": {
             "bound": "hbm", "achieved": round(m["gbs"], 3), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(m["gbs"] / HBM_PEAK_GBS, 6),
-            "traffic": load_traffic(kname),
+            "traffic": load_traffic(kname, workload),
             "kernel": kname, "avg_launch_us": round(m["avg_launch_us"], 3),
             "algorithmic_bytes_per_launch": m["bytes_launch"],
             "algorithmic_bytes_per_op": m["bytes_op"],
+            "frac_survey_bytes": (round(n2_bytes * nops / avg_s / 1e9 / HBM_PEAK_GBS, 6)
+                                  if n2_bytes else None),
         },
     }
 
-    if not args.no_share and args.mode == "system" and coll == "allreduce":
+    fl = None
+    if not args.no_floor:
+        threads = 64 * nranks if res["geo"]["kernel"] == "wide" else 64
+        line["placement"] = measure_placement(torch, abi, res["geo"]["blocks"], threads)
+        fl = measure_floor(torch, abi)
+        fl["frac_of_op"] = round(fl["sol_us"] / m["kernel_us_per_op"], 4)
+        fl.update(measure_launch_and_copy(torch, abi))
+        if fl["copy_gbs"]:
+            line["roofline"]["frac_of_copy"] = round(m["gbs"] / fl["copy_gbs"], 6)
+        line["floor"] = fl
+
+    if not args.no_extras and default_workload:
+        floor_us = fl["sol_us"] if fl else None
+        side = {}
+        for name, wl in named.items():
+            if name == HEADLINE:
+                continue
+            try:
+                skew = 20.0 if name == "n16_8x4096_64ops_pick" else 0.0
+                side[name] = side_workload(torch, abi, buffers, inputs, name, wl,
+                                           args.steps, args.warmup, floor_us, skew)
+            except RuntimeError as e:
+                side[name] = {"error": str(e)}
+        # share mode (rank 0's receive side) and one op per launch of the
+        # 8-rank [1,4096] sentinel workload
+        c2 = named["n8_sentinel_1x4096_64ops"]
+        x2 = inputs.payload(c2[4], (c2[5], c2[0], c2[2]), c2[3])
         try:
-            rs = measure(torch, abi, buffers, x, proto, nranks, count, nops, "share",
-                         args.steps, args.warmup, args.waves_per_rank, flags)
-            ms = summarize(rs, proto, nranks, count, nops, args.steps)
-            line["share_mode"] = {
-                "us_per_op": round(ms["us_per_op"], 4),
+            rs = measure(torch, abi, buffers, x2, "sentinel", c2[0], c2[2], c2[5], "share",
+                         args.steps, args.warmup)
+            ms = summarize(rs, "sentinel", c2[0], c2[2], c2[5], args.steps)
+            side["n8_sentinel_1x4096_64ops"]["share_mode"] = {
                 "kernel_us_per_op": round(ms["kernel_us_per_op"], 4),
-                "achieved_gbs": round(ms["gbs"], 3),
-                "frac": round(ms["gbs"] / HBM_PEAK_GBS, 6),
-                "algorithmic_bytes_per_op": ms["bytes_op"],
-            }
-        except RuntimeError as e:
-            line["share_mode"] = {"error": str(e)}
+                "achieved_gbs": round(ms["gbs"], 3)}
+            r1 = measure(torch, abi, buffers, x2[:1], "sentinel", c2[0], c2[2], 1, "system",
+                         max(args.steps, 30), 3)
+            side["n8_sentinel_1x4096_64ops"]["single_op_launch"] = {
+                "kernel_us": round(statistics.median(r1["launch_ms"]) * 1e3, 3),
+                "empty_kernel_us": fl["empty_kernel_us"] if fl else None}
+        except (RuntimeError, KeyError) as e:
+            side["n8_sentinel_1x4096_64ops"]["share_mode"] = {"error": str(e)}
+        line["workloads"] = side
 
     if args.skew_us > 0 and args.mode == "system":
         try:
@@ -593,29 +796,15 @@ def main() -> int:
         except RuntimeError as e:
             line["chain"] = {"error": str(e)}
 
-    if not args.no_floor:
-        threads = 64 * nranks if res["geo"]["kernel"] == "wide" else 64
-        line["placement"] = measure_placement(torch, abi, res["geo"]["blocks"], threads)
-        fl = measure_floor(torch, abi)
-        fl["frac_of_op"] = round(fl["sol_us"] / m["kernel_us_per_op"], 4)
-        fl.update(measure_launch_and_copy(torch, abi))
-        if fl["copy_gbs"]:
-            line["roofline"]["frac_of_copy"] = round(m["gbs"] / fl["copy_gbs"], 6)
-        line["floor"] = fl
-        if coll == "allreduce":
-            # the same workload one op per launch: what a stream-ordered
-            # caller that launches each op pays
-            try:
-                r1 = measure(torch, abi, buffers, x[:1], proto, nranks, count, 1, args.mode,
-                             min(args.steps, 50), 3, 0, flags, coll)
-                line["single_op_launch"] = {
-                    "kernel_us": round(statistics.median(r1["launch_ms"]) * 1e3, 3),
-                    "empty_kernel_us": fl["empty_kernel_us"]}
-            except RuntimeError as e:
-                line["single_op_launch"] = {"error": str(e)}
-
     if not args.no_cpu_baseline:
-        us, ops = cpu_baseline(x, proto, args.cpu_seconds, coll)
+        if coll == "allgather":
+            us, ops = cpu_baseline(x, proto, args.cpu_seconds, coll)
+            checked = None
+        else:
+            us, ops, bad = cpu_baseline_checked(torch, x, proto, coll, res["out"],
+                                                res["nconsumers"], args.cpu_seconds)
+            checked = {"ops": ops, "consumers": res["nconsumers"],
+                       "mismatched_consumer_ops": bad, "bit_exact": bad == 0}
         what = {"allreduce": "encode N + validate/decode N + fixed-order reduce",
                 "allgather": "encode N + validate/decode N",
                 "twoshot": "per share: encode N + validate/decode N + fixed-order "
@@ -623,10 +812,17 @@ def main() -> int:
         line["cpu_baseline"] = {
             "value": round(us, 3), "unit": unit, "cores": 1,
             "kind": "oracle", "cpu": cpu_model(),
-            "sample": (f"{ops} ops of the same workload (N={nranks}, [{args.rows},"
-                       f"{args.hidden}], {proto}: {what} for one receiving rank, "
+            "sample": (f"{ops} ops of the timed step's inputs (N={nranks}, [{rows},"
+                       f"{hidden}], {proto}: {what} for one receiving rank, "
                        f"single thread, ~{args.cpu_seconds:g} s)"),
         }
+        if checked is not None:
+            line["verified"] = checked
+            if bad:
+                print(f"bench.py: {bad} consumer outputs of the timed step differ from "
+                      "the oracle", file=sys.stderr)
+                print(json.dumps(line), flush=True)
+                return 1
 
     print(json.dumps(line), flush=True)
     return 0

@@ -24,6 +24,3 @@ CONFIGS = {
             dist="normal", protos=("ll", "ll128", "sentinel"), nops=64, seed=1005,
             delay_max_us=20.0, shuffle=True),
 }
-
-# The workload the headline measurement is quoted on.
-BENCH_CONFIG = "n8_sentinel_1x4096_64ops"

@@ -68,9 +68,9 @@ def test_twoshot_bytes(proto, nranks, count):
 @pytest.mark.gpu
 def test_bench_line_fields():
     cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "5",
-           "--warmup", "1", "--cpu-seconds", "0.5", "--no-share", "--chain"]
+           "--warmup", "1", "--cpu-seconds", "0.5"]
     print("[bench]", " ".join(cmd[1:]), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
     assert len(lines) == 1
@@ -80,22 +80,50 @@ def test_bench_line_fields():
         assert key in line, key
     assert line["n_gpus"] == 1 and line["steps"] == 5 and line["warmup"] == 1
     assert line["higher_is_better"] is False and line["value"] > 0
-    assert line["config"]["workload"] == "n8_sentinel_1x4096_64ops"
+    cfg = line["config"]
+    assert cfg["workload"] == "n8_sweep_4MiB_oneshot_64ops"
+    assert cfg["nranks"] == 8 and cfg["payload_bytes_per_rank"] == 4 << 20
+    assert cfg["collective"] == "allreduce" and cfg["mode"] == "system"
+    assert cfg["selected_by_cost_table"]["protocol"] == cfg["protocol"]
     roof = line["roofline"]
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
-    assert roof["algorithmic_bytes_per_op"] == 1_507_328
+    assert roof["algorithmic_bytes_per_op"] == bench.algorithmic_bytes(
+        cfg["protocol"], 8, 2 << 20, 8)
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-5
     # achieved = algorithmic bytes per launch over the average launch
     assert abs(roof["achieved"] - roof["algorithmic_bytes_per_launch"] /
                (roof["avg_launch_us"] * 1e3)) / roof["achieved"] < 1e-3
     cpu = line["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] == 1 and cpu["value"] > 0 and cpu["cpu"]
+    assert line["verified"]["bit_exact"] and line["verified"]["ops"] >= 1
     fl = line["floor"]
     assert 0 < fl["oneway_us"] < 10 and 0 < fl["load_us"] < 10
     assert fl["empty_kernel_us"] > 0 and fl["copy_gbs"] > 100
     assert line["placement"]["on_expected_xcd"] == 1.0
     assert line["placement"]["device"] and "gfx950" in line["placement"]["arch"]
-    assert line["single_op_launch"]["kernel_us"] > 0
+    wl = line["workloads"]
+    for name in ("n8_sentinel_1x4096_64ops", "n8_pick_1x4096_64ops", "n4_ll128_16x8192_160ops",
+                 "n16_8x4096_64ops_oneshot", "n16_8x4096_64ops_pick",
+                 "n8_sweep_4MiB_pick_64ops"):
+        assert wl[name]["kernel_us_per_op"] > 0, name
+        assert 0 < wl[name]["floor_frac"] and 0 < wl[name]["frac"] < 1, name
+    assert wl["n4_ll_1x4096_1op_share"]["kernel_us_per_launch"] > 0
+    assert wl["n8_sentinel_1x4096_64ops"]["algorithmic_bytes_per_op"] == 1_507_328
+    assert wl["n8_sentinel_1x4096_64ops"]["single_op_launch"]["kernel_us"] > 0
+    assert wl["n16_8x4096_64ops_pick"]["skew"]["us_per_op"] > 0
+
+
+@pytest.mark.gpu
+def test_bench_chain_line():
+    cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "5",
+           "--warmup", "1", "--rows", "1", "--hidden", "4096", "--proto", "sentinel",
+           "--no-cpu-baseline", "--no-floor", "--chain"]
+    print("[bench]", " ".join(cmd[1:]), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][0])
+    assert line["config"]["workload"] == "n8_sentinel_1x4096_64ops_system"
+    assert line["roofline"]["algorithmic_bytes_per_op"] == 1_507_328
     ch = line["chain"]
     assert ch["kernel_us_per_op"] > 0 and ch["launch"] in ("ordinary", "cooperative")
 
