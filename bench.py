@@ -75,8 +75,9 @@ def _timeout_ns():
 
 TIMEOUT_NS, TIMEOUT_ERROR = _timeout_ns()
 KERNEL_SOURCES = [
-    os.path.join(ROOT, "collective_synchronization_amd", "csrc", n)
-    for n in ("ar_kernels.hip", "ar_protocols.h", "ar_device.h")
+    os.path.join(ROOT, "collective_synchronization_amd", "csrc", "ar_kernels.hip"),
+    os.path.join(ROOT, "include", "ar_protocols.h"),
+    os.path.join(ROOT, "include", "ar_device.h"),
 ]
 
 
@@ -730,6 +731,16 @@ def main() -> int:
                                   if n2_bytes else None),
         },
     }
+
+    if selected:
+        # the committed table's regret: on its own points and on held-out
+        # sizes it was not fitted to
+        from collective_synchronization_amd import selector
+        t = selector.load_table()
+        line["selector"] = {"in_sample_max_regret": round(t["max_regret"], 4),
+                            "heldout_max_regret": (round(t["heldout_max_regret"], 4)
+                                                   if "heldout_max_regret" in t else None),
+                            "heldout_sizes": t.get("heldout_sizes")}
 
     fl = None
     if not args.no_floor:

@@ -16,7 +16,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcsync_ar.so")
+# AR_LIBRARY: load a variant build instead (for example the library built
+# with AR_FORMAL_FENCES=1); unset, the in-tree build
+LIB_PATH = os.environ.get("AR_LIBRARY") or os.path.join(_HERE, "libcsync_ar.so")
 
 AR_OK, AR_EINVAL, AR_EALIGN, AR_ESIZE, AR_ELAUNCH = 0, -1, -2, -3, -4
 AR_ETIMEOUT, AR_ECORRUPT, AR_ENODEV, AR_ECAPACITY = -5, -6, -7, -8
@@ -362,7 +364,8 @@ def ar_wallclock_hz() -> float:
 def cost_table(entries) -> "ctypes.Array":
     """entries: iterable of dicts {nranks, alpha_us[4], beta_us_per_byte[4]}
     and optionally max_bytes (upper end of the size range; absent or <= 0:
-    no upper end) and collective (name or id; absent: one-shot all-reduce)."""
+    no upper end) and collective (name or id; absent: one-shot all-reduce).
+    A None coefficient (an unavailable protocol) is passed as NaN."""
     entries = list(entries)
     arr = (ar_cost_entry * len(entries))()
     for i, e in enumerate(entries):
@@ -370,8 +373,9 @@ def cost_table(entries) -> "ctypes.Array":
         arr[i].collective = collective_id(e.get("collective", AR_ALLREDUCE))
         arr[i].max_bytes = int(e.get("max_bytes", 0))
         for p in range(4):
-            arr[i].alpha_us[p] = float(e["alpha_us"][p])
-            arr[i].beta_us_per_byte[p] = float(e["beta_us_per_byte"][p])
+            a, b = e["alpha_us"][p], e["beta_us_per_byte"][p]
+            arr[i].alpha_us[p] = float("nan") if a is None else float(a)
+            arr[i].beta_us_per_byte[p] = float("nan") if b is None else float(b)
     return arr
 
 

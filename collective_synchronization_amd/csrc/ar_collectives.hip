@@ -20,7 +20,7 @@
 #include "../../include/ar.h"
 #include "../../include/ar_dev.h"
 #include "ar_host.h"
-#include "ar_protocols.h"
+#include "../../include/ar_protocols.h"
 
 namespace ar {
 

@@ -10,7 +10,7 @@
 #include <mutex>
 
 #include "../../include/ar.h"
-#include "ar_device.h"
+#include "../../include/ar_device.h"
 
 namespace ar {
 

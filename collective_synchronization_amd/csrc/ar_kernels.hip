@@ -12,7 +12,7 @@
 #include "../../include/ar.h"
 #include "../../include/ar_dev.h"
 #include "ar_host.h"
-#include "ar_protocols.h"
+#include "../../include/ar_protocols.h"
 
 namespace ar {
 
@@ -1237,7 +1237,7 @@ const char* ar_status_string(int code) {
   }
 }
 
-int ar_abi_version(void) { return 5; }
+int ar_abi_version(void) { return 6; }
 
 int64_t ar_encoded_bytes(int32_t proto, int64_t count) {
   return encoded_bytes(proto, count);

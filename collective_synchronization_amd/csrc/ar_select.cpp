@@ -9,7 +9,8 @@
 // as the next step.  Here the model is the two-term latency/bandwidth form
 // T_p(S) = alpha_p + beta_p * S per collective, protocol p, rank count and
 // size range (the simulator kernels change regime with size, so one line per
-// regime), fitted to measurements from this GPU by the Python side and
+// range; the committed table has a range per interval between measured
+// sizes), fitted to measurements from this GPU by the Python side and
 // passed in as a table.  Beyond the pages' protocol choice, the same model
 // chooses between the one-shot and the two-shot all-reduce.
 #include <math.h>
@@ -56,7 +57,7 @@ static int select_in(const ar_cost_entry* table, int32_t nentries, int32_t colle
   for (int p = 0; p < 4; ++p) {
     const double a = e.alpha_us[p];
     const double b = e.beta_us_per_byte[p];
-    if (!(a >= 0.0) || !isfinite(a) || !isfinite(b)) continue;   // unavailable
+    if (!isfinite(a) || !isfinite(b)) continue;   // unavailable (NaN)
     const double t = a + b * (double)payload_bytes;
     if (choice < 0 || t < t_best) {   // strict: ties keep the lower id
       choice = p;

@@ -16,9 +16,10 @@ LIB = os.path.join(PKG, "libcsync_ar.so")
 SOURCES = [os.path.join(HERE, "ar_kernels.hip"), os.path.join(HERE, "ar_collectives.hip"),
            os.path.join(HERE, "ar_static.hip"),
            os.path.join(HERE, "ar_select.cpp")]
-HEADERS = [os.path.join(HERE, "ar_device.h"), os.path.join(HERE, "ar_protocols.h"),
-           os.path.join(HERE, "ar_host.h"),
-           os.path.join(os.path.dirname(PKG), "include", "ar.h")]
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HEADERS = [os.path.join(INCLUDE, "ar_device.h"), os.path.join(INCLUDE, "ar_protocols.h"),
+           os.path.join(HERE, "ar_host.h"), os.path.join(INCLUDE, "ar.h"),
+           os.path.join(INCLUDE, "ar_dev.h")]
 ARCH = os.environ.get("AR_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -494,8 +494,11 @@ int ar_wallclock_hz(double* hz);
  * holds S: the smallest max_bytes >= S, where max_bytes <= 0 means no upper
  * bound; if every range ends below S, the one that ends last.  Several
  * entries per rank count give a piecewise model (the kernels change regime
- * with size).  A protocol with alpha_us < 0 is unavailable.  Ties go to the
- * lower protocol id (LL < LL128 < SENTINEL < BARRIER).  Host only; writes the
+ * with size; the committed table has one range per interval between two
+ * measured sizes, each line through those two measurements).  alpha_us and
+ * beta_us_per_byte may be negative; a protocol whose alpha_us or
+ * beta_us_per_byte is not a finite number (NaN marks it) is unavailable.
+ * Ties go to the lower protocol id (LL < LL128 < SENTINEL < BARRIER).  Host only; writes the
  * chosen id and, if non-NULL, its predicted time.  AR_EINVAL for a NULL
  * table or proto_out, nentries < 1, S < 0, nranks outside 1..16, or no
  * available protocol in the chosen entry.

@@ -42,7 +42,7 @@
 #include <stdint.h>
 
 #include "ar.h"
-#include "../collective_synchronization_amd/csrc/ar_protocols.h"
+#include "ar_protocols.h"
 
 namespace ar_dev {
 

@@ -11,7 +11,8 @@
  * rule: nearest rank count (ties: the smaller), then the range holding S
  * (the smallest max_bytes >= S, max_bytes <= 0 unbounded; if every range
  * ends below S, the one that ends last), then the lowest predicted time
- * (ties: the lower protocol id).
+ * among the protocols whose coefficients are finite (NaN: unavailable;
+ * negative lines are valid), ties to the lower protocol id.
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -84,7 +85,7 @@ static int brute(const ar_cost_entry* t, int m, int32_t coll, int64_t S, int32_t
     int bp = -1;
     double bt = 0.0;
     for (int p = 0; p < 4; ++p) {
-        if (!(pick->alpha_us[p] >= 0.0))
+        if (!isfinite(pick->alpha_us[p]) || !isfinite(pick->beta_us_per_byte[p]))
             continue;
         double tp = pick->alpha_us[p] + pick->beta_us_per_byte[p] * (double)S;
         if (bp < 0 || tp < bt) {
@@ -120,7 +121,7 @@ int main(void)
     CHECK(ar_select_allreduce(one, 1, 4096, 8, &coll, &proto, &pred) == AR_OK &&
           coll == AR_ALLREDUCE, "no two-shot entries: one-shot");
     for (int p = 0; p < 4; ++p)
-        one->alpha_us[p] = -1.0;
+        one->alpha_us[p] = NAN;
     CHECK(ar_select_protocol(one, 1, 4096, 8, &proto, &pred) == AR_EINVAL,
           "no available protocol");
     free(one);
@@ -136,9 +137,12 @@ int main(void)
             t[i].max_bytes = (next_u64() % 3) == 0 ? 0 : (int64_t)(1u << (next_u64() % 23));
             for (int p = 0; p < 4; ++p) {
                 /* a coarse grid of values makes exact ties common */
-                t[i].alpha_us[p] = (next_u64() % 5) == 0 ? -1.0
-                                                          : (double)(next_u64() % 4);
-                t[i].beta_us_per_byte[p] = (next_u64() % 2) ? 0.0 : uniform(0.0, 1e-4);
+                /* negative intercepts and slopes are valid lines */
+                t[i].alpha_us[p] = (next_u64() % 5) == 0 ? NAN
+                                                          : (double)(next_u64() % 4) - 1.0;
+                t[i].beta_us_per_byte[p] = (next_u64() % 2) ? 0.0 : uniform(-2e-5, 1e-4);
+                if ((next_u64() % 11) == 0)
+                    t[i].beta_us_per_byte[p] = NAN;
             }
         }
         for (int q = 0; q < 8; ++q) {

@@ -36,7 +36,7 @@ def test_header_symbols_all_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert abi.raw().ar_abi_version() == 5
+    assert abi.raw().ar_abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert abi.status_string(code).startswith("AR_")
     assert abi.status_string(-99) == "AR_UNKNOWN"
@@ -225,11 +225,16 @@ def test_selector_argmin_and_crossover():
 def test_selector_ties_nearest_and_unavailable():
     t = _table([
         dict(nranks=4, alpha_us=[1.0, 1.0, 1.0, 1.0], beta_us_per_byte=[0, 0, 0, 0]),
-        dict(nranks=16, alpha_us=[-1.0, 5.0, 4.0, 9.0], beta_us_per_byte=[0, 0, 0, 0]),
+        dict(nranks=16, alpha_us=[None, 5.0, 4.0, 9.0], beta_us_per_byte=[0, 0, 0, 0]),
+        dict(nranks=8, alpha_us=[-3.0, 1.0, 2.0, 3.0], beta_us_per_byte=[1e-3, 0, 0, 0]),
     ])
     assert abi.ar_select_protocol(t, 100, 4)[0] == abi.AR_LL          # tie -> lowest id
     assert abi.ar_select_protocol(t, 100, 10)[0] == abi.AR_LL         # nearest: 4 (tie -> smaller)
-    assert abi.ar_select_protocol(t, 100, 12)[0] == abi.AR_SENTINEL   # nearest: 16, LL unavailable
+    assert abi.ar_select_protocol(t, 100, 14)[0] == abi.AR_SENTINEL   # nearest: 16, LL unavailable
+    # a negative intercept is a valid line: -3 + 1e-3 * 3000 = 0 beats LL128's 1
+    p, pred = abi.ar_select_protocol(t, 3000, 8)
+    assert p == abi.AR_LL and pred == pytest.approx(0.0, abs=1e-12)
+    assert abi.ar_select_protocol(t, 5000, 8)[0] == abi.AR_LL128
     with pytest.raises(abi.ArError):
         abi.ar_select_protocol(t, -1, 4)
     with pytest.raises(abi.ArError):

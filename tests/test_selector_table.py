@@ -35,10 +35,42 @@ def test_fit_table_and_regret_on_synthetic_points():
         for s in selector.SIZES:
             for p, (a, b) in model.items():
                 pts.append({"nranks": n, "proto": p, "bytes": s, "us": a + b * s})
-    entries = selector.fit_table(pts)
-    assert [e["nranks"] for e in entries] == [4, 8]
-    reg = selector.regret(pts, entries)
-    assert all(r["regret"] == pytest.approx(1.0) for r in reg)
+    lsq = selector.fit_table(pts, method="lsq")
+    assert [e["nranks"] for e in lsq] == [4, 8]
+    interp = selector.fit_table(pts)
+    assert [e["nranks"] for e in interp] == [4] * 11 + [8] * 11
+    for entries in (lsq, interp):
+        reg = selector.regret(pts, entries)
+        assert all(r["regret"] == pytest.approx(1.0) for r in reg)
+
+
+def test_interpolating_table_by_hand():
+    """Three measured sizes, two protocols: the table holds the line through
+    each pair of neighbouring points, so it reproduces the measurements,
+    interpolates between them and extends the end lines beyond them."""
+    pts = [{"nranks": 8, "proto": "ll", "bytes": 1000, "us": 1.0},
+           {"nranks": 8, "proto": "ll", "bytes": 2000, "us": 1.2},
+           {"nranks": 8, "proto": "ll", "bytes": 4000, "us": 3.2},
+           {"nranks": 8, "proto": "sentinel", "bytes": 1000, "us": 1.5},
+           {"nranks": 8, "proto": "sentinel", "bytes": 2000, "us": 1.6},
+           {"nranks": 8, "proto": "sentinel", "bytes": 4000, "us": 1.8}]
+    e = selector.fit_table(pts)
+    assert [x["max_bytes"] for x in e] == [2000, 0]
+    # first interval: LL 1.0 + 2e-4 (S - 1000); sentinel 1.5 + 1e-4 (S - 1000)
+    assert e[0]["beta_us_per_byte"][0] == pytest.approx(2e-4)
+    assert e[0]["alpha_us"][0] == pytest.approx(0.8)
+    assert e[0]["alpha_us"][1] is None and e[0]["alpha_us"][3] is None
+    # second interval: LL 1.2 + 1e-3 (S - 2000) -> alpha -0.8 (a valid line)
+    assert e[1]["beta_us_per_byte"][0] == pytest.approx(1e-3)
+    assert e[1]["alpha_us"][0] == pytest.approx(-0.8)
+    t = abi.cost_table(e)
+    for s, want in ((1000, 1.0), (2000, 1.2), (4000, 1.8), (1500, 1.1), (500, 0.9)):
+        assert abi.ar_select_protocol(t, s, 8)[1] == pytest.approx(want), s
+    # LL 1.2 + 1e-3 * 300 = 1.5 against the sentinel's 1.6 + 1e-4 * 300 = 1.63
+    assert abi.ar_select_protocol(t, 2300, 8)[0] == abi.AR_LL
+    # LL 2.2 against 1.7 at 3000: the sentinel
+    assert abi.ar_select_protocol(t, 3000, 8)[0] == abi.AR_SENTINEL
+    assert abi.ar_select_protocol(t, 8000, 8)[0] == abi.AR_SENTINEL
 
 
 def test_library_argmin_matches_python():
@@ -66,6 +98,14 @@ def test_committed_table():
     worst = max(r["regret"] for r in recomputed if r["regret"])
     assert worst == pytest.approx(t["max_regret"])
     assert worst < 1.5
+    # out of sample: sizes between the fitted ones, never used by the fit
+    if "heldout_points" in t:
+        fitted = {p["bytes"] for p in t["points"]}
+        assert not fitted & {p["bytes"] for p in t["heldout_points"]}
+        held = selector.regret(t["heldout_points"], t["entries"])
+        hworst = max(r["regret"] for r in held if r["regret"])
+        assert hworst == pytest.approx(t["heldout_max_regret"])
+        assert hworst <= 1.10
 
 
 def test_library_ranges_match_python():
@@ -110,8 +150,8 @@ def test_fit_finds_regime_change():
         for proto, us in (("ll", ll), ("ll128", sent + 1.0), ("sentinel", sent),
                           ("barrier", 4.0 + 4e-4 * s)):
             pts.append({"nranks": 8, "proto": proto, "bytes": s, "us": us})
-    one = selector.fit_table(pts, max_ranges=1)
-    two = selector.fit_table(pts, max_ranges=2)
+    one = selector.fit_table(pts, max_ranges=1, method="lsq")
+    two = selector.fit_table(pts, max_ranges=2, method="lsq")
     assert len(one) == 1 and len(two) == 2
     assert sorted(e["max_bytes"] for e in two) == [0, 16384]
     assert max(r["regret"] for r in selector.regret(pts, one)) > 1.05
@@ -126,7 +166,7 @@ def _random_entries(rng, colls=("allreduce", "twoshot", "allgather")):
             for hi in list(cuts) + [0]:
                 a = list(rng.uniform(1, 6, 4))
                 if coll != "allreduce":
-                    a[3] = -1.0                      # no barrier form
+                    a[3] = None                      # no barrier form
                 entries.append({"nranks": n, "collective": coll, "max_bytes": int(hi),
                                 "alpha_us": a,
                                 "beta_us_per_byte": list(rng.uniform(5e-5, 3e-4, 4))})
@@ -218,7 +258,7 @@ def test_joint_split_never_worse_than_separate_splits():
     better = 0
     for _ in range(12):
         pts = _kinked_sweep(rng)
-        joint = selector.fit_table(pts)
+        joint = selector.fit_table(pts, method="lsq")
         sep = []
         for coll in ("allreduce", "twoshot"):
             _, cands = selector._candidates(pts, coll, 8, 2)
