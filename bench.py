@@ -324,22 +324,26 @@ def measure_placement(torch, abi, blocks, threads):
 
 def measure_skew(torch, abi, buffers, inputs, x, proto, nranks, count, nops, steps,
                  warmup, skew_us, seed, collective):
-    """Ops with a seeded producer delay U[0, skew_us) per (op, producer) and
-    the wall-clock trace: per-op time and the post-arrival latency (op done
-    at the last consumer minus the last producer's last store).  The trace
-    makes every sender wait for its stores before its timestamp, so these
-    runs are slower than the untraced ones."""
+    """Ops with a seeded producer delay U[0, skew_us) per (op, producer)
+    (none when skew_us is 0) and the wall-clock trace: per-op time, the
+    post-arrival latency (op done at the last consumer minus the last
+    producer's last store), and the first op's timeline from the first wave's
+    start.  The trace makes every sender wait for its stores before its
+    timestamp, so these runs are slower than the untraced ones."""
     import numpy as np
     xd, stride = buffers.rows_to_device(x)
     ws = buffers.Workspace(nranks, count, proto, nranks, collective=collective)
     ostride = ws.gather_stride() if collective == "allgather" else stride
     outd = torch.zeros((nops * nranks, ostride), dtype=torch.int16, device="cuda")
     hz = abi.ar_wallclock_hz()
-    d_us = inputs.delays_us(seed + 1, nops, nranks, skew_us)
-    ticks = torch.from_numpy(np.round(d_us * hz * 1e-6).astype(np.int32)).to("cuda")
+    ticks = None
+    d_us = np.zeros((nops, nranks))
+    if skew_us > 0:
+        d_us = inputs.delays_us(seed + 1, nops, nranks, skew_us)
+        ticks = torch.from_numpy(np.round(d_us * hz * 1e-6).astype(np.int32)).to("cuda")
     trace = torch.zeros(nops * 2 * nranks + 1, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream()
-    post, per_op = [], []
+    post, per_op, first_store, first_done, last_done = [], [], [], [], []
     for k in range(warmup + steps):
         trace.zero_()
         trace[-1] = -1
@@ -354,13 +358,21 @@ def measure_skew(torch, abi, buffers, inputs, x, proto, nranks, count, nops, ste
             raise RuntimeError(f"device status {abi.status_string(ws.status())}")
         if k < warmup:
             continue
-        t = trace.cpu().numpy()[:-1].reshape(nops, 2, nranks).astype(np.float64)
+        raw = trace.cpu().numpy()
+        start = float(raw[-1])
+        t = raw[:-1].reshape(nops, 2, nranks).astype(np.float64)
         post.extend(((t[:, 1, :].max(axis=1) - t[:, 0, :].max(axis=1)) / hz * 1e6).tolist())
+        first_store.append((t[0, 0, :].max() - start) / hz * 1e6)
+        first_done.append((t[0, 1, :].max() - start) / hz * 1e6)
+        last_done.append((t[-1, 1, :].max() - start) / hz * 1e6)
         per_op.append(a.elapsed_time(b) * 1e3 / nops)
     return {"skew_us": skew_us, "mean_delay_us": round(float(d_us.mean()), 3),
             "us_per_op": round(statistics.median(per_op), 3),
             "post_arrival_us_median": round(float(np.median(post)), 3),
-            "post_arrival_us_p90": round(float(np.percentile(post, 90)), 3)}
+            "post_arrival_us_p90": round(float(np.percentile(post, 90)), 3),
+            "timeline_us": {"first_op_last_store": round(float(np.median(first_store)), 3),
+                            "first_op_done": round(float(np.median(first_done)), 3),
+                            "last_op_done": round(float(np.median(last_done)), 3)}}
 
 
 def measure_epilogue(torch, abi, buffers, x, proto, nranks, count, steps, warmup):
@@ -597,6 +609,9 @@ def main() -> int:
     ap.add_argument("--skew-us", type=float, default=0.0,
                     help="also run with a seeded producer delay U[0, D) us per (op, "
                          "producer) and report the post-arrival latency")
+    ap.add_argument("--timeline", action="store_true",
+                    help="also run with the wall-clock trace and no delays: the first "
+                         "op's last store and completion after the first wave's start")
     ap.add_argument("--epilogue", action="store_true",
                     help="also time stream-ordered ops whose producer (a per-rank "
                          "scale) sends from its epilogue, against a separate pack")
@@ -784,6 +799,14 @@ def main() -> int:
         except (RuntimeError, KeyError) as e:
             side["n8_sentinel_1x4096_64ops"]["share_mode"] = {"error": str(e)}
         line["workloads"] = side
+
+    if args.timeline and args.mode == "system":
+        try:
+            line["timeline"] = measure_skew(torch, abi, buffers, inputs, x, proto, nranks,
+                                            count, nops, min(args.steps, 30), 2, 0.0, seed,
+                                            coll)
+        except RuntimeError as e:
+            line["timeline"] = {"error": str(e)}
 
     if args.skew_us > 0 and args.mode == "system":
         try:
