@@ -508,6 +508,16 @@ def named_workloads():
     }
 
 
+def workload_name(nranks, proto, rows, hidden, nops, mode, coll, waves_per_rank=0,
+                  launch="auto"):
+    """Name of a workload given on the command line (the key of its counter
+    summary in profiles/traffic.json)."""
+    return (f"n{nranks}_{proto}_{rows}x{hidden}_{nops}ops_{mode}" +
+            ("" if coll == "allreduce" else f"_{coll}") +
+            ("" if waves_per_rank == 0 else f"_wpr{waves_per_rank}") +
+            ("" if launch == "auto" else f"_{launch}"))
+
+
 def resolve(abi, proto, coll, count, nranks):
     """The protocol and collective a workload runs; with "auto", the
     committed cost table's choice.  Returns (proto, coll, selected or None)."""
@@ -552,6 +562,7 @@ def side_workload(torch, abi, buffers, inputs, name, wl, steps, warmup, floor_us
     r = measure(torch, abi, buffers, x, proto, nranks, count, nops, mode, steps, warmup,
                 collective=coll)
     m = summarize(r, proto, nranks, count, nops, steps, coll)
+    kname = kernel_label(proto, nranks, r["geo"], mode, coll)
     out.update({
         "us_per_op": round(m["us_per_op"], 4),
         "kernel_us_per_op": round(m["kernel_us_per_op"], 4),
@@ -559,8 +570,11 @@ def side_workload(torch, abi, buffers, inputs, name, wl, steps, warmup, floor_us
         "achieved_gbs": round(m["gbs"], 3), "frac": round(m["gbs"] / HBM_PEAK_GBS, 6),
         "algorithmic_bytes_per_op": m["bytes_op"],
         "floor_frac": round(floor_us / m["kernel_us_per_op"], 4) if floor_us else None,
-        "kernel": kernel_label(proto, nranks, r["geo"], mode, coll),
+        "kernel": kname,
         "launch": r["geo"]["launch"],
+        # the same workload run on its own: `bench.py --nranks ... --rows ...`
+        "traffic": load_traffic(kname, workload_name(nranks, proto, rows, hidden, nops, mode,
+                                                     coll)),
     })
     if skew_us > 0:
         out["skew"] = measure_skew(torch, abi, buffers, inputs, x, proto, nranks, count, nops,
@@ -671,10 +685,8 @@ def main() -> int:
     else:
         seed = args.seed if args.seed is not None else (
             SWEEP_SEED + 2 * count if not shaped else 1002)
-        workload = f"n{nranks}_{proto}_{rows}x{hidden}_{nops}ops_{args.mode}" + \
-            ("" if coll == "allreduce" else f"_{coll}") + \
-            ("" if args.waves_per_rank == 0 else f"_wpr{args.waves_per_rank}") + \
-            ("" if args.launch == "auto" else f"_{args.launch}")
+        workload = workload_name(nranks, proto, rows, hidden, nops, args.mode, coll,
+                                 args.waves_per_rank, args.launch)
     flags = {"auto": 0, "cooperative": abi.AR_SIM_COOPERATIVE,
              "ordinary": abi.AR_SIM_ORDINARY}[args.launch]
 
