@@ -122,6 +122,12 @@ def test_pack_argument_checks():
 def test_size_limits():
     big = abi.make_desc(16, 2 ** 29, "ll", nconsumers=16)     # slot 1 GiB -> too big
     assert _code("ar_scratch_bytes", ctypes.byref(big)) == abi.AR_ESIZE
+    # receive buffers below 4 GiB: 16 consumers x 2 parities x 16 slots of LL
+    # at 2 MiB per rank (4 MiB slots) take 2 GiB; at 4 MiB per rank, 4 GiB
+    ok = abi.make_desc(16, 1 << 20, "ll", nconsumers=16)
+    assert _code("ar_scratch_bytes", ctypes.byref(ok)) == 16 * 2 * 16 * (4 << 20)
+    edge = abi.make_desc(16, 1 << 21, "ll", nconsumers=16)
+    assert _code("ar_scratch_bytes", ctypes.byref(edge)) == abi.AR_ESIZE
 
 
 def test_reduce_argument_checks():

@@ -273,3 +273,31 @@ def test_skew_shuffle_n16_8x4096_64ops(proto):
     print(f"[n16 skew {proto}] median post-arrival latency {np.median(post):.3f} us, "
           f"kernel {geo['kernel']}", flush=True)
     assert np.all(last_store > 0) and np.all(done >= last_store)
+
+
+@functools.lru_cache(maxsize=1)
+def _largest_n16_payload():
+    return inputs.payload(SWEEP["seed"] + 16 * (2 << 20), (32, 16, 1 << 20), "uniform")
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128", "sentinel", "barrier"])
+def test_oneshot_largest_n16_2MiB(proto):
+    """The largest one-shot the library accepts at 16 ranks for every
+    protocol (2 MiB per rank: LL's 16 receive buffers then take 2 GiB, and
+    4 MiB would reach the 4 GiB limit), 32 ops with distinct payloads, every
+    op of every consumer against the oracle."""
+    n, count = 16, 1 << 20
+    x = _largest_n16_payload()
+    nops = x.shape[0]
+    ws = buffers.Workspace(n, count, proto, n)
+    xd, stride = buffers.rows_to_device(x)
+    outd = torch.zeros((nops * n, stride), dtype=torch.int16, device="cuda")
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, stride))
+    print(f"[n16 2 MiB] {proto} geo={geo}", flush=True)
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, stride, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    del xd, ws
+    check_ops_on_device(outd, oracle.allreduce_ops(x, proto, seq0), n, count,
+                        f"n16 2 MiB {proto}")
