@@ -143,16 +143,15 @@ inline int check_rows(const void* p, int64_t stride, int64_t count) {
 // ops).  It is taken when the device supports it, the launch holds at least
 // kCoopMinOps ops, and its grid lets the waves walk fewer tiles in the same
 // kernel, or run the workgroup kernel where the ordinary grid needs the
-// one-wave kernel (or the ordinary grid does not fit at all).  A launch whose
-// waves walk several tiles either way (payloads of hundreds of KiB and up per
-// rank, launches of a millisecond and more) is also taken cooperatively: the
-// runtime then guarantees the residency every wave relies on, for about 1%
-// of such a launch.
+// one-wave kernel (or the ordinary grid does not fit at all).  (Taking every
+// many-tile launch cooperatively, for the residency guarantee, was tried: the
+// profiler's kernel trace of such launches then ends without its results, so
+// those launches stay ordinary where the geometry is the same.)
 constexpr int kCoopMinOps = 32;
 
 inline bool coop_pays(int rc_ord, int tpw_ord, bool wide_ord, int tpw_co, bool wide_co) {
   if (rc_ord != AR_OK) return true;
-  if (wide_co == wide_ord) return tpw_co < tpw_ord || (tpw_co == tpw_ord && tpw_co > 1);
+  if (wide_co == wide_ord) return tpw_co < tpw_ord;
   return wide_co;
 }
 

@@ -336,9 +336,7 @@ int ar_scale_rows(int32_t nranks, int64_t count, const void* in, int64_t in_stri
  *   AR_SIM_ORDINARY: ordinary;
  *   neither: cooperative where the device supports it, nops >= 32 and its
  *        larger grid lets each wave or workgroup walk fewer tiles or run the
- *        workgroup kernel, or each walks several tiles either way (then the
- *        fixed cost is about 1% of the launch and the runtime guarantees
- *        residency); ordinary otherwise.  If the runtime refuses such
+ *        workgroup kernel; ordinary otherwise.  If the runtime refuses such
  *        a cooperative launch, the op runs as an ordinary launch instead
  *        (not with a tile_order, whose shape follows the first geometry:
  *        then the error is returned).

@@ -125,17 +125,18 @@ def test_sim_launch_choice():
         assert long_auto["tiles_per_wave"] == forced_coop["tiles_per_wave"]
     else:
         assert long_auto["launch"] == "ordinary"
-    # many tiles per wave either way (8 ranks, 4 MiB, sentinel): cooperative
-    # whenever the device supports it, with no fewer waves than ordinary
+    # many tiles per wave either way (8 ranks, 4 MiB, sentinel): the same
+    # geometry both ways, so the launch stays ordinary
     big = buffers.Workspace(8, 1 << 21, "sentinel", 8)
     xb = torch.zeros((1, 1 << 21), dtype=torch.int16, device="cuda")
     gb = lambda nops, flags=0: abi.ar_sim_geometry(
         big.sim_params(nops, xb, 0, xb, 0, flags=flags))
-    ord_big, auto_big = gb(64, abi.AR_SIM_ORDINARY), gb(64)
-    print(f"[launch 4 MiB] {ord_big} {auto_big}", flush=True)
+    ord_big, coop_big, auto_big = gb(64, abi.AR_SIM_ORDINARY), \
+        gb(64, abi.AR_SIM_COOPERATIVE), gb(64)
+    print(f"[launch 4 MiB] {ord_big} {coop_big} {auto_big}", flush=True)
     assert ord_big["tiles_per_wave"] > 1
-    assert auto_big["tiles_per_wave"] <= ord_big["tiles_per_wave"]
-    assert auto_big["launch"] == "cooperative"
+    fewer = coop_big["tiles_per_wave"] < ord_big["tiles_per_wave"]
+    assert auto_big["launch"] == ("cooperative" if fewer else "ordinary")
 
 
 @pytest.mark.parametrize("blocks,threads", [(64, 512), (128, 1024), (2048, 64), (384, 512)])
