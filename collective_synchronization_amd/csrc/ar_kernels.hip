@@ -341,6 +341,13 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
           fence_acquire();
         }
         uint16_t* orow = a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride;
+        // Where an op's chunks fill half of the memory-side cache (the 256 MB
+        // MALL) or more, read the tiles written last first: they are the ones
+        // still cached.  8 ranks, 4 MiB: sentinel 127.4 -> 126.2 us per op, LL
+        // 206.6 -> 195.3; at 1 MiB (a quarter of the cache) the send order
+        // is 1-1.5% faster.
+        const bool newest_first =
+            (uint64_t)a.nconsumers * (uint64_t)a.nranks * a.E >= (uint64_t(128) << 20);
         // LL128: one flag per producer wave orders all of its data of the op
         if (P == kLL128 &&
             probe_line_flags(rs, src0, a.slot_bytes, a.nranks, wr, a.E, seq, stale, g,
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
           // the rank's own chunks (input loads of the batch together)
 #pragma unroll
           for (int j = 0; j < kReadBatch; ++j) {
-            tl[j] = wr + (k0 + j) * a.W;
+            tl[j] = wr + (newest_first ? mine - 1 - (k0 + j) : k0 + j) * a.W;
             load_chunk<P>(row, j < nb ? row_bytes : 0u, tl[j], lane, wv[j]);
           }
 #pragma unroll
