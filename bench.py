@@ -76,6 +76,7 @@ def _timeout_ns():
 TIMEOUT_NS, TIMEOUT_ERROR = _timeout_ns()
 KERNEL_SOURCES = [
     os.path.join(ROOT, "collective_synchronization_amd", "csrc", "ar_kernels.hip"),
+    os.path.join(ROOT, "collective_synchronization_amd", "csrc", "ar_collectives.hip"),
     os.path.join(ROOT, "include", "ar_protocols.h"),
     os.path.join(ROOT, "include", "ar_device.h"),
 ]
