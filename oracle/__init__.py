@@ -24,7 +24,11 @@ arithmetic is in the C file, which cites the pages it follows:
   becoming part of GPU execution" -- send/receive/reduce called from inside
   the producing kernel (the producer epilogue used for it: a per-rank scale),
   and the chain in which each all-reduce's result feeds that producer for
-  the next all-reduce (``chain_ops``).
+  the next all-reduce (``chain_ops``);
+* "SiFAR" abstract -- communication and model execution designed together,
+  the all-reduce result being the next layer's input: the chain whose
+  producer is a row-parallel linear layer shard (``linear_chain_ops``; its
+  dot products are pairwise binary32 sums, ``linear_dot``).
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against
 something other than itself (exhaustive sweeps against torch and numpy, an
@@ -97,6 +101,10 @@ def _load():
     lib.o_twoshot.restype = ctypes.c_int
     lib.o_scale.argtypes = [u16p, i64, ctypes.c_float, u16p]
     lib.o_scale.restype = None
+    lib.o_linear_dot.argtypes = [u16p, u16p, i64]
+    lib.o_linear_dot.restype = ctypes.c_float
+    lib.o_linear_shard.argtypes = [u16p, i64, u16p, i64, u16p]
+    lib.o_linear_shard.restype = None
     lib.o_bf16_rne_array.argtypes = [f32p, i64, u16p]
     lib.o_bf16_rne_array.restype = None
     lib.o_canon_in_array.argtypes = [u16p, i64, u16p]
@@ -258,6 +266,68 @@ def chain_ops(x0: np.ndarray, scales: np.ndarray, proto="ll", seq0: int = 1) -> 
             raise RuntimeError(f"oracle chained op {i} not ready: status {st}")
         if i + 1 < K:
             x = np.stack([scale(out[i], float(s[i + 1, r])) for r in range(n)])
+        seq = epoch_next(seq)
+    return out
+
+
+def linear_dot(v: np.ndarray, w: np.ndarray) -> float:
+    """Pairwise binary32 sum of the products f32(v[k]) * f32(w[k]) (the
+    linear producer's dot product before its bf16 rounding).  v, w: uint16
+    [kr], kr >= 1.  Returns the binary32 value as a Python float."""
+    v = _u16(v).reshape(-1)
+    w = _u16(w).reshape(-1)
+    if v.size != w.size or v.size < 1:
+        raise ValueError("v and w must have the same length >= 1")
+    return float(_load().o_linear_dot(_ptr(v, ctypes.c_uint16), _ptr(w, ctypes.c_uint16),
+                                      v.size))
+
+
+def linear_shard(v: np.ndarray, wt: np.ndarray) -> np.ndarray:
+    """One rank's row-parallel linear partial output: v uint16 [kr] (its
+    input slice), wt uint16 [count, kr] (row j = output j's weights over the
+    slice) -> uint16 [count], y[j] = bf16_rne(linear_dot(v, wt[j]))."""
+    v = _u16(v).reshape(-1)
+    wt = _u16(wt)
+    if wt.ndim != 2 or wt.shape[1] != v.size or v.size < 1:
+        raise ValueError("wt must be [count, kr] with kr = len(v) >= 1")
+    count = wt.shape[0]
+    out = np.zeros(max(count, 1), dtype=np.uint16)
+    _load().o_linear_shard(_ptr(v, ctypes.c_uint16), v.size, _ptr(wt, ctypes.c_uint16),
+                           count, _ptr(out, ctypes.c_uint16))
+    return out[:count]
+
+
+def linear_chain_ops(x0: np.ndarray, weights: np.ndarray, nops: int, proto="ll",
+                     seq0: int = 1) -> np.ndarray:
+    """Expected outputs of `nops` chained all-reduces whose producer is a
+    row-parallel linear layer shard ("SiFAR" abstract: the all-reduce result
+    is the next layer's input; "Why Microseconds Matter in AI
+    Infrastructure", section "Communication is becoming part of GPU
+    execution": the producer sends from its own kernel).
+
+    x0: uint16 [n, count], the layer input of op 0 as rank r holds it (rank
+    r reads only its slice [r*kr, (r+1)*kr), kr = count / n).  weights:
+    uint16 [L, n, count, kr]; op i uses layer i % L, rank r's shard
+    weights[i % L, r].  Op i: rank r's payload is linear_shard(slice r of
+    its layer input, weights[i % L, r]); the payloads are all-reduced
+    (allreduce); op i+1's layer input, on every rank, is op i's result.
+    Returns uint16 [nops, count]."""
+    x = _u16(x0)
+    w = _u16(weights)
+    n, count = x.shape
+    if w.ndim != 4 or w.shape[1] != n or w.shape[2] != count or w.shape[3] * n != count:
+        raise ValueError("weights must be [L, n, count, count // n]")
+    L, kr = w.shape[0], w.shape[3]
+    out = np.empty((nops, count), dtype=np.uint16)
+    seq = seq0
+    inputs = [x[r] for r in range(n)]
+    for i in range(nops):
+        y = np.stack([linear_shard(inputs[r][r * kr:(r + 1) * kr], w[i % L, r])
+                      for r in range(n)])
+        st, out[i] = allreduce(y, proto, seq)
+        if st != READY:
+            raise RuntimeError(f"oracle linear op {i} not ready: status {st}")
+        inputs = [out[i]] * n
         seq = epoch_next(seq)
     return out
 

@@ -525,3 +525,49 @@ void o_scale(const uint16_t* x, int64_t count, float s, uint16_t* out)
         out[j] = o_bf16_rne(p);
     }
 }
+
+/* --------------------------------------- row-parallel linear producer --- */
+/*
+ * "SiFAR: Synchronization-Free All-Reduce for Low-Latency LLM Inference",
+ * abstract: communication and model execution are designed together, the
+ * all-reduce's result being the next layer's input; "Why Microseconds
+ * Matter in AI Infrastructure", section "Communication is becoming part of
+ * GPU execution": the kernel that produces a payload sends it itself.  The
+ * producer here is one decode token's row-parallel linear layer shard (a
+ * reading: the pages name the pattern, not a layer).  Rank g holds the
+ * inputs v[0..kr) (elements [g*kr, (g+1)*kr) of the layer's input row) and,
+ * for every output j, the weight row wt[j][0..kr) of its input slice; its
+ * partial output is
+ *     y[j] = bf16_rne( S(0, kr) )
+ *     S(a, b) = f32(v[a]) * f32(wt[j][a])                        if b - a == 1
+ *             = S(a, m) + S(m, b),  m = a + (b - a) / 2          otherwise
+ * every product one binary32 multiplication and every '+' one binary32
+ * addition, round to nearest even, denormals kept: the textbook pairwise
+ * (recursive halving) summation of the kr products.
+ */
+static float pairwise_dot(const uint16_t* v, const uint16_t* w, int64_t a, int64_t b)
+{
+    if (b - a == 1)
+        return o_bf16_to_f32(v[a]) * o_bf16_to_f32(w[a]);
+    int64_t m = a + (b - a) / 2;
+    float left = pairwise_dot(v, w, a, m);
+    float right = pairwise_dot(v, w, m, b);
+    return left + right;
+}
+
+/* The binary32 sum S(0, kr) for one weight row (kr >= 1). */
+float o_linear_dot(const uint16_t* v, const uint16_t* w, int64_t kr)
+{
+    if (kr < 1)
+        return 0.0f;
+    return pairwise_dot(v, w, 0, kr);
+}
+
+/* One rank's partial output: wt is `count` rows of kr bf16 (row j at
+ * wt + j*kr); out[j] = bf16_rne(S(0, kr)) of row j. */
+void o_linear_shard(const uint16_t* v, int64_t kr, const uint16_t* wt, int64_t count,
+                    uint16_t* out)
+{
+    for (int64_t j = 0; j < count; ++j)
+        out[j] = o_bf16_rne(o_linear_dot(v, wt + j * kr, kr));
+}
