@@ -126,6 +126,11 @@ _SIGS = {
     "ar_sim_chain_run": ([ctypes.POINTER(ar_sim_params), _vp, _vp], ctypes.c_int),
     "ar_sim_chain_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
                                ctypes.POINTER(_i32)], ctypes.c_int),
+    "ar_linear_work_bytes": ([ctypes.POINTER(ar_desc)], _i64),
+    "ar_sim_linear_run": ([ctypes.POINTER(ar_sim_params), _vp, _i32, _vp, _vp], ctypes.c_int),
+    "ar_sim_linear_geometry": ([ctypes.POINTER(ar_sim_params), _vp, _i32, _vp,
+                                ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                                ctypes.POINTER(_i32)], ctypes.c_int),
     "ar_sim_geometry": ([ctypes.POINTER(ar_sim_params), ctypes.POINTER(_i32),
                          ctypes.POINTER(_i32), ctypes.POINTER(_i32),
                          ctypes.POINTER(_i32), ctypes.POINTER(_i32),
@@ -341,6 +346,26 @@ def ar_sim_chain_geometry(params: ar_sim_params) -> dict:
     _check(_lib.ar_sim_chain_geometry(ctypes.byref(params), ctypes.byref(b), ctypes.byref(coop)),
            "ar_sim_chain_geometry")
     return {"blocks": b.value, "launch": "cooperative" if coop.value else "ordinary"}
+
+
+def ar_linear_work_bytes(desc: ar_desc) -> int:
+    return _check(_lib.ar_linear_work_bytes(ctypes.byref(desc)), "ar_linear_work_bytes")
+
+
+def ar_sim_linear_run(params: ar_sim_params, weights, layers: int, work, stream=None) -> None:
+    """weights: device bf16 [layers, nranks, count, count // nranks]; work:
+    device, ar_linear_work_bytes(desc) bytes, zero-filled when allocated."""
+    _check(_lib.ar_sim_linear_run(ctypes.byref(params), _ptr(weights), layers, _ptr(work),
+                                  _stream(stream)), "ar_sim_linear_run")
+
+
+def ar_sim_linear_geometry(params: ar_sim_params, weights, layers: int, work) -> dict:
+    b, wk, coop = _i32(), _i32(), _i32()
+    _check(_lib.ar_sim_linear_geometry(ctypes.byref(params), _ptr(weights), layers, _ptr(work),
+                                       ctypes.byref(b), ctypes.byref(wk), ctypes.byref(coop)),
+           "ar_sim_linear_geometry")
+    return {"blocks": b.value, "workers": wk.value,
+            "launch": "cooperative" if coop.value else "ordinary"}
 
 
 def ar_sim_geometry(params: ar_sim_params) -> dict:

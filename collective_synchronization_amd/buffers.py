@@ -128,6 +128,22 @@ class Workspace:
         abi.ar_sim_run(p, stream)
         self.flip(nops)
 
+    def linear_work(self) -> torch.Tensor:
+        """The work buffer of ar_sim_linear_run for this descriptor (zeroed
+        once, then kept with the epochs of this workspace)."""
+        if getattr(self, "_work", None) is None:
+            self._work = device_bytes(abi.ar_linear_work_bytes(self.desc), self.device)
+        return self._work
+
+    def sim_linear(self, nops, x_dev, in_stride, out_dev, out_stride, weights, layers,
+                   stream=None, **kw) -> None:
+        """nops chained ops whose producer is a row-parallel linear shard
+        (weights: device bf16 [layers, nranks, count, count // nranks]), in
+        one persistent launch; advances the epoch."""
+        p = self.sim_params(nops, x_dev, in_stride, out_dev, out_stride, **kw)
+        abi.ar_sim_linear_run(p, weights, layers, self.linear_work(), stream)
+        self.flip(nops)
+
     def sim_chain(self, nops, x_dev, in_stride, out_dev, out_stride, scales, stream=None,
                   **kw) -> None:
         """nops chained ops in one persistent launch (op i+1's payload is op

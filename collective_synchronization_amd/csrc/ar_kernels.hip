@@ -1244,7 +1244,7 @@ const char* ar_status_string(int code) {
   }
 }
 
-int ar_abi_version(void) { return 6; }
+int ar_abi_version(void) { return 7; }
 
 int64_t ar_encoded_bytes(int32_t proto, int64_t count) {
   return encoded_bytes(proto, count);

@@ -38,6 +38,21 @@ def payload(seed: int, shape, dist: str = "normal") -> np.ndarray:
     return f32_to_bf16_bits(f)
 
 
+def weights(seed: int, layers: int, nranks: int, count: int) -> np.ndarray:
+    """bf16 bit patterns [layers, nranks, count, count // nranks] of
+    row-parallel linear layers: N(0, 1/count) in binary32 (random
+    initialisation at the hidden size, so a chain of layers keeps its scale);
+    [l, r, j] is output j's row over rank r's input slice."""
+    kr = count // nranks
+    rng = _rng(seed)
+    out = np.empty((layers, nranks, count, kr), dtype=np.uint16)
+    scale = np.float32(1.0 / np.sqrt(count))
+    for l in range(layers):
+        f = rng.standard_normal((nranks, count, kr), dtype=np.float32) * scale
+        out[l] = f32_to_bf16_bits(f)
+    return out
+
+
 def inject(x: np.ndarray, seed: int, rate: float,
            values=(0xFFFF, 0xFFC0, 0xFF81)) -> np.ndarray:
     """Copy of x with a `rate` fraction of positions replaced by `values`

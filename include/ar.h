@@ -478,6 +478,59 @@ int ar_sim_chain_run(const ar_sim_params* p, const float* scales, void* stream);
  * workgroups and 1 for a cooperative launch.  Either output may be NULL. */
 int ar_sim_chain_geometry(const ar_sim_params* p, int32_t* blocks, int32_t* cooperative);
 
+/*
+ * ar_sim_linear_run -- `nops` chained one-shot all-reduces in one persistent
+ * kernel whose producer is one decode token's row-parallel linear layer
+ * shard ("SiFAR: Synchronization-Free All-Reduce for Low-Latency LLM
+ * Inference", abstract: communication and model execution designed
+ * together, the all-reduce result being the next layer's input; "Why
+ * Microseconds Matter in AI Infrastructure", section "Communication is
+ * becoming part of GPU execution": the producing kernel sends its payload).
+ * With kr = count / nranks, op i's payload of rank r is
+ *     y_r[j] = bf16_rne( S(0, kr) )   for j < count,
+ * S(a, b) the pairwise binary32 sum of f32(z[r*kr + k]) * f32(W[l][r][j][k])
+ * over k in [a, b) (S(a, b) = S(a, m) + S(m, b), m = a + (b - a) / 2; every
+ * product and every sum one binary32 operation, nearest even; NaN ->
+ * 0x7FC0), l = i mod layers, z = op i-1's result (op 0: row r of `in`, of
+ * which only elements [r*kr, (r+1)*kr) are read).  The payloads are
+ * all-reduced as by ar_sim_run; every rank's output of op i at out +
+ * (i*nranks + r)*out_stride.
+ *   p: as for ar_sim_run, restricted to desc.collective = AR_ALLREDUCE,
+ *      nconsumers = nranks, proto AR_LL / AR_LL128 / AR_SENTINEL, count =
+ *      nranks * kr with kr one of 256, 512, 1024, 2048; waves_per_rank = 0,
+ *      no tile_order, delay_ticks or trace; flags AR_SIM_COOPERATIVE,
+ *      AR_SIM_ORDINARY or 0 (0: ordinary when half the occupancy holds the
+ *      exchange workgroups and one worker workgroup per rank, else
+ *      cooperative where the device supports it).
+ *   weights: device, bf16 [layers][nranks][count][kr], 16-byte aligned;
+ *      W[l][r][j] is output j's row of weights over rank r's input slice.
+ *   layers: >= 1.
+ *   work: device, ar_linear_work_bytes(&p->desc) bytes, 256-byte aligned,
+ *      caller-owned: zero-filled when allocated and then used only with the
+ *      epochs of the scratch it goes with (like the scratch, it holds
+ *      epoch-tagged words between launches).  It carries the payload rows
+ *      from the GEMV workgroups to the exchange workgroups and each rank's
+ *      reduced input slice back to the workers, as LL words.
+ * One exchange workgroup per (rank, 1 KiB tile) and GEMV worker workgroups
+ * beside them must all be resident: the worker count fills what the
+ * occupancy query leaves (halved for an ordinary launch); AR_ECAPACITY when
+ * not even one worker workgroup per rank fits.  Errors as for ar_sim_run
+ * (AR_EINVAL for the restrictions above, AR_EALIGN for alignment).
+ */
+int ar_sim_linear_run(const ar_sim_params* p, const void* weights, int32_t layers, void* work,
+                      void* stream);
+
+/* Bytes of the work buffer of ar_sim_linear_run for descriptor d (a
+ * multiple of 256): 8*nranks*count + 8*nranks*kr; < 0 on a bad descriptor. */
+int64_t ar_linear_work_bytes(const ar_desc* d);
+
+/* Launch ar_sim_linear_run would make: total workgroups, GEMV worker
+ * workgroups among them, and whether it is cooperative.  Any output pointer
+ * may be NULL. */
+int ar_sim_linear_geometry(const ar_sim_params* p, const void* weights, int32_t layers,
+                           const void* work, int32_t* blocks, int32_t* workers,
+                           int32_t* cooperative);
+
 /* Wall-clock counter frequency of the current device in Hz. */
 int ar_wallclock_hz(double* hz);
 

@@ -36,7 +36,7 @@ def test_header_symbols_all_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert abi.raw().ar_abi_version() == 6
+    assert abi.raw().ar_abi_version() == 7
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert abi.status_string(code).startswith("AR_")
     assert abi.status_string(-99) == "AR_UNKNOWN"
@@ -353,3 +353,43 @@ def test_placement_probe_argument_checks():
     assert pp(8, 64, None, FAKE, None) == abi.AR_EINVAL
     assert pp(8, 64, FAKE + 4, FAKE, None) == abi.AR_EALIGN
     assert pp(8, 64, FAKE, FAKE + 2, None) == abi.AR_EALIGN
+
+
+def test_linear_sim_argument_checks():
+    """ar_sim_linear_run / ar_linear_work_bytes reject what the header
+    excludes before touching a device."""
+    ep = abi.ar_epoch(1, 0)
+
+    def run(nranks=8, count=4096, proto="sentinel", weights=FAKE, layers=2, work=FAKE,
+            nops=4, flags=0, **kw):
+        d = abi.make_desc(nranks, count, proto, nranks)
+        p = abi.sim_params(d, nops, FAKE, max(count, 8), FAKE, max(count, 8), FAKE, FAKE, ep,
+                           flags=flags, **kw)
+        return _code("ar_sim_linear_run", ctypes.byref(p), weights, layers, work, None)
+
+    assert run(count=4000) == abi.AR_EINVAL          # kr = 500 is no power of two
+    assert run(count=8 * 128) == abi.AR_EINVAL       # kr = 128 below 256
+    assert run(count=8 * 4096) == abi.AR_EINVAL      # kr = 4096 above 2048
+    assert run(nranks=3, count=1000) == abi.AR_EINVAL  # count not a multiple of nranks
+    assert run(proto="barrier") == abi.AR_EINVAL
+    assert run(layers=0) == abi.AR_EINVAL
+    assert run(weights=None) == abi.AR_EINVAL
+    assert run(work=None) == abi.AR_EINVAL
+    assert run(weights=FAKE + 8) == abi.AR_EALIGN
+    assert run(work=FAKE + 128) == abi.AR_EALIGN
+    assert run(nops=0) == abi.AR_EINVAL
+    assert run(flags=abi.AR_SIM_NARROW) == abi.AR_EINVAL
+    assert run(flags=abi.AR_SIM_COOPERATIVE | abi.AR_SIM_ORDINARY) == abi.AR_EINVAL
+    assert run(waves_per_rank=8) == abi.AR_EINVAL
+    assert run(delay_ticks=FAKE) == abi.AR_EINVAL
+    assert run(timeout_ns=abi.AR_MAX_TIMEOUT_NS + 1) == abi.AR_EINVAL
+    d1 = abi.make_desc(8, 4096, "ll", 1)                # share mode is not offered
+    p = abi.sim_params(d1, 4, FAKE, 4096, FAKE, 4096, FAKE, FAKE, ep)
+    assert _code("ar_sim_linear_run", ctypes.byref(p), FAKE, 2, FAKE, None) == abi.AR_EINVAL
+    # work bytes: payload words (8 B per two elements, two parities) and the
+    # slice words, for every rank
+    for n, count in ((8, 4096), (16, 4096), (4, 8192), (1, 256)):
+        d = abi.make_desc(n, count, "ll", n)
+        want = 8 * n * count + 8 * n * (count // n)
+        assert abi.ar_linear_work_bytes(d) == (want + 255) // 256 * 256
+    assert _code("ar_linear_work_bytes", None) == abi.AR_EINVAL

@@ -1,0 +1,111 @@
+"""GPU parity of the chained all-reduce whose producer is a row-parallel
+linear layer shard (ar_sim_linear_run), through the C ABI, against the
+oracle's linear_chain_ops, bit for bit on every op and every rank's output.
+
+Each rank reads only its slice of its own input row: the rest of every row
+holds the sentinel pattern and other negative NaNs, which would poison the
+result if read.  Cases: one to sixteen ranks, slices of 256 to 2048 inputs
+(the GEMV's four lane widths), several layers taken in turn, two launches
+in a row (the epoch, the receive slots and the work buffer carry over), the
+decode workload's full size (8 ranks, hidden 4096, 64 ops), inputs with
+signed zeros and subnormals, and an infinity that turns the chain into NaN
+(canonical 0x7FC0 through every protocol)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from collective_synchronization_amd import abi, buffers, inputs
+
+pytestmark = pytest.mark.gpu
+
+PROTOS = ("ll", "ll128", "sentinel")
+TIMEOUT_NS = 2_000_000_000
+
+
+def _rows(seed, nranks, count, specials=None):
+    """Per-rank input rows: N(0,1) in rank r's slice, negative NaNs elsewhere."""
+    kr = count // nranks
+    x = np.full((nranks, count), 0xFFFF, dtype=np.uint16)
+    x[:, 1::3] = 0xFFC0
+    body = inputs.payload(seed, (nranks, count), "normal")
+    if specials is not None:
+        body = inputs.inject(body, seed + 1, 1 / 32, values=specials)
+    for r in range(nranks):
+        x[r, r * kr:(r + 1) * kr] = body[r, r * kr:(r + 1) * kr]
+    return x
+
+
+def _run(proto, nranks, count, nops, layers, seed, runs=2, specials=None, flags=0):
+    ws = buffers.Workspace(nranks, count, proto, nranks)
+    x0 = _rows(seed, nranks, count, specials)
+    w = inputs.weights(seed + 7, layers, nranks, count)
+    wd = torch.from_numpy(w.view(np.int16)).to("cuda")
+    xd, stride = buffers.rows_to_device(x0)
+    outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    p = ws.sim_params(nops, xd, stride, outd, stride, flags=flags)
+    geo = abi.ar_sim_linear_geometry(p, wd, layers, ws.linear_work())
+    print(f"[linear] {proto} N={nranks} count={count} ops={nops} layers={layers} geo={geo}",
+          flush=True)
+    want = oracle.linear_chain_ops(x0, w, nops, proto, ws.epoch.seq)
+    for run in range(runs):
+        ws.sim_linear(nops, xd, stride, outd, stride, wd, layers, timeout_ns=TIMEOUT_NS,
+                      flags=flags)
+        torch.cuda.synchronize()
+        assert ws.status() == 0, abi.status_string(ws.status())
+        got = buffers.rows_from_device(outd, count, (nops, nranks))
+        for i in range(nops):
+            for c in range(nranks):
+                assert np.array_equal(got[i, c], want[i]), (run, i, c)
+        outd.zero_()
+    if proto == "sentinel":
+        assert np.all(ws.slot_view() == 0xFF)
+    return want
+
+
+CASES = [(1, 256, 4, 2), (2, 512, 5, 2), (3, 768, 5, 3), (4, 1024, 6, 2), (5, 1280, 4, 2),
+         (8, 2048, 6, 3), (16, 4096, 5, 2), (4, 4096, 5, 2), (8, 4096, 6, 2), (4, 8192, 3, 2)]
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("nranks,count,nops,layers", CASES)
+def test_sim_linear_parity(proto, nranks, count, nops, layers):
+    if nranks == 16 and proto != "sentinel":
+        # 16 ranks, LL / LL128: 16 or more tiles per rank make 256 exchange
+        # workgroups of 16 waves, which fill the chip at the kernel's
+        # register use: the capacity error the header documents
+        ws = buffers.Workspace(nranks, count, proto, nranks)
+        w = torch.zeros((layers, nranks, count, count // nranks), dtype=torch.int16,
+                        device="cuda")
+        xd, stride = buffers.rows_to_device(np.zeros((nranks, count), np.uint16))
+        outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+        p = ws.sim_params(nops, xd, stride, outd, stride)
+        with pytest.raises(abi.ArError) as e:
+            abi.ar_sim_linear_run(p, w, layers, ws.linear_work())
+        assert e.value.code == abi.AR_ECAPACITY
+        return
+    _run(proto, nranks, count, nops, layers, seed=5100 + count + nranks)
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+def test_sim_linear_decode_size_64_ops(proto):
+    """8 ranks, hidden 4096 (slices of 512), 64 chained ops over 4 layers."""
+    out = _run(proto, 8, 4096, 64, 4, seed=5200, runs=1)
+    # the chain keeps its scale: the last op is neither flushed nor blown up
+    f = (out[-1].astype(np.uint32) << 16).view(np.float32)
+    assert np.isfinite(f).all() and 0.05 < float(np.abs(f).mean()) < 20.0
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+def test_sim_linear_signed_zeros_and_subnormals(proto):
+    _run(proto, 4, 1024, 4, 2, seed=5300, specials=(0x8000, 0x0000, 0x0001, 0x8001, 0x007F))
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+def test_sim_linear_infinity_becomes_canonical_nan(proto):
+    want = _run(proto, 2, 512, 3, 1, seed=5400, runs=1, specials=(0x7F80,))
+    assert (want[-1] == 0x7FC0).all()
+
+
+def test_sim_linear_cooperative_launch():
+    _run("ll", 8, 4096, 8, 2, seed=5500, runs=1, flags=abi.AR_SIM_COOPERATIVE)
