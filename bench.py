@@ -461,6 +461,73 @@ def measure_chain(torch, abi, buffers, x0, proto, nranks, count, nops, steps, wa
     }
 
 
+def linear_bytes(proto: str, nranks: int, count: int) -> int:
+    """Algorithmic bytes of one op of the chain whose producer is a
+    row-parallel linear shard: every rank's weight rows over its input slice
+    (count x count/nranks bf16), its slice of the layer input, and the
+    one-shot exchange without the producer's payload read (the payload is
+    made in registers)."""
+    kr = count // nranks
+    return (nranks * count * kr * 2 + nranks * kr * 2 +
+            algorithmic_bytes(proto, nranks, count, nranks) - nranks * 2 * count)
+
+
+def measure_linear(torch, abi, buffers, inputs, proto, nranks, count, nops, layers, steps,
+                   warmup, flags=0, seed=5200):
+    """The chain whose producer is one decode token's row-parallel linear
+    shard (ar_sim_linear_run): op i's payload of rank r is its shard of a
+    layer applied to its slice of op i-1's result; `layers` layers of
+    N(0, 1/count) weights taken in turn.  HIP events per launch on the
+    launch stream, median over `steps` launches, plus the wall clock."""
+    import numpy as np
+    ws = buffers.Workspace(nranks, count, proto, nranks)
+    x0 = inputs.payload(seed, (nranks, count), "normal")
+    xd, stride = buffers.rows_to_device(x0)
+    w = inputs.weights(seed + 7, layers, nranks, count)
+    wd = torch.from_numpy(w.view(np.int16)).to("cuda")
+    del w
+    outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    geo = abi.ar_sim_linear_geometry(ws.sim_params(nops, xd, stride, outd, stride, flags=flags),
+                                     wd, layers, ws.linear_work())
+    kw = dict(timeout_ns=TIMEOUT_NS, flags=flags)
+    for _ in range(warmup):
+        ws.sim_linear(nops, xd, stride, outd, stride, wd, layers, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        ws.sim_linear(nops, xd, stride, outd, stride, wd, layers, **kw)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ws.status() != 0:
+        raise RuntimeError(f"device status {abi.status_string(ws.status())}")
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    k_us = statistics.median(ms) * 1e3 / nops
+    kr = count // nranks
+    nmax = 4 if nranks <= 4 else (8 if nranks <= 8 else 16)
+    b_op = linear_bytes(proto, nranks, count)
+    return {
+        "nranks": nranks, "shape": [1, count], "protocol": proto, "ops_per_launch": nops,
+        "layers": layers, "weight_bytes_per_layer": nranks * count * kr * 2,
+        "us_per_op": round(wall * 1e6 / (steps * nops), 4),
+        "kernel_us_per_op": round(k_us, 4),
+        "kernel_us_per_op_p10_p90": [round(float(np.percentile(ms, 10)) * 1e3 / nops, 4),
+                                     round(float(np.percentile(ms, 90)) * 1e3 / nops, 4)],
+        "algorithmic_bytes_per_op": b_op,
+        "achieved_gbs": round(b_op / (k_us * 1e-6) / 1e9, 3),
+        "frac": round(b_op / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
+        "launch": geo["launch"], "blocks": geo["blocks"], "gemv_workgroups": geo["workers"],
+        "kernel": f"k_sim_linear<{abi.proto_id(proto)},{nmax},{kr // 64}>",
+        "producer": ("row-parallel linear shard of a decode token: pairwise binary32 dot "
+                     f"products over {kr} inputs per rank, bf16; weights N(0,1/{count}), "
+                     f"{layers} layers in turn"),
+    }
+
+
 def summarize(res, proto, nranks, count, nops, steps, collective="allreduce"):
     import numpy as np
     launch_ms = res["launch_ms"]
@@ -636,6 +703,13 @@ def main() -> int:
     ap.add_argument("--chain", action="store_true",
                     help="also time the chained simulator: each op's result, scaled "
                          "per rank, is the next op's payload, in one launch")
+    ap.add_argument("--linear", action="store_true",
+                    help="also time the chain whose producer is a row-parallel linear "
+                         "layer shard (each op's result is the next layer's input), in "
+                         "one launch, with the --proto protocol (auto: LL)")
+    ap.add_argument("--layers", type=int, default=16,
+                    help="weight layers of --linear, taken in turn (default 16: 512 MiB "
+                         "at 8 ranks and hidden 4096, more than the memory-side cache)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run ar_probe_copy over BYTES, 3 times (reference "
                          "dispatches for hardware byte counters)")
@@ -814,6 +888,14 @@ def main() -> int:
                 "empty_kernel_us": fl["empty_kernel_us"] if fl else None}
         except (RuntimeError, KeyError) as e:
             side["n8_sentinel_1x4096_64ops"]["share_mode"] = {"error": str(e)}
+        # the decode chain whose producer is a row-parallel linear layer (8
+        # ranks, hidden 4096, LL, 64 ops over 16 layers of weights)
+        try:
+            side["n8_linear_ll_1x4096_64ops"] = measure_linear(
+                torch, abi, buffers, inputs, "ll", c2[0], c2[2], c2[5], 16, args.steps,
+                args.warmup)
+        except (RuntimeError, abi.ArError) as e:
+            side["n8_linear_ll_1x4096_64ops"] = {"error": str(e)}
         line["workloads"] = side
 
     if args.timeline and args.mode == "system":
@@ -845,6 +927,15 @@ def main() -> int:
                                           nops, args.steps, args.warmup)
         except RuntimeError as e:
             line["chain"] = {"error": str(e)}
+
+    if args.linear and args.mode == "system" and proto != "barrier":
+        try:
+            line["linear"] = measure_linear(torch, abi, buffers, inputs,
+                                            "ll" if args.proto == "auto" else proto, nranks,
+                                            count, nops, args.layers, args.steps,
+                                            args.warmup, flags)
+        except (RuntimeError, abi.ArError) as e:
+            line["linear"] = {"error": str(e)}
 
     if not args.no_cpu_baseline:
         if coll == "allgather":

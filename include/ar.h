@@ -499,9 +499,9 @@ int ar_sim_chain_geometry(const ar_sim_params* p, int32_t* blocks, int32_t* coop
  *      nconsumers = nranks, proto AR_LL / AR_LL128 / AR_SENTINEL, count =
  *      nranks * kr with kr one of 256, 512, 1024, 2048; waves_per_rank = 0,
  *      no tile_order, delay_ticks or trace; flags AR_SIM_COOPERATIVE,
- *      AR_SIM_ORDINARY or 0 (0: ordinary when half the occupancy holds the
- *      exchange workgroups and one worker workgroup per rank, else
- *      cooperative where the device supports it).
+ *      AR_SIM_ORDINARY or 0 (0: cooperative where the device supports it,
+ *      for its larger resident grid; if the runtime refuses that launch, the
+ *      ordinary grid).
  *   weights: device, bf16 [layers][nranks][count][kr], 16-byte aligned;
  *      W[l][r][j] is output j's row of weights over rank r's input slice.
  *   layers: >= 1.
@@ -509,8 +509,9 @@ int ar_sim_chain_geometry(const ar_sim_params* p, int32_t* blocks, int32_t* coop
  *      caller-owned: zero-filled when allocated and then used only with the
  *      epochs of the scratch it goes with (like the scratch, it holds
  *      epoch-tagged words between launches).  It carries the payload rows
- *      from the GEMV workgroups to the exchange workgroups and each rank's
- *      reduced input slice back to the workers, as LL words.
+ *      from the GEMV workgroups to the exchange workgroups, which send each
+ *      tile whole, and each rank's reduced input slice back to the workers,
+ *      as LL words.
  * One exchange workgroup per (rank, 1 KiB tile) and GEMV worker workgroups
  * beside them must all be resident: the worker count fills what the
  * occupancy query leaves (halved for an ordinary launch); AR_ECAPACITY when
@@ -521,7 +522,9 @@ int ar_sim_linear_run(const ar_sim_params* p, const void* weights, int32_t layer
                       void* stream);
 
 /* Bytes of the work buffer of ar_sim_linear_run for descriptor d (a
- * multiple of 256): 8*nranks*count + 8*nranks*kr; < 0 on a bad descriptor. */
+ * multiple of 256): 8*nranks*count (payload rows, as LL words, two
+ * parities) + 8*count (each rank's reduced input slice, as LL words, two
+ * parities); < 0 on a bad descriptor. */
 int64_t ar_linear_work_bytes(const ar_desc* d);
 
 /* Launch ar_sim_linear_run would make: total workgroups, GEMV worker

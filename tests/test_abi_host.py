@@ -386,10 +386,12 @@ def test_linear_sim_argument_checks():
     d1 = abi.make_desc(8, 4096, "ll", 1)                # share mode is not offered
     p = abi.sim_params(d1, 4, FAKE, 4096, FAKE, 4096, FAKE, FAKE, ep)
     assert _code("ar_sim_linear_run", ctypes.byref(p), FAKE, 2, FAKE, None) == abi.AR_EINVAL
-    # work bytes: payload words (8 B per two elements, two parities) and the
-    # slice words, for every rank
-    for n, count in ((8, 4096), (16, 4096), (4, 8192), (1, 256)):
-        d = abi.make_desc(n, count, "ll", n)
-        want = 8 * n * count + 8 * n * (count // n)
+    # work bytes: payload words (8 B per two elements, two parities, every
+    # rank) and the slice words (8 B per two elements of a slice, two
+    # parities, every rank)
+    for n, count, proto in ((8, 4096, "ll"), (16, 4096, "sentinel"), (4, 8192, "ll128"),
+                            (1, 256, "ll")):
+        d = abi.make_desc(n, count, proto, n)
+        want = 8 * n * count + 8 * count
         assert abi.ar_linear_work_bytes(d) == (want + 255) // 256 * 256
     assert _code("ar_linear_work_bytes", None) == abi.AR_EINVAL
