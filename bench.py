@@ -77,6 +77,7 @@ TIMEOUT_NS, TIMEOUT_ERROR = _timeout_ns()
 KERNEL_SOURCES = [
     os.path.join(ROOT, "collective_synchronization_amd", "csrc", "ar_kernels.hip"),
     os.path.join(ROOT, "collective_synchronization_amd", "csrc", "ar_collectives.hip"),
+    os.path.join(ROOT, "collective_synchronization_amd", "csrc", "ar_linear.hip"),
     os.path.join(ROOT, "include", "ar_protocols.h"),
     os.path.join(ROOT, "include", "ar_device.h"),
 ]
@@ -510,6 +511,8 @@ def measure_linear(torch, abi, buffers, inputs, proto, nranks, count, nops, laye
     kr = count // nranks
     nmax = 4 if nranks <= 4 else (8 if nranks <= 8 else 16)
     b_op = linear_bytes(proto, nranks, count)
+    kname = f"k_sim_linear<{abi.proto_id(proto)},{nmax},{kr // 64}>"
+    wname = f"n{nranks}_linear_{proto}_1x{count}_{nops}ops"
     return {
         "nranks": nranks, "shape": [1, count], "protocol": proto, "ops_per_launch": nops,
         "layers": layers, "weight_bytes_per_layer": nranks * count * kr * 2,
@@ -520,8 +523,15 @@ def measure_linear(torch, abi, buffers, inputs, proto, nranks, count, nops, laye
         "algorithmic_bytes_per_op": b_op,
         "achieved_gbs": round(b_op / (k_us * 1e-6) / 1e9, 3),
         "frac": round(b_op / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
+        "avg_launch_us": round(statistics.mean(ms) * 1e3, 3),
         "launch": geo["launch"], "blocks": geo["blocks"], "gemv_workgroups": geo["workers"],
-        "kernel": f"k_sim_linear<{abi.proto_id(proto)},{nmax},{kr // 64}>",
+        "kernel": kname, "workload": wname,
+        # counters of the same kernel and workload; rocprofv3 records nothing
+        # for cooperative launches here, so the summary is of the ordinary
+        # launch (bench.py --linear --launch ordinary)
+        "traffic": (load_traffic(kname, wname + "_ordinary")
+                    if geo["launch"] == "ordinary" else None),
+        "traffic_ordinary_launch": load_traffic(kname, wname + "_ordinary"),
         "producer": ("row-parallel linear shard of a decode token: pairwise binary32 dot "
                      f"products over {kr} inputs per rank, bf16; weights N(0,1/{count}), "
                      f"{layers} layers in turn"),
@@ -707,6 +717,9 @@ def main() -> int:
                     help="also time the chain whose producer is a row-parallel linear "
                          "layer shard (each op's result is the next layer's input), in "
                          "one launch, with the --proto protocol (auto: LL)")
+    ap.add_argument("--linear-hidden", type=int, default=4096,
+                    help="hidden size of --linear (its own workload: --nranks ranks, one "
+                         "decode token, 64 ops)")
     ap.add_argument("--layers", type=int, default=16,
                     help="weight layers of --linear, taken in turn (default 16: 512 MiB "
                          "at 8 ranks and hidden 4096, more than the memory-side cache)")
@@ -894,7 +907,7 @@ def main() -> int:
             side["n8_linear_ll_1x4096_64ops"] = measure_linear(
                 torch, abi, buffers, inputs, "ll", c2[0], c2[2], c2[5], 16, args.steps,
                 args.warmup)
-        except (RuntimeError, abi.ArError) as e:
+        except (RuntimeError, ValueError, abi.ArError) as e:
             side["n8_linear_ll_1x4096_64ops"] = {"error": str(e)}
         line["workloads"] = side
 
@@ -932,9 +945,9 @@ def main() -> int:
         try:
             line["linear"] = measure_linear(torch, abi, buffers, inputs,
                                             "ll" if args.proto == "auto" else proto, nranks,
-                                            count, nops, args.layers, args.steps,
-                                            args.warmup, flags)
-        except (RuntimeError, abi.ArError) as e:
+                                            args.linear_hidden, 64, args.layers,
+                                            args.steps, args.warmup, flags)
+        except (RuntimeError, ValueError, abi.ArError) as e:
             line["linear"] = {"error": str(e)}
 
     if not args.no_cpu_baseline:

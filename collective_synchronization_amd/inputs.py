@@ -44,6 +44,9 @@ def weights(seed: int, layers: int, nranks: int, count: int) -> np.ndarray:
     initialisation at the hidden size, so a chain of layers keeps its scale);
     [l, r, j] is output j's row over rank r's input slice."""
     kr = count // nranks
+    if layers * nranks * count * kr > (1 << 32):
+        raise ValueError(f"{layers} layers of a hidden size of {count} need more than "
+                         "8 GiB of weights")
     rng = _rng(seed)
     out = np.empty((layers, nranks, count, kr), dtype=np.uint16)
     scale = np.float32(1.0 / np.sqrt(count))
