@@ -109,3 +109,59 @@ def test_sim_linear_infinity_becomes_canonical_nan(proto):
 
 def test_sim_linear_cooperative_launch():
     _run("ll", 8, 4096, 8, 2, seed=5500, runs=1, flags=abi.AR_SIM_COOPERATIVE)
+
+
+def test_sim_linear_one_op_launches_in_a_row():
+    """nops = 1, five launches: each launch's op 0 reads the input rows; the
+    epoch, the slots and the work buffer carry over."""
+    nranks, count = 8, 4096
+    ws = buffers.Workspace(nranks, count, "sentinel", nranks)
+    w = inputs.weights(5601, 1, nranks, count)
+    wd = torch.from_numpy(w.view(np.int16)).to("cuda")
+    for k in range(5):
+        x0 = _rows(5600 + k, nranks, count)
+        xd, stride = buffers.rows_to_device(x0)
+        outd = torch.zeros((nranks, stride), dtype=torch.int16, device="cuda")
+        want = oracle.linear_chain_ops(x0, w, 1, "sentinel", ws.epoch.seq)
+        ws.sim_linear(1, xd, stride, outd, stride, wd, 1, timeout_ns=TIMEOUT_NS)
+        torch.cuda.synchronize()
+        assert ws.status() == 0, abi.status_string(ws.status())
+        got = buffers.rows_from_device(outd, count, (1, nranks))
+        for c in range(nranks):
+            assert np.array_equal(got[0, c], want[0]), (k, c)
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+def test_sim_linear_tiny_deadline_ends_cleanly(proto):
+    """A poll deadline of one wall-clock tick, set from the host: every wait
+    gives up at once or finds its data, the launch ends, and the status is
+    OK or AR_ETIMEOUT -- never a hang."""
+    nranks, count, nops = 8, 4096, 16
+    ws = buffers.Workspace(nranks, count, proto, nranks)
+    w = torch.zeros((2, nranks, count, count // nranks), dtype=torch.int16, device="cuda")
+    xd, stride = buffers.rows_to_device(_rows(5700, nranks, count))
+    outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    ws.sim_linear(nops, xd, stride, outd, stride, w, 2, timeout_ns=1)
+    torch.cuda.synchronize()
+    assert ws.status() in (0, abi.AR_ETIMEOUT), abi.status_string(ws.status())
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+def test_sim_linear_impossible_slice_flag_is_corrupt(proto):
+    """A slice word holding an epoch that can never be there (planted from
+    the host in the work buffer before the launch) is reported as
+    AR_ECORRUPT by the workers that read it, and the launch ends."""
+    nranks, count, nops = 4, 1024, 3
+    ws = buffers.Workspace(nranks, count, proto, nranks)
+    work = ws.linear_work()
+    kr = count // nranks
+    # slice words [nranks][2][kr/2] of 8 bytes after the payload words
+    act0 = 8 * nranks * count
+    words = work[act0:act0 + 8 * count].view(torch.int32).view(nranks, 2, kr // 2, 2)
+    words[:, :, :, 1] = 0x5A5A5A5A          # neither this op's, two ops before, nor 0
+    w = torch.zeros((1, nranks, count, kr), dtype=torch.int16, device="cuda")
+    xd, stride = buffers.rows_to_device(_rows(5800, nranks, count))
+    outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    ws.sim_linear(nops, xd, stride, outd, stride, w, 1, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == abi.AR_ECORRUPT, abi.status_string(ws.status())
