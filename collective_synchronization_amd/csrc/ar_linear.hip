@@ -130,14 +130,9 @@ __device__ __forceinline__ float lane_part(const float (&z)[KL], const uint32_t 
   return p[0];
 }
 
-// Sums of R rows over the wave's lanes, v[u] holding the lane's part of row
-// u.  Level s adds the partial sums of lane blocks l and l ^ 2^s (aligned
-// blocks of 2^s lanes joined into blocks of 2^(s+1)), which is the pairwise
-// tree over the lanes.  The first log2(R) levels halve the rows a lane
-// carries (the lane keeps one half and sends its partner the other), the
-// remaining ones are a plain butterfly.  Returns the sum of row
-// lane_row<R>(lane) (every lane of an aligned block of R lanes holds a
-// different row).
+// The row whose sum rows_sum<R> leaves in a lane: bit s of the lane picks
+// the upper half at level s, so row = sum over s of bit_s(lane) * R/2^(s+1)
+// (every lane of an aligned block of R lanes holds a different row).
 template <int R>
 __device__ __forceinline__ int lane_row(int lane) {
   int r = 0;
@@ -146,6 +141,13 @@ __device__ __forceinline__ int lane_row(int lane) {
   return r;
 }
 
+// Sums of R rows over the wave's lanes, v[u] holding the lane's part of row
+// u.  Level s adds the partial sums of lane blocks l and l ^ 2^s (aligned
+// blocks of 2^s lanes joined into blocks of 2^(s+1)), which is the pairwise
+// tree over the lanes.  The first log2(R) levels halve the rows a lane
+// carries (the lane keeps one half and sends its partner the other), the
+// remaining ones are a plain butterfly.  Returns the sum of row
+// lane_row<R>(lane).
 template <int R>
 __device__ __forceinline__ float rows_sum(float (&v)[R], int lane) {
 #pragma unroll
@@ -166,7 +168,8 @@ __device__ __forceinline__ float rows_sum(float (&v)[R], int lane) {
 }
 
 // Rows per wave and block (host and device): 32 bf16 of weights a lane
-// for a block (at least two rows: a payload word holds two).
+// for a block, except for slices of 2048 (KL = 32), whose block is the two
+// rows a payload word holds.
 __host__ __device__ constexpr int lin_rows_per_wave(int kl) { return kl <= 16 ? 32 / kl : 2; }
 // Weight buffers of a worker wave (the ring of blocks in flight).
 __host__ __device__ constexpr int lin_buffers(int kl) { return kl <= 16 ? 4 : 2; }
@@ -185,6 +188,8 @@ __global__ __launch_bounds__(kWave * NMAX) void k_sim_linear(LinArgs a) {
   using S = LinSmem<NMAX, KL>;
   constexpr int RW = S::kRw;
   constexpr int NBUF = S::kBufs;
+  static_assert(NBUF >= 2 && NBUF <= 4, "the worker's step loop serves 2 to 4 buffers");
+  static_assert(RW >= 2 && (RW & (RW - 1)) == 0, "rows a block: a power of two >= 2");
   __shared__ __align__(16) uint8_t smem[S::kBytes];
   __shared__ int err;
   const int lane = threadIdx.x & (kWave - 1);
@@ -219,9 +224,6 @@ __global__ __launch_bounds__(kWave * NMAX) void k_sim_linear(LinArgs a) {
       for (int u = 0; u < RW; ++u)
         load_wrow<KL>(wl, lane_off, (uint32_t)row_of(j, u) * (uint32_t)a.kr * 2u, d[u]);
     };
-    // the block's RW sums, then its RW/2 payload words: lane l < RW holds
-    // row lane_row(l), and its partner l ^ RW/2 the next row, so the lanes
-    // with an even row write one word each
     const int myrow = lane_row<RW>(lane);
     // the block's RW sums, then its RW/2 payload words for the exchange
     // workgroup: lane l < RW holds row lane_row(l), and its partner l ^ RW/2
