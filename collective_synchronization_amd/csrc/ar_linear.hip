@@ -383,26 +383,30 @@ __global__ __launch_bounds__(kWave * NMAX) void k_sim_linear(LinArgs a) {
   const int g = q / a.Q;
   const int qq = q - g * a.Q;
   if (g >= a.nranks) return;                               // whole workgroup
-  const int tg = qq * 8 + ((x - (g & 7)) & 7);
-  if (tg >= a.T) return;                                   // whole workgroup
+  // tile group: tiles tgrp, tgrp + 8Q, ... (one tile unless the grid needs
+  // fewer exchange workgroups), taken in turn within each op
+  const int tgrp = qq * 8 + ((x - (g & 7)) & 7);
+  if (tgrp >= a.T) return;                                 // whole workgroup
+  const int tstride = 8 * a.Q;
   u32x4* peers = reinterpret_cast<u32x4*>(smem);           // [NMAX][64]
   u32x4* mine = peers + NMAX * kWave;                      // [64]
   const bool role = w < a.nranks;
   const bool own = w == g;
   const int stager = a.nranks == 1 ? g : (g + 1) % a.nranks;
   const rsrc_t rs = make_rsrc(a.scratch, a.scratch_bytes);
-  const uint32_t loff = (uint32_t)tg * kTileBytes + (uint32_t)lane * 16u;
-  const bool active = loff < a.E;
-  int64_t first;
-  int n;
-  lane_elems<P>(tg, lane, first, n);
-  const int keep = chunk_keep<P>(a.count, tg, lane);
-  const int nwords = (keep + 1) >> 1;                      // payload words of the lane
   const int64_t slo = (int64_t)g * a.kr, shi = slo + a.kr;
   uint32_t seq = a.seq0;
   uint32_t par = a.parity0;
   for (int op = 0; op < a.nops; ++op) {
-    const uint32_t stale = seq_prev(seq_prev(seq));
+   const uint32_t stale = seq_prev(seq_prev(seq));
+   for (int tg = tgrp; tg < a.T; tg += tstride) {
+    const uint32_t loff = (uint32_t)tg * kTileBytes + (uint32_t)lane * 16u;
+    const bool active = loff < a.E;
+    int64_t first;
+    int n;
+    lane_elems<P>(tg, lane, first, n);
+    const int keep = chunk_keep<P>(a.count, tg, lane);
+    const int nwords = (keep + 1) >> 1;                    // payload words of the lane
     if (w == stager) {
       // the rank's payload words of this tile, as the workers publish them
       const uint32_t base = ((uint32_t)g * 2u + par) * half * 8u + (uint32_t)(first >> 1) * 8u;
@@ -507,6 +511,7 @@ __global__ __launch_bounds__(kWave * NMAX) void k_sim_linear(LinArgs a) {
           st8(ws, abase + (uint32_t)((e - slo) >> 1) * 8u, u32x2{o[qw], seq});
       }
     }
+   }
     seq = seq_next(seq);
     par ^= 1u;
   }
@@ -606,8 +611,6 @@ static int lin_geometry(const ar_sim_params* p, const DeviceInfo& di, LinGeom* g
   const int kl = (int)(kr / 64);
   const int nmax = lin_nmax(d->nranks);
   const int64_t T = ceil_div64(encoded_bytes(d->proto, d->count), kTileBytes);
-  const int64_t Q = ceil_div64(T, 8);
-  const int64_t comm = 8 * Q * d->nranks;
   const int64_t rows_wg = (int64_t)nmax * lin_rows_per_wave(kl);
   if (d->count % rows_wg != 0) return AR_EINVAL;          // every row in a block
   const int64_t bpr = d->count / rows_wg;
@@ -625,12 +628,20 @@ static int lin_geometry(const ar_sim_params* p, const DeviceInfo& di, LinGeom* g
   else
     coop = di.coop != 0;
   const int64_t cap = coop ? full : full / 2;
+  // exchange workgroups: one per tile where that leaves room for a worker
+  // workgroup per rank, else each takes several tiles in turn
+  int64_t Q = ceil_div64(T, 8), comm = 8 * Q * d->nranks;
+  while (Q > 1 && comm + d->nranks > cap) {
+    --Q;
+    comm = 8 * Q * d->nranks;
+  }
   int64_t wpr = (cap - comm) / d->nranks;
   if (wpr > bpr) wpr = bpr;
   if (wpr < 1) return AR_ECAPACITY;
   // an even share of blocks per worker workgroup
   const int64_t per = ceil_div64(bpr, wpr);
   wpr = ceil_div64(bpr, per);
+  if ((int64_t)p->nops * per >= (int64_t(1) << 31)) return AR_ESIZE;   // worker block count
   g->Q = (int32_t)Q;
   g->T = (int32_t)T;
   g->comm_blocks = (int32_t)comm;

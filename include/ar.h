@@ -512,10 +512,11 @@ int ar_sim_chain_geometry(const ar_sim_params* p, int32_t* blocks, int32_t* coop
  *      from the GEMV workgroups to the exchange workgroups, which send each
  *      tile whole, and each rank's reduced input slice back to the workers,
  *      as LL words.
- * One exchange workgroup per (rank, 1 KiB tile) and GEMV worker workgroups
- * beside them must all be resident: the worker count fills what the
- * occupancy query leaves (halved for an ordinary launch); AR_ECAPACITY when
- * not even one worker workgroup per rank fits.  Errors as for ar_sim_run
+ * Exchange workgroups (one per rank and 1 KiB tile, or per group of tiles
+ * taken in turn where one per tile would leave no room for a worker per
+ * rank) and GEMV worker workgroups beside them must all be resident: the
+ * worker count fills what the occupancy query leaves (halved for an ordinary
+ * launch); AR_ECAPACITY when not even one worker workgroup per rank fits.  Errors as for ar_sim_run
  * (AR_EINVAL for the restrictions above, AR_EALIGN for alignment).
  */
 int ar_sim_linear_run(const ar_sim_params* p, const void* weights, int32_t layers, void* work,

@@ -4,7 +4,8 @@ oracle's linear_chain_ops, bit for bit on every op and every rank's output.
 
 Each rank reads only its slice of its own input row: the rest of every row
 holds the sentinel pattern and other negative NaNs, which would poison the
-result if read.  Cases: one to sixteen ranks, slices of 256 to 2048 inputs
+result if read.  Cases: one to sixteen ranks (at sixteen, LL and LL128 with
+exchange workgroups that take two tiles each), slices of 256 to 2048 inputs
 (the GEMV's four lane widths), several layers taken in turn, two launches
 in a row (the epoch, the receive slots and the work buffer carry over), the
 decode workload's full size (8 ranks, hidden 4096, 64 ops), inputs with
@@ -70,20 +71,7 @@ CASES = [(1, 256, 4, 2), (2, 512, 5, 2), (3, 768, 5, 3), (4, 1024, 6, 2), (5, 12
 @pytest.mark.parametrize("proto", PROTOS)
 @pytest.mark.parametrize("nranks,count,nops,layers", CASES)
 def test_sim_linear_parity(proto, nranks, count, nops, layers):
-    if nranks == 16 and proto != "sentinel":
-        # 16 ranks, LL / LL128: 16 or more tiles per rank make 256 exchange
-        # workgroups of 16 waves, which fill the chip at the kernel's
-        # register use: the capacity error the header documents
-        ws = buffers.Workspace(nranks, count, proto, nranks)
-        w = torch.zeros((layers, nranks, count, count // nranks), dtype=torch.int16,
-                        device="cuda")
-        xd, stride = buffers.rows_to_device(np.zeros((nranks, count), np.uint16))
-        outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
-        p = ws.sim_params(nops, xd, stride, outd, stride)
-        with pytest.raises(abi.ArError) as e:
-            abi.ar_sim_linear_run(p, w, layers, ws.linear_work())
-        assert e.value.code == abi.AR_ECAPACITY
-        return
+    # (16 ranks, LL / LL128: an exchange workgroup takes two tiles in turn)
     _run(proto, nranks, count, nops, layers, seed=5100 + count + nranks)
 
 
