@@ -342,11 +342,16 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
         }
         uint16_t* orow = a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride;
         // Where an op's chunks fill half of the memory-side cache (the 256 MB
-        // MALL) or more, read the tiles written last first: they are the ones
-        // still cached.  8 ranks, 4 MiB: sentinel 127.4 -> 126.2 us per op, LL
-        // 206.6 -> 195.3; at 1 MiB (a quarter of the cache) the send order
-        // is 1-1.5% faster.
+        // MALL) or more and a wave walks many tiles, read the tiles written
+        // last first: they are the ones still cached.  Send order -> newest
+        // first, us per op, one box: sentinel 8 ranks 4 MiB 132.8 -> 127.6,
+        // 2 MiB 73.6 -> 68.1 (8 tiles a wave), 16 ranks 1 MiB 125.8 -> 121.9
+        // (8), 512 KiB 64.9 -> 66.0 (4 tiles a wave); LL 8 ranks 4 MiB 209.3
+        // -> 197.9 (32 tiles), 2 MiB 88.6 -> 88.3 (16), 16 ranks 1 MiB 200.7
+        // -> 200.0 (16), 512 KiB 84.5 -> 86.4 (8); at 8 ranks 1 MiB (a
+        // quarter of the cache) the send order is 1-1.5% faster.
         const bool newest_first =
+            a.TPW >= (P == kLL ? 16 : 8) &&
             (uint64_t)a.nconsumers * (uint64_t)a.nranks * a.E >= (uint64_t(128) << 20);
         // LL128: one flag per producer wave orders all of its data of the op
         if (P == kLL128 &&
