@@ -800,8 +800,8 @@ def main() -> int:
     m = summarize(res, proto, nranks, count, nops, args.steps, coll)
     kname = kernel_label(proto, nranks, res["geo"], args.mode, coll)
     unit = "us per all-gather" if coll == "allgather" else "us per all-reduce"
-    # the survey's count of the same op: every rank's slot in every consumer's
-    # buffer, its own included (this build keeps a rank's own chunk in
+    # the same op counted with every rank's slot in every consumer's
+    # buffer, its own included (the kernels keep a rank's own chunk in
     # registers, so `achieved` counts N-1 slots per consumer)
     n2_bytes = None
     if coll == "allreduce":
@@ -845,7 +845,7 @@ def main() -> int:
             "kernel": kname, "avg_launch_us": round(m["avg_launch_us"], 3),
             "algorithmic_bytes_per_launch": m["bytes_launch"],
             "algorithmic_bytes_per_op": m["bytes_op"],
-            "frac_survey_bytes": (round(n2_bytes * nops / avg_s / 1e9 / HBM_PEAK_GBS, 6)
+            "frac_all_slots": (round(n2_bytes * nops / avg_s / 1e9 / HBM_PEAK_GBS, 6)
                                   if n2_bytes else None),
         },
     }

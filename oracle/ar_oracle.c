@@ -29,7 +29,7 @@
  *         Inference", abstract: one-shot all-reduce, dual buffering removes
  *         the bottom (write-after-write) barrier.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - result: out[j] = bf16_rne(((f32(x0[j]) + f32(x1[j])) + ...) + f32(x_{N-1}[j]))
  *    with every '+' one IEEE binary32 round-to-nearest-even addition, in rank
  *    order 0..N-1, starting from x0 (not from +0.0), denormals kept.
@@ -397,7 +397,7 @@ void o_canon_in_array(const uint16_t* b, int64_t n, uint16_t* out)
  * reduce-scatter, each rank reducing one share, then an all-gather of the
  * reduced shares) is the form that scales to more GPUs.
  *
- * Readings (listed in the design doc):
+ * Readings:
  *  - shares: rank k owns elements [lo_k, hi_k) with width C = ceil(count/n)
  *    rounded up to a multiple of 8 elements (16 bytes), lo_k = min(k*C,
  *    count), hi_k = min(lo_k + C, count); trailing shares may be empty.
