@@ -4,7 +4,7 @@
  * include/ar.h).  Built by tests/test_host_sanitize.py with gcc/g++ and
  * AddressSanitizer + UndefinedBehaviorSanitizer.
  *
- * Every table is an exact-size heap block.  The driver checks the argument
+ * Every table is an exact-size heap block.  This program checks the argument
  * errors the header documents (NULL table or output, no entries, nranks
  * outside 1..16, negative sizes, no available protocol) and compares every
  * choice on random tables with a brute-force reading of the documented
