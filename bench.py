@@ -421,6 +421,89 @@ def measure_epilogue(torch, abi, buffers, x, proto, nranks, count, steps, warmup
     return out
 
 
+def measure_graph(torch, abi, buffers, x, proto, nranks, count, steps):
+    """Calls captured in a HIP graph against the same calls issued eagerly.
+    Two sequences of K = x.shape[0] ops (system mode): K one-op persistent
+    launches (ar_sim_run), and K stream-ordered pack + reduce pairs; each
+    sequence starts with ar_state_reset, which makes its replays sound (a
+    replay repeats the captured epochs).  Eagerly, the arguments of every
+    call are built before the timed region, and the sequence starts from the
+    same reset.  Microseconds per op: HIP events around a replay, or around
+    the eager sequence, on the launch stream; median over `steps`.  proto:
+    LL, LL128 or SENTINEL (the barrier baseline's launches need a counter
+    reset each)."""
+    import ctypes
+    if proto not in ("ll", "ll128", "sentinel"):
+        raise RuntimeError(f"graph replay timing: no {proto} sequence")
+    K = x.shape[0]
+    xd, stride = buffers.rows_to_device(x)
+    stream = torch.cuda.current_stream()
+    lib = abi.raw()
+    pack = getattr(lib, {"ll": "ar_pack_ll", "ll128": "ar_pack_ll128",
+                         "sentinel": "ar_pack_sentinel"}[proto])
+    flags = abi.AR_FLAG_REARM if proto == "sentinel" else 0
+    out = {"ops": K}
+    for kind in ("one_op_launches", "pack_reduce"):
+        ws = buffers.Workspace(nranks, count, proto, nranks)
+        outd = torch.zeros((K * nranks, stride), dtype=torch.int16, device="cuda")
+        rows = [(xd[j * nranks:].data_ptr(), outd[j * nranks:].data_ptr()) for j in range(K)]
+        calls = []
+        for j in range(K):
+            if kind == "one_op_launches":
+                p = ws.sim_params(1, rows[j][0], stride, rows[j][1], stride,
+                                  timeout_ns=TIMEOUT_NS)
+                calls.append(lambda sh, p=p: lib.ar_sim_run(ctypes.byref(p), sh))
+            else:
+                e = abi.ar_epoch(ws.epoch.seq, ws.epoch.parity)
+                d = ws.desc
+                calls.append(lambda sh, j=j, e=e, d=d: (
+                    pack(ctypes.byref(d), rows[j][0], stride, ws.scratch.data_ptr(), e, sh),
+                    lib.ar_reduce_validate(ctypes.byref(d), ws.scratch.data_ptr(), rows[j][1],
+                                           stride, e, ws.ctrl.data_ptr(), TIMEOUT_NS, flags,
+                                           sh)))
+            ws.flip()
+
+        def seq():
+            # the current stream: under capture, the capturing one
+            sh = torch.cuda.current_stream().cuda_stream
+            ws.reset_state(sh)
+            for c in calls:
+                r = c(sh)
+                if (r if isinstance(r, int) else min(r)) != abi.AR_OK:
+                    raise RuntimeError(f"{kind}: call returned {r}")
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            seq()
+        res = {}
+        ref = None
+        for mode in ("eager", "graph"):
+            if mode == "graph":               # the replays must write what eager calls wrote
+                ref = outd.clone()
+                outd.fill_(-1)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                  for _ in range(steps + 2)]
+            for k, (a, b) in enumerate(ev):
+                torch.cuda.synchronize()
+                a.record(stream)
+                if mode == "graph":
+                    g.replay()
+                else:
+                    seq()
+                b.record(stream)
+            torch.cuda.synchronize()
+            if ws.status() != 0:
+                raise RuntimeError(f"{kind} {mode}: device status "
+                                   f"{abi.status_string(ws.status())}")
+            res[mode] = round(statistics.median(a.elapsed_time(b) for a, b in ev[2:])
+                              * 1e3 / K, 3)
+        if not torch.equal(outd, ref):
+            raise RuntimeError(f"{kind}: graph replays wrote other outputs than eager calls")
+        out[kind + "_us_per_op"] = res
+        del g
+    return out
+
+
 def measure_chain(torch, abi, buffers, x0, proto, nranks, count, nops, steps, warmup,
                   seed=7):
     """The chained simulator (ar_sim_chain_run): op i+1's payload of rank r
@@ -901,6 +984,13 @@ def main() -> int:
                 "empty_kernel_us": fl["empty_kernel_us"] if fl else None}
         except (RuntimeError, KeyError) as e:
             side["n8_sentinel_1x4096_64ops"]["share_mode"] = {"error": str(e)}
+        # the same 64 ops as one-op launches and as stream-ordered pairs,
+        # captured in a HIP graph and replayed, against eager calls
+        try:
+            side["n8_sentinel_1x4096_64ops"]["graph_replay"] = measure_graph(
+                torch, abi, buffers, x2, "sentinel", c2[0], c2[2], max(args.steps, 20))
+        except (RuntimeError, abi.ArError) as e:
+            side["n8_sentinel_1x4096_64ops"]["graph_replay"] = {"error": str(e)}
         # the decode chain whose producer is a row-parallel linear layer (8
         # ranks, hidden 4096, LL, 64 ops over 16 layers of weights)
         try:

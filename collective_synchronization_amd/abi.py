@@ -106,6 +106,7 @@ _SIGS = {
                         ctypes.c_int),
     "ar_ctrl_bytes": ([], _i64),
     "ar_ctrl_reset": ([_vp, _vp], ctypes.c_int),
+    "ar_state_reset": ([ctypes.POINTER(ar_desc), _vp, _vp, _vp, _vp], ctypes.c_int),
     "ar_epoch_init": ([ctypes.POINTER(ar_epoch)], ctypes.c_int),
     "ar_epoch_flip": ([ctypes.POINTER(ar_epoch)], ctypes.c_int),
     "ar_epoch_advance": ([ctypes.POINTER(ar_epoch), _u64], ctypes.c_int),
@@ -258,6 +259,13 @@ def ar_epoch_advance(e: ar_epoch, nops: int) -> ar_epoch:
 
 def ar_ctrl_reset(ctrl, stream=None) -> None:
     _check(_lib.ar_ctrl_reset(_ptr(ctrl), _stream(stream)), "ar_ctrl_reset")
+
+
+def ar_state_reset(desc, scratch=None, ctrl=None, work=None, stream=None) -> None:
+    """Initial state of the given buffers (None: left alone), with fill
+    kernels: the head of a captured sequence that is to be replayed."""
+    _check(_lib.ar_state_reset(ctypes.byref(desc), _ptr(scratch), _ptr(ctrl), _ptr(work),
+                               _stream(stream)), "ar_state_reset")
 
 
 def _pack(name, desc, inp, in_stride, scratch, epoch, stream):

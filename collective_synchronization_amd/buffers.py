@@ -83,6 +83,15 @@ class Workspace:
     def reset_ctrl(self, stream=None) -> None:
         abi.ar_ctrl_reset(self.ctrl, stream)
 
+    def reset_state(self, stream=None) -> None:
+        """Control block, receive buffers and (if allocated) the linear work
+        buffer back to their initial state, with fill kernels on the stream.
+        Put first in a captured graph, it makes every replay start afresh
+        (a replay repeats the epochs captured).  The workspace's epoch stays
+        where the capture left it, which is the state a replay leaves."""
+        abi.ar_state_reset(self.desc, self.scratch, self.ctrl,
+                           getattr(self, "_work", None), stream)
+
     def slot_view(self) -> np.ndarray:
         """Host copy of the receive buffers: uint8 [nconsumers, 2, nranks, slot]
         ([2 regions, nconsumers, 2, nranks, slot] for the two-shot all-reduce:

@@ -197,5 +197,9 @@ int chain_sim_run(const ar_sim_params* p, const float* scales, hipStream_t s);
 // Every host-side check ar_sim_run makes, including the grid it would launch,
 // without enqueuing anything (ar_kernels.hip).
 int sim_validate(const ar_sim_params* p);
+// Fill [0, bytes) of a device buffer with a 32-bit pattern: a kernel with
+// device-scope coherent 16-byte stores, so it can be captured in a graph
+// (ar_state.hip).  bytes: a multiple of 16, below 4 GiB.
+hipError_t fill_words(void* base, int64_t bytes, uint32_t word, hipStream_t s);
 
 }  // namespace ar

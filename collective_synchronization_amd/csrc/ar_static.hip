@@ -62,31 +62,11 @@ int static_base(uint8_t** out) {
 
 }  // namespace
 
-// Fill [0, bytes) of `base` with the 32-bit pattern `word`, 16 bytes a lane,
-// with device-scope coherent stores (the simulator polls with such loads).
-__global__ __launch_bounds__(kBlock) void k_static_fill(uint8_t* base, uint32_t bytes,
-                                                        uint32_t word) {
-  const rsrc_t rs = make_rsrc(base, bytes);
-  const u32x4 v = u32x4{word, word, word, word};
-  const uint32_t step = gridDim.x * (uint32_t)kBlock * 16u;
-  for (uint32_t off = (blockIdx.x * (uint32_t)kBlock + threadIdx.x) * 16u; off < bytes;
-       off += step)
-    st16(rs, off, v);
-}
-
 // The status word of the control block, copied to the caller's output.
 __global__ void k_static_status(const int* ctrl, int32_t* status) {
   if (threadIdx.x == 0)
     *status = __hip_atomic_load(ctrl + kCtrlStatus, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
-}
-
-static hipError_t fill(uint8_t* base, int64_t bytes, uint32_t word, hipStream_t s) {
-  if (bytes <= 0) return hipSuccess;
-  int64_t blocks = ceil_div64(bytes, (int64_t)kBlock * 16);
-  if (blocks > 4096) blocks = 4096;
-  return launch(k_static_fill, dim3((unsigned)blocks), dim3(kBlock), s, base,
-                (uint32_t)bytes, word);
 }
 
 }  // namespace ar
@@ -110,10 +90,10 @@ extern "C" int ar_sim_run_static(const ar_sim_params* p, int32_t* status, void* 
   rc = sim_validate(&q);                 // every host-side check, nothing enqueued
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = map_hip(fill(base, kStaticCtrlBytes, 0u, s));
+  rc = map_hip(fill_words(base, kStaticCtrlBytes, 0u, s));
   if (rc) return rc;
   const uint32_t armed = p->desc.proto == kSentinel ? 0xFFFFFFFFu : 0u;
-  rc = map_hip(fill(base + kStaticCtrlBytes, need, armed, s));
+  rc = map_hip(fill_words(base + kStaticCtrlBytes, need, armed, s));
   if (rc) return rc;
   rc = ar_sim_run(&q, stream);
   if (rc) return rc;

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 LIB = os.path.join(PKG, "libcsync_ar.so")
 SOURCES = [os.path.join(HERE, "ar_kernels.hip"), os.path.join(HERE, "ar_collectives.hip"),
-           os.path.join(HERE, "ar_static.hip"), os.path.join(HERE, "ar_linear.hip"),
+           os.path.join(HERE, "ar_static.hip"), os.path.join(HERE, "ar_state.hip"),
+           os.path.join(HERE, "ar_linear.hip"),
            os.path.join(HERE, "ar_select.cpp")]
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 HEADERS = [os.path.join(INCLUDE, "ar_device.h"), os.path.join(INCLUDE, "ar_protocols.h"),

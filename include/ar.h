@@ -182,6 +182,34 @@ int64_t ar_ctrl_bytes(void);
 /* Zero the control block with a small fill kernel (safe inside graphs). */
 int ar_ctrl_reset(void* ctrl, void* stream);
 
+/* ------------------------------------------------------- graph capture --- */
+/*
+ * Every device call of this library is one or more kernel launches on
+ * `stream` -- no memset or copy nodes, no host waits -- so a sequence of
+ * calls can be captured in a HIP graph (hipStreamBeginCapture, or a
+ * framework's graph capture) and replayed; cooperative launches are captured
+ * as cooperative kernel nodes.  A replay repeats the epochs its calls were
+ * captured with, so flags left by the previous replay would look current (or
+ * corrupt) to it.  Start the captured sequence with ar_state_reset of every
+ * buffer the sequence uses: each replay then begins from the initial state,
+ * in which any epoch is valid.  (ar_sim_run_static clears its own buffers.)
+ *
+ * ar_state_reset -- returns the buffers of descriptor d to their initial
+ * state with fill kernels on `stream`:
+ *   ctrl:    ar_ctrl_bytes() bytes, to zero;
+ *   scratch: ar_scratch_bytes(d) bytes, to zero (LL, LL128, BARRIER: a zero
+ *            flag is "never written"), or every element to 0xFFFF for
+ *            AR_SENTINEL (both parities; both regions of AR_TWOSHOT);
+ *   work:    ar_linear_work_bytes(d) bytes (the work buffer of
+ *            ar_sim_linear_run), to zero.
+ * Each may be NULL (left alone), but not all three (AR_EINVAL); each other
+ * one 256-byte aligned (AR_EALIGN); a buffer of 4 GiB or more: AR_ESIZE.
+ * After a replay the buffers hold what the captured calls left, as after
+ * the same calls made eagerly: an eager call on them next takes the epoch
+ * that followed the last captured call, or comes after an ar_state_reset.
+ */
+int ar_state_reset(const ar_desc* d, void* scratch, void* ctrl, void* work, void* stream);
+
 /* ------------------------------------------------------------ producer --- */
 /*
  * Producers: encode every simulated rank's payload for epoch `e` into slot r
@@ -654,7 +682,8 @@ int ar_probe_placement(int32_t blocks, int32_t threads, void* work, void* result
 int ar_probe_litmus(void* work, int32_t iters, int32_t xcd_a, int32_t xcd_b,
                     int32_t kind, void* result, void* stream);
 
-/* Library ABI version (bumped on any signature change). */
+/* Library ABI version (bumped when an existing signature or struct changes;
+ * entry points may be added between bumps). */
 int ar_abi_version(void);
 
 /* hipError_t code of the last HIP call that made an entry point return

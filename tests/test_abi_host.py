@@ -130,6 +130,24 @@ def test_size_limits():
     assert _code("ar_scratch_bytes", ctypes.byref(edge)) == abi.AR_ESIZE
 
 
+def test_state_reset_argument_checks():
+    """ar_state_reset checks its arguments before it enqueues a fill."""
+    d = abi.make_desc(8, 4096, "sentinel", 8)
+    rs = lambda *a: _code("ar_state_reset", *a)
+    assert rs(None, FAKE, FAKE, FAKE, None) == abi.AR_EINVAL              # no descriptor
+    assert rs(ctypes.byref(d), None, None, None, None) == abi.AR_EINVAL   # nothing to reset
+    assert rs(ctypes.byref(d), FAKE + 128, None, None, None) == abi.AR_EALIGN
+    assert rs(ctypes.byref(d), None, FAKE + 4, None, None) == abi.AR_EALIGN
+    assert rs(ctypes.byref(d), None, None, FAKE + 16, None) == abi.AR_EALIGN
+    bad = abi.make_desc(8, 4096, "ll", 8)
+    bad.nranks = 0
+    assert rs(ctypes.byref(bad), FAKE, None, None, None) == abi.AR_EINVAL
+    edge = abi.make_desc(16, 1 << 21, "ll", nconsumers=16)            # 4 GiB of slots
+    assert rs(ctypes.byref(edge), FAKE, None, None, None) == abi.AR_ESIZE
+    empty = abi.make_desc(4, 0, "ll", 4)                               # no linear work
+    assert rs(ctypes.byref(empty), None, None, FAKE, None) == abi.AR_EINVAL
+
+
 def test_reduce_argument_checks():
     d = abi.make_desc(8, 4096, "sentinel")
     ep = abi.ar_epoch(1, 0)
