@@ -249,14 +249,18 @@ def kernel_label(proto, nranks, geo, mode, collective):
 
 def load_traffic(kernel_name: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this kernel on this workload, if it was taken on the current kernel
-    source."""
+    this kernel (None: the one kernel summarized for the workload) on this
+    workload, if it was taken on the current kernel source."""
     try:
         with open(PROFILE_TRAFFIC) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    ent = t.get(f"{kernel_name}@{workload}")
+    if kernel_name is None:        # whichever kernel that workload ran
+        ents = [v for k, v in t.items() if k.endswith("@" + workload)]
+        ent = ents[0] if len(ents) == 1 else None
+    else:
+        ent = t.get(f"{kernel_name}@{workload}")
     if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
     return ent.get("bytes_per_launch")
@@ -740,6 +744,12 @@ def side_workload(torch, abi, buffers, inputs, name, wl, steps, warmup, floor_us
         "traffic": load_traffic(kname, workload_name(nranks, proto, rows, hidden, nops, mode,
                                                      coll)),
     })
+    if r["geo"]["launch"] == "cooperative":
+        # the profiler records no cooperative launch: the counters of the
+        # same workload launched ordinarily (`... --launch ordinary`)
+        out["traffic_ordinary_launch"] = load_traffic(
+            None, workload_name(nranks, proto, rows, hidden, nops, mode, coll,
+                                launch="ordinary"))
     if skew_us > 0:
         out["skew"] = measure_skew(torch, abi, buffers, inputs, x, proto, nranks, count, nops,
                                    min(steps, 10), 2, skew_us, seed, coll)
