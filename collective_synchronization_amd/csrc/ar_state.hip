@@ -26,10 +26,11 @@ __global__ __launch_bounds__(kBlock) void k_fill_words(uint8_t* base, uint32_t b
                                                        uint32_t word) {
   const rsrc_t rs = make_rsrc(base, bytes);
   const u32x4 v = u32x4{word, word, word, word};
-  const uint32_t step = gridDim.x * (uint32_t)kBlock * 16u;
-  for (uint32_t off = (blockIdx.x * (uint32_t)kBlock + threadIdx.x) * 16u; off < bytes;
+  // 64-bit offsets, so that the last step cannot wrap below `bytes`
+  const uint64_t step = (uint64_t)gridDim.x * kBlock * 16u;
+  for (uint64_t off = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * 16u; off < bytes;
        off += step)
-    st16(rs, off, v);
+    st16(rs, (uint32_t)off, v);
 }
 
 hipError_t fill_words(void* base, int64_t bytes, uint32_t word, hipStream_t s) {
