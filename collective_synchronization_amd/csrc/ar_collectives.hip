@@ -292,8 +292,9 @@ __device__ __forceinline__ bool sim_place(const CollSimArgs& a, int& g, int& tg)
 // consumer w, then polls peer w's tiles and decodes them straight into row
 // w of rank g's output (no staging: nothing is reduced); the rank's own
 // wave writes its own row.  One workgroup barrier per op: a rank starts op
-// i+1 once it holds all of op i.  TB: tiles whose input loads overlap when a
-// wave walks several (1: one load, then its stores, at a time).
+// i+1 once it holds all of op i (LL with one tile per group: none, below).
+// TB: tiles whose input loads overlap when a wave walks several (1: one
+// load, then its stores, at a time).
 template <int P, int NMAX, int TB, bool EXTRAS>
 __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
   if constexpr (!EXTRAS) {
@@ -315,6 +316,11 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
   // one tile per group: the next op's payload chunk is loaded while this op
   // is exchanged, so no input load sits between two ops' sends
   const bool pipelined = mine == 1;
+  // LL, one tile per group, no delays or trace: no barrier at all.  Wave w
+  // sends op i+1 to peer w once it holds peer w's op i, which peer w sent
+  // after reading this rank's op i-1: the licence is pairwise, and each
+  // wave goes at its own pace (a wave whose poll gives up just ends).
+  const bool unpaced = !EXTRAS && P == kLL && pipelined;
   const int keep = chunk_keep<P>(a.count, tg, lane);
   uint32_t wnext[4] = {0u, 0u, 0u, 0u};
   if (pipelined) load_chunk<P>(a.in + (int64_t)g * a.in_stride, row_bytes, tg, lane, wnext);
@@ -386,6 +392,7 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
         if (poll_chunk<P>(rs, src0 + loff, loff < a.E, seq, stale, true, a.ctrl,
                           a.timeout_ticks, lane, v) != 0) {
           if (lane == 0) lds_err = 1;
+          if (unpaced) return;                     // no barrier to meet
           break;
         }
         store_chunk_elems<P>(orow + (int64_t)w * a.row_stride, a.count, tile, a.E, lane, v);
@@ -417,8 +424,10 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
         }
       }
     }
-    __syncthreads();
-    if (lds_err) return;                           // whole workgroup
+    if (!unpaced) {
+      __syncthreads();
+      if (lds_err) return;                         // whole workgroup
+    }
     if (a.trace && own && lane == 0) trace_max(a, (int64_t)op * tstride + a.nranks + g);
     seq = seq_next(seq);
     par ^= 1u;
@@ -446,14 +455,17 @@ __global__ __launch_bounds__(1024) void k_sim_gather(CollSimArgs a) {
 // slots it polled) complete before that licence is sent.
 // BATCH: share tiles received, reduced and all-gathered per pair of
 // workgroup barriers (1 when every workgroup owns one tile, 2 otherwise; a
-// wave polls its peer's two chunks together).
+// wave polls its peer's two chunks together).  LL with one tile per group
+// takes one barrier per op instead (the pairwise loop below).
 template <int P, int NMAX, int BATCH, bool EXTRAS>
 __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
   if constexpr (!EXTRAS) {
     a.delay = nullptr;
     a.trace = nullptr;
   }
-  __shared__ u32x4 lds[BATCH][NMAX][kWave];
+  // the pairwise LL loop below stages op i's rows in buffer parity(i)
+  constexpr bool kPairwise = BATCH == 1 && !EXTRAS && P == kLL;
+  __shared__ u32x4 lds[kPairwise ? 2 : BATCH][NMAX][kWave];
   __shared__ u32x4 red[BATCH][kWave];
   __shared__ int lds_err;
   const int lane = threadIdx.x & (kWave - 1);
@@ -489,6 +501,80 @@ __global__ __launch_bounds__(1024) void k_sim_twoshot(CollSimArgs a) {
                                (int64_t)a.nops * tstride,
                            (unsigned long long)now_ticks(), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // One tile per group, LL: one workgroup barrier per op.  After it every
+  // wave sums the staged rows itself (the same rank-order sum, so the same
+  // bits) and wave w sends the reduced tile to peer w at once, then polls
+  // peer w's reduced share and goes on to the next op without waiting for
+  // the other waves.  Licences, pairwise: wave w sends op i+1's chunk to
+  // peer w after it has received peer w's reduced share of op i, which peer
+  // w sent after reading this rank's chunk of op i (and of op i-1 before
+  // it), so the reduce-scatter slot of op i+1's parity is free; and it
+  // sends op i+1's reduced tile after receiving peer w's chunk of op i+1,
+  // which peer w sent after reading the reduced tile of op i-1.  Staging
+  // rows alternate between two LDS buffers by parity: wave w writes its row
+  // of op i+2 after it has passed the barrier of op i+1, which every wave
+  // reaches only after it has read the rows of op i.
+  if constexpr (kPairwise) {
+    const uint32_t loff = (uint32_t)tg * kTileBytes + (uint32_t)lane * 16u;
+    const int keep_g = chunk_keep<P>(m_g, tg, lane);
+    int64_t first_g;
+    int n_g;
+    lane_elems<P>(tg, lane, first_g, n_g);
+    uint32_t seq = a.seq0;
+    uint32_t par = a.parity0;
+    bool failed = false;                           // this wave's last poll gave up
+    for (int op = 0; op < a.nops; ++op) {
+      const uint32_t stale = seq_prev(seq_prev(seq));
+      const uint16_t* row = a.in + ((int64_t)op * a.nranks + g) * a.in_stride;
+      uint16_t* orow = a.out + ((int64_t)op * a.nranks + g) * a.out_stride;
+      const uint32_t rs_dst = (((uint32_t)w * 2u + par) * N + (uint32_t)g) * a.slot_bytes;
+      const uint32_t rs_src = (((uint32_t)g * 2u + par) * N + (uint32_t)w) * a.slot_bytes;
+      mask_words(wnext, keep);
+      const u32x4 mine_v = encode_words<P>(wnext, lane, seq);
+      if (!own) store_chunk<P>(rs, rs_dst, 0u, 1, -1, tg, E_w, lane, mine_v);
+      if (op + 1 < a.nops)
+        load_chunk<P>(row + (int64_t)a.nranks * a.in_stride + lo_mine, rb_mine, tg, lane,
+                      wnext);
+      if (!own) {
+        u32x4 got;
+        if (failed || poll_chunk<P>(rs, rs_src + loff, loff < E_g, seq, stale, true,
+                                    a.ctrl, a.timeout_ticks, lane, got) != 0) {
+          if (lane == 0) lds_err = 1;
+        } else {
+          lds[par][w][lane] = got;
+        }
+      } else {
+        lds[par][g][lane] = mine_v;
+      }
+      __syncthreads();
+      if (lds_err) return;                         // whole workgroup
+      u32x4 v[NMAX];
+#pragma unroll
+      for (int r = 0; r < NMAX; ++r)
+        v[r] = (r < a.nranks) ? lds[par][r][lane] : u32x4{0u, 0u, 0u, 0u};
+      uint32_t o[4];
+      reduce_words<P, NMAX>(v, a.nranks, o);
+      mask_words(o, keep_g);
+      if (own) {
+        if (loff < E_g) store_elems(orow + lo_g, m_g, first_g, n_g, o);
+      } else {
+        store_chunk<P>(rs, a.ag0 + rs_dst, 0u, 1, -1, tg, E_g, lane,
+                       encode_words<P>(o, lane, seq));
+        u32x4 got;
+        if (poll_chunk<P>(rs, a.ag0 + rs_src + loff, loff < E_w, seq, stale, true, a.ctrl,
+                          a.timeout_ticks, lane, got) != 0) {
+          // the next op's barrier ends the workgroup (after the last op,
+          // the status word holds the error)
+          failed = true;
+        } else {
+          store_chunk_elems<P>(orow + lo_w, m_w, tg, E_w, lane, got);
+        }
+      }
+      seq = seq_next(seq);
+      par ^= 1u;
+    }
+    return;
   }
   uint32_t seq = a.seq0;
   uint32_t par = a.parity0;
