@@ -980,9 +980,18 @@ __global__ __launch_bounds__(kWave) void k_sim_twoshot_narrow(CollSimArgs a) {
 // second barrier also covers both LDS buffers' reuse, and each op's sends
 // come after the op before it has been consumed (consume(i), then
 // produce(i+1)), which is the dual-buffer licence.
+// LL and LL128 up to 8 ranks take one barrier per op instead: every wave
+// sums the staged rows itself (the same rank-order sum, so the same bits)
+// and scales its own next payload chunk, and the staging rows alternate
+// between two LDS buffers by parity (a wave stages op i+1 only after the
+// barrier of op i, and its row of op i+2 only after that of op i+1, which
+// every wave reaches after reading op i's rows).  At 16 ranks the sixteen
+// copies of the sum cost more than the barrier saves, and the sentinel's
+// wait for its re-arm stores before each send then falls on the path.
 template <int P, int NMAX>
 __global__ __launch_bounds__(1024) void k_sim_chain(CollSimArgs a) {
-  __shared__ u32x4 lds[NMAX][kWave];
+  constexpr bool kEach = P != kSentinel && NMAX <= 8;
+  __shared__ u32x4 lds[kEach ? 2 : 1][NMAX][kWave];
   __shared__ u32x4 next[kWave];
   __shared__ int lds_err;
   const int lane = threadIdx.x & (kWave - 1);
@@ -1006,6 +1015,11 @@ __global__ __launch_bounds__(1024) void k_sim_chain(CollSimArgs a) {
   uint32_t par = a.parity0;
   for (int op = 0; op < a.nops; ++op) {
     const uint32_t stale = seq_prev(seq_prev(seq));
+    const int b = kEach ? (int)par : 0;            // staging buffer of this op
+    // every wave scales its own next chunk: the factor, loaded before this
+    // op's exchange
+    const float s_next =
+        kEach && op + 1 < a.nops ? a.scales[(int64_t)(op + 1) * a.nranks + g] : 0.f;
     const u32x4 enc = encode_words<P>(x, lane, seq);
     if (!own) {
       // sentinel: this wave's re-arm stores of the previous op complete
@@ -1023,38 +1037,48 @@ __global__ __launch_bounds__(1024) void k_sim_chain(CollSimArgs a) {
                         got) != 0) {
         if (lane == 0) lds_err = 1;
       } else {
-        lds[w][lane] = got;
+        lds[b][w][lane] = got;
       }
     }
-    if (w == stager) lds[g][lane] = enc;
+    if (w == stager) lds[b][g][lane] = enc;
     __syncthreads();
     if (lds_err) return;                           // whole workgroup
-    if (own) {
+    if (kEach || own) {
       u32x4 v[NMAX];
 #pragma unroll
       for (int r = 0; r < NMAX; ++r)
-        v[r] = (r < a.nranks) ? lds[r][lane] : u32x4{0u, 0u, 0u, 0u};
+        v[r] = (r < a.nranks) ? lds[b][r][lane] : u32x4{0u, 0u, 0u, 0u};
       uint32_t o[4];
       reduce_words<P, NMAX>(v, a.nranks, o);
       mask_words(o, keep);
-      int64_t first;
-      int n;
-      lane_elems<P>(tg, lane, first, n);
-      if (loff < a.E)
-        store_elems(a.out + ((int64_t)op * a.nranks + g) * a.out_stride, a.count, first, n, o);
+      if (own) {
+        int64_t first;
+        int n;
+        lane_elems<P>(tg, lane, first, n);
+        if (loff < a.E)
+          store_elems(a.out + ((int64_t)op * a.nranks + g) * a.out_stride, a.count, first, n,
+                      o);
+      }
       if (op + 1 < a.nops) {
-        scale_words(o, a.scales[(int64_t)(op + 1) * a.nranks + g]);
+        scale_words(o, kEach ? s_next : a.scales[(int64_t)(op + 1) * a.nranks + g]);
         mask_words(o, keep);
-        next[lane] = u32x4{o[0], o[1], o[2], o[3]};
+        if constexpr (kEach) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[k] = o[k];
+        } else {
+          next[lane] = u32x4{o[0], o[1], o[2], o[3]};
+        }
       }
     }
-    __syncthreads();
-    if (op + 1 < a.nops) {
-      const u32x4 nx = next[lane];
-      x[0] = nx.x;
-      x[1] = nx.y;
-      x[2] = nx.z;
-      x[3] = nx.w;
+    if constexpr (!kEach) {
+      __syncthreads();
+      if (op + 1 < a.nops) {
+        const u32x4 nx = next[lane];
+        x[0] = nx.x;
+        x[1] = nx.y;
+        x[2] = nx.z;
+        x[3] = nx.w;
+      }
     }
     seq = seq_next(seq);
     par ^= 1u;
