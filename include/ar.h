@@ -391,7 +391,9 @@ int ar_scale_rows(int32_t nranks, int64_t count, const void* in, int64_t in_stri
  *   AR_ALLGATHER: op i's output at consumer c is the all-gather layout of
  *        ar_gather_validate at out + (i*nranks + c)*out_stride.  A rank
  *        starts op i+1 once it holds all of op i (one workgroup barrier per
- *        op), as a rank whose next payload depends on this result would.
+ *        op), as a rank whose next payload depends on this result would;
+ *        with LL and one tile per workgroup, each pair of ranks licenses
+ *        its own next op instead (no barrier).
  *        One kernel (a workgroup of one wave per peer); AR_SIM_NARROW and
  *        AR_SIM_WIDE are rejected.
  *   AR_TWOSHOT: per op and tile of a share, the reduce-scatter exchange, the
@@ -498,7 +500,8 @@ int ar_sim_geometry(const ar_sim_params* p, int32_t* waves_per_rank,
  * AR_ECAPACITY when no resident grid holds every tile (payloads above a
  * few tens of KiB per rank at 16 ranks).  Per op: the sends, the polls,
  * one workgroup barrier, the rank-order reduce and the scaling, a second
- * barrier.  Errors as for ar_sim_run.
+ * barrier (LL and LL128 up to 8 ranks: every wave reduces and scales
+ * itself, and the second barrier goes).  Errors as for ar_sim_run.
  */
 int ar_sim_chain_run(const ar_sim_params* p, const float* scales, void* stream);
 
