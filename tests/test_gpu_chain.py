@@ -92,3 +92,33 @@ def test_sim_chain_argument_errors():
     big = buffers.Workspace(16, 65536, "ll", 16)
     assert _chain_error(big) == abi.AR_ECAPACITY
     assert ws.status() == 0
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+def test_sim_chain_tiny_deadline_then_reset(proto):
+    """A poll deadline of one wall-clock tick, set from the host (LL and
+    LL128 at 8 ranks run the one-barrier form, the sentinel the two-barrier
+    one): every wait gives up at once or finds its data, and the launch ends
+    with OK or AR_ETIMEOUT, never a hang.  After ar_state_reset the same
+    buffers run bit-exact again."""
+    nranks, count, nops = 8, 4096, 16
+    ws = buffers.Workspace(nranks, count, proto, nranks)
+    x0 = inputs.payload(6950, (nranks, count), "normal")
+    xd, stride = buffers.rows_to_device(x0)
+    s = _scales(6951, nops, nranks)
+    sd = torch.from_numpy(s).to("cuda")
+    outd = torch.zeros((nops * nranks, stride), dtype=torch.int16, device="cuda")
+    print(f"[chain-deadline] {proto}", flush=True)
+    ws.sim_chain(nops, xd, stride, outd, stride, sd, timeout_ns=1)
+    torch.cuda.synchronize()
+    assert ws.status() in (0, abi.AR_ETIMEOUT), abi.status_string(ws.status())
+    ws.reset_state()
+    seq0 = ws.epoch.seq
+    ws.sim_chain(nops, xd, stride, outd, stride, sd, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    want = oracle.chain_ops(x0, s, proto, seq0)
+    got = buffers.rows_from_device(outd, count, (nops, nranks))
+    for i in range(nops):
+        for c in range(nranks):
+            assert np.array_equal(got[i, c], want[i]), (i, c)

@@ -327,3 +327,43 @@ def test_allgather_n8_1x4096_64ops(proto):
             assert np.array_equal(got[i, c], want[i]), (i, c)
     if proto == "sentinel":
         assert not np.any(got == 0xFFFF)
+
+
+@pytest.mark.parametrize("collective,nranks,count", [("twoshot", 16, 32768),
+                                                     ("allgather", 8, 4096)])
+def test_sim_pairwise_tiny_deadline_then_reset(collective, nranks, count):
+    """LL with one tile per workgroup runs the pairwise loops (the two-shot
+    with one barrier per op, the all-gather with none).  A poll deadline of
+    one wall-clock tick, set from the host, makes every wait give up at once
+    or find its data: the launch ends with OK or AR_ETIMEOUT, never a hang.
+    After ar_state_reset the same buffers run bit-exact again."""
+    nops = 16
+    ws = buffers.Workspace(nranks, count, "ll", nranks, collective=collective)
+    x = _x(6900, (nops, nranks, count), specials=False)
+    xd, stride = buffers.rows_to_device(x)
+    ostride = ws.gather_stride() if collective == "allgather" else stride
+    outd = torch.zeros((nops * nranks, ostride), dtype=torch.int16, device="cuda")
+    geo = abi.ar_sim_geometry(ws.sim_params(nops, xd, stride, outd, ostride))
+    print(f"[pairwise-deadline] {collective} N={nranks} count={count} geo={geo}", flush=True)
+    assert geo["tiles_per_wave"] == 1 and geo["kernel"] == "wide"
+    ws.sim(nops, xd, stride, outd, ostride, timeout_ns=1)
+    torch.cuda.synchronize()
+    assert ws.status() in (0, abi.AR_ETIMEOUT), abi.status_string(ws.status())
+    ws.reset_state()
+    seq0 = ws.epoch.seq
+    ws.sim(nops, xd, stride, outd, ostride, timeout_ns=TIMEOUT_NS)
+    torch.cuda.synchronize()
+    assert ws.status() == 0, abi.status_string(ws.status())
+    if collective == "twoshot":
+        want = oracle.twoshot_ops(x, "ll", seq0)
+        got = buffers.rows_from_device(outd, count, (nops, nranks))
+        for i in range(nops):
+            for c in range(nranks):
+                assert np.array_equal(got[i, c], want[i]), (i, c)
+    else:
+        want = oracle.allgather_ops(x, "ll", seq0)
+        rs = buffers.row_stride(count)
+        got = outd.cpu().numpy().view(np.uint16).reshape(nops, nranks, nranks, rs)[..., :count]
+        for i in range(nops):
+            for c in range(nranks):
+                assert np.array_equal(got[i, c], want[i]), (i, c)
