@@ -112,6 +112,7 @@ def test_sim_chain_tiny_deadline_then_reset(proto):
     ws.sim_chain(nops, xd, stride, outd, stride, sd, timeout_ns=1)
     torch.cuda.synchronize()
     assert ws.status() in (0, abi.AR_ETIMEOUT), abi.status_string(ws.status())
+    print(f"  one-tick deadline: {abi.status_string(ws.status())}", flush=True)
     ws.reset_state()
     seq0 = ws.epoch.seq
     ws.sim_chain(nops, xd, stride, outd, stride, sd, timeout_ns=TIMEOUT_NS)

@@ -349,6 +349,7 @@ def test_sim_pairwise_tiny_deadline_then_reset(collective, nranks, count):
     ws.sim(nops, xd, stride, outd, ostride, timeout_ns=1)
     torch.cuda.synchronize()
     assert ws.status() in (0, abi.AR_ETIMEOUT), abi.status_string(ws.status())
+    print(f"  one-tick deadline: {abi.status_string(ws.status())}", flush=True)
     ws.reset_state()
     seq0 = ws.epoch.seq
     ws.sim(nops, xd, stride, outd, ostride, timeout_ns=TIMEOUT_NS)
