@@ -158,7 +158,9 @@ def fit_interp(points):
     measurements there (alpha = T(s_lo) - beta * s_lo, beta = (T(s_hi) -
     T(s_lo)) / (s_hi - s_lo); None where a protocol lacks either point).  The
     first range also covers sizes below the first measurement and the last
-    one, with no upper end, those above the last: the end lines extended.
+    one, with no upper end, those above the last: the end lines extended
+    (the last one drawn from the largest size at most 4/5 of the last, so
+    that a narrow interval does not set its slope).
     The table reproduces every measured time, so the in-sample regret is 1,
     and between two measured sizes it predicts by linear interpolation."""
     entries = []
@@ -171,6 +173,11 @@ def fit_interp(points):
                 continue
             for i in range(1, len(sizes)):
                 lo, hi = sizes[i - 1], sizes[i]
+                if i == len(sizes) - 1:
+                    # the line extended past the last size: through a size at
+                    # most 4/5 of it, not across a narrow interval between
+                    # two sides of a regime change
+                    lo = max([x for x in sizes[:-1] if x * 5 <= hi * 4], default=lo)
                 alpha, beta = [None] * 4, [None] * 4
                 for pi, proto in enumerate(PROTOS):
                     if (proto, lo) in meas and (proto, hi) in meas:
@@ -382,24 +389,88 @@ def measure_point(torch, abi, buffers, inputs, proto, nranks, nbytes, nops, reps
     return statistics.median(ms) * 1e3 / nops
 
 
+# a device address for geometry queries, which check alignment and read nothing
+_GEO_ADDR = 1 << 20
+
+
+def _nops_of(nbytes: int) -> int:
+    # launches long enough for the library's cooperative-launch choice (at
+    # least 32 ops), as in a decode step
+    return 64 if nbytes <= (256 << 10) else 32
+
+
+def geometry_key(abi, coll, n, proto, nbytes):
+    """Kernel, whether a wave or workgroup walks one tile or several, and
+    launch the simulator takes at this size (None where it cannot run):
+    where one of them changes, the per-op time can jump.  (The number of
+    tiles beyond the first grows with the size and adds time smoothly.)"""
+    count = nbytes // 2
+    rs = (count + 7) // 8 * 8
+    d = abi.make_desc(n, count, proto, n, coll)
+    p = abi.sim_params(d, _nops_of(nbytes), _GEO_ADDR, rs, _GEO_ADDR,
+                       n * rs if coll == "allgather" else rs, _GEO_ADDR, _GEO_ADDR,
+                       abi.ar_epoch_init())
+    try:
+        g = abi.ar_sim_geometry(p)
+    except abi.ArError:
+        return None
+    return (g["kernel"], g["tiles_per_wave"] > 1, g["launch"])
+
+
+def regime_sizes(abi, coll, n, proto, sizes, avoid=()):
+    """The sizes on both sides of every regime change (geometry_key) between
+    consecutive `sizes`, found by bisection on multiples of 16 bytes: the
+    last size of one regime and the first of the next.  Measuring there keeps
+    the interpolation from drawing a line across a jump."""
+    out = set()
+    for lo, hi in zip(sizes, sizes[1:]):
+        k_hi = geometry_key(abi, coll, n, proto, hi)
+        a, k_a = lo, geometry_key(abi, coll, n, proto, lo)
+        for _ in range(8):                         # a few changes at most
+            if k_a == k_hi or k_a is None or k_hi is None:
+                break
+            b = hi                                 # key(a) = k_a, key(b) != k_a
+            while b - a > 16:
+                mid = max(a + 16, (a + b) // 32 * 16)
+                if geometry_key(abi, coll, n, proto, mid) == k_a:
+                    a = mid
+                else:
+                    b = mid
+            out.update(x for x in (a, b) if x not in avoid)
+            a, k_a = b, geometry_key(abi, coll, n, proto, b)
+    return out
+
+
 def sweep(ranks=(4, 8, 16), sizes=SIZES, protos=PROTOS, reps=7, collectives=COLLECTIVES,
-          tag=""):
+          tag="", regimes=False):
+    """Per-op times of every protocol at every size; with `regimes`, also at
+    the sizes on both sides of each regime change of any protocol between
+    two of `sizes` (never one of HELDOUT_SIZES)."""
     import torch
     from . import abi, buffers, inputs
     torch.cuda.set_device(0)
     points = []
     for coll in collectives:
         for n in ranks:
-            for s in sizes:
+            grid = set(sizes)
+            if regimes:
+                for proto in protos:
+                    if coll != "allreduce" and proto == "barrier":
+                        continue
+                    top = [x for x in sorted(sizes)
+                           if not (coll == "allgather" and x > GATHER_MAX)]
+                    grid |= regime_sizes(abi, coll, n, proto, top, avoid=HELDOUT_SIZES)
+                print(tag + json.dumps({"collective": coll, "nranks": n,
+                                        "regime_sizes": sorted(grid - set(sizes))}),
+                      flush=True)
+            for s in sorted(grid):
                 if coll == "allgather" and s > GATHER_MAX:
                     continue
                 # system-mode receive buffers must stay below 4 GiB in total
                 E_max = 2 * s
                 if n * 2 * n * E_max >= (1 << 32):
                     continue
-                # launches long enough for the library's cooperative-launch
-                # choice (at least 32 ops), as in a decode step
-                nops = 64 if s <= (256 << 10) else 32
+                nops = _nops_of(s)
                 for proto in protos:
                     if coll != "allreduce" and proto == "barrier":
                         continue
@@ -428,6 +499,9 @@ def main() -> int:
     ap.add_argument("--reps", type=int, default=7)
     ap.add_argument("--refit", metavar="TABLE",
                     help="refit the points stored in an existing table instead of measuring")
+    ap.add_argument("--no-regimes", action="store_true",
+                    help="measure only the powers of two, not also the sizes on both "
+                         "sides of each kernel-regime change between them")
     ap.add_argument("--no-heldout", action="store_true",
                     help="skip the held-out sizes (measured between the fitted ones to "
                          "score the table out of sample)")
@@ -441,11 +515,12 @@ def main() -> int:
         heldout = old.get("heldout_points", [])
         measured_with = old["measured_with"]
     else:
-        points = sweep(ranks, reps=args.reps)
+        points = sweep(ranks, reps=args.reps, regimes=not args.no_regimes)
         heldout = [] if args.no_heldout else sweep(ranks, sizes=HELDOUT_SIZES,
                                                    reps=args.reps, tag="heldout ")
         measured_with = ("python -m collective_synchronization_amd.selector "
-                         f"--ranks {args.ranks} --reps {args.reps} (one MI355X, "
+                         f"--ranks {args.ranks} --reps {args.reps}"
+                         f"{' --no-regimes' if args.no_regimes else ''} (one MI355X, "
                          "system mode, persistent simulator, median per-op time)")
     entries = fit_table(points)
     reg = regret(points, entries)
