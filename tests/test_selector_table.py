@@ -268,3 +268,40 @@ def test_joint_split_never_worse_than_separate_splits():
         assert wj <= ws + 1e-12
         better += wj < ws - 1e-9
     assert better >= 1
+
+
+def test_regime_sizes_bisect_both_sides(monkeypatch):
+    """The sweep's extra sizes: both sides of each regime change between two
+    measured sizes (multiples of 16 bytes), none of the avoided sizes, and
+    no search past a size the simulator cannot run."""
+    def key(abi_, coll, n, proto, nbytes):
+        if nbytes > 100000:
+            return None
+        return (nbytes >= 5008, nbytes >= 40000)
+    monkeypatch.setattr(selector, "geometry_key", key)
+    sizes = [2048, 4096, 8192, 16384, 32768, 65536, 131072]
+    assert selector.regime_sizes(None, "allreduce", 8, "ll", sizes) == {4992, 5008, 39984,
+                                                                         40000}
+    got = selector.regime_sizes(None, "allreduce", 8, "ll", sizes, avoid={5008})
+    assert got == {4992, 39984, 40000}
+
+    def two(abi_, coll, n, proto, nbytes):             # two changes in one interval
+        return (nbytes >= 9000, nbytes >= 12000)
+    monkeypatch.setattr(selector, "geometry_key", two)
+    assert selector.regime_sizes(None, "allreduce", 8, "ll", [8192, 16384]) == {
+        8992, 9008, 11984, 12000}
+
+
+def test_last_range_extends_a_wide_interval():
+    """Past the last measured size the table extends the line from the
+    largest size at most 4/5 of it, not the line across a 16-byte interval."""
+    pts = [{"nranks": 8, "proto": "ll", "bytes": b, "us": u}
+           for b, u in ((1000, 1.0), (2000, 2.0), (2016, 10.0))]
+    pts += [{"nranks": 8, "proto": "sentinel", "bytes": b, "us": u}
+            for b, u in ((1000, 3.0), (2000, 3.5), (2016, 3.6))]
+    e = selector.fit_interp(pts)
+    last = [x for x in e if x["max_bytes"] == 0][0]
+    assert last["beta_us_per_byte"][0] == pytest.approx((10.0 - 1.0) / 1016)
+    assert last["alpha_us"][0] + last["beta_us_per_byte"][0] * 2016 == pytest.approx(10.0)
+    mid = [x for x in e if x["max_bytes"] == 2000][0]
+    assert mid["beta_us_per_byte"][0] == pytest.approx(1.0 / 1000)
