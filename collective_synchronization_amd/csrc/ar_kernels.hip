@@ -117,6 +117,10 @@ __global__ __launch_bounds__(kBlock) void k_fill_zero(uint32_t* p, uint32_t word
 
 // ------------------------------------------------------------- simulator --
 
+// The barrier baseline's counter of wave index wr sits at progress word
+// (wr % 128) * 32 + wr / 128, a permutation of the progress words.
+static_assert(kCtrlMaxProgress == 128 * 32, "counter layout covers the progress words");
+
 struct SimArgs {
   const uint16_t* in;
   int64_t in_stride;
@@ -134,7 +138,6 @@ struct SimArgs {
   const uint32_t* delay;
   const uint16_t* order;
   uint64_t* trace;
-  uint32_t p_total, c_total;
 };
 
 __device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
@@ -154,8 +157,9 @@ __device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
 //
 // A rank's own contribution never goes through memory: its consumer takes
 // the encoded chunk from registers and its producer skips its own buffer.
-// ONE: every wave owns at most one tile (the small-message case; not the
-// barrier baseline).  The op loop is then software-pipelined: the next op's
+// ONE: every wave owns at most one tile (the small-message case).  For the
+// barrier baseline only its read batch differs.  Otherwise the op loop is
+// then software-pipelined: the next op's
 // payload is loaded while this op is polled, and this op's output is stored
 // after the next op's stores are out, so neither input load nor output store
 // sits between one op's validation and the next op's transmission.
@@ -172,7 +176,13 @@ __device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
 template <int P, int NMAX, bool SHARE, bool EXTRAS, bool ONE>
 __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
   constexpr bool kFast = ONE && P != kBarrier;
-  constexpr int kReadBatch = NMAX <= 4 ? 4 : (NMAX <= 8 ? 2 : 1);
+  // The barrier baseline reads data known to be there (after its top
+  // barrier): where waves walk many tiles, 4 tiles a round up to 8 ranks (8
+  // ranks 4 MiB: 93.8 -> 90.4 us per op; at 16 ranks the registers of 4
+  // tiles cost more than they save, and with one tile a wave, 8 ranks 2-64
+  // KiB, 4.5 -> 5.6 us).
+  constexpr int kReadBatch =
+      (P == kBarrier && NMAX <= 8 && !ONE) ? 4 : (NMAX <= 4 ? 4 : (NMAX <= 8 ? 2 : 1));
   if constexpr (!EXTRAS) {
     a.delay = nullptr;
     a.order = nullptr;
@@ -200,8 +210,20 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
   const uint32_t N = (uint32_t)a.nranks;
   const uint32_t cstride = 2u * N * a.slot_bytes;
   uint32_t* const progress = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlProgress;
-  uint32_t* const arrive = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlArrive;
-  uint32_t* const done = reinterpret_cast<uint32_t*>(a.ctrl) + kCtrlDone;
+  // Barrier baseline: one counter per wave index.  Waves wr of the N ranks
+  // are the only producers of the tiles that waves wr of the consumers read
+  // (the same tiles in every rank), so the top and bottom barriers are kept
+  // among those waves: per op the counter takes N producer arrivals, then
+  // the nconsumers completions (each waits for all N arrivals first, and the
+  // next arrivals wait for all completions), so op i's arrivals are complete
+  // at i*K + N and its completions at (i+1)*K.  (The progress words are
+  // otherwise unused by this protocol; the control block is zero at launch.)
+  // Counters of neighbouring wave indices sit 128 bytes apart (a line each
+  // up to 128 indices): adjacent counters in one line made every group's
+  // atomics and polls contend (measured, 8 ranks: 8 KiB 9.4 -> 4.5 us per
+  // op, 4 MiB 121 -> 98 us).  wr < 4096, so the index stays below 4096.
+  uint32_t* const bar = progress + ((wr & 127) * 32 + (wr >> 7));
+  const uint32_t K = N + (uint32_t)a.nconsumers;
   const int tstride = 2 * a.nranks;
   const int64_t op_rows = a.nranks;
 
@@ -228,7 +250,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
     if (P == kBarrier) {
       if (op >= 1) {
         Waiter wt(a.timeout_ticks, a.ctrl);
-        if (!wait_geq(done, (uint32_t)op * a.c_total, wt, lane)) return;
+        if (!wait_geq(bar, (uint32_t)op * K, wt, lane)) return;
         fence_acquire();
       }
     } else if (SHARE && g != 0 && op >= 2) {
@@ -282,9 +304,9 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
           a.order ? a.order + ((int64_t)op * a.nranks + g) * a.TPW : nullptr;
       // the loads of up to TB tiles in flight together, then their stores (a
       // tile past the payload reads nothing and stores nothing).  Measured:
-      // 1-5% per op at 0.5-4 MiB for LL, LL128 and the sentinel; up to 8%
-      // slower for the barrier baseline, which keeps one tile at a time.
-      constexpr int TB = P == kBarrier ? 1 : 4;
+      // 1-5% per op at 0.5-4 MiB for LL, LL128 and the sentinel; 4-6% for the
+      // barrier baseline at 1-4 MiB (8 and 16 ranks).
+      constexpr int TB = 4;
       for (int j0 = 0; j0 < a.TPW; j0 += TB) {
         uint32_t wv[TB][4];
         int kk[TB];
@@ -312,8 +334,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
       if (P == kBarrier) {
         fence_release();
         if (lane == 0)
-          __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (a.trace) {
@@ -337,7 +358,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
       } else {
         if (P == kBarrier) {
           Waiter wt(a.timeout_ticks, a.ctrl);
-          if (!wait_geq(arrive, (uint32_t)(op + 1) * a.p_total, wt, lane)) return;
+          if (!wait_geq(bar, (uint32_t)op * K + N, wt, lane)) return;
           fence_acquire();
         }
         uint16_t* orow = a.out + ((int64_t)op * a.nconsumers + cself) * a.out_stride;
@@ -387,8 +408,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
         if (P == kBarrier) {
           fence_release();
           if (lane == 0)
-            __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       // SENTINEL: the re-arm stores of this op complete before any store of
@@ -980,8 +1000,7 @@ static hipError_t launch_reduce_n(const ReduceArgs& a, int blocks, hipStream_t s
 template <int P, int NMAX, bool SHARE, bool EXTRAS>
 static const void* sim_kernel(bool wide, bool one) {
   if (!wide) {
-    if constexpr (P != kBarrier)
-      if (one) return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS, true>);
+    if (one) return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS, true>);
     return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS, false>);
   }
   return one ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 1, EXTRAS>)
@@ -1121,9 +1140,7 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
   // (the variant launched is always the one whose occupancy sized the grid)
   int64_t Q = 0;
   bool one = false;
-  if (wide || d->proto != kBarrier) {
-    if (sim_plan(p, di, wide, coop, true, T, &Q) == AR_OK && T <= per_q * Q) one = true;
-  }
+  if (sim_plan(p, di, wide, coop, true, T, &Q) == AR_OK && T <= per_q * Q) one = true;
   if (!one) {
     const int rc = sim_plan(p, di, wide, coop, false, T, &Q);
     if (rc) return rc;
@@ -1473,10 +1490,10 @@ static int sim_launch(const ar_sim_params* p, const DeviceInfo& di, const SimGeo
   a.delay = p->delay_ticks;
   a.order = p->tile_order;
   a.trace = p->trace;
-  const uint32_t wt = (uint32_t)(g.T < g.W ? g.T : g.W);   // waves with tiles per rank
-  a.p_total = wt * (uint32_t)d->nranks;
-  a.c_total = wt * (uint32_t)d->nconsumers;
-  if ((uint64_t)a.p_total * (uint64_t)(p->nops + 1) >= 0xFFFFFFFFull) return AR_ESIZE;
+  // the barrier baseline's per-wave counter reaches (nranks + nconsumers) * nops
+  if ((uint64_t)(d->nranks + d->nconsumers) * (uint64_t)(p->nops + 1) >= 0xFFFFFFFFull)
+    return AR_ESIZE;
+  if (g.W > kCtrlMaxProgress) return AR_ECAPACITY;   // one counter / progress word a wave
   hipError_t e;
   switch (d->proto) {
     case kLL: e = dispatch_sim_p<kLL>(a, share, g.blocks, g.coop, g.wide, g.one, s); break;

@@ -176,7 +176,8 @@ int64_t ar_scratch_bytes(const ar_desc* d);
  * Control block, caller-owned device memory of ar_ctrl_bytes() bytes,
  * 256-byte aligned, zero-filled before first use and after any error:
  *   int32 word 0 = status (0 or a negative ar_status, first error wins),
- *   word 1 = abort flag, words 2.. = barrier counters of the simulator.
+ *   word 1 = abort flag, words 64.. = one word per simulator wave (rank 0's
+ *   progress in share mode, the barrier baseline's counter).
  */
 int64_t ar_ctrl_bytes(void);
 /* Zero the control block with a small fill kernel (safe inside graphs). */
@@ -350,8 +351,11 @@ int ar_scale_rows(int32_t nranks, int64_t count, const void* in, int64_t in_stri
  * Microseconds Matter in AI Infrastructure", "Latency can matter more than
  * bandwidth").  With nconsumers = 1 the producers of ranks 1..N-1 take that
  * license from rank 0's block of the previous op.  AR_BARRIER runs the plain
- * baseline instead: one buffer, a top barrier (arrival counter) and a bottom
- * barrier (completion counter) per op, both global.
+ * baseline instead: one buffer, a top barrier (all N producers arrived) and a
+ * bottom barrier (all consumers done) per op, kept by one counter for each
+ * wave index: the waves with index w in every rank exchange the same tiles,
+ * so each such group is its own barrier domain, as the blocks of a rank with
+ * the same index would be across GPUs.
  *
  * Every wave of the grid must be resident at once (waves wait on each
  * other).  A cooperative launch (hipLaunchCooperativeKernel) has the runtime

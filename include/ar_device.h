@@ -43,9 +43,9 @@ constexpr int kEcorrupt = -6;
 // Control block words.
 constexpr int kCtrlStatus = 0;
 constexpr int kCtrlAbort = 1;
-constexpr int kCtrlArrive = 16;     // barrier baseline: producer arrivals
-constexpr int kCtrlDone = 32;       // barrier baseline: consumer completions
-constexpr int kCtrlProgress = 64;   // share mode: rank-0 progress per wave
+// One word per wave index from kCtrlProgress on: rank 0's progress in share
+// mode, or the barrier baseline's arrival-and-completion counter.
+constexpr int kCtrlProgress = 64;
 constexpr int kCtrlMaxProgress = 4096;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
