@@ -241,7 +241,7 @@ def kernel_label(proto, nranks, geo, mode, collective):
     if collective == "twoshot":
         return ("k_sim_twoshot" if geo["kernel"] == "wide" else "k_sim_twoshot_narrow") + \
             f"<{pid},{nmax}>"
-    one = geo["tiles_per_wave"] <= 1
+    one = geo["tiles_per_wave"] <= 1 and (geo["kernel"] == "wide" or proto != "barrier")
     if geo["kernel"] == "wide":
         return f"k_sim_wide<{pid},{nmax},{mode},{1 if one else 2}>"
     return f"k_sim<{pid},{nmax},{mode},{'one' if one else 'many'}>"

@@ -157,9 +157,8 @@ __device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
 //
 // A rank's own contribution never goes through memory: its consumer takes
 // the encoded chunk from registers and its producer skips its own buffer.
-// ONE: every wave owns at most one tile (the small-message case).  For the
-// barrier baseline only its read batch differs.  Otherwise the op loop is
-// then software-pipelined: the next op's
+// ONE: every wave owns at most one tile (the small-message case; not the
+// barrier baseline).  The op loop is then software-pipelined: the next op's
 // payload is loaded while this op is polled, and this op's output is stored
 // after the next op's stores are out, so neither input load nor output store
 // sits between one op's validation and the next op's transmission.
@@ -176,13 +175,11 @@ __device__ __forceinline__ bool wait_geq(const uint32_t* p, uint32_t target,
 template <int P, int NMAX, bool SHARE, bool EXTRAS, bool ONE>
 __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
   constexpr bool kFast = ONE && P != kBarrier;
-  // The barrier baseline reads data known to be there (after its top
-  // barrier): where waves walk many tiles, 4 tiles a round up to 8 ranks (8
-  // ranks 4 MiB: 93.8 -> 90.4 us per op; at 16 ranks the registers of 4
-  // tiles cost more than they save, and with one tile a wave, 8 ranks 2-64
-  // KiB, 4.5 -> 5.6 us).
-  constexpr int kReadBatch =
-      (P == kBarrier && NMAX <= 8 && !ONE) ? 4 : (NMAX <= 4 ? 4 : (NMAX <= 8 ? 2 : 1));
+  // (Measured for the barrier baseline, not adopted: 4 tiles a round at 8
+  // ranks, 4 MiB 93.8 -> 90.4 us per op, but 202 vector registers instead of
+  // 123 halve the occupancy, so the launch turns cooperative, and one-tile
+  // sizes lose 4.5 -> 5.6 us.)
+  constexpr int kReadBatch = NMAX <= 4 ? 4 : (NMAX <= 8 ? 2 : 1);
   if constexpr (!EXTRAS) {
     a.delay = nullptr;
     a.order = nullptr;
@@ -1000,7 +997,8 @@ static hipError_t launch_reduce_n(const ReduceArgs& a, int blocks, hipStream_t s
 template <int P, int NMAX, bool SHARE, bool EXTRAS>
 static const void* sim_kernel(bool wide, bool one) {
   if (!wide) {
-    if (one) return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS, true>);
+    if constexpr (P != kBarrier)
+      if (one) return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS, true>);
     return reinterpret_cast<const void*>(&k_sim<P, NMAX, SHARE, EXTRAS, false>);
   }
   return one ? reinterpret_cast<const void*>(&k_sim_wide<P, NMAX, SHARE, 1, EXTRAS>)
@@ -1140,7 +1138,9 @@ static int sim_geometry_as(const ar_sim_params* p, const DeviceInfo& di, bool wi
   // (the variant launched is always the one whose occupancy sized the grid)
   int64_t Q = 0;
   bool one = false;
-  if (sim_plan(p, di, wide, coop, true, T, &Q) == AR_OK && T <= per_q * Q) one = true;
+  if (wide || d->proto != kBarrier) {
+    if (sim_plan(p, di, wide, coop, true, T, &Q) == AR_OK && T <= per_q * Q) one = true;
+  }
   if (!one) {
     const int rc = sim_plan(p, di, wide, coop, false, T, &Q);
     if (rc) return rc;
