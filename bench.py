@@ -1041,7 +1041,7 @@ def main() -> int:
         except RuntimeError as e:
             line["chain"] = {"error": str(e)}
 
-    if args.linear and args.mode == "system" and proto != "barrier":
+    if args.linear and args.mode == "system" and (args.proto == "auto" or proto != "barrier"):
         try:
             line["linear"] = measure_linear(torch, abi, buffers, inputs,
                                             "ll" if args.proto == "auto" else proto, nranks,
