@@ -50,6 +50,11 @@ SIZES = tuple(2 ** k for k in range(11, 23))          # 2 KiB .. 4 MiB per rank
 HELDOUT_SIZES = (3 << 10, 12 << 10, 48 << 10, 96 << 10, 192 << 10, 384 << 10, 768 << 10,
                  3 << 19, 3 << 20)
 GATHER_MAX = 1 << 20                                  # all-gather sweep: up to 1 MiB
+# from 64 KiB on, per-op times bend between the powers of two without a
+# change of kernel, tile class or launch (the working set of an op outgrows
+# a cache level): the fit also measures 5/4 and 7/4 of each power there
+QUARTER_SIZES = tuple(m * 2 ** k // 4 for k in range(16, 22) for m in (5, 7))
+FIT_SIZES = tuple(sorted(SIZES + QUARTER_SIZES))
 
 
 def _coll(p) -> str:
@@ -441,7 +446,7 @@ def regime_sizes(abi, coll, n, proto, sizes, avoid=()):
     return out
 
 
-def sweep(ranks=(4, 8, 16), sizes=SIZES, protos=PROTOS, reps=7, collectives=COLLECTIVES,
+def sweep(ranks=(4, 8, 16), sizes=FIT_SIZES, protos=PROTOS, reps=7, collectives=COLLECTIVES,
           tag="", regimes=False):
     """Per-op times of every protocol at every size; with `regimes`, also at
     the sizes on both sides of each regime change of any protocol between

@@ -305,3 +305,15 @@ def test_last_range_extends_a_wide_interval():
     assert last["alpha_us"][0] + last["beta_us_per_byte"][0] * 2016 == pytest.approx(10.0)
     mid = [x for x in e if x["max_bytes"] == 2000][0]
     assert mid["beta_us_per_byte"][0] == pytest.approx(1.0 / 1000)
+
+
+def test_fit_sizes_keep_the_heldout_sizes_out():
+    """The fit measures the powers of two and, from 64 KiB on, 5/4 and 7/4 of
+    each; none of them is a held-out size, and all are 16-byte multiples
+    (whole encoded chunks for every protocol's row alignment)."""
+    assert set(selector.SIZES) <= set(selector.FIT_SIZES)
+    assert not set(selector.FIT_SIZES) & set(selector.HELDOUT_SIZES)
+    assert list(selector.FIT_SIZES) == sorted(set(selector.FIT_SIZES))
+    assert all(s % 16 == 0 for s in selector.FIT_SIZES)
+    q = [s for s in selector.FIT_SIZES if s not in selector.SIZES]
+    assert min(q) == 80 << 10 and max(q) == 3584 << 10 and len(q) == 12
