@@ -301,9 +301,11 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
           a.order ? a.order + ((int64_t)op * a.nranks + g) * a.TPW : nullptr;
       // the loads of up to TB tiles in flight together, then their stores (a
       // tile past the payload reads nothing and stores nothing).  Measured:
-      // 1-5% per op at 0.5-4 MiB for LL, LL128 and the sentinel; 4-6% for the
-      // barrier baseline at 1-4 MiB (8 and 16 ranks).
-      constexpr int TB = 4;
+      // 1-5% per op at 0.5-4 MiB for LL, LL128 and the sentinel; for the
+      // barrier baseline, whose wave sends all its tiles between two
+      // barriers, 4 tiles 4-6% and 8 tiles another 2-6% at 1-4 MiB (16 tiles
+      // take more than 128 vector registers, which halves the occupancy).
+      constexpr int TB = P == kBarrier ? 8 : 4;
       for (int j0 = 0; j0 < a.TPW; j0 += TB) {
         uint32_t wv[TB][4];
         int kk[TB];
@@ -368,8 +370,11 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
         // -> 197.9 (32 tiles), 2 MiB 88.6 -> 88.3 (16), 16 ranks 1 MiB 200.7
         // -> 200.0 (16), 512 KiB 84.5 -> 86.4 (8); at 8 ranks 1 MiB (a
         // quarter of the cache) the send order is 1-1.5% faster.
+        // (Not the barrier baseline, which reads only after the whole group's
+        // sends: send order, 8 ranks 4 MiB 91.7 -> 91.0 us, 16 ranks 1 MiB
+        // 90.6 -> 88.9.)
         const bool newest_first =
-            a.TPW >= (P == kLL ? 16 : 8) &&
+            P != kBarrier && a.TPW >= (P == kLL ? 16 : 8) &&
             (uint64_t)a.nconsumers * (uint64_t)a.nranks * a.E >= (uint64_t(128) << 20);
         // LL128: one flag per producer wave orders all of its data of the op
         if (P == kLL128 &&
