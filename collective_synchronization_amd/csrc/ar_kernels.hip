@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kSimBlock) void k_sim(SimArgs a) {
   constexpr bool kFast = ONE && P != kBarrier;
   // (Measured for the barrier baseline, not adopted: 4 tiles a round at 8
   // ranks, 4 MiB 93.8 -> 90.4 us per op, but 202 vector registers instead of
-  // 123 halve the occupancy, so the launch turns cooperative, and one-tile
+  // 109 halve the occupancy, so the launch turns cooperative, and one-tile
   // sizes lose 4.5 -> 5.6 us.)
   constexpr int kReadBatch = NMAX <= 4 ? 4 : (NMAX <= 8 ? 2 : 1);
   if constexpr (!EXTRAS) {
